@@ -1,0 +1,439 @@
+"""Plain CPU oracle for co-activation statistics, deduplicated dispatch,
+permute, combine and token-shuffle prediction.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the engine.  It shares no code with the
+HIP engine.  Everything is written for clarity, not speed: Python loops over
+tokens, exact integers, float64 for real arithmetic unless a step fixes a
+narrower type.
+
+Sources (cited by page title and section):
+  [EC]  "Expert Coupling in MoE Pretraining: Reducing All-to-All Overhead with
+        Correlated Placement and Token Shuffling" -- abstract: co-selection of
+        experts within a layer, cross-layer predictability, a dispatcher that
+        sends each token to each GPU once, token shuffling toward the GPU
+        predicted to hold the token's next-layer experts.
+  [CB]  "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
+        Training" -- Key Observation (Ochiai similarity over the token sets of
+        two experts; node-level deduplication) and Problem Formulation (the
+        cross-node volume V with D_t, s_t, N(r), r_t^e).
+  [EP]  "Expert Parallelism > Expert Placement Strategies" -- uniform
+        contiguous placement, device = expert // experts_per_device.
+  [CE]  "Training Communication-Efficient Mixture-of-Experts Language Models
+        with Layer Re-Configuration" -- footnote 3: routed probabilities are
+        dispatched alongside hidden states and the hidden states are combined.
+
+Readings where the pages leave a step open are listed beside each function.
+Every function here is pinned by tests in ``tests/test_oracle_pins.py``.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+
+class OracleInputError(ValueError):
+    """A precondition of the method is violated by the inputs."""
+
+
+# --------------------------------------------------------------- validation
+
+def validate_routing(topk: np.ndarray, E: int) -> None:
+    """Each token selects k distinct experts out of E ([CB] Problem
+    Formulation: D_t is a *set* of selected experts)."""
+    topk = np.asarray(topk)
+    if topk.ndim != 2:
+        raise OracleInputError("topk must be [T, k]")
+    for t in range(topk.shape[0]):
+        row = [int(e) for e in topk[t]]
+        for e in row:
+            if e < 0 or e >= E:
+                raise OracleInputError(f"token {t}: expert id {e} not in [0, {E})")
+        if len(set(row)) != len(row):
+            raise OracleInputError(f"token {t}: expert listed twice")
+
+
+def validate_placement(expert_rank: np.ndarray, E: int, G: int) -> None:
+    """One replica per expert: expert e lives on rank p(e) in [0, G)."""
+    expert_rank = np.asarray(expert_rank)
+    if expert_rank.shape != (E,):
+        raise OracleInputError("expert_rank must have E entries")
+    for e in range(E):
+        if not 0 <= int(expert_rank[e]) < G:
+            raise OracleInputError(f"expert {e}: rank {int(expert_rank[e])} not in [0, {G})")
+
+
+def source_offsets(T: int, G: int, src_offsets=None) -> list:
+    """Token ranges per source rank.
+
+    Reading: sequence parallelism shards the tokens across the EP group
+    ([EC] abstract), taken as contiguous shards in token order.  With no
+    explicit offsets the shards are equal, s_t = t div (T/G).
+    """
+    if src_offsets is None:
+        if T % G != 0:
+            raise OracleInputError("equal shards need T divisible by G")
+        return [s * (T // G) for s in range(G + 1)]
+    off = [int(v) for v in src_offsets]
+    if len(off) != G + 1 or off[0] != 0 or off[-1] != T:
+        raise OracleInputError("src_offsets must run from 0 to T over G+1 entries")
+    for s in range(G):
+        if off[s + 1] < off[s]:
+            raise OracleInputError("src_offsets must be nondecreasing")
+    return off
+
+
+def source_rank_of_tokens(T: int, G: int, src_offsets=None) -> np.ndarray:
+    """s_t of [CB] Problem Formulation: the rank that holds token t."""
+    off = source_offsets(T, G, src_offsets)
+    s_of = np.empty(T, dtype=np.int64)
+    for s in range(G):
+        for t in range(off[s], off[s + 1]):
+            s_of[t] = s
+    return s_of
+
+
+# ------------------------------------------------------- co-activation stats
+
+def ochiai(pair_count: np.ndarray, expert_count: np.ndarray) -> np.ndarray:
+    """Ochiai(A, B) = |A n B| / sqrt(|A| |B|) over the token sets of two
+    experts ([CB] Key Observation).
+
+    Computed in float64 (the product |A||B| as a double, a correctly rounded
+    square root and quotient) and rounded once to float32.  Reading: 0 where
+    either set is empty (the formula is 0/0 there); the diagonal follows the
+    formula, so it is 1 for every expert that some token selected.
+    """
+    E = len(expert_count)
+    out = np.zeros((E, E), dtype=np.float32)
+    for i in range(E):
+        for j in range(E):
+            d = float(expert_count[i]) * float(expert_count[j])
+            if d > 0.0:
+                out[i, j] = np.float32(float(pair_count[i, j]) / math.sqrt(d))
+    return out
+
+
+def coact_stats(topk: np.ndarray, E: int, topk_next: Optional[np.ndarray] = None,
+                E_next: Optional[int] = None) -> dict:
+    """Per-expert counts, E x E co-selection counts, Ochiai similarity and
+    layer-to-layer transition counts.
+
+    * expert_count[e] = |A_e| with A_e = {t : e in D_t}  ([CB] Key Observation:
+      the set of active tokens of each expert).
+    * pair_count[i][j] = |A_i n A_j|: the number of tokens that select both i
+      and j ([EC] abstract: expert pairs selected together).  Full symmetric
+      matrix, diagonal = expert_count.
+    * ochiai as above.
+    * transition[i][j] = #{t : i in D_t at this layer, j in D'_t at the next}
+      ([EC] abstract: the experts a token selects at one layer predict those it
+      selects at the next).  Rows index this layer, columns the next.
+    """
+    topk = np.asarray(topk)
+    validate_routing(topk, E)
+    T = topk.shape[0]
+    n = np.zeros(E, dtype=np.int64)
+    C = np.zeros((E, E), dtype=np.int64)
+    for t in range(T):
+        D = [int(e) for e in topk[t]]
+        for i in D:
+            n[i] += 1
+            for j in D:
+                C[i, j] += 1
+    out = {"expert_count": n, "pair_count": C, "ochiai": ochiai(C, n)}
+    if topk_next is not None:
+        topk_next = np.asarray(topk_next)
+        validate_routing(topk_next, E_next)
+        if topk_next.shape[0] != T:
+            raise OracleInputError("both layers must cover the same tokens")
+        X = np.zeros((E, E_next), dtype=np.int64)
+        for t in range(T):
+            for i in topk[t]:
+                for j in topk_next[t]:
+                    X[int(i), int(j)] += 1
+        out["transition"] = X
+    return out
+
+
+# ----------------------------------------------------------- dispatch plan
+
+def dispatch_plan(topk: np.ndarray, gates: Optional[np.ndarray], expert_rank: np.ndarray,
+                  G: int, ranks_per_node: int, src_offsets=None) -> dict:
+    """Deduplicated dispatch plan: every token goes to every rank that holds
+    at least one of its experts exactly once ([EC] abstract, the dispatcher
+    that sends each token to each GPU once).
+
+    With one replica per expert the rank of task (t, e) is forced,
+    r_t^e = p(e) ([CB] Problem Formulation).  R_t = {p(e) : e in D_t} is the
+    token's set of destination ranks; one send row per (t, r in R_t).
+
+    Reading (the pages give no buffer layout): rows are ordered by
+    (source rank s_t, destination rank r, token t), so each (s, r) block is
+    one all-to-all message and is contiguous per source.
+
+    row_weight(t, r) is the token's gate mass on rank r, a float32 running sum
+    over ascending slot j starting from 0 (reading: the routed probabilities
+    travel with the hidden rows, [CE] footnote 3, and the combine applies
+    them).
+
+    Counters: N (rows), T*k (assignments), local_rows (#(t, r) with r = s_t),
+    local_assign (#(t, j) with p(D_t[j]) = s_t), node_rows = sum_t |N_t| with
+    N_t = {node(r) : r in R_t}, V = sum_t |N_t minus {node(s_t)}| (the
+    cross-node volume of [CB] Problem Formulation), max rows received by one
+    rank, and a reserved 0.  node(r) = r div ranks_per_node.
+    """
+    topk = np.asarray(topk)
+    expert_rank = np.asarray(expert_rank)
+    T, k = topk.shape
+    E = expert_rank.shape[0]
+    validate_routing(topk, E)
+    validate_placement(expert_rank, E, G)
+    if G % ranks_per_node != 0:
+        raise OracleInputError("ranks_per_node must divide G")
+    s_of = source_rank_of_tokens(T, G, src_offsets)
+
+    def p(e):
+        return int(expert_rank[int(e)])
+
+    rows = []
+    for t in range(T):
+        for r in sorted({p(e) for e in topk[t]}):
+            rows.append((int(s_of[t]), r, t))
+    rows.sort()
+    index = {}
+    for i, (s, r, t) in enumerate(rows):
+        index[(t, r)] = i
+    N = len(rows)
+
+    S = np.zeros((G, G), dtype=np.int64)
+    for (s, r, t) in rows:
+        S[s, r] += 1
+    send_offsets = np.zeros(G * G + 1, dtype=np.int64)
+    flat = S.reshape(-1)
+    for q in range(G * G):
+        send_offsets[q + 1] = send_offsets[q] + flat[q]
+
+    row_token = np.array([t for (s, r, t) in rows], dtype=np.int64)
+    row_weight = np.zeros(N, dtype=np.float32)
+    if gates is not None:
+        gates = np.asarray(gates, dtype=np.float32)
+        for i, (s, r, t) in enumerate(rows):
+            a = np.float32(0.0)
+            for j in range(k):
+                if p(topk[t, j]) == r:
+                    a = np.float32(a + gates[t, j])
+            row_weight[i] = a
+
+    token_rows = np.full((T, k), -1, dtype=np.int64)
+    slot_row = np.empty((T, k), dtype=np.int64)
+    for t in range(T):
+        for q, r in enumerate(sorted({p(e) for e in topk[t]})):
+            token_rows[t, q] = index[(t, r)]
+        for j in range(k):
+            slot_row[t, j] = index[(t, p(topk[t, j]))]
+
+    local_rows = sum(1 for (s, r, t) in rows if r == s)
+    local_assign = 0
+    node_rows = 0
+    V = 0
+    for t in range(T):
+        s = int(s_of[t])
+        local_assign += sum(1 for e in topk[t] if p(e) == s)
+        nodes = {p(e) // ranks_per_node for e in topk[t]}
+        node_rows += len(nodes)
+        V += len(nodes - {s // ranks_per_node})
+    max_recv = int(S.sum(axis=0).max()) if G > 0 else 0
+    counters = np.array([N, T * k, local_rows, local_assign, node_rows, V, max_recv, 0],
+                        dtype=np.int64)
+    return {"send_counts": S, "send_offsets": send_offsets, "row_token": row_token,
+            "row_weight": row_weight, "token_rows": token_rows, "slot_row": slot_row,
+            "counters": counters, "N": N}
+
+
+# ---------------------------------------------------------------- permute
+
+def permute_rows(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
+    """Send buffer: row i is a bit copy of x[row_token[i]] (the dispatched
+    hidden state of [CE] footnote 3).  Works on any dtype, bf16 included as
+    uint16 bit patterns."""
+    return np.asarray(x)[np.asarray(row_token, dtype=np.int64)]
+
+
+def scatter_rows(x: np.ndarray, dest: np.ndarray, out_rows: int) -> np.ndarray:
+    """out[dest[t]] = x[t] for every t with dest[t] >= 0 (a one-row-per-token
+    move, e.g. the token shuffle); untouched rows stay zero."""
+    x = np.asarray(x)
+    out = np.zeros((out_rows,) + x.shape[1:], dtype=x.dtype)
+    for t in range(x.shape[0]):
+        if int(dest[t]) >= 0:
+            out[int(dest[t])] = x[t]
+    return out
+
+
+# ---------------------------------------------------------------- bf16
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """A bf16 value is the upper half of the float32 with the same bits."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (8 significant bits), nearest, ties to an
+    even last bit; result as uint16 bit patterns.
+
+    Written from the definition: the two bf16 neighbours of x are the value
+    with the low 16 bits cleared (toward zero) and the next one away from
+    zero; the nearer one wins, a tie goes to the one whose last kept bit is 0.
+    Magnitudes at or past the midpoint between the largest finite bf16 and
+    2^128 become infinity.  NaN stays NaN (quiet), infinities stay.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    lo = bits >> 16                                   # neighbour toward zero
+    mag_lo = ((lo & 0x7FFF) << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    exp_field = ((lo >> 7) & 0xFF).astype(np.int64)
+    # spacing of bf16 values in lo's binade (subnormals share binade 1)
+    ulp = np.ldexp(1.0, np.maximum(exp_field, 1) - 127 - 7)
+    mag_hi = mag_lo + ulp                             # 2^128 past the largest finite
+    a = np.abs(x.astype(np.float64))
+    with np.errstate(invalid="ignore"):           # inf/NaN lanes are replaced below
+        d_lo = a - mag_lo
+        d_hi = mag_hi - a
+    take_lo = (d_lo < d_hi) | ((d_lo == d_hi) & ((lo & 1) == 0))
+    # lo + 1 is the next magnitude; a carry into the exponent is exact,
+    # and 0x7F7F + 1 = 0x7F80 is infinity.
+    out = np.where(take_lo, lo, lo + 1)
+    out = np.where(np.isinf(x), lo, out)
+    out = np.where(np.isnan(x), lo | 0x0040, out)     # quiet NaN, payload kept
+    return (out & 0xFFFF).astype(np.uint16)
+
+
+def _as_f64(z: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_to_f32(z).astype(np.float64)
+    return np.asarray(z, dtype=np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- combine
+
+def combine(Z: np.ndarray, z_dtype: str, slot_row: np.ndarray, gates: np.ndarray,
+            out_dtype: str) -> np.ndarray:
+    """Weighted combine back to token order: y_t = sum_j w_tj * Z[row of
+    (t, p(D_t[j]))] (the hidden-state combine of [CE] footnote 3; with the
+    deduplicated dispatch of [EC] every assignment of t on rank r reads the
+    single row (t, r)).
+
+    Sum in float64, rounded once to float32; a bf16 output is the bf16
+    rounding of that float32 value.  ``Z`` holds the expert-side rows, indexed
+    by ``slot_row`` [T, k].
+    """
+    slot_row = np.asarray(slot_row, dtype=np.int64)
+    gates = np.asarray(gates, dtype=np.float32)
+    T, k = slot_row.shape
+    Zf = _as_f64(Z, z_dtype)
+    y = np.zeros((T, Zf.shape[1]), dtype=np.float64)
+    for j in range(k):
+        y += gates[:, j].astype(np.float64)[:, None] * Zf[slot_row[:, j]]
+    y32 = y.astype(np.float32)
+    return bf16_round(y32) if out_dtype == "bf16" else y32
+
+
+def combine_unweighted(Z: np.ndarray, z_dtype: str, token_rows: np.ndarray,
+                       out_dtype: str) -> np.ndarray:
+    """y_t = sum over the token's rows (one per rank in R_t) of Z[row]: the
+    combine for an expert side that already applied the gates."""
+    token_rows = np.asarray(token_rows, dtype=np.int64)
+    T, k = token_rows.shape
+    Zf = _as_f64(Z, z_dtype)
+    y = np.zeros((T, Zf.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for q in range(k):
+            if token_rows[t, q] >= 0:
+                y[t] += Zf[token_rows[t, q]]
+    y32 = y.astype(np.float32)
+    return bf16_round(y32) if out_dtype == "bf16" else y32
+
+
+# ---------------------------------------------------------- token shuffle
+
+def shuffle_predict(topk: np.ndarray, transition: np.ndarray, expert_rank_next: np.ndarray,
+                    G: int) -> dict:
+    """Predict the rank holding each token's next-layer experts and order the
+    tokens by it ([EC] abstract: token shuffling moves each token to the GPU
+    predicted to hold its next-layer experts).
+
+    Readings: the prediction scores rank r by the transition counts from the
+    token's current experts into the next-layer experts placed on r,
+    score_t[r] = sum_{i in D_t} sum_{j : p'(j) = r} X[i][j], raw integer
+    counts; pred_t = the highest-scoring rank, lowest rank on ties (an
+    all-zero score gives rank 0); no capacity limit, so shard sizes vary.
+    The new order is stable: tokens keep ascending t within a rank.
+    """
+    topk = np.asarray(topk)
+    X = np.asarray(transition, dtype=np.int64)
+    E, E_next = X.shape
+    validate_routing(topk, E)
+    validate_placement(expert_rank_next, E_next, G)
+    T = topk.shape[0]
+    M = np.zeros((E, G), dtype=np.int64)
+    for i in range(E):
+        for j in range(E_next):
+            M[i, int(expert_rank_next[j])] += X[i, j]
+    pred = np.empty(T, dtype=np.int64)
+    for t in range(T):
+        score = np.zeros(G, dtype=np.int64)
+        for i in topk[t]:
+            score += M[int(i)]
+        best = 0
+        for r in range(1, G):
+            if score[r] > score[best]:
+                best = r
+        pred[t] = best
+    # stable counting sort by predicted rank
+    counts = np.zeros(G, dtype=np.int64)
+    for t in range(T):
+        counts[pred[t]] += 1
+    shard_offsets = np.zeros(G + 1, dtype=np.int64)
+    for r in range(G):
+        shard_offsets[r + 1] = shard_offsets[r] + counts[r]
+    fill = shard_offsets[:G].copy()
+    dest_pos = np.empty(T, dtype=np.int64)
+    perm = np.empty(T, dtype=np.int64)
+    for t in range(T):
+        dest_pos[t] = fill[pred[t]]
+        perm[fill[pred[t]]] = t
+        fill[pred[t]] += 1
+    return {"pred_rank": pred, "dest_pos": dest_pos, "perm": perm,
+            "shard_offsets": shard_offsets, "rank_score": M}
+
+
+def two_layer_pipeline(topk1: np.ndarray, topk2: np.ndarray, gates2: np.ndarray,
+                       x: np.ndarray, expert_rank2: np.ndarray, E: int, E2: int,
+                       G: int, ranks_per_node: int) -> dict:
+    """Two consecutive MoE layers with token shuffling ([EC] abstract):
+    statistics of layer 1 with the layer-1 -> layer-2 transitions, prediction
+    of each token's layer-2 rank, the shuffle (tokens and their layer-2
+    routing move together), then the layer-2 deduplicated plan with the new
+    shards as source ranks, and the layer-2 permute.
+
+    Reading: the transition counts come from the same batch (in-sample).
+    """
+    T = topk1.shape[0]
+    stats = coact_stats(topk1, E, topk2, E2)
+    sh = shuffle_predict(topk1, stats["transition"], expert_rank2, G)
+    perm = sh["perm"]
+    x_s = np.asarray(x)[perm]
+    topk2_s = np.asarray(topk2)[perm]
+    gates2_s = np.asarray(gates2)[perm]
+    plan_before = dispatch_plan(topk2, gates2, expert_rank2, G, ranks_per_node)
+    plan = dispatch_plan(topk2_s, gates2_s, expert_rank2, G, ranks_per_node,
+                         src_offsets=sh["shard_offsets"])
+    send = permute_rows(x_s, plan["row_token"])
+    k2 = topk2.shape[1]
+    return {"stats": stats, "shuffle": sh, "x_shuffled": x_s, "topk2_shuffled": topk2_s,
+            "gates2_shuffled": gates2_s, "plan": plan, "send": send,
+            "local_share_before": plan_before["counters"][3] / (T * k2),
+            "local_share_after": plan["counters"][3] / (T * k2)}
