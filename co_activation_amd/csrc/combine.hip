@@ -1,0 +1,176 @@
+// Weighted combine back to token order: the hidden-state combine of
+// "Training Communication-Efficient Mixture-of-Experts Language Models with
+// Layer Re-Configuration" (footnote 3) over the rows of the deduplicated
+// dispatch of "Expert Coupling in MoE Pretraining ..." (abstract).
+//
+//   y[t] = sum_q a(row_q) * z[row_q],  q over the token's rows in order,
+//
+// fp32 fused multiply-adds in ascending q, one rounding to the output type
+// (bf16: round to nearest even).  One wave per token; the token's row list and
+// weights are wave-uniform (scalar registers); each lane owns groups of 8
+// (or 4 for fp32 -> fp32) consecutive elements, 16-byte loads and stores.
+// HBM-bound: algorithmic bytes per token are rows * (z row bytes + 4) +
+// y row bytes + 4 * k.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCombThreads = 256;
+constexpr int kCombWaves = kCombThreads / kWave;
+constexpr int kCombUnroll = 2;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// EPL elements of one row starting at element group g.
+template <bool ZBF16, int EPL>
+__device__ __forceinline__ void load_group(const u32x4* __restrict__ row, int64_t g, float (&f)[EPL]) {
+  if constexpr (ZBF16) {
+    static_assert(EPL == 8, "bf16 groups are 8 elements");
+    const u32x4 v = __builtin_nontemporal_load(row + g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(v[i]);
+      f[2 * i + 1] = bf16_hi(v[i]);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < EPL / 4; ++h) {
+      const u32x4 v = __builtin_nontemporal_load(row + g * (EPL / 4) + h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[4 * h + i] = __uint_as_float(v[i]);
+    }
+  }
+}
+
+template <bool YBF16, int EPL>
+__device__ __forceinline__ void store_group(u32x4* __restrict__ row, int64_t g, const float (&f)[EPL]) {
+  if constexpr (YBF16) {
+    static_assert(EPL == 8, "bf16 groups are 8 elements");
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = to_bf16(f[2 * i]) | (to_bf16(f[2 * i + 1]) << 16);
+    __builtin_nontemporal_store(v, row + g);
+  } else {
+#pragma unroll
+    for (int h = 0; h < EPL / 4; ++h) {
+      u32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[4 * h + i]);
+      __builtin_nontemporal_store(v, row + g * (EPL / 4) + h);
+    }
+  }
+}
+
+template <bool ZBF16, bool YBF16, int EPL>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(
+    const u32x4* __restrict__ z, int64_t z_rows, int64_t groups, const int32_t* __restrict__ rows,
+    int k, const float* __restrict__ weight, int T, u32x4* __restrict__ y, int32_t* d_err) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * kCombWaves + wave_id();
+  if (t >= T) return;
+
+  // 16-byte vectors per row of z and of y.
+  const int64_t zvec = groups * (ZBF16 ? EPL / 8 : EPL / 4);
+  const int64_t yvec = groups * (YBF16 ? EPL / 8 : EPL / 4);
+
+  int rid[MOE_MAX_K];
+  float a[MOE_MAX_K];
+  int errbits = 0;
+#pragma unroll
+  for (int q = 0; q < MOE_MAX_K; ++q) {
+    rid[q] = -1;
+    a[q] = 0.f;
+    if (q < k) {
+      const int r = __builtin_amdgcn_readfirstlane(rows[static_cast<int64_t>(t) * k + q]);
+      if (r >= 0 && r < z_rows) {
+        rid[q] = r;
+        if (weight != nullptr)
+          a[q] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(weight[r])));
+        else
+          a[q] = 1.f;
+      } else if (r >= z_rows) {
+        errbits = MOE_DERR_ROW_RANGE;
+      }
+    }
+  }
+  if (lane == 0) report(d_err, errbits);
+
+  u32x4* yrow = y + static_cast<int64_t>(t) * yvec;
+  for (int64_t g0 = lane; g0 < groups; g0 += kWave * kCombUnroll) {
+    float acc[kCombUnroll][EPL];
+#pragma unroll
+    for (int u = 0; u < kCombUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) acc[u][i] = 0.f;
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_K; ++q) {
+      if (q >= k) break;
+      if (rid[q] < 0) continue;
+      const u32x4* zrow = z + static_cast<int64_t>(rid[q]) * zvec;
+      float f[kCombUnroll][EPL];
+#pragma unroll
+      for (int u = 0; u < kCombUnroll; ++u) {
+        const int64_t g = g0 + u * kWave;
+        if (g < groups) load_group<ZBF16, EPL>(zrow, g, f[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kCombUnroll; ++u)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[u][i] = __builtin_fmaf(a[q], f[u][i], acc[u][i]);
+    }
+#pragma unroll
+    for (int u = 0; u < kCombUnroll; ++u) {
+      const int64_t g = g0 + u * kWave;
+      if (g < groups) store_group<YBF16, EPL>(yrow, g, acc[u]);
+    }
+  }
+}
+
+template <bool ZBF16, bool YBF16, int EPL>
+int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k, const float* w,
+           int64_t T, void* y, int32_t* d_err, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((T + kCombWaves - 1) / kCombWaves);
+  combine_kernel<ZBF16, YBF16, EPL><<<blocks, kCombThreads, 0, s>>>(
+      static_cast<const u32x4*>(z), z_rows, H / EPL, rows, k, w, static_cast<int>(T),
+      static_cast<u32x4*>(y), d_err);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_combine(const void* z, int z_dtype, int64_t z_rows, int64_t H,
+                           const int32_t* rows, int k, const float* row_weight, int64_t T,
+                           void* y, int y_dtype, int32_t* d_err, void* stream) {
+  if ((z_dtype != MOE_F32 && z_dtype != MOE_BF16) || (y_dtype != MOE_F32 && y_dtype != MOE_BF16))
+    return MOE_ERR_DTYPE;
+  if (T < 0 || H <= 0 || z_rows < 0 || k < 1 || k > MOE_MAX_K ||
+      T * static_cast<int64_t>(k) >= (int64_t{1} << 31))
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (z == nullptr || rows == nullptr || y == nullptr) return MOE_ERR_NULL;
+  const int zb = z_dtype == MOE_BF16 ? 2 : 4, yb = y_dtype == MOE_BF16 ? 2 : 4;
+  if ((H * zb) % 16 != 0 || (H * yb) % 16 != 0 || reinterpret_cast<uintptr_t>(z) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(y) % 16 != 0)
+    return MOE_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (z_dtype == MOE_BF16 && y_dtype == MOE_BF16)
+    return moe::launch<true, true, 8>(z, z_rows, H, rows, k, row_weight, T, y, d_err, s);
+  if (z_dtype == MOE_BF16 && y_dtype == MOE_F32)
+    return moe::launch<true, false, 8>(z, z_rows, H, rows, k, row_weight, T, y, d_err, s);
+  if (z_dtype == MOE_F32 && y_dtype == MOE_BF16)
+    return moe::launch<false, true, 8>(z, z_rows, H, rows, k, row_weight, T, y, d_err, s);
+  return moe::launch<false, false, 4>(z, z_rows, H, rows, k, row_weight, T, y, d_err, s);
+}

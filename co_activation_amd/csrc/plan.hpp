@@ -1,0 +1,43 @@
+// Internal launcher of the dispatch-plan kernels, shared by the plan entry
+// point and by the token shuffle (which is a plan with one source rank,
+// one "expert" per token and the identity placement: a stable counting sort).
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kPlanTile = 256;  // tokens per tile = threads per block
+
+// Upper bound of the number of token tiles: sum_s ceil(len_s / tile).
+inline int64_t plan_max_tiles(int64_t T, int G) { return (T + kPlanTile - 1) / kPlanTile + G; }
+
+inline size_t plan_workspace_bytes(int64_t T, int G) {
+  const int64_t nt = plan_max_tiles(T, G);
+  size_t b = static_cast<size_t>(nt) * (G + 4) * sizeof(int32_t);
+  return (b + 255) & ~static_cast<size_t>(255);
+}
+
+struct PlanArgs {
+  const int32_t* topk;
+  const float* gates;
+  int T, k, E;
+  const int32_t* expert_rank;
+  int G, ranks_per_node;
+  const int32_t* src_offsets;
+  int64_t row_capacity;
+  int32_t* send_counts;
+  int32_t* send_offsets;
+  int32_t* row_token;
+  float* row_weight;
+  int32_t* token_rows;
+  int32_t* slot_row;
+  int64_t* counters;
+  int32_t* d_err;
+  void* ws;
+};
+
+// Enqueues the three plan kernels; arguments already validated.
+int launch_plan(const PlanArgs& a, hipStream_t stream);
+
+}  // namespace moe

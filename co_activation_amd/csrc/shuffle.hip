@@ -1,0 +1,175 @@
+// Token shuffle prediction.
+//
+// "Expert Coupling in MoE Pretraining ..." (abstract): token shuffling moves
+// each token to the GPU predicted to hold its next-layer experts; the experts
+// a token picks at one layer predict those it picks at the next.
+//
+//   M[i][r]     = sum_{j : p'(j) = r} X[i][j]       (64-bit, one block per i)
+//   score_t[r]  = sum_{i in D_t} M[i][r],  pred_t = argmax_r, lowest r on ties
+//
+// The new token order is a stable counting sort by pred.  That sort is the
+// dispatch plan with one source rank, one "expert" per token (its predicted
+// rank) and the identity placement, so it reuses the plan kernels: the plan's
+// row of token t is its new position and row_token is the inverse
+// permutation.
+#include "plan.hpp"
+
+namespace moe {
+namespace {
+
+inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+struct ShuffleWs {
+  int64_t* M;
+  int32_t* identity;
+  int32_t* src1;
+  int32_t* send_counts;
+  int32_t* send_offsets;
+  int64_t* counters;
+  int32_t* perm_scratch;
+  void* plan_ws;
+  size_t bytes;
+};
+
+ShuffleWs shuffle_layout(void* base, int64_t T, int E, int G) {
+  ShuffleWs w{};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + off : nullptr;
+    off += align256(bytes);
+    return q;
+  };
+  w.M = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * E * G));
+  w.identity = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * G));
+  w.src1 = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (G + 1)));
+  w.send_counts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * G * G));
+  w.send_offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (G * G + 1)));
+  w.counters = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * 8));
+  w.perm_scratch = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (T > 0 ? T : 1)));
+  w.plan_ws = take(plan_workspace_bytes(T, G));
+  w.bytes = off;
+  return w;
+}
+
+// One block per expert i of this layer; lane r sums X[i][j] over the
+// next-layer experts j placed on rank r.  Block 0 also writes the identity
+// placement and the one-source offsets [0, T, ..., T] used by the sort.
+__global__ __launch_bounds__(kWave) void rank_score_kernel(
+    const int32_t* __restrict__ X, int E_next, const int32_t* __restrict__ expert_rank_next, int G,
+    int T, int64_t* __restrict__ M, int32_t* __restrict__ identity, int32_t* __restrict__ src1,
+    int32_t* d_err) {
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x;
+  long long acc = 0;
+  int bad = 0;
+  for (int j = 0; j < E_next; ++j) {
+    const int r = expert_rank_next[j];
+    if (r < 0 || r >= G) {
+      bad = 1;
+      continue;
+    }
+    if (r == lane) acc += X[static_cast<int64_t>(i) * E_next + j];
+  }
+  if (lane < G) M[static_cast<int64_t>(i) * G + lane] = acc;
+  if (i == 0) {
+    if (lane == 0 && bad) report(d_err, MOE_DERR_RANK_RANGE);
+    if (lane < G) {
+      identity[lane] = lane;
+      src1[lane] = lane == 0 ? 0 : T;
+    }
+    if (lane == 0) src1[G] = T;
+  }
+}
+
+constexpr int kPredThreads = 256;
+
+__global__ __launch_bounds__(kPredThreads) void predict_kernel(
+    const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
+    int32_t* __restrict__ pred_rank, int32_t* d_err) {
+  const int t = blockIdx.x * kPredThreads + threadIdx.x;
+  if (t >= T) return;
+  int e[MOE_MAX_K];
+  int errbits = 0;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_K; ++j) {
+    e[j] = -1;
+    if (j < k) {
+      const int v = topk[static_cast<int64_t>(t) * k + j];
+      if (v >= 0 && v < E)
+        e[j] = v;
+      else
+        errbits |= MOE_DERR_EXPERT_RANGE;
+    }
+  }
+  long long best = 0;
+  int best_r = 0;
+  for (int r = 0; r < G; ++r) {
+    long long sc = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j)
+      if (e[j] >= 0) sc += M[static_cast<int64_t>(e[j]) * G + r];
+    if (r == 0 || sc > best) {
+      best = sc;
+      best_r = r;
+    }
+  }
+  pred_rank[t] = best_r;
+  report(d_err, errbits);
+}
+
+__global__ void copy_offsets_kernel(const int32_t* __restrict__ send_offsets, int G,
+                                    int32_t* __restrict__ shard_offsets) {
+  const int r = threadIdx.x;
+  if (r <= G) shard_offsets[r] = send_offsets[r];
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_shuffle_predict_workspace_size(int64_t T, int E, int G, size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return MOE_ERR_NULL;
+  if (T < 0 || E < 1 || E > MOE_MAX_E || G < 1 || G > MOE_MAX_G) return MOE_ERR_SHAPE;
+  *ws_bytes = moe::shuffle_layout(nullptr, T, E, G).bytes;
+  return MOE_OK;
+}
+
+extern "C" int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E,
+                                   const int32_t* transition, int E_next,
+                                   const int32_t* expert_rank_next, int G, int32_t* pred_rank,
+                                   int32_t* dest_pos, int32_t* perm, int32_t* shard_offsets,
+                                   int32_t* d_err, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_K || E < 1 || E > MOE_MAX_E || E_next < 1 ||
+      E_next > MOE_MAX_E || G < 1 || G > MOE_MAX_G ||
+      T * static_cast<int64_t>(k) >= (int64_t{1} << 31))
+    return MOE_ERR_SHAPE;
+  if (transition == nullptr || expert_rank_next == nullptr || shard_offsets == nullptr ||
+      ws == nullptr)
+    return MOE_ERR_NULL;
+  if (T > 0 && (topk == nullptr || pred_rank == nullptr || dest_pos == nullptr))
+    return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return MOE_ERR_ALIGN;
+  const moe::ShuffleWs w = moe::shuffle_layout(ws, T, E, G);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int Ti = static_cast<int>(T);
+
+  moe::rank_score_kernel<<<E, moe::kWave, 0, s>>>(transition, E_next, expert_rank_next, G, Ti,
+                                                  w.M, w.identity, w.src1, d_err);
+  MOE_CHECK_LAUNCH();
+  if (Ti > 0) {
+    moe::predict_kernel<<<(Ti + moe::kPredThreads - 1) / moe::kPredThreads, moe::kPredThreads, 0,
+                          s>>>(topk, Ti, k, E, w.M, G, pred_rank, d_err);
+    MOE_CHECK_LAUNCH();
+  }
+  moe::PlanArgs a{pred_rank,      nullptr,        Ti,        1,
+                  G,              w.identity,     G,         G,
+                  w.src1,         T,              w.send_counts, w.send_offsets,
+                  perm ? perm : w.perm_scratch,   nullptr,   dest_pos,
+                  nullptr,        w.counters,     d_err,     w.plan_ws};
+  int st = moe::launch_plan(a, s);
+  if (st != MOE_OK) return st;
+  moe::copy_offsets_kernel<<<1, moe::kWave * 2, 0, s>>>(w.send_offsets, G, shard_offsets);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

@@ -1,0 +1,236 @@
+"""torch-facing wrappers of the C ABI (argument marshalling only).
+
+Every function takes device tensors, checks dtype / contiguity / device /
+shape, passes raw pointers and ``torch.cuda.current_stream()`` to the
+library, and returns the output tensors.  All compute happens in the HIP
+kernels; outputs may be preallocated through ``out=`` to keep allocations out
+of a timed loop.  Device-side data errors are OR-ed into ``d_err`` (an int32
+tensor of one element); ``raise_on_errors`` reads it back.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, check
+
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _want(t: torch.Tensor, name: str, dtype=None, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _alloc(out: Optional[dict], key: str, shape, dtype, device) -> torch.Tensor:
+    if out is not None and out.get(key) is not None:
+        return _want(out[key], key, dtype, shape)
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def new_error_word(device="cuda") -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def decode_errors(bits: int) -> list:
+    return [name for b, name in _lib.DERR_BITS.items() if bits & b]
+
+
+def raise_on_errors(d_err: torch.Tensor) -> None:
+    bits = int(d_err.item())
+    if bits:
+        raise RuntimeError(f"device data errors: {decode_errors(bits)}")
+
+
+# ----------------------------------------------------------------- stats
+
+def coact_stats(topk: torch.Tensor, E: int, topk_next: Optional[torch.Tensor] = None,
+                E_next: Optional[int] = None, *, pairs: bool = True, ochiai: bool = True,
+                out: Optional[dict] = None, d_err: Optional[torch.Tensor] = None) -> dict:
+    """moe_coact_stats: expert_count [E], pair_count [E,E], ochiai [E,E],
+    transition [E,E_next] (when topk_next is given)."""
+    _want(topk, "topk", torch.int32)
+    T, k = topk.shape
+    dev = topk.device
+    res = {"expert_count": _alloc(out, "expert_count", (E,), torch.int32, dev)}
+    if pairs:
+        res["pair_count"] = _alloc(out, "pair_count", (E, E), torch.int32, dev)
+        if ochiai:
+            res["ochiai"] = _alloc(out, "ochiai", (E, E), torch.float32, dev)
+    k2 = 0
+    if topk_next is not None:
+        _want(topk_next, "topk_next", torch.int32)
+        if topk_next.shape[0] != T:
+            raise ValueError("topk_next must cover the same tokens")
+        k2 = topk_next.shape[1]
+        res["transition"] = _alloc(out, "transition", (E, E_next), torch.int32, dev)
+    st = _lib.lib().moe_coact_stats(
+        _p(topk), T, k, E, _p(topk_next), k2, E_next or 0, _p(res["expert_count"]),
+        _p(res.get("pair_count")), _p(res.get("ochiai")), _p(res.get("transition")), _p(d_err),
+        _stream())
+    check("moe_coact_stats", st)
+    return res
+
+
+# ----------------------------------------------------------------- plan
+
+class Plan(NamedTuple):
+    send_counts: torch.Tensor   # [G, G] int32
+    send_offsets: torch.Tensor  # [G*G+1] int32
+    row_token: torch.Tensor     # [row_capacity] int32
+    row_weight: Optional[torch.Tensor]  # [row_capacity] float32
+    token_rows: torch.Tensor    # [T, k] int32
+    slot_row: Optional[torch.Tensor]    # [T, k] int32
+    counters: torch.Tensor      # [8] int64
+
+
+def plan_workspace_bytes(T: int, G: int) -> int:
+    n = ctypes.c_size_t()
+    check("moe_dispatch_plan_workspace_size",
+          _lib.lib().moe_dispatch_plan_workspace_size(T, G, ctypes.byref(n)))
+    return n.value
+
+
+def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank: torch.Tensor,
+                  G: int, ranks_per_node: int, src_offsets: Optional[torch.Tensor] = None, *,
+                  row_capacity: Optional[int] = None, with_weights: bool = True,
+                  with_slot_row: bool = True, out: Optional[dict] = None,
+                  ws: Optional[torch.Tensor] = None,
+                  d_err: Optional[torch.Tensor] = None) -> Plan:
+    """moe_dispatch_plan.  row_capacity defaults to T * min(k, G)."""
+    _want(topk, "topk", torch.int32)
+    T, k = topk.shape
+    E = expert_rank.numel()
+    _want(expert_rank, "expert_rank", torch.int32, (E,))
+    if gates is not None:
+        _want(gates, "gates", torch.float32, (T, k))
+    if src_offsets is not None:
+        _want(src_offsets, "src_offsets", torch.int32, (G + 1,))
+    cap = T * min(k, G) if row_capacity is None else int(row_capacity)
+    dev = topk.device
+    sc = _alloc(out, "send_counts", (G, G), torch.int32, dev)
+    so = _alloc(out, "send_offsets", (G * G + 1,), torch.int32, dev)
+    rt = _alloc(out, "row_token", (cap,), torch.int32, dev)
+    rw = _alloc(out, "row_weight", (cap,), torch.float32, dev) if with_weights else None
+    tr = _alloc(out, "token_rows", (T, k), torch.int32, dev)
+    sr = _alloc(out, "slot_row", (T, k), torch.int32, dev) if with_slot_row else None
+    cn = _alloc(out, "counters", (8,), torch.int64, dev)
+    need = plan_workspace_bytes(T, G)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _want(ws, "ws", torch.uint8)
+    st = _lib.lib().moe_dispatch_plan(
+        _p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node, _p(src_offsets), cap,
+        _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(d_err), _p(ws), ws.numel(),
+        _stream())
+    check("moe_dispatch_plan", st)
+    return Plan(sc, so, rt, rw, tr, sr, cn)
+
+
+# ----------------------------------------------------------------- permute
+
+def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
+            out: Optional[torch.Tensor] = None, d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_permute: out[dest[t, q]] = x[t] (bit copy).  dest is [T, width] or
+    [T] int32; out has out_rows rows shaped like x's rows."""
+    _want(x, "x")
+    _want(dest, "dest", torch.int32)
+    T = x.shape[0]
+    width = 1 if dest.dim() == 1 else dest.shape[1]
+    if dest.shape[0] != T:
+        raise ValueError("dest must have one row per token")
+    row_shape = tuple(x.shape[1:])
+    row_bytes = x.element_size() * (x[0].numel() if T > 0 else int(torch.tensor(row_shape).prod()))
+    if out is None:
+        out = torch.empty((out_rows,) + row_shape, dtype=x.dtype, device=x.device)
+    _want(out, "out", x.dtype)
+    if tuple(out.shape[1:]) != row_shape or out.shape[0] < out_rows:
+        raise ValueError("out rows must match x rows")
+    st = _lib.lib().moe_permute(_p(x), T, row_bytes, _p(dest), width, _p(out), out_rows, _p(d_err),
+                                _stream())
+    check("moe_permute", st)
+    return out
+
+
+# ----------------------------------------------------------------- combine
+
+def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tensor] = None, *,
+            out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+            d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_combine: y[t] = sum_q a(rows[t,q]) z[rows[t,q]], a = row_weight or 1."""
+    _want(z, "z")
+    if z.dtype not in _DT:
+        raise TypeError("z must be float32 or bfloat16")
+    _want(rows, "rows", torch.int32)
+    T, k = rows.shape
+    H = z.shape[1]
+    if row_weight is not None:
+        _want(row_weight, "row_weight", torch.float32)
+    out_dtype = out_dtype or z.dtype
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=z.device)
+    _want(out, "out", out_dtype, (T, H))
+    st = _lib.lib().moe_combine(_p(z), _DT[z.dtype], z.shape[0], H, _p(rows), k, _p(row_weight),
+                                T, _p(out), _DT[out_dtype], _p(d_err), _stream())
+    check("moe_combine", st)
+    return out
+
+
+# ----------------------------------------------------------------- shuffle
+
+def shuffle_workspace_bytes(T: int, E: int, G: int) -> int:
+    n = ctypes.c_size_t()
+    check("moe_shuffle_predict_workspace_size",
+          _lib.lib().moe_shuffle_predict_workspace_size(T, E, G, ctypes.byref(n)))
+    return n.value
+
+
+def shuffle_predict(topk: torch.Tensor, transition: torch.Tensor, expert_rank_next: torch.Tensor,
+                    G: int, *, with_perm: bool = True, out: Optional[dict] = None,
+                    ws: Optional[torch.Tensor] = None,
+                    d_err: Optional[torch.Tensor] = None) -> dict:
+    """moe_shuffle_predict: pred_rank [T], dest_pos [T], perm [T],
+    shard_offsets [G+1]."""
+    _want(topk, "topk", torch.int32)
+    T, k = topk.shape
+    E, E2 = transition.shape
+    _want(transition, "transition", torch.int32)
+    _want(expert_rank_next, "expert_rank_next", torch.int32, (E2,))
+    dev = topk.device
+    res = {
+        "pred_rank": _alloc(out, "pred_rank", (T,), torch.int32, dev),
+        "dest_pos": _alloc(out, "dest_pos", (T,), torch.int32, dev),
+        "perm": _alloc(out, "perm", (T,), torch.int32, dev) if with_perm else None,
+        "shard_offsets": _alloc(out, "shard_offsets", (G + 1,), torch.int32, dev),
+    }
+    need = shuffle_workspace_bytes(T, E, G)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _want(ws, "ws", torch.uint8)
+    st = _lib.lib().moe_shuffle_predict(
+        _p(topk), T, k, E, _p(transition), E2, _p(expert_rank_next), G, _p(res["pred_rank"]),
+        _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(d_err), _p(ws),
+        ws.numel(), _stream())
+    check("moe_shuffle_predict", st)
+    return res

@@ -1,0 +1,163 @@
+"""One step of the dispatch path, as a sequence of C-ABI calls on one stream.
+
+Single layer (workloads 1-4):
+    stats(topk) -> plan(topk, gates, placement) -> permute(x) -> combine(z)
+Two layers with token shuffling (workload 5, "Expert Coupling in MoE
+Pretraining ..." abstract: shuffle each token to the rank predicted to hold
+its next-layer experts):
+    stats(topk1, topk2) -> shuffle_predict(topk1, transition, placement2)
+    -> permute x, topk2, gates2 to the new order (one row per token)
+    -> plan(topk2', gates2', placement2, src_offsets = shard_offsets)
+    -> permute(x') -> combine(z)
+
+All buffers are allocated once in the constructor; ``run`` only enqueues
+kernels (no allocation, no host synchronisation).  ``z`` stands for the
+expert side's returned rows (one per send row).
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import ops
+
+
+def _timed(timers, name):
+    """Context that records start/end events around a call on the current
+    stream when ``timers`` (dict name -> list of event pairs) is given."""
+
+    class _Ctx:
+        def __enter__(self):
+            if timers is not None:
+                self.a = torch.cuda.Event(enable_timing=True)
+                self.b = torch.cuda.Event(enable_timing=True)
+                self.a.record()
+
+        def __exit__(self, *exc):
+            if timers is not None:
+                self.b.record()
+                timers.setdefault(name, []).append((self.a, self.b))
+
+    return _Ctx()
+
+
+class LayerStep:
+    """Stats + plan + permute + combine of one MoE layer."""
+
+    def __init__(self, topk, gates, expert_rank, x, z, G, ranks_per_node, *,
+                 out_dtype=None, src_offsets=None):
+        dev = topk.device
+        self.T, self.k = topk.shape
+        self.E = expert_rank.numel()
+        self.G, self.Rn = G, ranks_per_node
+        self.topk, self.gates, self.expert_rank = topk, gates, expert_rank
+        self.x, self.z = x, z
+        self.src_offsets = src_offsets
+        self.cap = self.T * min(self.k, G)
+        self.out_dtype = out_dtype or x.dtype
+        self.d_err = ops.new_error_word(dev)
+        E = self.E
+        self.stats_out = {
+            "expert_count": torch.empty(E, dtype=torch.int32, device=dev),
+            "pair_count": torch.empty(E, E, dtype=torch.int32, device=dev),
+            "ochiai": torch.empty(E, E, dtype=torch.float32, device=dev),
+        }
+        self.plan_out = self._plan_buffers(self.T, self.k, G, self.cap, dev)
+        self.plan_ws = torch.empty(ops.plan_workspace_bytes(self.T, G), dtype=torch.uint8, device=dev)
+        self.send = torch.empty((self.cap,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+        self.y = torch.empty((self.T, x.shape[1]), dtype=self.out_dtype, device=dev)
+        self.plan = None
+
+    @staticmethod
+    def _plan_buffers(T, k, G, cap, dev):
+        return {
+            "send_counts": torch.empty(G, G, dtype=torch.int32, device=dev),
+            "send_offsets": torch.empty(G * G + 1, dtype=torch.int32, device=dev),
+            "row_token": torch.empty(cap, dtype=torch.int32, device=dev),
+            "row_weight": torch.empty(cap, dtype=torch.float32, device=dev),
+            "token_rows": torch.empty(T, k, dtype=torch.int32, device=dev),
+            "slot_row": torch.empty(T, k, dtype=torch.int32, device=dev),
+            "counters": torch.empty(8, dtype=torch.int64, device=dev),
+        }
+
+    def run(self, timers: Optional[dict] = None):
+        with _timed(timers, "stats"):
+            ops.coact_stats(self.topk, self.E, out=self.stats_out, d_err=self.d_err)
+        with _timed(timers, "plan"):
+            self.plan = ops.dispatch_plan(self.topk, self.gates, self.expert_rank, self.G, self.Rn,
+                                          self.src_offsets, out=self.plan_out, ws=self.plan_ws,
+                                          d_err=self.d_err)
+        with _timed(timers, "permute"):
+            ops.permute(self.x, self.plan.token_rows, self.cap, out=self.send, d_err=self.d_err)
+        with _timed(timers, "combine"):
+            ops.combine(self.z, self.plan.token_rows, self.plan.row_weight,
+                        out_dtype=self.out_dtype, out=self.y, d_err=self.d_err)
+        return self
+
+
+class TwoLayerStep:
+    """Layer-1 statistics with transitions, shuffle prediction, the shuffle,
+    and the layer-2 deduplicated dispatch and combine."""
+
+    def __init__(self, topk1, topk2, gates2, expert_rank2, x, z, G, ranks_per_node, E1=None):
+        dev = topk1.device
+        self.T, self.k1 = topk1.shape
+        self.k2 = topk2.shape[1]
+        self.E1 = E1 if E1 is not None else expert_rank2.numel()
+        self.E2 = expert_rank2.numel()
+        self.G, self.Rn = G, ranks_per_node
+        self.topk1, self.topk2, self.gates2, self.expert_rank2 = topk1, topk2, gates2, expert_rank2
+        self.x, self.z = x, z
+        self.d_err = ops.new_error_word(dev)
+        E1, E2, T = self.E1, self.E2, self.T
+        self.stats_out = {
+            "expert_count": torch.empty(E1, dtype=torch.int32, device=dev),
+            "pair_count": torch.empty(E1, E1, dtype=torch.int32, device=dev),
+            "ochiai": torch.empty(E1, E1, dtype=torch.float32, device=dev),
+            "transition": torch.empty(E1, E2, dtype=torch.int32, device=dev),
+        }
+        self.shuffle_out = {
+            "pred_rank": torch.empty(T, dtype=torch.int32, device=dev),
+            "dest_pos": torch.empty(T, dtype=torch.int32, device=dev),
+            "perm": torch.empty(T, dtype=torch.int32, device=dev),
+            "shard_offsets": torch.empty(G + 1, dtype=torch.int32, device=dev),
+        }
+        self.shuffle_ws = torch.empty(ops.shuffle_workspace_bytes(T, E1, G), dtype=torch.uint8,
+                                      device=dev)
+        self.x_s = torch.empty_like(x)
+        self.topk2_s = torch.empty_like(topk2)
+        self.gates2_s = torch.empty_like(gates2)
+        self.cap = T * min(self.k2, G)
+        self.plan_out = LayerStep._plan_buffers(T, self.k2, G, self.cap, dev)
+        self.plan_ws = torch.empty(ops.plan_workspace_bytes(T, G), dtype=torch.uint8, device=dev)
+        self.send = torch.empty((self.cap,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+        self.y = torch.empty((T, x.shape[1]), dtype=x.dtype, device=dev)
+        self.plan = None
+        self.shuffle = None
+
+    def run(self, timers: Optional[dict] = None):
+        with _timed(timers, "stats"):
+            stats = ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
+                                    d_err=self.d_err)
+        with _timed(timers, "shuffle_predict"):
+            self.shuffle = ops.shuffle_predict(self.topk1, stats["transition"], self.expert_rank2,
+                                               self.G, out=self.shuffle_out, ws=self.shuffle_ws,
+                                               d_err=self.d_err)
+        dest = self.shuffle["dest_pos"]
+        with _timed(timers, "shuffle_permute"):
+            ops.permute(self.x, dest, self.T, out=self.x_s, d_err=self.d_err)
+        with _timed(timers, "shuffle_routing"):
+            ops.permute(self.topk2, dest, self.T, out=self.topk2_s, d_err=self.d_err)
+            ops.permute(self.gates2, dest, self.T, out=self.gates2_s, d_err=self.d_err)
+        with _timed(timers, "plan"):
+            self.plan = ops.dispatch_plan(self.topk2_s, self.gates2_s, self.expert_rank2, self.G,
+                                          self.Rn, self.shuffle["shard_offsets"],
+                                          out=self.plan_out, ws=self.plan_ws, d_err=self.d_err)
+        with _timed(timers, "permute"):
+            ops.permute(self.x_s, self.plan.token_rows, self.cap, out=self.send, d_err=self.d_err)
+        with _timed(timers, "combine"):
+            ops.combine(self.z, self.plan.token_rows, self.plan.row_weight, out=self.y,
+                        d_err=self.d_err)
+        return self

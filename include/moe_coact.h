@@ -1,0 +1,227 @@
+/*
+ * moe_coact.h -- C ABI of the co-activation-aware MoE token dispatch engine
+ * (HIP, gfx950).
+ *
+ * The engine takes top-k router output of one MoE layer and
+ *   1. counts expert co-activation (per-expert counts, E x E pair counts,
+ *      Ochiai similarity, next-layer transition counts),
+ *   2. builds a deduplicated dispatch plan for a given expert -> rank
+ *      placement (one send row per token and destination rank),
+ *   3. permutes token rows into rank-contiguous send buffers,
+ *   4. combines the returned rows back to token order with the gate weights,
+ *   5. predicts each token's next-layer rank and orders tokens by it (token
+ *      shuffling).
+ * The ranks of the expert-parallel group are logical: each (source rank,
+ * destination rank) block of the send buffer stands for one all-to-all
+ * message.
+ *
+ * Sources (page title, section):
+ *   [EC] "Expert Coupling in MoE Pretraining: Reducing All-to-All Overhead
+ *        with Correlated Placement and Token Shuffling", abstract.
+ *   [CB] "Cobalt: Leveraging Expert Co-activation for Efficient Distributed
+ *        MoE Training", Key Observation and Problem Formulation.
+ *   [CE] "Training Communication-Efficient Mixture-of-Experts Language Models
+ *        with Layer Re-Configuration", footnote 3 (hidden-state dispatch,
+ *        routed-probability dispatch, hidden-state combine).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  Every buffer is
+ *     owned by the caller; the library allocates nothing and keeps no state
+ *     between calls, so calls on different streams may run concurrently as
+ *     long as their buffers differ.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it and the call returns without synchronising.
+ *   - The return value is a moe_status.  A negative status means the
+ *     arguments were rejected on the host and NOTHING was enqueued.
+ *   - Errors that depend on device data set bits (MOE_DERR_*) in *d_err with
+ *     an atomic OR.  d_err is an int32 device word that the caller zeroes;
+ *     it may be NULL (then such errors go unreported).  When a bit is set the
+ *     outputs are unspecified, except as stated per bit, but no kernel reads
+ *     or writes outside the buffers described here.
+ *   - Index arrays are int32; T*k must stay below 2^31.
+ */
+#ifndef MOE_COACT_H
+#define MOE_COACT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,      /* a required pointer is NULL                      */
+  MOE_ERR_SHAPE = -2,     /* a size is out of range (limits below)           */
+  MOE_ERR_DTYPE = -3,     /* unknown dtype code                              */
+  MOE_ERR_ALIGN = -4,     /* row size or pointer alignment not supported     */
+  MOE_ERR_WORKSPACE = -5, /* workspace smaller than the size query returns   */
+  MOE_ERR_HIP = -6        /* a kernel launch failed                          */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Device-side error bits OR-ed into *d_err. */
+#define MOE_DERR_EXPERT_RANGE 1  /* a top-k id is outside [0, E): that slot is skipped   */
+#define MOE_DERR_EXPERT_DUP 2    /* a token lists one expert twice                       */
+#define MOE_DERR_RANK_RANGE 4    /* a placement entry is outside [0, G): slot skipped    */
+#define MOE_DERR_CAPACITY 8      /* plan: more rows than row_capacity (counters stay
+                                    valid; rows >= capacity are not written)             */
+#define MOE_DERR_SRC_OFFSETS 16  /* src_offsets not nondecreasing from 0 to T            */
+#define MOE_DERR_ROW_RANGE 32    /* permute/combine: a row index >= the buffer's rows    */
+
+/* Limits checked on the host. */
+#define MOE_MAX_K 8      /* experts per token           */
+#define MOE_MAX_E 256    /* experts per layer           */
+#define MOE_MAX_G 64     /* logical ranks in the group  */
+
+/* Human-readable name of a status code (static string, host). */
+const char* moe_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * moe_coact_stats -- co-activation statistics of one layer.
+ *
+ * [CB] Key Observation: the set of tokens that activate each expert, and the
+ * Ochiai similarity |A n B| / sqrt(|A| |B|) of two experts' token sets.
+ * [EC] abstract: expert pairs selected together within a layer, and the
+ * experts a token picks at one layer predicting those it picks at the next.
+ *
+ *   topk          [T*k]   int32, row-major [T][k]: the experts D_t of token t
+ *   topk_next     [T*k_next] int32 or NULL: the same tokens' experts at the
+ *                         next layer (E_next experts); needed for transition
+ *   expert_count  [E]     int32 out: |A_e|, tokens that selected e
+ *   pair_count    [E*E]   int32 out or NULL: C[i*E+j] = |A_i n A_j|, full
+ *                         symmetric, diagonal = expert_count
+ *   ochiai        [E*E]   float out or NULL (needs pair_count):
+ *                         C[i][j] / sqrt(n_i * n_j) evaluated in double and
+ *                         rounded once to float; 0 where n_i * n_j == 0
+ *   transition    [E*E_next] int32 out or NULL (needs topk_next):
+ *                         X[i*E_next+j] = #{t : i in D_t, j in D'_t}
+ * Limits: 1 <= k, k_next <= 8; 1 <= E, E_next <= 256; T >= 0.
+ * d_err bits: EXPERT_RANGE (slot skipped), EXPERT_DUP.
+ * Integer outputs are exact and independent of scheduling.
+ * ---------------------------------------------------------------------- */
+int moe_coact_stats(const int32_t* topk, int64_t T, int k, int E,
+                    const int32_t* topk_next, int k_next, int E_next,
+                    int32_t* expert_count, int32_t* pair_count, float* ochiai,
+                    int32_t* transition, int32_t* d_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_dispatch_plan -- deduplicated dispatch plan.
+ *
+ * [EC] abstract: a dispatcher that sends each token to each GPU once.
+ * [CB] Problem Formulation: tokens t with selected experts D_t, source rank
+ * s_t, node N(r) of rank r, cross-node volume
+ * V = sum_t |{N(r_t^e) : e in D_t} minus {N(s_t)}|; with one replica per
+ * expert, r_t^e = expert_rank[e].
+ *
+ * R_t = {expert_rank[e] : e in D_t}.  One send row per (t, r in R_t).  Rows
+ * are ordered by (source rank s, destination rank r, token t ascending), so
+ * block (s, r) = rows [send_offsets[s*G+r], send_offsets[s*G+r+1]) is the
+ * message from s to r.  Source ranks hold contiguous token ranges:
+ * s_t = the s with src_offsets[s] <= t < src_offsets[s+1].
+ *
+ *   topk          [T*k] int32: experts of each token
+ *   gates         [T*k] float or NULL: gate weight of each slot
+ *   expert_rank   [E]   int32: the placement p(e)
+ *   G             logical ranks (1..64); ranks_per_node divides G;
+ *                 node(r) = r / ranks_per_node
+ *   src_offsets   [G+1] int32 or NULL (NULL = equal shards, T % G == 0)
+ *   row_capacity  rows available in row_token / row_weight;
+ *                 T * min(k, G) always suffices
+ *   send_counts   [G*G]   int32 out: S[s*G+r]
+ *   send_offsets  [G*G+1] int32 out: exclusive prefix of S; last = N
+ *   row_token     [row_capacity] int32 out: token of each row
+ *   row_weight    [row_capacity] float out or NULL: the token's gate mass on
+ *                 the row's rank, a float running sum over ascending slot j
+ *                 (0 if gates is NULL)
+ *   token_rows    [T*k] int32 out: rows of token t by ascending rank, then -1
+ *   slot_row      [T*k] int32 out or NULL: row carrying slot (t, j)
+ *   counters      [8] int64 out: N, T*k, local_rows (r == s_t),
+ *                 local_assign (slots with p(e) == s_t), node_rows
+ *                 (sum_t distinct destination nodes), V, max rows received
+ *                 by one rank, 0
+ *   ws, ws_bytes  workspace of at least moe_dispatch_plan_workspace_size()
+ *                 bytes, 16-byte aligned
+ * d_err bits: EXPERT_RANGE, EXPERT_DUP, RANK_RANGE, CAPACITY, SRC_OFFSETS.
+ * ---------------------------------------------------------------------- */
+int moe_dispatch_plan_workspace_size(int64_t T, int G, size_t* ws_bytes /* host */);
+int moe_dispatch_plan(const int32_t* topk, const float* gates, int64_t T, int k, int E,
+                      const int32_t* expert_rank, int G, int ranks_per_node,
+                      const int32_t* src_offsets, int64_t row_capacity,
+                      int32_t* send_counts, int32_t* send_offsets, int32_t* row_token,
+                      float* row_weight, int32_t* token_rows, int32_t* slot_row,
+                      int64_t* counters, int32_t* d_err, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute -- row scatter into send buffers (the dispatched hidden
+ * states of [CE] footnote 3; also the token shuffle of [EC] abstract).
+ *
+ *   out[dest[t*width + q]] = x[t]   for t < T, q < width, dest >= 0
+ * Rows are copied bit for bit, so any element type works.
+ *   x          [T * row_bytes] bytes
+ *   dest       [T*width] int32: destination rows (-1 = none), e.g. a plan's
+ *              token_rows (width = k) or a shuffle's dest_pos (width = 1)
+ *   out        [out_rows * row_bytes] bytes; rows nobody targets are untouched
+ * row_bytes must be a positive multiple of 4 and x, out 4-byte aligned; rows
+ * that are multiples of 16 bytes with 16-byte aligned buffers take the wide
+ * path.  width in 1..8.
+ * d_err bits: ROW_RANGE (dest >= out_rows; that copy is skipped).
+ * ---------------------------------------------------------------------- */
+int moe_permute(const void* x, int64_t T, int64_t row_bytes, const int32_t* dest, int width,
+                void* out, int64_t out_rows, int32_t* d_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine -- weighted combine back to token order (the hidden-state
+ * combine of [CE] footnote 3 over the deduplicated rows of [EC] abstract).
+ *
+ *   y[t] = sum_{q : rows[t*k+q] >= 0} a(rows[t*k+q]) * z[rows[t*k+q]]
+ * with a = row_weight (NULL: a = 1, for expert sides that applied the gates
+ * themselves).  Summed in float in ascending q, rounded once to y_dtype
+ * (bf16: round to nearest even).
+ *   z        [z_rows * H] of z_dtype (MOE_F32 or MOE_BF16)
+ *   rows     [T*k] int32, e.g. a plan's token_rows
+ *   y        [T * H] of y_dtype
+ * H * sizeof(z_dtype) and H * sizeof(y_dtype) must be multiples of 16 bytes,
+ * z and y 16-byte aligned.  k in 1..8.
+ * d_err bits: ROW_RANGE (row >= z_rows; that term is skipped).
+ * ---------------------------------------------------------------------- */
+int moe_combine(const void* z, int z_dtype, int64_t z_rows, int64_t H, const int32_t* rows,
+                int k, const float* row_weight, int64_t T, void* y, int y_dtype,
+                int32_t* d_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_shuffle_predict -- token shuffling ([EC] abstract: move each token to
+ * the GPU predicted to hold its next-layer experts).
+ *
+ * score_t[r] = sum_{i in D_t} sum_{j : expert_rank_next[j] == r} X[i][j]
+ * (64-bit integer sums of the transition counts), pred_t = the highest
+ * scoring rank, the lowest rank on ties.  Tokens are then ordered by pred,
+ * stably (ascending t within a rank).
+ *
+ *   topk              [T*k] int32: this layer's experts
+ *   transition        [E*E_next] int32: X, e.g. from moe_coact_stats
+ *   expert_rank_next  [E_next] int32: next-layer placement
+ *   pred_rank         [T] int32 out
+ *   dest_pos          [T] int32 out: new position of token t
+ *   perm              [T] int32 out or NULL: token at new position q
+ *   shard_offsets     [G+1] int32 out: first position of each rank's tokens
+ *                     (usable as the next plan's src_offsets)
+ *   ws, ws_bytes      workspace of moe_shuffle_predict_workspace_size() bytes,
+ *                     256-byte aligned
+ * Limits: 1 <= k <= 8, 1 <= E, E_next <= 256, 1 <= G <= 64.
+ * d_err bits: EXPERT_RANGE, RANK_RANGE (entries skipped).
+ * ---------------------------------------------------------------------- */
+int moe_shuffle_predict_workspace_size(int64_t T, int E, int G, size_t* ws_bytes /* host */);
+int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E, const int32_t* transition,
+                        int E_next, const int32_t* expert_rank_next, int G, int32_t* pred_rank,
+                        int32_t* dest_pos, int32_t* perm, int32_t* shard_offsets,
+                        int32_t* d_err, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_COACT_H */

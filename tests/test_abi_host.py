@@ -1,0 +1,112 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host (negative status,
+nothing enqueued, no HIP call made)."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from co_activation_amd import _lib
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "moe_coact.h"
+
+NULL = None
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def _declared():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_exports_agree(built_lib):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(built_lib, n), n
+
+
+def test_status_strings(built_lib):
+    for code in _lib.STATUS:
+        assert built_lib.moe_status_string(code)
+    assert built_lib.moe_status_string(12345) == b"unknown status"
+
+
+def test_workspace_queries(built_lib):
+    n = ctypes.c_size_t()
+    assert built_lib.moe_dispatch_plan_workspace_size(65536, 8, ctypes.byref(n)) == 0
+    assert n.value >= (65536 // 256 + 8) * (8 + 4) * 4 and n.value % 256 == 0
+    assert built_lib.moe_dispatch_plan_workspace_size(10, 65, ctypes.byref(n)) == -2
+    assert built_lib.moe_dispatch_plan_workspace_size(10, 8, None) == -1
+    assert built_lib.moe_shuffle_predict_workspace_size(4096, 64, 8, ctypes.byref(n)) == 0
+    assert n.value > 4096 * 4
+    assert built_lib.moe_shuffle_predict_workspace_size(4096, 257, 8, ctypes.byref(n)) == -2
+
+
+def test_stats_rejects(built_lib):
+    f = built_lib.moe_coact_stats
+    assert f(FAKE, 10, 9, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, NULL) == -2  # k > 8
+    assert f(FAKE, 10, 2, 257, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, NULL) == -2  # E > 256
+    assert f(FAKE, -1, 2, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, NULL) == -2
+    assert f(FAKE, 10, 2, 8, NULL, 0, 0, NULL, NULL, NULL, NULL, NULL, NULL) == -1  # counts
+    assert f(FAKE, 10, 2, 8, NULL, 0, 0, FAKE, NULL, FAKE, NULL, NULL, NULL) == -1  # ochiai w/o pairs
+    assert f(FAKE, 10, 2, 8, NULL, 2, 8, FAKE, NULL, NULL, FAKE, NULL, NULL) == -1  # no topk_next
+    assert f(FAKE, 10, 2, 8, FAKE, 0, 8, FAKE, NULL, NULL, FAKE, NULL, NULL) == -2  # k_next 0
+    assert f(FAKE, 2**30, 2, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, NULL) == -2  # T*k
+
+
+def _plan(lib, **kw):
+    a = dict(topk=FAKE, gates=NULL, T=64, k=2, E=8, er=FAKE, G=4, Rn=4, src=NULL, cap=128,
+             sc=FAKE, so=FAKE, rt=FAKE, rw=NULL, tr=FAKE, sr=NULL, cn=FAKE, derr=NULL, ws=FAKE,
+             wsb=1 << 20)
+    a.update(kw)
+    return lib.moe_dispatch_plan(a["topk"], a["gates"], a["T"], a["k"], a["E"], a["er"], a["G"],
+                                 a["Rn"], a["src"], a["cap"], a["sc"], a["so"], a["rt"], a["rw"],
+                                 a["tr"], a["sr"], a["cn"], a["derr"], a["ws"], a["wsb"], NULL)
+
+
+def test_plan_rejects(built_lib):
+    L = built_lib
+    assert _plan(L, G=65) == -2
+    assert _plan(L, G=0) == -2
+    assert _plan(L, Rn=3) == -2          # does not divide G
+    assert _plan(L, T=63) == -2          # equal shards need T % G == 0
+    assert _plan(L, k=0) == -2
+    assert _plan(L, E=300) == -2
+    assert _plan(L, cap=-1) == -2
+    assert _plan(L, er=NULL) == -1
+    assert _plan(L, ws=NULL) == -1
+    assert _plan(L, tr=NULL) == -1
+    assert _plan(L, rt=NULL) == -1
+    assert _plan(L, ws=FAKE + 4) == -4   # workspace alignment
+    assert _plan(L, wsb=16) == -5        # workspace too small
+
+
+def test_permute_combine_shuffle_reject(built_lib):
+    L = built_lib
+    assert L.moe_permute(FAKE, 8, 0, FAKE, 1, FAKE, 8, NULL, NULL) == -2
+    assert L.moe_permute(FAKE, 8, 16, FAKE, 9, FAKE, 8, NULL, NULL) == -2
+    assert L.moe_permute(FAKE, 8, 6, FAKE, 1, FAKE, 8, NULL, NULL) == -4
+    assert L.moe_permute(FAKE + 2, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL) == -4
+    assert L.moe_permute(NULL, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL) == -1
+    assert L.moe_permute(NULL, 0, 16, NULL, 1, NULL, 0, NULL, NULL) == 0   # empty: no-op
+    assert L.moe_combine(FAKE, 7, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL) == -3
+    assert L.moe_combine(FAKE, 1, 8, 60, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL) == -4  # 120 B rows
+    assert L.moe_combine(FAKE, 1, 8, 64, FAKE, 0, NULL, 8, FAKE, 1, NULL, NULL) == -2
+    assert L.moe_combine(FAKE, 1, 8, 64, NULL, 2, NULL, 8, FAKE, 1, NULL, NULL) == -1
+    assert L.moe_combine(FAKE + 8, 1, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL) == -4
+    sp = L.moe_shuffle_predict
+    assert sp(FAKE, 8, 2, 8, FAKE, 8, FAKE, 65, FAKE, FAKE, NULL, FAKE, NULL, FAKE, 1 << 20, NULL) == -2
+    assert sp(FAKE, 8, 2, 8, NULL, 8, FAKE, 4, FAKE, FAKE, NULL, FAKE, NULL, FAKE, 1 << 20, NULL) == -1
+    assert sp(FAKE, 8, 2, 8, FAKE, 8, FAKE, 4, FAKE, FAKE, NULL, FAKE, NULL, FAKE + 16, 1 << 20, NULL) == -4
+    assert sp(FAKE, 8, 2, 8, FAKE, 8, FAKE, 4, FAKE, FAKE, NULL, FAKE, NULL, FAKE, 64, NULL) == -5
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No CPU fallback: without the built library every call raises."""
+    monkeypatch.setattr(_lib, "LIB_PATH", tmp_path / "missing.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

@@ -1,0 +1,398 @@
+"""Parity of the HIP engine with the CPU oracle, through the C ABI.
+
+Sizes here let the oracle finish in seconds while spanning several 256-token
+tiles and a ragged last tile; the full-size workloads run in
+``test_gpu_fullsize.py``.  Integers, plans and permuted rows are compared bit
+for bit; the combine within 1e-5 relative (fp32 output) or 1 bf16 ulp of the
+oracle's fp32 value rounded once (bf16 output)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from co_activation_amd import ops
+from co_activation_amd.pipeline import LayerStep, TwoLayerStep
+from gpu_util import (assert_equal, check_combine, dev, f32_ulps, host, i32, say, x_tensor)
+from workloads import make, expert_outputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(built_lib):
+    assert torch.cuda.is_available()
+    return built_lib
+
+
+def _err():
+    return ops.new_error_word()
+
+
+def _no_errors(err):
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, ops.decode_errors(int(err.item()))
+
+
+# ------------------------------------------------------------------ stats
+
+STATS_CASES = [(1, 2048), (2, 3000), (3, 2900), (4, 1500), (5, 4001), (4, 257), (3, 1)]
+
+
+@pytest.mark.parametrize("cfg,T", STATS_CASES)
+def test_stats_parity(cfg, T):
+    w = make(cfg, T=T, with_x=False)
+    nxt = w.topk2 if cfg == 5 else None
+    say("stats", cfg, T)
+    err = _err()
+    res = ops.coact_stats(i32(w.topk), w.E, i32(nxt) if nxt is not None else None,
+                          w.E if nxt is not None else None, d_err=err)
+    _no_errors(err)
+    ref = oracle.coact_stats(w.topk, w.E, nxt, w.E if nxt is not None else None)
+    assert_equal(host(res["expert_count"]), ref["expert_count"], "expert_count")
+    assert_equal(host(res["pair_count"]), ref["pair_count"], "pair_count")
+    assert f32_ulps(host(res["ochiai"]), ref["ochiai"]).max() <= 1
+    assert_equal(host(res["ochiai"]), ref["ochiai"], "ochiai (expected bit-exact)")
+    if nxt is not None:
+        assert_equal(host(res["transition"]), ref["transition"], "transition")
+
+
+def test_stats_counts_only_and_large_E():
+    rng = np.random.default_rng(11)
+    T, E, k = 5000, 256, 8
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    nxt = np.stack([rng.permutation(200)[:3] for _ in range(T)]).astype(np.int32)
+    say("stats counts-only / E=256 transitions")
+    err = _err()
+    res = ops.coact_stats(i32(topk), E, pairs=False, d_err=err)
+    _no_errors(err)
+    ref = oracle.coact_stats(topk, E, nxt, 200)
+    assert_equal(host(res["expert_count"]), ref["expert_count"], "expert_count")
+    res = ops.coact_stats(i32(topk), E, i32(nxt), 200, d_err=err)
+    _no_errors(err)
+    assert_equal(host(res["pair_count"]), ref["pair_count"], "pair_count")
+    assert_equal(host(res["transition"]), ref["transition"], "transition")
+    assert_equal(host(res["ochiai"]), ref["ochiai"], "ochiai")
+
+
+# ------------------------------------------------------------------ plan
+
+def _check_plan(plan, ref, T, k):
+    N = int(ref["N"])
+    assert_equal(host(plan.counters), ref["counters"], "counters")
+    assert_equal(host(plan.send_counts), ref["send_counts"], "send_counts")
+    assert_equal(host(plan.send_offsets), ref["send_offsets"], "send_offsets")
+    assert_equal(host(plan.row_token)[:N], ref["row_token"], "row_token")
+    if plan.row_weight is not None:
+        assert_equal(host(plan.row_weight)[:N].view(np.uint32),
+                     ref["row_weight"].view(np.uint32), "row_weight bits")
+    assert_equal(host(plan.token_rows), ref["token_rows"], "token_rows")
+    if plan.slot_row is not None:
+        assert_equal(host(plan.slot_row), ref["slot_row"], "slot_row")
+
+
+PLAN_CASES = [(1, 2048, "main"), (2, 3000, "main"), (2, 3000, "alt"), (3, 3104, "main"),
+              (3, 3104, "alt"), (4, 1472, "main"), (4, 1472, "alt"), (5, 4104, "main")]
+
+
+@pytest.mark.parametrize("cfg,T,placement", PLAN_CASES)
+def test_plan_parity(cfg, T, placement):
+    w = make(cfg, T=T, with_x=False)
+    er = w.expert_rank if placement == "main" else w.alt_expert_rank
+    say("plan", cfg, T, placement)
+    err = _err()
+    plan = ops.dispatch_plan(i32(w.topk), dev(w.gates), i32(er), w.G, w.ranks_per_node, d_err=err)
+    _no_errors(err)
+    ref = oracle.dispatch_plan(w.topk, w.gates, er, w.G, w.ranks_per_node)
+    _check_plan(plan, ref, w.T, w.k)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_plan_uneven_shards(seed):
+    """Explicit source offsets: uneven, empty shards, a shard of one token."""
+    rng = np.random.default_rng(100 + seed)
+    w = make(3, T=3000, with_x=False)
+    cuts = np.sort(rng.integers(0, w.T + 1, size=w.G - 1))
+    cuts[:3] = cuts[3]           # empty shards
+    cuts[-1] = w.T               # empty last shard
+    off = np.concatenate([[0], cuts, [w.T]]).astype(np.int32)
+    say("plan uneven", seed)
+    err = _err()
+    plan = ops.dispatch_plan(i32(w.topk), dev(w.gates), i32(w.expert_rank), w.G,
+                             w.ranks_per_node, i32(off), d_err=err)
+    _no_errors(err)
+    ref = oracle.dispatch_plan(w.topk, w.gates, w.expert_rank, w.G, w.ranks_per_node, off)
+    _check_plan(plan, ref, w.T, w.k)
+
+
+EDGE = [
+    # T, E, k, G, Rn, seed
+    (0, 8, 2, 4, 2, 0),
+    (1, 8, 2, 1, 1, 1),
+    (5, 4, 1, 1, 1, 2),
+    (256, 16, 4, 16, 4, 3),
+    (257, 16, 4, 1, 1, 4),
+    (4096, 256, 8, 64, 8, 5),
+    (640, 64, 8, 64, 1, 6),
+    (512, 8, 8, 8, 2, 7),        # E = G = k: every token goes to every rank
+]
+
+
+@pytest.mark.parametrize("T,E,k,G,Rn,seed", EDGE)
+def test_plan_edges(T, E, k, G, Rn, seed):
+    rng = np.random.default_rng(seed)
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) if T else \
+        np.zeros((0, k), np.int32)
+    gates = rng.random((T, k)).astype(np.float32)
+    er = rng.integers(0, G, size=E).astype(np.int32)
+    say("plan edge", T, E, k, G, Rn)
+    err = _err()
+    plan = ops.dispatch_plan(i32(topk), dev(gates), i32(er), G, Rn,
+                             row_capacity=max(T * min(k, G), 1), d_err=err)
+    _no_errors(err)
+    ref = oracle.dispatch_plan(topk, gates, er, G, Rn)
+    _check_plan(plan, ref, T, k)
+
+
+# ------------------------------------------------------------------ permute
+
+@pytest.mark.parametrize("cfg,T,H", [(1, 2048, 128), (2, 3000, 512), (4, 1472, 7168), (3, 1056, 4096)])
+def test_permute_parity(cfg, T, H):
+    w = make(cfg, T=T, H=H)
+    say("permute", cfg, T, H)
+    err = _err()
+    plan = ops.dispatch_plan(i32(w.topk), dev(w.gates), i32(w.expert_rank), w.G,
+                             w.ranks_per_node, d_err=err)
+    ref = oracle.dispatch_plan(w.topk, w.gates, w.expert_rank, w.G, w.ranks_per_node)
+    N = int(ref["N"])
+    cap = w.T * min(w.k, w.G)
+    x = x_tensor(w)
+    out = torch.empty((cap, H), dtype=x.dtype, device=x.device)
+    ops.permute(x, plan.token_rows, cap, out=out, d_err=err)
+    _no_errors(err)
+    _check_plan(plan, ref, w.T, w.k)
+    want = oracle.permute_rows(w.x, ref["row_token"])
+    assert_equal(host(out)[:N], want, "send rows")
+
+
+def test_permute_narrow_rows_and_untouched():
+    """4-byte path (8-byte rows), width 1, and rows nobody targets stay as
+    they were."""
+    rng = np.random.default_rng(12)
+    T = 1000
+    rows = rng.integers(-2**31, 2**31 - 1, size=(T, 2), dtype=np.int64).astype(np.int32)
+    dest = rng.permutation(T + 37)[:T].astype(np.int32)
+    say("permute narrow")
+    err = _err()
+    out = torch.full((T + 37, 2), -7, dtype=torch.int32, device="cuda")
+    ops.permute(i32(rows), i32(dest), T + 37, out=out, d_err=err)
+    _no_errors(err)
+    got = host(out)
+    exp = oracle.scatter_rows(rows, dest, T + 37)
+    targeted = np.isin(np.arange(T + 37), dest)
+    assert_equal(got[targeted], exp[targeted], "scattered rows")
+    assert (got[~targeted] == -7).all()
+
+
+# ------------------------------------------------------------------ combine
+
+COMBINE_CASES = [(1, 2048, 128, "f32", "f32"), (1, 2048, 128, "f32", "bf16"),
+                 (2, 3000, 512, "bf16", "bf16"), (2, 3000, 512, "bf16", "f32"),
+                 (3, 1056, 4096, "bf16", "bf16"), (4, 1472, 7168, "bf16", "bf16")]
+
+
+@pytest.mark.parametrize("cfg,T,H,zd,yd", COMBINE_CASES)
+def test_combine_parity(cfg, T, H, zd, yd):
+    w = make(cfg, T=T, H=H, with_x=False)
+    say("combine", cfg, T, H, zd, yd)
+    err = _err()
+    plan = ops.dispatch_plan(i32(w.topk), dev(w.gates), i32(w.expert_rank), w.G,
+                             w.ranks_per_node, d_err=err)
+    ref = oracle.dispatch_plan(w.topk, w.gates, w.expert_rank, w.G, w.ranks_per_node)
+    N = int(ref["N"])
+    Z = expert_outputs(N, H, zd, seed=1)
+    tdt = torch.bfloat16 if yd == "bf16" else torch.float32
+    y = ops.combine(dev(Z), plan.token_rows, plan.row_weight, out_dtype=tdt, d_err=err)
+    _no_errors(err)
+    check_combine(y, Z, zd, ref["slot_row"], w.gates, yd, what=f"combine cfg{cfg}")
+    # unweighted mode: the plain sum of the token's rows
+    yu = ops.combine(dev(Z), plan.token_rows, None, out_dtype=torch.float32, d_err=err)
+    _no_errors(err)
+    refu = oracle.combine_unweighted(Z, zd, ref["token_rows"], "f32")
+    Zf = oracle.bf16_to_f32(Z) if zd == "bf16" else Z
+    scale = np.zeros_like(refu, dtype=np.float64)
+    for q in range(w.k):
+        m = ref["token_rows"][:, q] >= 0
+        scale[m] += np.abs(Zf[ref["token_rows"][m, q]])
+    assert (np.abs(host(yu) - refu) <= 1e-5 * scale + 1e-30).all()
+
+
+def test_combine_of_permute_is_identity():
+    """permute then weighted combine returns x bit-exact in bf16 (gates sum
+    to 1 within 2^-10), and the unweighted combine gives |R_t| * x exactly."""
+    w = make(3, T=1056, H=1024)
+    say("combine(permute(x))")
+    err = _err()
+    plan = ops.dispatch_plan(i32(w.topk), dev(w.gates), i32(w.expert_rank), w.G,
+                             w.ranks_per_node, d_err=err)
+    x = x_tensor(w)
+    send = ops.permute(x, plan.token_rows, w.T * min(w.k, w.G), d_err=err)
+    y = ops.combine(send, plan.token_rows, plan.row_weight, d_err=err)
+    yu = ops.combine(send, plan.token_rows, None, out_dtype=torch.float32, d_err=err)
+    _no_errors(err)
+    assert_equal(host(y), w.x, "combine(permute(x)) == x")
+    nr = (host(plan.token_rows) >= 0).sum(axis=1).astype(np.float32)
+    assert_equal(host(yu), oracle.bf16_to_f32(w.x) * nr[:, None], "unweighted == |R_t| x")
+
+
+# ------------------------------------------------------------------ shuffle
+
+@pytest.mark.parametrize("T", [4104, 1, 300])
+def test_shuffle_parity(T):
+    w = make(5, T=T, with_x=False)
+    say("shuffle", T)
+    err = _err()
+    st = ops.coact_stats(i32(w.topk), w.E, i32(w.topk2), w.E, d_err=err)
+    sh = ops.shuffle_predict(i32(w.topk), st["transition"], i32(w.expert_rank2), w.G, d_err=err)
+    _no_errors(err)
+    ref_st = oracle.coact_stats(w.topk, w.E, w.topk2, w.E)
+    ref = oracle.shuffle_predict(w.topk, ref_st["transition"], w.expert_rank2, w.G)
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert_equal(host(sh[key]), ref[key], key)
+
+
+@pytest.mark.parametrize("E,E2,k,G,seed", [(256, 256, 8, 64, 0), (16, 40, 3, 5, 1), (8, 8, 1, 3, 2)])
+def test_shuffle_ties_and_shapes(E, E2, k, G, seed):
+    """Small integer transitions (many ties), odd G, E up to 256."""
+    rng = np.random.default_rng(seed)
+    T = 2000
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    X = rng.integers(0, 3, size=(E, E2)).astype(np.int32)
+    er2 = rng.integers(0, G, size=E2).astype(np.int32)
+    say("shuffle shapes", E, E2, k, G)
+    err = _err()
+    sh = ops.shuffle_predict(i32(topk), i32(X), i32(er2), G, d_err=err)
+    _no_errors(err)
+    ref = oracle.shuffle_predict(topk, X, er2, G)
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert_equal(host(sh[key]), ref[key], key)
+
+
+# ------------------------------------------------------------------ pipelines
+
+def test_layer_step_parity():
+    w = make(2, T=3000, H=256)
+    say("layer step cfg2")
+    ref = oracle.dispatch_plan(w.topk, w.gates, w.expert_rank, w.G, w.ranks_per_node)
+    cap = w.T * min(w.k, w.G)
+    Z = expert_outputs(cap, w.H, "bf16", seed=1)
+    step = LayerStep(i32(w.topk), dev(w.gates), i32(w.expert_rank), x_tensor(w), dev(Z), w.G,
+                     w.ranks_per_node)
+    step.run()
+    _no_errors(step.d_err)
+    _check_plan(step.plan, ref, w.T, w.k)
+    N = int(ref["N"])
+    assert_equal(host(step.send)[:N], oracle.permute_rows(w.x, ref["row_token"]), "send")
+    check_combine(step.y, Z, "bf16", ref["slot_row"], w.gates, "bf16", "layer step")
+    st = oracle.coact_stats(w.topk, w.E)
+    assert_equal(host(step.stats_out["pair_count"]), st["pair_count"], "pairs")
+
+
+def test_two_layer_step_parity():
+    w = make(5, T=4104, H=256)
+    say("two-layer step cfg5")
+    cap = w.T * min(w.k, w.G)
+    Z = expert_outputs(cap, w.H, "bf16", seed=1)
+    step = TwoLayerStep(i32(w.topk), i32(w.topk2), dev(w.gates2), i32(w.expert_rank2),
+                        x_tensor(w), dev(Z), w.G, w.ranks_per_node, E1=w.E)
+    step.run()
+    _no_errors(step.d_err)
+    ref = oracle.two_layer_pipeline(w.topk, w.topk2, w.gates2, w.x, w.expert_rank2, w.E, w.E,
+                                    w.G, w.ranks_per_node)
+    assert_equal(host(step.stats_out["transition"]), ref["stats"]["transition"], "transition")
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert_equal(host(step.shuffle[key]), ref["shuffle"][key], key)
+    assert_equal(host(step.x_s), ref["x_shuffled"], "x shuffled")
+    assert_equal(host(step.topk2_s), ref["topk2_shuffled"], "topk2 shuffled")
+    assert_equal(host(step.gates2_s), ref["gates2_shuffled"], "gates2 shuffled")
+    _check_plan(step.plan, ref["plan"], w.T, w.k)
+    N = int(ref["plan"]["N"])
+    assert_equal(host(step.send)[:N], ref["send"], "layer-2 send")
+    check_combine(step.y, Z, "bf16", ref["plan"]["slot_row"], ref["gates2_shuffled"], "bf16",
+                  "two-layer combine")
+    c = host(step.plan.counters)
+    assert c[3] / (w.T * w.k) > ref["local_share_before"]
+
+
+# ------------------------------------------------------------------ determinism
+
+def test_determinism():
+    w = make(3, T=3104, H=512)
+    say("determinism")
+    outs = []
+    for _ in range(2):
+        err = _err()
+        st = ops.coact_stats(i32(w.topk), w.E, d_err=err)
+        plan = ops.dispatch_plan(i32(w.topk), dev(w.gates), i32(w.expert_rank), w.G,
+                                 w.ranks_per_node, d_err=err)
+        Z = dev(expert_outputs(w.T * min(w.k, w.G), w.H, "bf16", seed=1))
+        y = ops.combine(Z, plan.token_rows, plan.row_weight, d_err=err)
+        _no_errors(err)
+        outs.append([host(st["pair_count"]), host(st["ochiai"]), host(plan.row_token),
+                     host(plan.row_weight), host(plan.token_rows), host(y)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# ------------------------------------------------------------------ device error bits
+
+def test_device_error_bits():
+    """Bad data is reported in d_err, never read or written out of bounds."""
+    rng = np.random.default_rng(13)
+    T, E, k, G = 512, 16, 2, 4
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    gates = rng.random((T, k)).astype(np.float32)
+    er = (np.arange(E) // (E // G)).astype(np.int32)
+
+    def plan_bits(tk=topk, ers=er, cap=None, off=None):
+        err = _err()
+        ops.dispatch_plan(i32(tk), dev(gates), i32(ers), G, G, None if off is None else i32(off),
+                          row_capacity=cap, d_err=err)
+        torch.cuda.synchronize()
+        return int(err.item())
+
+    say("device error bits")
+    bad = topk.copy(); bad[7, 1] = E
+    assert plan_bits(bad) & 1
+    bad = topk.copy(); bad[9, 1] = -3
+    assert plan_bits(bad) & 1
+    bad = topk.copy(); bad[11, 1] = bad[11, 0]
+    assert plan_bits(bad) & 2
+    ers = er.copy(); ers[5] = G
+    assert plan_bits(ers=ers) & 4
+    ref = oracle.dispatch_plan(topk, gates, er, G, G)
+    assert plan_bits(cap=int(ref["N"]) - 1) == 8
+    assert plan_bits(cap=int(ref["N"])) == 0
+    assert plan_bits(off=np.array([0, 100, 50, 300, T], np.int32)) & 16
+    assert plan_bits(off=np.array([0, 100, 200, 300, T - 1], np.int32)) & 16
+    # counters stay valid under a capacity overflow
+    err = _err()
+    p = ops.dispatch_plan(i32(topk), dev(gates), i32(er), G, G, row_capacity=10, d_err=err)
+    torch.cuda.synchronize()
+    assert_equal(host(p.counters), ref["counters"], "counters under overflow")
+    # stats
+    err = _err()
+    bad = topk.copy(); bad[3, 0] = 99
+    ops.coact_stats(i32(bad), E, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 1
+    # permute / combine row range
+    err = _err()
+    x = torch.zeros((4, 8), dtype=torch.float32, device="cuda")
+    ops.permute(x, i32([[0], [1], [9], [2]]), 4, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 32
+    err = _err()
+    ops.combine(x, i32([[0, 1], [5, -1]]), None, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 32

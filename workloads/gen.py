@@ -118,6 +118,23 @@ def expert_outputs(rows: int, H: int, dtype: str, seed: int = 1) -> np.ndarray:
     return _hidden(rng, rows, H, dtype)
 
 
+def device_normal(rows: int, H: int, dtype: str, seed: int, device="cuda"):
+    """N(0,1) [rows, H] drawn on the device by torch's seeded generator
+    (Philox), cast to bf16 by torch (RNE) or kept fp32.  Used for the large
+    stand-in expert outputs, where a host draw would dominate run time."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty((rows, H), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                      device=device)
+    step = max(1, (1 << 26) // max(H, 1))
+    for a in range(0, rows, step):
+        b = min(rows, a + step)
+        out[a:b] = torch.randn((b - a, H), generator=g, device=device, dtype=torch.float32)
+    return out
+
+
 def make(cfg: int, T: Optional[int] = None, H: Optional[int] = None, seed: int = 0,
          with_x: bool = True) -> Workload:
     """Build workload ``cfg`` (1..5); ``T``/``H`` override the sizes for
