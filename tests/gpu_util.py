@@ -66,22 +66,35 @@ def bf16_ulps(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     return np.abs(key(a_bits) - key(b_bits))
 
 
+def combine_scale(Z, z_dtype, slot_row, gates):
+    """sum_j |w_tj| |Z[slot_row[t, j]]| per element: the size of the terms."""
+    Zf = oracle.bf16_to_f32(Z) if z_dtype == "bf16" else np.asarray(Z, np.float32)
+    scale = np.zeros((slot_row.shape[0], Zf.shape[1]), np.float64)
+    for j in range(slot_row.shape[1]):
+        scale += np.abs(gates[:, j:j + 1].astype(np.float64)) * np.abs(Zf[slot_row[:, j]])
+    return scale
+
+
 def check_combine(y_gpu: torch.Tensor, Z: np.ndarray, z_dtype: str, slot_row: np.ndarray,
                   gates: np.ndarray, out_dtype: str, what=""):
-    """fp32 output: |y - y_ref| <= 1e-5 * sum_j |w_tj| |Z_row| per element;
-    bf16 output: within 1 bf16 ulp of the oracle's fp32 result rounded once."""
+    """fp32 output: |y - y_ref| <= 1e-5 * sum_j |w_tj| |Z_row| per element.
+    bf16 output: within 1 bf16 ulp of the oracle's fp32 result rounded once;
+    where the weighted sum cancels (|y| far below sum |w||Z|) no fp32
+    accumulation order can promise that, and the element is held to the fp32
+    bound instead."""
     y = host(y_gpu)
     ref32 = oracle.combine(Z, z_dtype, slot_row, gates, "f32")
+    scale = combine_scale(Z, z_dtype, slot_row, gates)
     if out_dtype == "f32":
-        Zf = oracle.bf16_to_f32(Z) if z_dtype == "bf16" else np.asarray(Z, np.float32)
-        scale = np.zeros(ref32.shape, np.float64)
-        for j in range(slot_row.shape[1]):
-            scale += np.abs(gates[:, j:j + 1].astype(np.float64)) * np.abs(Zf[slot_row[:, j]])
         err = np.abs(y.astype(np.float64) - ref32.astype(np.float64))
         ok = err <= 1e-5 * scale + 1e-30
         assert ok.all(), f"{what}: {np.count_nonzero(~ok)} elements outside 1e-5 relative"
     else:
         ref = oracle.bf16_round(ref32)
         d = bf16_ulps(y, ref)
-        assert d.max() <= 1, f"{what}: bf16 ulp distance up to {d.max()}"
+        yf = oracle.bf16_to_f32(y).astype(np.float64)
+        near = np.abs(yf - ref32.astype(np.float64)) <= 1e-5 * scale
+        ok = (d <= 1) | near
+        assert ok.all(), (f"{what}: {np.count_nonzero(~ok)} elements beyond 1 bf16 ulp and "
+                          f"the fp32 bound; worst {d[~ok].max()} ulp")
     return y
