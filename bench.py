@@ -33,7 +33,7 @@ def _args():
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--placement", default="main", choices=["main", "alt"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=24576)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--no-copy-probe", action="store_true")
     return ap.parse_args()
 
@@ -46,6 +46,28 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return platform.processor() or "unknown"
+
+
+def counter_traffic(workload: int, stage: str):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 counter
+    summary, or None when there is none or a kernel source changed since the
+    counters were taken."""
+    import hashlib
+    from pathlib import Path
+
+    root = Path(__file__).resolve().parent
+    summary = root / "profiles" / f"hbm_counters_workload{workload}.md"
+    if not summary.exists():
+        return None
+    lines = [ln.strip() for ln in summary.read_text().splitlines() if ln.strip().startswith("{")]
+    if not lines:
+        return None
+    rec = json.loads(lines[-1])
+    for path, digest in rec["sources"].items():
+        if hashlib.sha256((root / path).read_bytes()).hexdigest()[:16] != digest:
+            return None
+    k = rec["kernels"].get(stage)
+    return None if k is None else k["read_bytes"] + k["write_bytes"]
 
 
 def cpu_baseline(w, sample_tokens: int) -> dict:
@@ -93,7 +115,7 @@ def main() -> int:
     import torch
 
     import co_activation_amd
-    from co_activation_amd.pipeline import LayerStep, TwoLayerStep
+    from co_activation_amd.pipeline import LayerStep, StageTimers, TwoLayerStep
     from workloads import make
     from workloads.gen import device_normal
 
@@ -159,7 +181,17 @@ def main() -> int:
         print(json.dumps({"error": f"device data errors {int(step.d_err.item())}"}))
         return 1
 
-    timers: dict = {}
+    # Stage breakdown (events around every stage), outside the timed region.
+    stages = StageTimers(step.STAGES, args.steps)
+    for _ in range(args.steps):
+        step.run(stages)
+    torch.cuda.synchronize()
+    stage_ms = stages.mean_ms()
+    dom = max(("permute", "combine") + (("shuffle_permute",) if w.cfg == 5 else ()),
+              key=lambda n: stage_ms[n])
+
+    # Timed region: K steps; events only around the dominant kernel.
+    timers = StageTimers((dom,), args.steps)
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -172,8 +204,8 @@ def main() -> int:
     wall = time.perf_counter() - wall0
     gpu_ms = e_start.elapsed_time(e_end)
     ms_per_step = gpu_ms / args.steps
+    dom_ms = statistics.mean(timers.durations_ms(dom))
 
-    stage_ms = {k: statistics.mean(a.elapsed_time(b) for a, b in v) for k, v in timers.items()}
     counters = step.plan.counters.cpu().numpy()
     N = int(counters[0])
     T, k = w.T, w.k
@@ -184,8 +216,7 @@ def main() -> int:
     kernels = {"permute": bytes_perm, "combine": bytes_comb}
     if w.cfg == 5:
         kernels["shuffle_permute"] = 2 * T * rb + 4 * T
-    dom = max(kernels, key=lambda n: stage_ms[n])
-    achieved = kernels[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    achieved = kernels[dom] / (dom_ms * 1e-3) / 1e9
 
     line = {
         "metric": "dispatched rows/s (whole step) and permute+combine HBM GB/s at 1 MI355X",
@@ -210,8 +241,10 @@ def main() -> int:
                      "cross_node_V": int(counters[5]), "max_recv_rows": int(counters[6])},
         "copy_probe_gbps": copy_gbs,
         "wall_s_timed": wall,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": 1e3 * dom_ms,
+                     "algorithmic_bytes": kernels[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(w.cfg, dom)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)

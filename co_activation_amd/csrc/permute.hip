@@ -4,11 +4,11 @@
 // rank as in "Expert Coupling in MoE Pretraining ..." (abstract); the same
 // kernel moves tokens for the token shuffle.
 //
-// Token-major: one wave owns one token, reads its row once and writes it to
-// each of its (<= 8) destination rows.  The destination list is wave-uniform
-// and lives in scalar registers; each store instruction of the wave writes
-// 64 x 16 contiguous bytes.  HBM-bound: algorithmic bytes per token are
-// row_bytes * (1 + destinations) + 4 * width.
+// Token-major: a group of threads owns one token, reads its row once and
+// writes it to each of its (<= 8) destination rows.  The destination list is
+// uniform per token and lives in scalar registers; every store instruction of
+// a wave writes 64 x 16 contiguous bytes.  HBM-bound: algorithmic bytes per
+// token are row_bytes * (1 + destinations) + 4 * width.
 #include "common.hpp"
 
 namespace moe {
@@ -17,22 +17,40 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPermThreads = 256;
-constexpr int kPermWaves = kPermThreads / kWave;
 
-template <typename V, int UNROLL>
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+template <bool NT, typename V>
+__device__ __forceinline__ V load_row(const V* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+// TPT threads own one token (TPT = 64: four tokens per 256-thread block;
+// TPT >= 256: one token per block).  Each thread loads U vectors of the row
+// (stride TPT), then stores them to every destination of the token.  Loads
+// are plain (the row is read once; the caches may keep it for the next
+// destination), stores are nontemporal (send rows are not re-read here).
+// ONE: exactly one destination per token (a token move such as the shuffle).
+template <typename V, int TPT, int U, bool ONE>
+__global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void permute_kernel(
     const V* __restrict__ x, int T, int64_t vec_per_row, const int32_t* __restrict__ dest,
     int width, V* __restrict__ out, int64_t out_rows, int32_t* d_err) {
-  const int lane = lane_id();
-  const int t = blockIdx.x * kPermWaves + wave_id();
+  constexpr int kBlock = TPT < kPermThreads ? kPermThreads : TPT;
+  constexpr int kTokens = kBlock / TPT;
+  const int sub = kTokens == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / TPT);
+  const int t = blockIdx.x * kTokens + sub;
   if (t >= T) return;
+  const int l = kTokens == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x % TPT);
 
-  // Destination rows (wave-uniform); -1 marks an absent or rejected one.
+  // Destination rows (uniform per token); -1 marks an absent or rejected one.
   int drow[MOE_MAX_K];
+#pragma unroll
+  for (int q = 0; q < MOE_MAX_K; ++q) drow[q] = -1;
   int nd = 0;
   int errbits = 0;
 #pragma unroll
-  for (int q = 0; q < MOE_MAX_K; ++q) {
+  for (int q = 0; q < (ONE ? 1 : MOE_MAX_K); ++q) {
     drow[q] = -1;
     if (q < width) {
       const int r = __builtin_amdgcn_readfirstlane(dest[static_cast<int64_t>(t) * width + q]);
@@ -44,29 +62,96 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       }
     }
   }
-  if (lane == 0) report(d_err, errbits);
+  if (l == 0) report(d_err, errbits);
   if (nd == 0) return;
 
   const V* src = x + static_cast<int64_t>(t) * vec_per_row;
-  for (int64_t c0 = lane; c0 < vec_per_row; c0 += kWave * UNROLL) {
-    V v[UNROLL];
+  for (int64_t c0 = l; c0 < vec_per_row; c0 += TPT * U) {
+    V v[U];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t c = c0 + u * kWave;
-      if (c < vec_per_row) v[u] = __builtin_nontemporal_load(src + c);
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * TPT;
+      if (c < vec_per_row) v[u] = load_row<false>(src + c);
     }
 #pragma unroll
-    for (int q = 0; q < MOE_MAX_K; ++q) {
+    for (int q = 0; q < (ONE ? 1 : MOE_MAX_K); ++q) {
       if (q >= width) break;
       if (drow[q] < 0) continue;
       V* dst = out + static_cast<int64_t>(drow[q]) * vec_per_row;
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int64_t c = c0 + u * kWave;
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * TPT;
         if (c < vec_per_row) __builtin_nontemporal_store(v[u], dst + c);
       }
     }
   }
+}
+
+// Rows narrower than one wave's width of vectors: one thread per
+// (token, vector), so every lane moves data.
+template <typename V>
+__global__ __launch_bounds__(kPermThreads) void permute_flat_kernel(
+    const V* __restrict__ x, int T, int vec_per_row, const int32_t* __restrict__ dest, int width,
+    V* __restrict__ out, int64_t out_rows, int32_t* d_err) {
+  const int64_t n = static_cast<int64_t>(T) * vec_per_row;
+  int errbits = 0;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kPermThreads) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kPermThreads) {
+    const int t = static_cast<int>(i / vec_per_row);
+    const int c = static_cast<int>(i - static_cast<int64_t>(t) * vec_per_row);
+    const V v = __builtin_nontemporal_load(x + i);
+    for (int q = 0; q < width; ++q) {
+      const int r = dest[static_cast<int64_t>(t) * width + q];
+      if (r >= 0 && r < out_rows)
+        __builtin_nontemporal_store(v, out + static_cast<int64_t>(r) * vec_per_row + c);
+      else if (r >= out_rows)
+        errbits = MOE_DERR_ROW_RANGE;
+    }
+  }
+  report(d_err, errbits);
+}
+
+template <typename V, int TPT, int U>
+void launch_rows(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
+                 void* out, int64_t out_rows, int32_t* d_err, hipStream_t s) {
+  constexpr int kBlock = TPT < kPermThreads ? kPermThreads : TPT;
+  constexpr int kTokens = kBlock / TPT;
+  const unsigned blocks = static_cast<unsigned>((T + kTokens - 1) / kTokens);
+  if (width == 1)
+    permute_kernel<V, TPT, U, true><<<blocks, kBlock, 0, s>>>(
+        static_cast<const V*>(x), T, vec_per_row, dest, width, static_cast<V*>(out), out_rows,
+        d_err);
+  else
+    permute_kernel<V, TPT, U, false><<<blocks, kBlock, 0, s>>>(
+        static_cast<const V*>(x), T, vec_per_row, dest, width, static_cast<V*>(out), out_rows,
+        d_err);
+}
+
+// Launch shape by row size (vectors per row R), as measured on MI355X:
+//   R < 64                 one thread per (token, vector)
+//   64 <= R < 256          one wave per token, 4 vectors per lane per pass
+//   384 < R <= 512 and at most 2 destinations
+//                          512 threads per token, one vector each
+//   otherwise              256 threads per token, one vector per pass
+template <typename V>
+int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
+                   void* out, int64_t out_rows, int32_t* d_err, hipStream_t s) {
+  if (vec_per_row < kWave) {
+    const int64_t n = static_cast<int64_t>(T) * vec_per_row;
+    int64_t blocks = (n + kPermThreads - 1) / kPermThreads;
+    if (blocks > 8192) blocks = 8192;
+    permute_flat_kernel<V><<<static_cast<unsigned>(blocks), kPermThreads, 0, s>>>(
+        static_cast<const V*>(x), T, static_cast<int>(vec_per_row), dest, width,
+        static_cast<V*>(out), out_rows, d_err);
+  } else if (vec_per_row < 256) {
+    launch_rows<V, 64, 4>(x, T, vec_per_row, dest, width, out, out_rows, d_err, s);
+  } else if (vec_per_row > 384 && vec_per_row <= 512 && width <= 2) {
+    launch_rows<V, 512, 1>(x, T, vec_per_row, dest, width, out, out_rows, d_err, s);
+  } else {
+    launch_rows<V, 256, 1>(x, T, vec_per_row, dest, width, out, out_rows, d_err, s);
+  }
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
 }
 
 }  // namespace
@@ -81,17 +166,10 @@ extern "C" int moe_permute(const void* x, int64_t T, int64_t row_bytes, const in
   if (x == nullptr || dest == nullptr || out == nullptr) return MOE_ERR_NULL;
   const auto xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(out);
   if (row_bytes % 4 != 0 || xa % 4 != 0 || oa % 4 != 0) return MOE_ERR_ALIGN;
-  const unsigned blocks = static_cast<unsigned>((T + moe::kPermWaves - 1) / moe::kPermWaves);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0) {
-    moe::permute_kernel<moe::u32x4, 4><<<blocks, moe::kPermThreads, 0, s>>>(
-        static_cast<const moe::u32x4*>(x), static_cast<int>(T), row_bytes / 16, dest, width,
-        static_cast<moe::u32x4*>(out), out_rows, d_err);
-  } else {
-    moe::permute_kernel<uint32_t, 4><<<blocks, moe::kPermThreads, 0, s>>>(
-        static_cast<const uint32_t*>(x), static_cast<int>(T), row_bytes / 4, dest, width,
-        static_cast<uint32_t*>(out), out_rows, d_err);
-  }
-  MOE_CHECK_LAUNCH();
-  return MOE_OK;
+  if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0)
+    return moe::launch_permute<moe::u32x4>(x, static_cast<int>(T), row_bytes / 16, dest, width,
+                                           out, out_rows, d_err, s);
+  return moe::launch_permute<uint32_t>(x, static_cast<int>(T), row_bytes / 4, dest, width, out,
+                                       out_rows, d_err, s);
 }

@@ -17,6 +17,7 @@ expert side's returned rows (one per send row).
 
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
@@ -24,21 +25,93 @@ import torch
 from . import ops
 
 
+class _Hip:
+    """The few HIP runtime event calls the timers need (same runtime torch
+    loaded; recording through torch's Event wrapper costs far more host time
+    than the runtime call itself)."""
+
+    _h = None
+
+    @classmethod
+    def get(cls):
+        if cls._h is None:
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._h = h
+        return cls._h
+
+
+class StageTimers:
+    """HIP event pairs per stage, created up front so that a timed loop only
+    records events on the stream the stage's kernels run on."""
+
+    def __init__(self, names, steps):
+        h = _Hip.get()
+        self.pairs = {}
+        for n in names:
+            lst = []
+            for _ in range(steps):
+                a, b = ctypes.c_void_p(), ctypes.c_void_p()
+                if h.hipEventCreateWithFlags(ctypes.byref(a), 0) or \
+                        h.hipEventCreateWithFlags(ctypes.byref(b), 0):
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                lst.append((a, b))
+            self.pairs[n] = lst
+        self.used = {n: 0 for n in names}
+
+    def begin(self, name):
+        if name not in self.pairs:
+            return None
+        pair = self.pairs[name][self.used[name]]
+        _Hip.get().hipEventRecord(pair[0], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        return pair
+
+    def end(self, name, pair):
+        if pair is None:
+            return
+        _Hip.get().hipEventRecord(pair[1], ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        self.used[name] += 1
+
+    def durations_ms(self, name):
+        """Per-launch durations of a stage (call after synchronising)."""
+        h = _Hip.get()
+        out = []
+        for a, b in self.pairs[name][:self.used[name]]:
+            f = ctypes.c_float()
+            if h.hipEventElapsedTime(ctypes.byref(f), a, b):
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(f.value)
+        return out
+
+    def mean_ms(self):
+        return {n: sum(self.durations_ms(n)) / self.used[n] for n in self.pairs if self.used[n]}
+
+    def __del__(self):
+        try:
+            h = _Hip.get()
+            for lst in self.pairs.values():
+                for a, b in lst:
+                    h.hipEventDestroy(a)
+                    h.hipEventDestroy(b)
+        except Exception:
+            pass
+
+
 def _timed(timers, name):
-    """Context that records start/end events around a call on the current
-    stream when ``timers`` (dict name -> list of event pairs) is given."""
+    """Records the stage's event pair around a block when timers are given."""
 
     class _Ctx:
         def __enter__(self):
             if timers is not None:
-                self.a = torch.cuda.Event(enable_timing=True)
-                self.b = torch.cuda.Event(enable_timing=True)
-                self.a.record()
+                self.pair = timers.begin(name)
 
         def __exit__(self, *exc):
             if timers is not None:
-                self.b.record()
-                timers.setdefault(name, []).append((self.a, self.b))
+                timers.end(name, self.pair)
 
     return _Ctx()
 
@@ -82,7 +155,9 @@ class LayerStep:
             "counters": torch.empty(8, dtype=torch.int64, device=dev),
         }
 
-    def run(self, timers: Optional[dict] = None):
+    STAGES = ("stats", "plan", "permute", "combine")
+
+    def run(self, timers: Optional[StageTimers] = None):
         with _timed(timers, "stats"):
             ops.coact_stats(self.topk, self.E, out=self.stats_out, d_err=self.d_err)
         with _timed(timers, "plan"):
@@ -137,7 +212,10 @@ class TwoLayerStep:
         self.plan = None
         self.shuffle = None
 
-    def run(self, timers: Optional[dict] = None):
+    STAGES = ("stats", "shuffle_predict", "shuffle_permute", "shuffle_routing", "plan", "permute",
+              "combine")
+
+    def run(self, timers: Optional[StageTimers] = None):
         with _timed(timers, "stats"):
             stats = ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
                                     d_err=self.d_err)

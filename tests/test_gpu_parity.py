@@ -156,7 +156,8 @@ def test_plan_edges(T, E, k, G, Rn, seed):
 
 # ------------------------------------------------------------------ permute
 
-@pytest.mark.parametrize("cfg,T,H", [(1, 2048, 128), (2, 3000, 512), (4, 1472, 7168), (3, 1056, 4096)])
+@pytest.mark.parametrize("cfg,T,H", [(1, 2048, 128), (2, 3000, 512), (4, 1472, 7168),
+                                     (3, 1056, 4096), (5, 1032, 4096), (2, 1000, 2048)])
 def test_permute_parity(cfg, T, H):
     w = make(cfg, T=T, H=H)
     say("permute", cfg, T, H)
@@ -197,6 +198,7 @@ def test_permute_narrow_rows_and_untouched():
 # ------------------------------------------------------------------ combine
 
 COMBINE_CASES = [(1, 2048, 128, "f32", "f32"), (1, 2048, 128, "f32", "bf16"),
+                 (5, 1032, 4096, "bf16", "bf16"), (2, 1000, 2048, "bf16", "f32"),
                  (2, 3000, 512, "bf16", "bf16"), (2, 3000, 512, "bf16", "f32"),
                  (3, 1056, 4096, "bf16", "bf16"), (4, 1472, 7168, "bf16", "bf16")]
 
@@ -398,3 +400,45 @@ def test_device_error_bits():
     ops.combine(x, i32([[0, 1], [5, -1]]), None, d_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 32
+
+
+@pytest.mark.parametrize("H,width", [(4096, 1), (7168, 1), (4096, 2), (2048, 1)])
+def test_permute_token_moves(H, width):
+    """One destination per token (the shuffle's move) and two, on the
+    launch shapes of the wide rows."""
+    rng = np.random.default_rng(H + width)
+    T = 700
+    x = rng.integers(0, 2**16, size=(T, H), dtype=np.int64).astype(np.uint16)
+    out_rows = T * width
+    dest = rng.permutation(out_rows).reshape(T, width).astype(np.int32)
+    say("permute token moves", H, width)
+    err = _err()
+    out = ops.permute(dev(x), i32(dest), out_rows, d_err=err)
+    _no_errors(err)
+    want = np.empty((out_rows, H), np.uint16)
+    for q in range(width):
+        want[dest[:, q]] = x
+    assert_equal(host(out), want, "moved rows")
+
+
+@pytest.mark.parametrize("words,width", [(65, 3), (16, 2), (1, 1), (300, 8)])
+def test_permute_word_rows(words, width):
+    """Rows whose size is a multiple of 4 but not of 16 bytes (4-byte path,
+    flat and wave-per-token variants), several destinations per token."""
+    rng = np.random.default_rng(words)
+    T = 777
+    rows = rng.integers(-2**31, 2**31 - 1, size=(T, words), dtype=np.int64).astype(np.int32)
+    out_rows = T * width + 5
+    dest = rng.permutation(out_rows)[:T * width].reshape(T, width).astype(np.int32)
+    dest[rng.random((T, width)) < 0.2] = -1
+    say("permute words", words, width)
+    err = _err()
+    out = torch.full((out_rows, words), 3, dtype=torch.int32, device="cuda")
+    ops.permute(i32(rows), i32(dest), out_rows, out=out, d_err=err)
+    _no_errors(err)
+    want = np.full((out_rows, words), 3, np.int32)
+    for t in range(T):
+        for q in range(width):
+            if dest[t, q] >= 0:
+                want[dest[t, q]] = rows[t]
+    assert_equal(host(out), want, "word rows")
