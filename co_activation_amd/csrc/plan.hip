@@ -171,7 +171,8 @@ __device__ __forceinline__ int shard_of_tile(int j, const int* incl, int G) {
 __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
     const int32_t* __restrict__ src_offsets, int T, int k, int G, int32_t* __restrict__ tile_cnt,
     const int32_t* __restrict__ tile_stats, int64_t row_capacity, int32_t* __restrict__ send_counts,
-    int32_t* __restrict__ send_offsets, int64_t* __restrict__ counters, int32_t* d_err) {
+    int32_t* __restrict__ send_offsets, int64_t* __restrict__ counters,
+    int32_t* __restrict__ first_offsets, int32_t* d_err) {
   __shared__ int s_incl[kWave];
   __shared__ int s_first[kWave];
   __shared__ int s_S[MOE_MAX_G * MOE_MAX_G];
@@ -192,13 +193,29 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
   __syncthreads();
 
   // Per destination rank r: exclusive prefix of the tile counts within each
-  // source rank (segments), and the segment totals S[s][r].
+  // source rank (segments), and the segment totals S[s][r].  The first
+  // kPrefetch chunks of 64 tiles are loaded before any is scanned, so their
+  // load latencies overlap.
+  constexpr int kPrefetch = 8;
   for (int r = wave; r < G; r += kScanWaves) {
+    int pre[kPrefetch];
+#pragma unroll
+    for (int c = 0; c < kPrefetch; ++c) {
+      const int j = c * kWave + lane;
+      pre[c] = j < NT ? tile_cnt[static_cast<int64_t>(j) * G + r] : 0;
+    }
     int carry = 0;
-    for (int base = 0; base < NT; base += kWave) {
+    for (int base = 0, c = 0; base < NT; base += kWave, ++c) {
       const int j = base + lane;
       const bool in = j < NT;
-      const int v = in ? tile_cnt[static_cast<int64_t>(j) * G + r] : 0;
+      int v = 0;
+      if (c < kPrefetch) {
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q)
+          if (q == c) v = pre[q];
+      } else if (in) {
+        v = tile_cnt[static_cast<int64_t>(j) * G + r];
+      }
       const int s = in ? shard_of_tile(j, s_incl, G) : 0;
       const bool head = in && s_first[s] == j;
       const bool last = in && j + 1 == s_incl[s];
@@ -262,6 +279,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
   }
   if (tid == 0) send_offsets[n] = total_rows;
   __syncthreads();
+  if (first_offsets != nullptr && tid <= G) first_offsets[tid] = tid < n ? s_S[tid] : total_rows;
 
   // Each tile's first row per destination rank.
   for (int idx = tid; idx < NT * G; idx += kScanThreads) {
@@ -395,7 +413,7 @@ int launch_plan(const PlanArgs& a, hipStream_t stream) {
   }
   plan_scan_kernel<<<dim3(1), dim3(kScanThreads), 0, stream>>>(
       a.src_offsets, a.T, a.k, a.G, tile_cnt, tile_stats, a.row_capacity, a.send_counts,
-      a.send_offsets, a.counters, a.d_err);
+      a.send_offsets, a.counters, a.first_offsets, a.d_err);
   MOE_CHECK_LAUNCH();
   if (nt > 0) {
     plan_write_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(kPlanTile), 0, stream>>>(

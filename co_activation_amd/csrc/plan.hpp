@@ -35,6 +35,9 @@ struct PlanArgs {
   int64_t* counters;
   int32_t* d_err;
   void* ws;
+  // Optional: receives send_offsets[0..G] (the row offsets of source rank 0's
+  // blocks), i.e. the bucket offsets when the plan serves as a sort.
+  int32_t* first_offsets = nullptr;
 };
 
 // Enqueues the three plan kernels; arguments already validated.

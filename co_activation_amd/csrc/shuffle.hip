@@ -52,33 +52,40 @@ ShuffleWs shuffle_layout(void* base, int64_t T, int E, int G) {
   return w;
 }
 
-// One block per expert i of this layer; lane r sums X[i][j] over the
-// next-layer experts j placed on rank r.  Block 0 also writes the identity
-// placement and the one-source offsets [0, T, ..., T] used by the sort.
-__global__ __launch_bounds__(kWave) void rank_score_kernel(
+constexpr int kScoreThreads = 256;
+
+// One block per expert i of this layer: thread j adds X[i][j] into the sum of
+// the rank that holds next-layer expert j (64-bit LDS atomics, exact), then
+// thread r writes M[i][r].  Block 0 also writes the identity placement and
+// the one-source offsets [0, T, ..., T] used by the sort.
+__global__ __launch_bounds__(kScoreThreads) void rank_score_kernel(
     const int32_t* __restrict__ X, int E_next, const int32_t* __restrict__ expert_rank_next, int G,
     int T, int64_t* __restrict__ M, int32_t* __restrict__ identity, int32_t* __restrict__ src1,
     int32_t* d_err) {
+  __shared__ unsigned long long sums[MOE_MAX_G];
   const int i = blockIdx.x;
-  const int lane = threadIdx.x;
-  long long acc = 0;
+  const int tid = threadIdx.x;
+  if (tid < MOE_MAX_G) sums[tid] = 0;
+  __syncthreads();
   int bad = 0;
-  for (int j = 0; j < E_next; ++j) {
+  for (int j = tid; j < E_next; j += kScoreThreads) {
     const int r = expert_rank_next[j];
     if (r < 0 || r >= G) {
       bad = 1;
       continue;
     }
-    if (r == lane) acc += X[static_cast<int64_t>(i) * E_next + j];
+    const long long v = X[static_cast<int64_t>(i) * E_next + j];
+    atomicAdd(&sums[r], static_cast<unsigned long long>(v));
   }
-  if (lane < G) M[static_cast<int64_t>(i) * G + lane] = acc;
+  __syncthreads();
+  if (tid < G) M[static_cast<int64_t>(i) * G + tid] = static_cast<int64_t>(sums[tid]);
   if (i == 0) {
-    if (lane == 0 && bad) report(d_err, MOE_DERR_RANK_RANGE);
-    if (lane < G) {
-      identity[lane] = lane;
-      src1[lane] = lane == 0 ? 0 : T;
+    if (bad) report(d_err, MOE_DERR_RANK_RANGE);
+    if (tid < G) {
+      identity[tid] = tid;
+      src1[tid] = tid == 0 ? 0 : T;
     }
-    if (lane == 0) src1[G] = T;
+    if (tid == 0) src1[G] = T;
   }
 }
 
@@ -118,12 +125,6 @@ __global__ __launch_bounds__(kPredThreads) void predict_kernel(
   report(d_err, errbits);
 }
 
-__global__ void copy_offsets_kernel(const int32_t* __restrict__ send_offsets, int G,
-                                    int32_t* __restrict__ shard_offsets) {
-  const int r = threadIdx.x;
-  if (r <= G) shard_offsets[r] = send_offsets[r];
-}
-
 }  // namespace
 }  // namespace moe
 
@@ -154,7 +155,7 @@ extern "C" int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Ti = static_cast<int>(T);
 
-  moe::rank_score_kernel<<<E, moe::kWave, 0, s>>>(transition, E_next, expert_rank_next, G, Ti,
+  moe::rank_score_kernel<<<E, moe::kScoreThreads, 0, s>>>(transition, E_next, expert_rank_next, G, Ti,
                                                   w.M, w.identity, w.src1, d_err);
   MOE_CHECK_LAUNCH();
   if (Ti > 0) {
@@ -166,10 +167,7 @@ extern "C" int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E,
                   G,              w.identity,     G,         G,
                   w.src1,         T,              w.send_counts, w.send_offsets,
                   perm ? perm : w.perm_scratch,   nullptr,   dest_pos,
-                  nullptr,        w.counters,     d_err,     w.plan_ws};
-  int st = moe::launch_plan(a, s);
-  if (st != MOE_OK) return st;
-  moe::copy_offsets_kernel<<<1, moe::kWave * 2, 0, s>>>(w.send_offsets, G, shard_offsets);
-  MOE_CHECK_LAUNCH();
-  return MOE_OK;
+                  nullptr,        w.counters,     d_err,     w.plan_ws,
+                  shard_offsets};
+  return moe::launch_plan(a, s);
 }

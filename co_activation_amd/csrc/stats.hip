@@ -25,10 +25,28 @@ constexpr int kTokensPerBlock = 1024;
 
 enum StatMode { kCounts = 0, kPairs = 1, kTransitions = 2 };
 
-__global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[i] = 0;
+// Work of one statistics call, split into histogram slices of matrix rows:
+// slices [0, a_slices) belong to matrix A (per-expert counts, or the pair
+// matrix counted on and above its diagonal), slices [a_slices, a_slices +
+// b_slices) to the transition matrix B.
+struct StatsJob {
+  int a_mode;  // kCounts or kPairs
+  int a_rows, a_cols, a_rps, a_slices;
+  int32_t* a_out;
+  int b_rows, b_cols, b_rps, b_slices;
+  int32_t* b_out;
+};
+
+// Zeroes the output arrays the count pass accumulates into.
+__global__ void zero_kernel(int32_t* __restrict__ a, int64_t na, int32_t* __restrict__ b, int64_t nb) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < na + nb;
+       i += stride) {
+    if (i < na)
+      a[i] = 0;
+    else
+      b[i - na] = 0;
+  }
 }
 
 // Reads one token's ids into e[]; out-of-range slots become -1.
@@ -52,16 +70,18 @@ __device__ __forceinline__ int load_ids(const int32_t* __restrict__ row, int k, 
   return err;
 }
 
-// MODE kCounts: bins = experts.  kPairs: bins = (i, j), i <= j, rows of the
-// slice.  kTransitions: bins = (i in this layer, j in the next layer).
-template <int MODE>
 __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int32_t* __restrict__ topk2,
-    int k2, int E2, int ncols, int rows_per_slice, int nrows, int tokens_per_block,
-    int32_t* __restrict__ out, int32_t* d_err, int report_errors) {
+    int k2, int E2, StatsJob job, int tokens_per_block, int32_t* d_err) {
   __shared__ int hist[kHistBins];
-  const int r0 = blockIdx.y * rows_per_slice;
-  const int r1 = min(r0 + rows_per_slice, nrows);
+  const int slice = blockIdx.y;
+  const bool in_a = slice < job.a_slices;
+  const int mode = in_a ? job.a_mode : kTransitions;
+  const int rps = in_a ? job.a_rps : job.b_rps;
+  const int nrows = in_a ? job.a_rows : job.b_rows;
+  const int ncols = in_a ? job.a_cols : job.b_cols;
+  const int r0 = (in_a ? slice : slice - job.a_slices) * rps;
+  const int r1 = min(r0 + rps, nrows);
   const int slice_bins = (r1 - r0) * ncols;
   for (int i = threadIdx.x; i < slice_bins; i += kStatThreads) hist[i] = 0;
   __syncthreads();
@@ -72,11 +92,11 @@ __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
   for (int t = tb0 + static_cast<int>(threadIdx.x); t < tb1; t += kStatThreads) {
     int e[MOE_MAX_K];
     errbits |= load_ids(topk + static_cast<int64_t>(t) * k, k, E, e);
-    if constexpr (MODE == kCounts) {
+    if (mode == kCounts) {
 #pragma unroll
       for (int a = 0; a < MOE_MAX_K; ++a)
         if (a < k && e[a] >= 0) atomicAdd(&hist[e[a]], 1);
-    } else if constexpr (MODE == kPairs) {
+    } else if (mode == kPairs) {
 #pragma unroll
       for (int a = 0; a < MOE_MAX_K; ++a) {
         if (a >= k || e[a] < 0) continue;
@@ -99,9 +119,10 @@ __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
       }
     }
   }
-  if (report_errors && blockIdx.y == 0) report(d_err, errbits);
+  // One slice of each matrix reports the data errors it saw.
+  if (slice == 0 || slice == job.a_slices) report(d_err, errbits);
   __syncthreads();
-  int32_t* dst = out + static_cast<int64_t>(r0) * ncols;
+  int32_t* dst = (in_a ? job.a_out : job.b_out) + static_cast<int64_t>(r0) * ncols;
   for (int i = threadIdx.x; i < slice_bins; i += kStatThreads) {
     const int v = hist[i];
     if (v != 0) atomicAdd(dst + i, v);
@@ -127,28 +148,9 @@ __global__ void stats_finish_kernel(int E, int32_t* __restrict__ pair_count,
   }
 }
 
-int launch_fill(int32_t* p, int64_t n, hipStream_t s) {
-  if (n <= 0) return MOE_OK;
-  const int64_t blocks = (n + 255) / 256;
-  fill_zero_kernel<<<static_cast<unsigned>(blocks < 1024 ? blocks : 1024), 256, 0, s>>>(p, n);
-  MOE_CHECK_LAUNCH();
-  return MOE_OK;
-}
-
-template <int MODE>
-int launch_count(const int32_t* topk, int T, int k, int E, const int32_t* topk2, int k2, int E2,
-                 int32_t* out, int32_t* d_err, int report_errors, hipStream_t s) {
-  if (T == 0) return MOE_OK;
-  const int ncols = MODE == kCounts ? E : (MODE == kPairs ? E : E2);
-  const int nrows = MODE == kCounts ? 1 : E;
-  const int rows_per_slice = MODE == kCounts ? 1 : kHistBins / ncols;
-  const int slices = (nrows + rows_per_slice - 1) / rows_per_slice;
-  const int bx = (T + kTokensPerBlock - 1) / kTokensPerBlock;
-  stats_count_kernel<MODE><<<dim3(bx, slices), kStatThreads, 0, s>>>(
-      topk, T, k, E, topk2, k2, E2, ncols, rows_per_slice, nrows, kTokensPerBlock, out, d_err,
-      report_errors);
-  MOE_CHECK_LAUNCH();
-  return MOE_OK;
+unsigned grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return static_cast<unsigned>(b < 1 ? 1 : (b > 1024 ? 1024 : b));
 }
 
 }  // namespace
@@ -171,29 +173,45 @@ extern "C" int moe_coact_stats(const int32_t* topk, int64_t T, int k, int E,
   if (transition != nullptr && T > 0 && topk_next == nullptr) return MOE_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Ti = static_cast<int>(T);
-  int st;
+
+  moe::StatsJob job{};
   if (pair_count != nullptr) {
-    if ((st = moe::launch_fill(pair_count, static_cast<int64_t>(E) * E, s)) != MOE_OK) return st;
-    if ((st = moe::launch_count<moe::kPairs>(topk, Ti, k, E, nullptr, 0, 0, pair_count, d_err, 1,
-                                             s)) != MOE_OK)
-      return st;
-    const int64_t n = static_cast<int64_t>(E) * E;
-    const int64_t blocks = (n + 255) / 256;
-    moe::stats_finish_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(E, pair_count,
-                                                                           expert_count, ochiai);
-    MOE_CHECK_LAUNCH();
+    job.a_mode = moe::kPairs;
+    job.a_rows = E;
+    job.a_cols = E;
+    job.a_rps = moe::kHistBins / E;
+    job.a_out = pair_count;
   } else {
-    if ((st = moe::launch_fill(expert_count, E, s)) != MOE_OK) return st;
-    if ((st = moe::launch_count<moe::kCounts>(topk, Ti, k, E, nullptr, 0, 0, expert_count, d_err,
-                                              1, s)) != MOE_OK)
-      return st;
+    job.a_mode = moe::kCounts;
+    job.a_rows = 1;
+    job.a_cols = E;
+    job.a_rps = 1;
+    job.a_out = expert_count;
   }
+  job.a_slices = (job.a_rows + job.a_rps - 1) / job.a_rps;
+  const int64_t na = static_cast<int64_t>(job.a_rows) * job.a_cols;
+  int64_t nb = 0;
   if (transition != nullptr) {
-    if ((st = moe::launch_fill(transition, static_cast<int64_t>(E) * E_next, s)) != MOE_OK)
-      return st;
-    if ((st = moe::launch_count<moe::kTransitions>(topk, Ti, k, E, topk_next, k_next, E_next,
-                                                   transition, d_err, 1, s)) != MOE_OK)
-      return st;
+    job.b_rows = E;
+    job.b_cols = E_next;
+    job.b_rps = moe::kHistBins / E_next;
+    job.b_slices = (E + job.b_rps - 1) / job.b_rps;
+    job.b_out = transition;
+    nb = static_cast<int64_t>(E) * E_next;
+  }
+
+  moe::zero_kernel<<<moe::grid_for(na + nb), 256, 0, s>>>(job.a_out, na, job.b_out, nb);
+  MOE_CHECK_LAUNCH();
+  if (Ti > 0) {
+    const int bx = (Ti + moe::kTokensPerBlock - 1) / moe::kTokensPerBlock;
+    moe::stats_count_kernel<<<dim3(bx, job.a_slices + job.b_slices), moe::kStatThreads, 0, s>>>(
+        topk, Ti, k, E, topk_next, k_next, E_next, job, moe::kTokensPerBlock, d_err);
+    MOE_CHECK_LAUNCH();
+  }
+  if (pair_count != nullptr) {
+    moe::stats_finish_kernel<<<moe::grid_for(static_cast<int64_t>(E) * E), 256, 0, s>>>(
+        E, pair_count, expert_count, ochiai);
+    MOE_CHECK_LAUNCH();
   }
   return MOE_OK;
 }
