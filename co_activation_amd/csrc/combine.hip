@@ -6,10 +6,10 @@
 //   y[t] = sum_q a(row_q) * z[row_q],  q over the token's rows in order,
 //
 // fp32 fused multiply-adds in ascending q, one rounding to the output type
-// (bf16: round to nearest even).  A group of threads owns one token; the
-// token's row list and weights are uniform (scalar registers); each thread
-// owns groups of 8 (or 4 for fp32 -> fp32) consecutive elements, 16-byte
-// nontemporal loads and stores.
+// (bf16: round to nearest even).  A wave owns a chunk of one token's output
+// row; the token's row list and weights are uniform (scalar registers); each
+// lane owns groups of 8 (or 4 for fp32 -> fp32) consecutive elements,
+// 16-byte nontemporal loads and stores.
 // HBM-bound: algorithmic bytes per token are rows * (z row bytes + 4) +
 // y row bytes + 4 * k.
 #include "common.hpp"
@@ -72,19 +72,22 @@ __device__ __forceinline__ void store_group(u32x4* __restrict__ row, int64_t g, 
   }
 }
 
-// TPT threads own one token (TPT = 64: four tokens per 256-thread block;
-// larger TPT: one token per block); each thread handles kCombUnroll element
-// groups per pass, all of the token's rows for them, then stores.
-template <bool ZBF16, bool YBF16, int EPL, int TPT>
-__global__ __launch_bounds__(TPT < kCombThreads ? kCombThreads : TPT) void combine_kernel(
-    const u32x4* __restrict__ z, int64_t z_rows, int64_t groups, const int32_t* __restrict__ rows,
-    int k, const float* __restrict__ weight, int T, u32x4* __restrict__ y, int32_t* d_err) {
-  constexpr int kBlock = TPT < kCombThreads ? kCombThreads : TPT;
-  constexpr int kTokens = kBlock / TPT;
-  const int sub = kTokens == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / TPT);
-  const int t = blockIdx.x * kTokens + sub;
+// One wave per (token, chunk of kChunkGroups element groups): a row is split
+// into chunks of 2 groups per lane, and each chunk of each token is an
+// independent work item (four per 256-thread block).  The token's row list
+// and weights are read per wave into scalar registers.
+constexpr int kChunkGroups = kWave * kCombUnroll;
+
+template <bool ZBF16, bool YBF16, int EPL>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(
+    const u32x4* __restrict__ z, int64_t z_rows, int64_t groups, int chunks,
+    const int32_t* __restrict__ rows, int k, const float* __restrict__ weight, int T,
+    u32x4* __restrict__ y, int32_t* d_err) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * (kCombThreads / kWave) + wave_id();
+  const int t = static_cast<int>(item / chunks);
   if (t >= T) return;
-  const int l = kTokens == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x % TPT);
+  const int chunk = static_cast<int>(item - static_cast<int64_t>(t) * chunks);
+  const int lane = lane_id();
 
   // 16-byte vectors per row of z and of y.
   const int64_t zvec = groups * (ZBF16 ? EPL / 8 : EPL / 4);
@@ -110,62 +113,50 @@ __global__ __launch_bounds__(TPT < kCombThreads ? kCombThreads : TPT) void combi
       }
     }
   }
-  if (l == 0) report(d_err, errbits);
+  if (chunk == 0 && lane == 0) report(d_err, errbits);
 
   u32x4* yrow = y + static_cast<int64_t>(t) * yvec;
-  for (int64_t g0 = l; g0 < groups; g0 += TPT * kCombUnroll) {
-    float acc[kCombUnroll][EPL];
+  const int64_t g0 = static_cast<int64_t>(chunk) * kChunkGroups + lane;
+  float acc[kCombUnroll][EPL];
+#pragma unroll
+  for (int u = 0; u < kCombUnroll; ++u)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[u][i] = 0.f;
+#pragma unroll
+  for (int q = 0; q < MOE_MAX_K; ++q) {
+    if (q >= k) break;
+    if (rid[q] < 0) continue;
+    const u32x4* zrow = z + static_cast<int64_t>(rid[q]) * zvec;
+    float f[kCombUnroll][EPL];
+#pragma unroll
+    for (int u = 0; u < kCombUnroll; ++u) {
+      const int64_t g = g0 + u * kWave;
+      if (g < groups) load_group<ZBF16, EPL>(zrow, g, f[u]);
+    }
 #pragma unroll
     for (int u = 0; u < kCombUnroll; ++u)
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) acc[u][i] = 0.f;
+      for (int i = 0; i < EPL; ++i) acc[u][i] = __builtin_fmaf(a[q], f[u][i], acc[u][i]);
+  }
 #pragma unroll
-    for (int q = 0; q < MOE_MAX_K; ++q) {
-      if (q >= k) break;
-      if (rid[q] < 0) continue;
-      const u32x4* zrow = z + static_cast<int64_t>(rid[q]) * zvec;
-      float f[kCombUnroll][EPL];
-#pragma unroll
-      for (int u = 0; u < kCombUnroll; ++u) {
-        const int64_t g = g0 + u * TPT;
-        if (g < groups) load_group<ZBF16, EPL>(zrow, g, f[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kCombUnroll; ++u)
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) acc[u][i] = __builtin_fmaf(a[q], f[u][i], acc[u][i]);
-    }
-#pragma unroll
-    for (int u = 0; u < kCombUnroll; ++u) {
-      const int64_t g = g0 + u * TPT;
-      if (g < groups) store_group<YBF16, EPL>(yrow, g, acc[u]);
-    }
+  for (int u = 0; u < kCombUnroll; ++u) {
+    const int64_t g = g0 + u * kWave;
+    if (g < groups) store_group<YBF16, EPL>(yrow, g, acc[u]);
   }
 }
 
-template <bool ZBF16, bool YBF16, int EPL, int TPT>
-void launch_tpt(const void* z, int64_t z_rows, int64_t groups, const int32_t* rows, int k,
-                const float* w, int64_t T, void* y, int32_t* d_err, hipStream_t s) {
-  constexpr int kBlock = TPT < kCombThreads ? kCombThreads : TPT;
-  constexpr int kTokens = kBlock / TPT;
-  const unsigned blocks = static_cast<unsigned>((T + kTokens - 1) / kTokens);
-  combine_kernel<ZBF16, YBF16, EPL, TPT><<<blocks, kBlock, 0, s>>>(
-      static_cast<const u32x4*>(z), z_rows, groups, rows, k, w, static_cast<int>(T),
-      static_cast<u32x4*>(y), d_err);
-}
-
-// Launch shape by element groups per row, as measured on MI355X: a wave per
-// token below 256 groups, 256 threads up to 512 groups, 384 beyond.
 template <bool ZBF16, bool YBF16, int EPL>
 int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k, const float* w,
            int64_t T, void* y, int32_t* d_err, hipStream_t s) {
   const int64_t groups = H / EPL;
-  if (groups < 256)
-    launch_tpt<ZBF16, YBF16, EPL, 64>(z, z_rows, groups, rows, k, w, T, y, d_err, s);
-  else if (groups <= 512)
-    launch_tpt<ZBF16, YBF16, EPL, 256>(z, z_rows, groups, rows, k, w, T, y, d_err, s);
-  else
-    launch_tpt<ZBF16, YBF16, EPL, 384>(z, z_rows, groups, rows, k, w, T, y, d_err, s);
+  const int chunks = static_cast<int>((groups + kChunkGroups - 1) / kChunkGroups);
+  const int64_t items = T * chunks;
+  constexpr int kItemsPerBlock = kCombThreads / kWave;
+  const int64_t blocks = (items + kItemsPerBlock - 1) / kItemsPerBlock;
+  if (blocks > INT32_MAX) return MOE_ERR_SHAPE;
+  combine_kernel<ZBF16, YBF16, EPL><<<static_cast<unsigned>(blocks), kCombThreads, 0, s>>>(
+      static_cast<const u32x4*>(z), z_rows, groups, chunks, rows, k, w, static_cast<int>(T),
+      static_cast<u32x4*>(y), d_err);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
