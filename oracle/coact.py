@@ -437,3 +437,98 @@ def two_layer_pipeline(topk1: np.ndarray, topk2: np.ndarray, gates2: np.ndarray,
             "gates2_shuffled": gates2_s, "plan": plan, "send": send,
             "local_share_before": plan_before["counters"][3] / (T * k2),
             "local_share_after": plan["counters"][3] / (T * k2)}
+
+
+# ------------------------------------------------ destination-side expansion
+
+def expert_plan(topk: np.ndarray, gates: Optional[np.ndarray], expert_rank: np.ndarray, G: int,
+                slot_row: np.ndarray, n_send_rows: int) -> dict:
+    """Per-expert grouped layout on the destination side.
+
+    Every assignment (t, j) -- token t, slot j, expert e = D_t[j], rank
+    r = p(e) -- gets one expert row.  Reading: rows are ordered by
+    (rank r, expert e, token t), i.e. each rank's received tokens expanded
+    into one contiguous block per local expert (ascending expert id), tokens
+    ascending inside a block -- the layout a grouped expert GEMM consumes
+    ([CE] training stack: grouped GEMM after the alltoall dispatch; footnote
+    3: the routed probabilities travel with the rows, so each expert row
+    carries its gate).
+
+    Outputs: erow [T, k] (expert row of each slot), expert_first[e] and
+    expert_count[e], rank_offsets [G+1], erow_weight / erow_slot per expert
+    row (gate and t*k + j), and row_dest [n_send_rows, k]: for send row
+    (t, r), the expert rows of t's slots on r in ascending slot order, then -1.
+    """
+    topk = np.asarray(topk)
+    expert_rank = np.asarray(expert_rank)
+    T, k = topk.shape
+    E = expert_rank.shape[0]
+    validate_routing(topk, E)
+    validate_placement(expert_rank, E, G)
+    keys = sorted((int(expert_rank[int(topk[t, j])]), int(topk[t, j]), t, j)
+                  for t in range(T) for j in range(k))
+    erow = np.full((T, k), -1, dtype=np.int64)
+    erow_weight = np.zeros(T * k, dtype=np.float32)
+    erow_slot = np.full(T * k, -1, dtype=np.int64)
+    for i, (r, e, t, j) in enumerate(keys):
+        erow[t, j] = i
+        erow_slot[i] = t * k + j
+        if gates is not None:
+            erow_weight[i] = np.float32(gates[t, j])
+    expert_count = np.zeros(E, dtype=np.int64)
+    for (r, e, t, j) in keys:
+        expert_count[e] += 1
+    expert_first = np.zeros(E, dtype=np.int64)
+    rank_offsets = np.zeros(G + 1, dtype=np.int64)
+    pos = 0
+    for r in range(G):
+        rank_offsets[r] = pos
+        for e in range(E):
+            if int(expert_rank[e]) == r:
+                expert_first[e] = pos
+                pos += int(expert_count[e])
+    rank_offsets[G] = pos
+    row_dest = np.full((n_send_rows, k), -1, dtype=np.int64)
+    for t in range(T):
+        used = {}
+        for j in range(k):
+            i = int(slot_row[t, j])
+            q = used.get(i, 0)
+            row_dest[i, q] = erow[t, j]
+            used[i] = q + 1
+    return {"erow": erow, "expert_first": expert_first, "expert_count": expert_count,
+            "rank_offsets": rank_offsets, "erow_weight": erow_weight, "erow_slot": erow_slot,
+            "row_dest": row_dest}
+
+
+def partial_combine(Y: np.ndarray, y_dtype: str, erow: np.ndarray, gates: np.ndarray,
+                    slot_row: np.ndarray, n_send_rows: int, out_dtype: str) -> np.ndarray:
+    """The expert side's reply rows: for send row (t, r),
+    Z[(t, r)] = sum_{j : p(D_t[j]) = r} w_tj * Y[erow(t, j)]
+    (the expert outputs of t on rank r, weighted by their gates), summed in
+    float64 and rounded once.  Rows no slot maps to stay zero."""
+    erow = np.asarray(erow, dtype=np.int64)
+    slot_row = np.asarray(slot_row, dtype=np.int64)
+    T, k = erow.shape
+    Yf = _as_f64(Y, y_dtype)
+    Z = np.zeros((n_send_rows, Yf.shape[1]), dtype=np.float64)
+    for t in range(T):
+        for j in range(k):
+            Z[slot_row[t, j]] += float(np.float32(gates[t, j])) * Yf[erow[t, j]]
+    Z32 = Z.astype(np.float32)
+    return bf16_round(Z32) if out_dtype == "bf16" else Z32
+
+
+def moe_output(x: np.ndarray, x_dtype: str, topk: np.ndarray, gates: np.ndarray,
+               expert_scale: np.ndarray) -> np.ndarray:
+    """Plain MoE layer output for experts that scale their input row by a
+    per-expert constant: y_t = sum_j w_tj * c_{D_t[j]} * x_t, in float64.
+    The reference the dispatched path must reproduce (routing and expert
+    parameters are untouched by the dispatch, [EC] abstract)."""
+    xf = _as_f64(x, x_dtype)
+    T, k = topk.shape
+    y = np.zeros_like(xf)
+    for t in range(T):
+        for j in range(k):
+            y[t] += float(np.float32(gates[t, j])) * float(expert_scale[int(topk[t, j])]) * xf[t]
+    return y

@@ -446,3 +446,97 @@ def test_two_layer_shuffle_raises_local_share():
     assert np.array_equal(res["topk2_shuffled"], w.topk2[perm])
     assert np.array_equal(res["x_shuffled"], w.x[perm])
     assert sorted(perm.tolist()) == list(range(w.T))
+
+
+# ------------------------------------------------------------ expert side
+
+def test_expert_plan_hand_example():
+    """p = [0, 0, 1, 1]; token 0 picks experts 1, 2 and token 1 picks 0, 1.
+    Rows in (rank, expert, token) order: (e0,t1) (e1,t0) (e1,t1) (e2,t0)."""
+    topk = np.array([[1, 2], [0, 1]], np.int32)
+    gates = np.array([[0.75, 0.25], [0.5, 0.5]], np.float32)
+    er = np.array([0, 0, 1, 1], np.int32)
+    plan = oracle.dispatch_plan(topk, gates, er, 2, 2)
+    ep = oracle.expert_plan(topk, gates, er, 2, plan["slot_row"], plan["N"])
+    assert ep["erow"].tolist() == [[1, 3], [0, 2]]
+    assert ep["expert_count"].tolist() == [1, 2, 1, 0]
+    assert ep["expert_first"].tolist() == [0, 1, 3, 4]
+    assert ep["rank_offsets"].tolist() == [0, 3, 4]
+    assert ep["erow_slot"].tolist() == [2, 0, 3, 1]
+    assert ep["erow_weight"].tolist() == [0.5, 0.75, 0.5, 0.25]
+
+
+def test_expert_plan_bruteforce_and_counts():
+    """erow(t, j) = number of slots whose (rank, expert, token) key is
+    smaller, counted directly; per-expert counts match the statistics."""
+    rng = np.random.default_rng(20)
+    for trial in range(40):
+        T = int(rng.integers(1, 30))
+        E = int(rng.integers(2, 9))
+        k = int(rng.integers(1, E + 1))
+        G = int(rng.integers(1, 5))
+        topk = _random_routing(rng, T, E, k)
+        gates = _random_gates(rng, T, k)
+        er = rng.integers(0, G, size=E).astype(np.int32)
+        plan = oracle.dispatch_plan(topk, gates, er, G, 1, src_offsets=[0] * G + [T])
+        ep = oracle.expert_plan(topk, gates, er, G, plan["slot_row"], plan["N"])
+        keys = [(int(er[topk[t, j]]), int(topk[t, j]), t) for t in range(T) for j in range(k)]
+        for t in range(T):
+            for j in range(k):
+                me = (int(er[topk[t, j]]), int(topk[t, j]), t)
+                assert ep["erow"][t, j] == sum(1 for q in keys if q < me)
+        st = oracle.coact_stats(topk, E)
+        assert (ep["expert_count"] == st["expert_count"]).all()
+        for r in range(G):
+            assert ep["rank_offsets"][r + 1] - ep["rank_offsets"][r] == \
+                sum(int(st["expert_count"][e]) for e in range(E) if er[e] == r)
+        # each send row lists exactly the expert rows of its token's slots on its rank
+        for t in range(T):
+            for j in range(k):
+                i = plan["slot_row"][t, j]
+                on_r = [ep["erow"][t, jj] for jj in range(k) if plan["slot_row"][t, jj] == i]
+                assert ep["row_dest"][i].tolist() == on_r + [-1] * (k - len(on_r))
+
+
+def test_expert_side_reproduces_moe_output():
+    """Dispatch, expansion, experts that scale their rows, partial combine
+    (rounded to bf16 as a reply row) and the unweighted combine give the
+    plain MoE output sum_j w_tj c_e x_t within the two bf16 roundings."""
+    w = make(3, T=640, H=32)
+    rng = np.random.default_rng(21)
+    c = rng.uniform(0.5, 2.0, size=w.E)
+    plan = oracle.dispatch_plan(w.topk, w.gates, w.expert_rank, w.G, w.ranks_per_node)
+    N = plan["N"]
+    ep = oracle.expert_plan(w.topk, w.gates, w.expert_rank, w.G, plan["slot_row"], N)
+    send = oracle.permute_rows(w.x, plan["row_token"])
+    # expansion: expert row i is a copy of the send row its slot points to
+    erows = np.zeros((w.T * w.k, w.H), np.uint16)
+    for i in range(N):
+        for q in range(w.k):
+            if ep["row_dest"][i, q] >= 0:
+                erows[ep["row_dest"][i, q]] = send[i]
+    tok = ep["erow_slot"] // w.k
+    assert np.array_equal(erows, w.x[tok])
+    # experts: scale each row by its expert's constant (float32, rounded to bf16)
+    e_of_row = w.topk.reshape(-1)[ep["erow_slot"]]
+    Y = oracle.bf16_round((oracle.bf16_to_f32(erows) * c[e_of_row][:, None]).astype(np.float32))
+    Z = oracle.partial_combine(Y, "bf16", ep["erow"], w.gates, plan["slot_row"], N, "bf16")
+    y = oracle.combine_unweighted(Z, "bf16", plan["token_rows"], "f32")
+    ref = oracle.moe_output(w.x, "bf16", w.topk, w.gates, c)
+    scale = np.zeros_like(ref)
+    xf = oracle.bf16_to_f32(w.x).astype(np.float64)
+    for j in range(w.k):
+        scale += np.abs(w.gates[:, j:j + 1]) * c[w.topk[:, j]][:, None] * np.abs(xf)
+    assert (np.abs(y - ref) <= 2.0 ** -7 * scale + 1e-30).all()
+
+
+def test_moe_output_special_cases():
+    """Unit experts with gates summing to 1 return x; one slot returns w*c*x."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((50, 8)).astype(np.float32)
+    topk = _random_routing(rng, 50, 6, 3)
+    gates = _random_gates(rng, 50, 3)
+    y = oracle.moe_output(x, "f32", topk, gates, np.ones(6))
+    assert np.allclose(y, x, rtol=1e-6, atol=1e-7)
+    y1 = oracle.moe_output(x, "f32", topk[:, :1], gates[:, :1], np.full(6, 3.0))
+    assert np.allclose(y1, 3.0 * gates[:, :1].astype(np.float64) * x, rtol=1e-12)
