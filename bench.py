@@ -35,6 +35,7 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--no-expert-side", action="store_true")
     return ap.parse_args()
 
 
@@ -68,6 +69,40 @@ def counter_traffic(workload: int, stage: str):
             return None
     k = rec["kernels"].get(stage)
     return None if k is None else k["read_bytes"] + k["write_bytes"]
+
+
+def expert_side(step, w, steps: int, device_normal) -> dict:
+    """Destination side after the step's dispatch (outside the timed step):
+    expert layout, expansion of the received rows into expert rows, reply
+    rows from stand-in expert outputs, and the reply combine.  Per-kernel
+    times from HIP events, with algorithmic bytes."""
+    import torch
+
+    from co_activation_amd.pipeline import ExpertSideStep, StageTimers
+
+    side = ExpertSideStep(step)
+    y_expert = device_normal(side.T * side.k, w.H, w.dtype, seed=2)
+    side.dispatch()
+    side.reply_and_combine(y_expert)
+    torch.cuda.synchronize()
+    timers = StageTimers(side.STAGES, steps)
+    for _ in range(steps):
+        side.dispatch(timers)
+        side.reply_and_combine(y_expert, timers)
+    torch.cuda.synchronize()
+    if int(side.d_err.item()) != 0:
+        return {"error": f"device data errors {int(side.d_err.item())}"}
+    ms = timers.mean_ms()
+    N = int(step.plan.counters[0].item())
+    TK, rb, T = side.T * side.k, w.row_bytes, side.T
+    bytes_ = {"expand": N * rb + TK * rb + 4 * N * side.k,
+              "partial_combine": TK * rb + 4 * TK + N * rb + 4 * N * side.k,
+              "reply_combine": N * rb + T * rb + 4 * T * side.k}
+    out = {"rows_expert": TK, "stage_us": {n: 1e3 * v for n, v in ms.items()}}
+    for n, b in bytes_.items():
+        out[f"{n}_gbps"] = b / (ms[n] * 1e-3) / 1e9
+        out[f"{n}_bytes"] = b
+    return out
 
 
 def cpu_baseline(w, sample_tokens: int) -> dict:
@@ -115,7 +150,7 @@ def main() -> int:
     import torch
 
     import co_activation_amd
-    from co_activation_amd.pipeline import LayerStep, StageTimers, TwoLayerStep
+    from co_activation_amd.pipeline import ExpertSideStep, LayerStep, StageTimers, TwoLayerStep
     from workloads import make
     from workloads.gen import device_normal
 
@@ -246,6 +281,8 @@ def main() -> int:
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic(w.cfg, dom)},
     }
+    if not args.no_expert_side:
+        line["expert_side"] = expert_side(step, w, args.steps, device_normal)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     print(json.dumps(line), flush=True)

@@ -33,6 +33,7 @@ EXPORTS = (
     "moe_status_string", "moe_coact_stats", "moe_dispatch_plan_workspace_size",
     "moe_dispatch_plan", "moe_permute", "moe_combine",
     "moe_shuffle_predict_workspace_size", "moe_shuffle_predict",
+    "moe_expert_plan_workspace_size", "moe_expert_plan",
 )
 
 _lib = None
@@ -49,15 +50,21 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.moe_dispatch_plan.argtypes = [P, P, c_int64, c_int, c_int, P, c_int, c_int, P, c_int64,
                                       P, P, P, P, P, P, P, P, P, c_size_t, P]
     lib.moe_dispatch_plan.restype = c_int
-    lib.moe_permute.argtypes = [P, c_int64, c_int64, P, c_int, P, c_int64, P, P]
+    lib.moe_permute.argtypes = [P, c_int64, c_int64, P, c_int, P, c_int64, P, P, P]
     lib.moe_permute.restype = c_int
-    lib.moe_combine.argtypes = [P, c_int, c_int64, c_int64, P, c_int, P, c_int64, P, c_int, P, P]
+    lib.moe_combine.argtypes = [P, c_int, c_int64, c_int64, P, c_int, P, c_int64, P, c_int, P, P,
+                                P]
     lib.moe_combine.restype = c_int
     lib.moe_shuffle_predict_workspace_size.argtypes = [c_int64, c_int, c_int, POINTER(c_size_t)]
     lib.moe_shuffle_predict_workspace_size.restype = c_int
     lib.moe_shuffle_predict.argtypes = [P, c_int64, c_int, c_int, P, c_int, P, c_int, P, P, P, P,
                                         P, P, c_size_t, P]
     lib.moe_shuffle_predict.restype = c_int
+    lib.moe_expert_plan_workspace_size.argtypes = [c_int64, c_int, POINTER(c_size_t)]
+    lib.moe_expert_plan_workspace_size.restype = c_int
+    lib.moe_expert_plan.argtypes = [P, P, c_int64, c_int, c_int, P, c_int, P, c_int64, P, P, P, P,
+                                    P, P, P, P, P, c_size_t, P]
+    lib.moe_expert_plan.restype = c_int
 
 
 def lib() -> ctypes.CDLL:

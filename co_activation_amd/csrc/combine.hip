@@ -82,10 +82,10 @@ template <bool ZBF16, bool YBF16, int EPL>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     const u32x4* __restrict__ z, int64_t z_rows, int64_t groups, int chunks,
     const int32_t* __restrict__ rows, int k, const float* __restrict__ weight, int T,
-    u32x4* __restrict__ y, int32_t* d_err) {
+    u32x4* __restrict__ y, const int32_t* __restrict__ n_valid, int32_t* d_err) {
   const int64_t item = static_cast<int64_t>(blockIdx.x) * (kCombThreads / kWave) + wave_id();
   const int t = static_cast<int>(item / chunks);
-  if (t >= T) return;
+  if (t >= T || (n_valid != nullptr && t >= *n_valid)) return;
   const int chunk = static_cast<int>(item - static_cast<int64_t>(t) * chunks);
   const int lane = lane_id();
 
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 
 template <bool ZBF16, bool YBF16, int EPL>
 int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k, const float* w,
-           int64_t T, void* y, int32_t* d_err, hipStream_t s) {
+           int64_t T, void* y, const int32_t* n_valid, int32_t* d_err, hipStream_t s) {
   const int64_t groups = H / EPL;
   const int chunks = static_cast<int>((groups + kChunkGroups - 1) / kChunkGroups);
   const int64_t items = T * chunks;
@@ -156,7 +156,7 @@ int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k,
   if (blocks > INT32_MAX) return MOE_ERR_SHAPE;
   combine_kernel<ZBF16, YBF16, EPL><<<static_cast<unsigned>(blocks), kCombThreads, 0, s>>>(
       static_cast<const u32x4*>(z), z_rows, groups, chunks, rows, k, w, static_cast<int>(T),
-      static_cast<u32x4*>(y), d_err);
+      static_cast<u32x4*>(y), n_valid, d_err);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -166,7 +166,8 @@ int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k,
 
 extern "C" int moe_combine(const void* z, int z_dtype, int64_t z_rows, int64_t H,
                            const int32_t* rows, int k, const float* row_weight, int64_t T,
-                           void* y, int y_dtype, int32_t* d_err, void* stream) {
+                           void* y, int y_dtype, const int32_t* n_valid, int32_t* d_err,
+                           void* stream) {
   if ((z_dtype != MOE_F32 && z_dtype != MOE_BF16) || (y_dtype != MOE_F32 && y_dtype != MOE_BF16))
     return MOE_ERR_DTYPE;
   if (T < 0 || H <= 0 || z_rows < 0 || k < 1 || k > MOE_MAX_K ||
@@ -180,10 +181,10 @@ extern "C" int moe_combine(const void* z, int z_dtype, int64_t z_rows, int64_t H
     return MOE_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (z_dtype == MOE_BF16 && y_dtype == MOE_BF16)
-    return moe::launch<true, true, 8>(z, z_rows, H, rows, k, row_weight, T, y, d_err, s);
+    return moe::launch<true, true, 8>(z, z_rows, H, rows, k, row_weight, T, y, n_valid, d_err, s);
   if (z_dtype == MOE_BF16 && y_dtype == MOE_F32)
-    return moe::launch<true, false, 8>(z, z_rows, H, rows, k, row_weight, T, y, d_err, s);
+    return moe::launch<true, false, 8>(z, z_rows, H, rows, k, row_weight, T, y, n_valid, d_err, s);
   if (z_dtype == MOE_F32 && y_dtype == MOE_BF16)
-    return moe::launch<false, true, 8>(z, z_rows, H, rows, k, row_weight, T, y, d_err, s);
-  return moe::launch<false, false, 4>(z, z_rows, H, rows, k, row_weight, T, y, d_err, s);
+    return moe::launch<false, true, 8>(z, z_rows, H, rows, k, row_weight, T, y, n_valid, d_err, s);
+  return moe::launch<false, false, 4>(z, z_rows, H, rows, k, row_weight, T, y, n_valid, d_err, s);
 }

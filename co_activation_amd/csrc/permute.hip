@@ -35,12 +35,13 @@ __device__ __forceinline__ V load_row(const V* p) {
 template <typename V, int TPT, int U, bool ONE>
 __global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void permute_kernel(
     const V* __restrict__ x, int T, int64_t vec_per_row, const int32_t* __restrict__ dest,
-    int width, V* __restrict__ out, int64_t out_rows, int32_t* d_err) {
+    int width, V* __restrict__ out, int64_t out_rows, const int32_t* __restrict__ n_valid,
+    int32_t* d_err) {
   constexpr int kBlock = TPT < kPermThreads ? kPermThreads : TPT;
   constexpr int kTokens = kBlock / TPT;
   const int sub = kTokens == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / TPT);
   const int t = blockIdx.x * kTokens + sub;
-  if (t >= T) return;
+  if (t >= T || (n_valid != nullptr && t >= *n_valid)) return;
   const int l = kTokens == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x % TPT);
 
   // Destination rows (uniform per token); -1 marks an absent or rejected one.
@@ -92,8 +93,9 @@ __global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void permu
 template <typename V>
 __global__ __launch_bounds__(kPermThreads) void permute_flat_kernel(
     const V* __restrict__ x, int T, int vec_per_row, const int32_t* __restrict__ dest, int width,
-    V* __restrict__ out, int64_t out_rows, int32_t* d_err) {
-  const int64_t n = static_cast<int64_t>(T) * vec_per_row;
+    V* __restrict__ out, int64_t out_rows, const int32_t* __restrict__ n_valid, int32_t* d_err) {
+  const int limit = n_valid != nullptr ? min(T, max(*n_valid, 0)) : T;
+  const int64_t n = static_cast<int64_t>(limit) * vec_per_row;
   int errbits = 0;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(kPermThreads) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kPermThreads) {
@@ -113,18 +115,19 @@ __global__ __launch_bounds__(kPermThreads) void permute_flat_kernel(
 
 template <typename V, int TPT, int U>
 void launch_rows(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
-                 void* out, int64_t out_rows, int32_t* d_err, hipStream_t s) {
+                 void* out, int64_t out_rows, const int32_t* n_valid, int32_t* d_err,
+                 hipStream_t s) {
   constexpr int kBlock = TPT < kPermThreads ? kPermThreads : TPT;
   constexpr int kTokens = kBlock / TPT;
   const unsigned blocks = static_cast<unsigned>((T + kTokens - 1) / kTokens);
   if (width == 1)
     permute_kernel<V, TPT, U, true><<<blocks, kBlock, 0, s>>>(
         static_cast<const V*>(x), T, vec_per_row, dest, width, static_cast<V*>(out), out_rows,
-        d_err);
+        n_valid, d_err);
   else
     permute_kernel<V, TPT, U, false><<<blocks, kBlock, 0, s>>>(
         static_cast<const V*>(x), T, vec_per_row, dest, width, static_cast<V*>(out), out_rows,
-        d_err);
+        n_valid, d_err);
 }
 
 // Launch shape by row size (vectors per row R), as measured on MI355X:
@@ -135,20 +138,21 @@ void launch_rows(const void* x, int T, int64_t vec_per_row, const int32_t* dest,
 //   otherwise              256 threads per token, one vector per pass
 template <typename V>
 int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
-                   void* out, int64_t out_rows, int32_t* d_err, hipStream_t s) {
+                   void* out, int64_t out_rows, const int32_t* n_valid, int32_t* d_err,
+                   hipStream_t s) {
   if (vec_per_row < kWave) {
     const int64_t n = static_cast<int64_t>(T) * vec_per_row;
     int64_t blocks = (n + kPermThreads - 1) / kPermThreads;
     if (blocks > 8192) blocks = 8192;
     permute_flat_kernel<V><<<static_cast<unsigned>(blocks), kPermThreads, 0, s>>>(
         static_cast<const V*>(x), T, static_cast<int>(vec_per_row), dest, width,
-        static_cast<V*>(out), out_rows, d_err);
+        static_cast<V*>(out), out_rows, n_valid, d_err);
   } else if (vec_per_row < 256) {
-    launch_rows<V, 64, 4>(x, T, vec_per_row, dest, width, out, out_rows, d_err, s);
+    launch_rows<V, 64, 4>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
   } else if (vec_per_row > 384 && vec_per_row <= 512 && width <= 2) {
-    launch_rows<V, 512, 1>(x, T, vec_per_row, dest, width, out, out_rows, d_err, s);
+    launch_rows<V, 512, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
   } else {
-    launch_rows<V, 256, 1>(x, T, vec_per_row, dest, width, out, out_rows, d_err, s);
+    launch_rows<V, 256, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
   }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
@@ -158,7 +162,8 @@ int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* des
 }  // namespace moe
 
 extern "C" int moe_permute(const void* x, int64_t T, int64_t row_bytes, const int32_t* dest,
-                           int width, void* out, int64_t out_rows, int32_t* d_err, void* stream) {
+                           int width, void* out, int64_t out_rows, const int32_t* n_valid,
+                           int32_t* d_err, void* stream) {
   if (T < 0 || row_bytes <= 0 || width < 1 || width > MOE_MAX_K || out_rows < 0 ||
       T * static_cast<int64_t>(width) >= (int64_t{1} << 31))
     return MOE_ERR_SHAPE;
@@ -169,7 +174,7 @@ extern "C" int moe_permute(const void* x, int64_t T, int64_t row_bytes, const in
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0)
     return moe::launch_permute<moe::u32x4>(x, static_cast<int>(T), row_bytes / 16, dest, width,
-                                           out, out_rows, d_err, s);
+                                           out, out_rows, n_valid, d_err, s);
   return moe::launch_permute<uint32_t>(x, static_cast<int>(T), row_bytes / 4, dest, width, out,
-                                       out_rows, d_err, s);
+                                       out_rows, n_valid, d_err, s);
 }

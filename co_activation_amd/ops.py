@@ -151,9 +151,11 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
 # ----------------------------------------------------------------- permute
 
 def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
-            out: Optional[torch.Tensor] = None, d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, n_valid: Optional[torch.Tensor] = None,
+            d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
     """moe_permute: out[dest[t, q]] = x[t] (bit copy).  dest is [T, width] or
-    [T] int32; out has out_rows rows shaped like x's rows."""
+    [T] int32; out has out_rows rows shaped like x's rows; n_valid (an int32
+    device element, e.g. a plan's row count) limits the tokens moved."""
     _want(x, "x")
     _want(dest, "dest", torch.int32)
     T = x.shape[0]
@@ -167,8 +169,10 @@ def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
     _want(out, "out", x.dtype)
     if tuple(out.shape[1:]) != row_shape or out.shape[0] < out_rows:
         raise ValueError("out rows must match x rows")
-    st = _lib.lib().moe_permute(_p(x), T, row_bytes, _p(dest), width, _p(out), out_rows, _p(d_err),
-                                _stream())
+    if n_valid is not None:
+        _want(n_valid, "n_valid", torch.int32)
+    st = _lib.lib().moe_permute(_p(x), T, row_bytes, _p(dest), width, _p(out), out_rows,
+                                _p(n_valid), _p(d_err), _stream())
     check("moe_permute", st)
     return out
 
@@ -177,6 +181,7 @@ def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
 
 def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tensor] = None, *,
             out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+            n_valid: Optional[torch.Tensor] = None,
             d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
     """moe_combine: y[t] = sum_q a(rows[t,q]) z[rows[t,q]], a = row_weight or 1."""
     _want(z, "z")
@@ -191,8 +196,10 @@ def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tens
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=z.device)
     _want(out, "out", out_dtype, (T, H))
+    if n_valid is not None:
+        _want(n_valid, "n_valid", torch.int32)
     st = _lib.lib().moe_combine(_p(z), _DT[z.dtype], z.shape[0], H, _p(rows), k, _p(row_weight),
-                                T, _p(out), _DT[out_dtype], _p(d_err), _stream())
+                                T, _p(out), _DT[out_dtype], _p(n_valid), _p(d_err), _stream())
     check("moe_combine", st)
     return out
 
@@ -233,4 +240,50 @@ def shuffle_predict(topk: torch.Tensor, transition: torch.Tensor, expert_rank_ne
         _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(d_err), _p(ws),
         ws.numel(), _stream())
     check("moe_shuffle_predict", st)
+    return res
+
+
+# ----------------------------------------------------------------- expert side
+
+def expert_workspace_bytes(T: int, E: int) -> int:
+    n = ctypes.c_size_t()
+    check("moe_expert_plan_workspace_size",
+          _lib.lib().moe_expert_plan_workspace_size(T, E, ctypes.byref(n)))
+    return n.value
+
+
+def expert_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank: torch.Tensor,
+                G: int, slot_row: torch.Tensor, send_rows: int, *, with_slots: bool = True,
+                out: Optional[dict] = None, ws: Optional[torch.Tensor] = None,
+                d_err: Optional[torch.Tensor] = None) -> dict:
+    """moe_expert_plan: erow [T,k], expert_first [E], expert_count [E],
+    rank_offsets [G+1], erow_weight [T*k], erow_slot [T*k], row_dest
+    [send_rows, k]."""
+    _want(topk, "topk", torch.int32)
+    T, k = topk.shape
+    E = expert_rank.numel()
+    _want(expert_rank, "expert_rank", torch.int32, (E,))
+    _want(slot_row, "slot_row", torch.int32, (T, k))
+    if gates is not None:
+        _want(gates, "gates", torch.float32, (T, k))
+    dev = topk.device
+    res = {
+        "erow": _alloc(out, "erow", (T, k), torch.int32, dev),
+        "expert_first": _alloc(out, "expert_first", (E,), torch.int32, dev),
+        "expert_count": _alloc(out, "expert_count", (E,), torch.int32, dev),
+        "rank_offsets": _alloc(out, "rank_offsets", (G + 1,), torch.int32, dev),
+        "erow_weight": _alloc(out, "erow_weight", (T * k,), torch.float32, dev),
+        "erow_slot": _alloc(out, "erow_slot", (T * k,), torch.int32, dev) if with_slots else None,
+        "row_dest": _alloc(out, "row_dest", (send_rows, k), torch.int32, dev),
+    }
+    need = expert_workspace_bytes(T, E)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _want(ws, "ws", torch.uint8)
+    st = _lib.lib().moe_expert_plan(
+        _p(topk), _p(gates), T, k, E, _p(expert_rank), G, _p(slot_row), send_rows, _p(res["erow"]),
+        _p(res["expert_first"]), _p(res["expert_count"]), _p(res["rank_offsets"]),
+        _p(res["erow_weight"]), _p(res["erow_slot"]), _p(res["row_dest"]), _p(d_err), _p(ws),
+        ws.numel(), _stream())
+    check("moe_expert_plan", st)
     return res

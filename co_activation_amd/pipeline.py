@@ -239,3 +239,73 @@ class TwoLayerStep:
             ops.combine(self.z, self.plan.token_rows, self.plan.row_weight, out=self.y,
                         d_err=self.d_err)
         return self
+
+
+class ExpertSideStep:
+    """Destination side of a dispatched layer: the per-expert layout, the
+    expansion of received rows into expert rows, and, once the experts have
+    produced their rows, the gate-weighted reply rows per (token, rank) and
+    the unweighted combine of the replies back to token order.
+
+    ``layer`` is a LayerStep (or TwoLayerStep) that has run; its plan's row
+    count stays on the device (``send_offsets[G*G]``), so nothing here waits
+    on the host.  The expert computation itself is not part of this path:
+    ``run`` takes the expert outputs ``expert_out`` [T*k, H] as an input (a
+    stand-in buffer in the benchmark, scaling experts in the tests)."""
+
+    STAGES = ("expert_plan", "expand", "partial_combine", "reply_combine")
+
+    def __init__(self, layer):
+        self.layer = layer
+        topk = layer.topk if hasattr(layer, "topk") else layer.topk2_s
+        self.topk = topk
+        self.gates = layer.gates if hasattr(layer, "gates") else layer.gates2_s
+        self.expert_rank = layer.expert_rank if hasattr(layer, "expert_rank") else layer.expert_rank2
+        dev = topk.device
+        self.T, self.k = topk.shape
+        self.E = self.expert_rank.numel()
+        self.G = layer.G
+        self.cap = layer.cap
+        H = layer.send.shape[1]
+        self.out = {
+            "erow": torch.empty(self.T, self.k, dtype=torch.int32, device=dev),
+            "expert_first": torch.empty(self.E, dtype=torch.int32, device=dev),
+            "expert_count": torch.empty(self.E, dtype=torch.int32, device=dev),
+            "rank_offsets": torch.empty(self.G + 1, dtype=torch.int32, device=dev),
+            "erow_weight": torch.empty(self.T * self.k, dtype=torch.float32, device=dev),
+            "erow_slot": torch.empty(self.T * self.k, dtype=torch.int32, device=dev),
+            "row_dest": torch.empty(self.cap, self.k, dtype=torch.int32, device=dev),
+        }
+        self.ws = torch.empty(ops.expert_workspace_bytes(self.T, self.E), dtype=torch.uint8,
+                              device=dev)
+        self.expert_in = torch.empty(self.T * self.k, H, dtype=layer.send.dtype, device=dev)
+        self.reply = torch.empty(self.cap, H, dtype=layer.send.dtype, device=dev)
+        self.y = torch.empty(self.T, H, dtype=layer.send.dtype, device=dev)
+        self.d_err = layer.d_err
+        self.plan = None
+
+    def n_rows(self):
+        """The dispatch plan's row count, as a device int32 element."""
+        so = self.layer.plan.send_offsets
+        return so[so.numel() - 1:]
+
+    def dispatch(self, timers: Optional[StageTimers] = None):
+        """Expert layout and expansion of the received rows."""
+        lp = self.layer.plan
+        with _timed(timers, "expert_plan"):
+            self.plan = ops.expert_plan(self.topk, self.gates, self.expert_rank, self.G,
+                                        lp.slot_row, self.cap, out=self.out, ws=self.ws,
+                                        d_err=self.d_err)
+        with _timed(timers, "expand"):
+            ops.permute(self.layer.send, self.plan["row_dest"], self.T * self.k,
+                        out=self.expert_in, n_valid=self.n_rows(), d_err=self.d_err)
+        return self
+
+    def reply_and_combine(self, expert_out, timers: Optional[StageTimers] = None):
+        """Reply rows from the expert outputs, then the token-order output."""
+        with _timed(timers, "partial_combine"):
+            ops.combine(expert_out, self.plan["row_dest"], self.plan["erow_weight"],
+                        out=self.reply, n_valid=self.n_rows(), d_err=self.d_err)
+        with _timed(timers, "reply_combine"):
+            ops.combine(self.reply, self.layer.plan.token_rows, None, out=self.y, d_err=self.d_err)
+        return self

@@ -10,7 +10,8 @@
  *   3. permutes token rows into rank-contiguous send buffers,
  *   4. combines the returned rows back to token order with the gate weights,
  *   5. predicts each token's next-layer rank and orders tokens by it (token
- *      shuffling).
+ *      shuffling),
+ *   6. lays the received rows out per expert on the destination side.
  * The ranks of the expert-parallel group are logical: each (source rank,
  * destination rank) block of the send buffer stands for one all-to-all
  * message.
@@ -165,13 +166,17 @@ int moe_dispatch_plan(const int32_t* topk, const float* gates, int64_t T, int k,
  *   dest       [T*width] int32: destination rows (-1 = none), e.g. a plan's
  *              token_rows (width = k) or a shuffle's dest_pos (width = 1)
  *   out        [out_rows * row_bytes] bytes; rows nobody targets are untouched
+ *   n_valid    int32 device word or NULL: when set, only tokens
+ *              t < min(T, *n_valid) are moved (e.g. a plan's row count, read
+ *              on the device so the host need not wait for it)
  * row_bytes must be a positive multiple of 4 and x, out 4-byte aligned; rows
  * that are multiples of 16 bytes with 16-byte aligned buffers take the wide
  * path.  width in 1..8.
  * d_err bits: ROW_RANGE (dest >= out_rows; that copy is skipped).
  * ---------------------------------------------------------------------- */
 int moe_permute(const void* x, int64_t T, int64_t row_bytes, const int32_t* dest, int width,
-                void* out, int64_t out_rows, int32_t* d_err, void* stream);
+                void* out, int64_t out_rows, const int32_t* n_valid, int32_t* d_err,
+                void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- weighted combine back to token order (the hidden-state
@@ -184,13 +189,15 @@ int moe_permute(const void* x, int64_t T, int64_t row_bytes, const int32_t* dest
  *   z        [z_rows * H] of z_dtype (MOE_F32 or MOE_BF16)
  *   rows     [T*k] int32, e.g. a plan's token_rows
  *   y        [T * H] of y_dtype
+ *   n_valid  int32 device word or NULL: when set, only outputs
+ *            t < min(T, *n_valid) are written (the rest are untouched)
  * H * sizeof(z_dtype) and H * sizeof(y_dtype) must be multiples of 16 bytes,
  * z and y 16-byte aligned.  k in 1..8.
  * d_err bits: ROW_RANGE (row >= z_rows; that term is skipped).
  * ---------------------------------------------------------------------- */
 int moe_combine(const void* z, int z_dtype, int64_t z_rows, int64_t H, const int32_t* rows,
                 int k, const float* row_weight, int64_t T, void* y, int y_dtype,
-                int32_t* d_err, void* stream);
+                const int32_t* n_valid, int32_t* d_err, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_shuffle_predict -- token shuffling ([EC] abstract: move each token to
@@ -219,6 +226,45 @@ int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E, const int3
                         int E_next, const int32_t* expert_rank_next, int G, int32_t* pred_rank,
                         int32_t* dest_pos, int32_t* perm, int32_t* shard_offsets,
                         int32_t* d_err, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_expert_plan -- destination-side layout for the expert computation.
+ *
+ * Every assignment (t, j) -- expert e = D_t[j] on rank r = expert_rank[e] --
+ * gets one expert row; rows are ordered by (r, e, t), so each rank's
+ * received tokens expand into one contiguous block per local expert
+ * (ascending expert id), the layout a grouped expert GEMM consumes
+ * ("Training Communication-Efficient Mixture-of-Experts Language Models with
+ * Layer Re-Configuration": alltoall dispatch, grouped GEMM; footnote 3: the
+ * routed probabilities travel with the rows).
+ *
+ *   topk, gates, T, k, E, expert_rank, G   as for moe_dispatch_plan
+ *   slot_row      [T*k] int32: the dispatch plan's row of each slot
+ *   send_rows     rows of row_dest (the send buffer's capacity)
+ *   erow          [T*k] int32 out: expert row of each slot (-1 if skipped)
+ *   expert_first  [E] int32 out: first expert row of expert e
+ *   expert_count  [E] int32 out: rows of expert e
+ *   rank_offsets  [G+1] int32 out: first expert row of each rank
+ *   erow_weight   [T*k] float out or NULL: the gate carried by each expert row
+ *   erow_slot     [T*k] int32 out or NULL: t*k + j of each expert row
+ *   row_dest      [send_rows*k] int32 out: for send row (t, r), the expert
+ *                 rows of t's slots on r in ascending slot order, then -1
+ *                 (all -1 for rows no slot maps to)
+ *   ws, ws_bytes  workspace of moe_expert_plan_workspace_size() bytes
+ * With these, moe_permute(send, send_rows, row_bytes, row_dest, k, ...)
+ * expands the received rows into expert rows, and moe_combine(expert_out,
+ * ..., row_dest, k, erow_weight, send_rows, reply, ...) forms each (t, r)
+ * reply row sum_{j on r} w_tj * expert_out[erow(t, j)]; the final
+ * moe_combine of the replies is then unweighted.
+ * d_err bits: EXPERT_RANGE, EXPERT_DUP, RANK_RANGE, ROW_RANGE (slot_row
+ * outside [0, send_rows)).
+ * ---------------------------------------------------------------------- */
+int moe_expert_plan_workspace_size(int64_t T, int E, size_t* ws_bytes /* host */);
+int moe_expert_plan(const int32_t* topk, const float* gates, int64_t T, int k, int E,
+                    const int32_t* expert_rank, int G, const int32_t* slot_row, int64_t send_rows,
+                    int32_t* erow, int32_t* expert_first, int32_t* expert_count,
+                    int32_t* rank_offsets, float* erow_weight, int32_t* erow_slot,
+                    int32_t* row_dest, int32_t* d_err, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -86,17 +86,28 @@ def test_plan_rejects(built_lib):
 
 def test_permute_combine_shuffle_reject(built_lib):
     L = built_lib
-    assert L.moe_permute(FAKE, 8, 0, FAKE, 1, FAKE, 8, NULL, NULL) == -2
-    assert L.moe_permute(FAKE, 8, 16, FAKE, 9, FAKE, 8, NULL, NULL) == -2
-    assert L.moe_permute(FAKE, 8, 6, FAKE, 1, FAKE, 8, NULL, NULL) == -4
-    assert L.moe_permute(FAKE + 2, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL) == -4
-    assert L.moe_permute(NULL, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL) == -1
-    assert L.moe_permute(NULL, 0, 16, NULL, 1, NULL, 0, NULL, NULL) == 0   # empty: no-op
-    assert L.moe_combine(FAKE, 7, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL) == -3
-    assert L.moe_combine(FAKE, 1, 8, 60, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL) == -4  # 120 B rows
-    assert L.moe_combine(FAKE, 1, 8, 64, FAKE, 0, NULL, 8, FAKE, 1, NULL, NULL) == -2
-    assert L.moe_combine(FAKE, 1, 8, 64, NULL, 2, NULL, 8, FAKE, 1, NULL, NULL) == -1
-    assert L.moe_combine(FAKE + 8, 1, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL) == -4
+    assert L.moe_permute(FAKE, 8, 0, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -2
+    assert L.moe_permute(FAKE, 8, 16, FAKE, 9, FAKE, 8, NULL, NULL, NULL) == -2
+    assert L.moe_permute(FAKE, 8, 6, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -4
+    assert L.moe_permute(FAKE + 2, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -4
+    assert L.moe_permute(NULL, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -1
+    assert L.moe_permute(NULL, 0, 16, NULL, 1, NULL, 0, NULL, NULL, NULL) == 0   # empty: no-op
+    assert L.moe_combine(FAKE, 7, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -3
+    assert L.moe_combine(FAKE, 1, 8, 60, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -4  # 120 B
+    assert L.moe_combine(FAKE, 1, 8, 64, FAKE, 0, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -2
+    assert L.moe_combine(FAKE, 1, 8, 64, NULL, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -1
+    assert L.moe_combine(FAKE + 8, 1, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -4
+    ep = L.moe_expert_plan
+    args = [FAKE, NULL, 64, 2, 8, FAKE, 4, FAKE, 128, FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE,
+            NULL, FAKE, 1 << 20, NULL]
+    assert ep(*args[:3], 9, *args[4:]) == -2                       # k > 8
+    assert ep(*args[:6], 65, *args[7:]) == -2                      # G > 64
+    assert ep(*args[:7], NULL, *args[8:]) == -1                    # slot_row
+    assert ep(*args[:15], NULL, *args[16:]) == -1                  # row_dest
+    assert ep(*args[:18], 16, NULL) == -5                          # workspace
+    n = ctypes.c_size_t()
+    assert L.moe_expert_plan_workspace_size(65536, 256, ctypes.byref(n)) == 0
+    assert n.value >= 256 * 256 * 4
     sp = L.moe_shuffle_predict
     assert sp(FAKE, 8, 2, 8, FAKE, 8, FAKE, 65, FAKE, FAKE, NULL, FAKE, NULL, FAKE, 1 << 20, NULL) == -2
     assert sp(FAKE, 8, 2, 8, NULL, 8, FAKE, 4, FAKE, FAKE, NULL, FAKE, NULL, FAKE, 1 << 20, NULL) == -1
