@@ -25,4 +25,6 @@ from .coact import (  # noqa: F401
     expert_plan,
     partial_combine,
     moe_output,
+    permute_scaled,
+    row_dot,
 )

@@ -532,3 +532,44 @@ def moe_output(x: np.ndarray, x_dtype: str, topk: np.ndarray, gates: np.ndarray,
         for j in range(k):
             y[t] += float(np.float32(gates[t, j])) * float(expert_scale[int(topk[t, j])]) * xf[t]
     return y
+
+
+# ------------------------------------------------------------ backward
+
+def permute_scaled(x: np.ndarray, x_dtype: str, dest: np.ndarray, scale: np.ndarray,
+                   out_rows: int, out_dtype: str) -> np.ndarray:
+    """out[dest[t, q]] = scale[dest[t, q]] * x[t], the product formed exactly
+    (float64) and rounded once to float32, then to bf16 for a bf16 output.
+    The adjoint of the weighted combine with respect to its rows: the
+    gradient of each dispatched row is its gate mass times the gradient of
+    its token's output (the inverse all-to-alls of [CE] footnote 3 and the
+    backward passes of [EC] abstract).  Untargeted rows stay zero."""
+    xf = _as_f64(x, x_dtype)
+    dest = np.asarray(dest, dtype=np.int64)
+    if dest.ndim == 1:
+        dest = dest[:, None]
+    out = np.zeros((out_rows, xf.shape[1]), dtype=np.float64)
+    for t in range(dest.shape[0]):
+        for q in range(dest.shape[1]):
+            r = int(dest[t, q])
+            if r >= 0:
+                out[r] = float(np.float32(scale[r])) * xf[t]
+    o32 = out.astype(np.float32)
+    return bf16_round(o32) if out_dtype == "bf16" else o32
+
+
+def row_dot(a: np.ndarray, a_dtype: str, b: np.ndarray, b_dtype: str,
+            rows: np.ndarray) -> np.ndarray:
+    """out[t, q] = <a[t], b[rows[t, q]]> (0 where rows[t, q] < 0), summed in
+    float64, rounded once to float32.  With a = dY and b the rows a slot
+    reads, this is the gradient of the output with respect to that slot's
+    gate weight."""
+    af = _as_f64(a, a_dtype)
+    bf = _as_f64(b, b_dtype)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros(rows.shape, dtype=np.float64)
+    for t in range(rows.shape[0]):
+        for q in range(rows.shape[1]):
+            if rows[t, q] >= 0:
+                out[t, q] = float(np.dot(af[t], bf[rows[t, q]]))
+    return out.astype(np.float32)

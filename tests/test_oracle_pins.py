@@ -540,3 +540,83 @@ def test_moe_output_special_cases():
     assert np.allclose(y, x, rtol=1e-6, atol=1e-7)
     y1 = oracle.moe_output(x, "f32", topk[:, :1], gates[:, :1], np.full(6, 3.0))
     assert np.allclose(y1, 3.0 * gates[:, :1].astype(np.float64) * x, rtol=1e-12)
+
+
+# ------------------------------------------------------------ backward
+
+def _f64(x, dt):
+    return oracle.bf16_to_f32(x).astype(np.float64) if dt == "bf16" else x.astype(np.float64)
+
+
+def test_backward_adjoint_identities():
+    """<dY, combine(Z)> = <permute_scaled(dY), Z> (the scaled scatter is the
+    adjoint of the weighted combine in its rows) and
+    <dS, permute(x)> = <combine_unweighted(dS), x> (the plain combine is the
+    adjoint of the permute), both in float64 on fp32 data."""
+    w = make(4, T=320, H=24)
+    rng = np.random.default_rng(40)
+    plan = oracle.dispatch_plan(w.topk, w.gates, w.expert_rank, w.G, w.ranks_per_node)
+    N = plan["N"]
+    Z = rng.standard_normal((N, w.H)).astype(np.float32)
+    dY = rng.standard_normal((w.T, w.H)).astype(np.float32)
+    # forward combine in float64 from the rows' gate mass
+    y = np.zeros((w.T, w.H))
+    for t in range(w.T):
+        for q in range(w.k):
+            i = plan["token_rows"][t, q]
+            if i >= 0:
+                y[t] += float(plan["row_weight"][i]) * Z[i].astype(np.float64)
+    dZ = oracle.permute_scaled(dY, "f32", plan["token_rows"], plan["row_weight"], N, "f32")
+    lhs = float(np.sum(dY.astype(np.float64) * y))
+    rhs = float(np.sum(dZ.astype(np.float64) * Z.astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-6 * float(np.sum(np.abs(dY.astype(np.float64) * y))) + 1e-9
+    x = rng.standard_normal((w.T, w.H)).astype(np.float32)
+    dS = rng.standard_normal((N, w.H)).astype(np.float32)
+    send = oracle.permute_rows(x, plan["row_token"])
+    dx = oracle.combine_unweighted(dS, "f32", plan["token_rows"], "f32")
+    lhs = float(np.sum(dS.astype(np.float64) * send.astype(np.float64)))
+    rhs = float(np.sum(dx.astype(np.float64) * x.astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-6 * float(np.sum(np.abs(dS.astype(np.float64) * send))) + 1e-9
+
+
+def test_gate_gradient_matches_finite_differences():
+    """dL/dw_tj for L = <dY, y(w)>, y_t = sum_j w_tj Z[slot_row(t, j)], equals
+    row_dot(dY, Z, slot_row); y is linear in w, so a central difference in
+    float64 is exact up to rounding."""
+    w = make(3, T=96, H=16)
+    rng = np.random.default_rng(41)
+    plan = oracle.dispatch_plan(w.topk, w.gates, w.expert_rank, w.G, w.ranks_per_node)
+    Z = rng.standard_normal((plan["N"], w.H)).astype(np.float32)
+    dY = rng.standard_normal((w.T, w.H)).astype(np.float32)
+    dw = oracle.row_dot(dY, "f32", Z, "f32", plan["slot_row"])
+
+    def loss(g):
+        y = np.zeros((w.T, w.H))
+        for t in range(w.T):
+            for j in range(w.k):
+                y[t] += g[t, j] * Z[plan["slot_row"][t, j]].astype(np.float64)
+        return float(np.sum(dY.astype(np.float64) * y))
+
+    g0 = w.gates.astype(np.float64)
+    for (t, j) in [(0, 0), (5, 3), (95, 5), (40, 1)]:
+        gp, gm = g0.copy(), g0.copy()
+        gp[t, j] += 0.5
+        gm[t, j] -= 0.5
+        fd = loss(gp) - loss(gm)
+        assert abs(fd - float(dw[t, j])) <= 1e-5 * (abs(fd) + 1.0)
+
+
+def test_permute_scaled_and_row_dot_small():
+    x = np.array([[1.0, -2.0], [3.0, 0.5]], np.float32)
+    dest = np.array([[1, -1], [0, 2]])
+    scale = np.array([0.5, 2.0, -1.0], np.float32)
+    out = oracle.permute_scaled(x, "f32", dest, scale, 4, "f32")
+    assert out.tolist() == [[1.5, 0.25], [2.0, -4.0], [-3.0, -0.5], [0.0, 0.0]]
+    d = oracle.row_dot(x, "f32", out, "f32", np.array([[1, 3], [2, -1]]))
+    assert d.tolist() == [[10.0, 0.0], [-9.25, 0.0]]
+    # a scaled scatter with bf16 output rounds the exact product once
+    xb = oracle.bf16_round(np.array([[1.0 + 2 ** -7]], np.float32))
+    ob = oracle.permute_scaled(xb, "bf16", np.array([[0]]), np.array([1.0 + 2 ** -8], np.float32),
+                               1, "bf16")
+    exact = (1.0 + 2 ** -7) * (1.0 + 2 ** -8)
+    assert ob[0, 0] == oracle.bf16_round(np.array([exact], np.float32))[0]
