@@ -74,34 +74,47 @@ def counter_traffic(workload: int, stage: str):
 def expert_side(step, w, steps: int, device_normal) -> dict:
     """Destination side after the step's dispatch (outside the timed step):
     expert layout, expansion of the received rows into expert rows, reply
-    rows from stand-in expert outputs, and the reply combine.  Per-kernel
-    times from HIP events, with algorithmic bytes."""
+    rows from stand-in expert outputs, the reply combine, and the backward
+    mirror of all of it.  Per-kernel times from HIP events, with
+    algorithmic bytes."""
     import torch
 
-    from co_activation_amd.pipeline import ExpertSideStep, StageTimers
+    from co_activation_amd.pipeline import ExpertSideBackward, ExpertSideStep, StageTimers
 
     side = ExpertSideStep(step)
+    bw = ExpertSideBackward(side)
     y_expert = device_normal(side.T * side.k, w.H, w.dtype, seed=2)
-    side.dispatch()
-    side.reply_and_combine(y_expert)
-    torch.cuda.synchronize()
-    timers = StageTimers(side.STAGES, steps)
-    for _ in range(steps):
+    dy = device_normal(side.T, w.H, w.dtype, seed=3)
+    d_expert_in = device_normal(side.T * side.k, w.H, w.dtype, seed=4)
+
+    def once(timers=None):
         side.dispatch(timers)
         side.reply_and_combine(y_expert, timers)
+        bw.run(dy, y_expert, d_expert_in, timers)
+
+    once()
+    torch.cuda.synchronize()
+    timers = StageTimers(side.STAGES + bw.STAGES, steps)
+    for _ in range(steps):
+        once(timers)
     torch.cuda.synchronize()
     if int(side.d_err.item()) != 0:
         return {"error": f"device data errors {int(side.d_err.item())}"}
     ms = timers.mean_ms()
     N = int(step.plan.counters[0].item())
-    TK, rb, T = side.T * side.k, w.row_bytes, side.T
-    bytes_ = {"expand": N * rb + TK * rb + 4 * N * side.k,
-              "partial_combine": TK * rb + 4 * TK + N * rb + 4 * N * side.k,
-              "reply_combine": N * rb + T * rb + 4 * T * side.k}
-    out = {"rows_expert": TK, "stage_us": {n: 1e3 * v for n, v in ms.items()}}
-    for n, b in bytes_.items():
-        out[f"{n}_gbps"] = b / (ms[n] * 1e-3) / 1e9
-        out[f"{n}_bytes"] = b
+    k = side.k
+    TK, rb, T = side.T * k, w.row_bytes, side.T
+    bytes_ = {"expand": N * rb + TK * rb + 4 * N * k,
+              "partial_combine": TK * rb + 4 * TK + N * rb + 4 * N * k,
+              "reply_combine": N * rb + T * rb + 4 * T * k,
+              "grad_replies": T * rb + N * rb + 4 * T * k,
+              "grad_expert_out": N * rb + TK * rb + 4 * N * k + 4 * TK,
+              "grad_gates": T * rb + TK * rb + 8 * TK,
+              "grad_send": TK * rb + N * rb + 4 * N * k,
+              "grad_tokens": N * rb + T * rb + 4 * T * k}
+    out = {"rows_expert": TK, "stage_us": {n: round(1e3 * v, 2) for n, v in ms.items()},
+           "gbps": {n: round(b / (ms[n] * 1e-3) / 1e9, 1) for n, b in bytes_.items()},
+           "algorithmic_bytes": bytes_}
     return out
 
 

@@ -34,6 +34,7 @@ EXPORTS = (
     "moe_dispatch_plan", "moe_permute", "moe_combine",
     "moe_shuffle_predict_workspace_size", "moe_shuffle_predict",
     "moe_expert_plan_workspace_size", "moe_expert_plan",
+    "moe_permute_scaled", "moe_row_dot",
 )
 
 _lib = None
@@ -65,6 +66,12 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.moe_expert_plan.argtypes = [P, P, c_int64, c_int, c_int, P, c_int, P, c_int64, P, P, P, P,
                                     P, P, P, P, P, c_size_t, P]
     lib.moe_expert_plan.restype = c_int
+    lib.moe_permute_scaled.argtypes = [P, c_int, c_int64, c_int64, P, c_int, P, P, c_int, c_int64,
+                                       P, P, P]
+    lib.moe_permute_scaled.restype = c_int
+    lib.moe_row_dot.argtypes = [P, c_int, c_int64, c_int64, P, c_int, c_int64, P, c_int, P, P, P,
+                                P]
+    lib.moe_row_dot.restype = c_int
 
 
 def lib() -> ctypes.CDLL:

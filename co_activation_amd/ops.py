@@ -287,3 +287,56 @@ def expert_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank: 
         ws.numel(), _stream())
     check("moe_expert_plan", st)
     return res
+
+
+# ----------------------------------------------------------------- backward
+
+def permute_scaled(x: torch.Tensor, dest: torch.Tensor, scale: torch.Tensor, out_rows: int, *,
+                   out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                   n_valid: Optional[torch.Tensor] = None,
+                   d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_permute_scaled: out[dest[t, q]] = scale[dest[t, q]] * x[t]."""
+    _want(x, "x")
+    if x.dtype not in _DT:
+        raise TypeError("x must be float32 or bfloat16")
+    _want(dest, "dest", torch.int32)
+    _want(scale, "scale", torch.float32)
+    T, H = x.shape
+    width = 1 if dest.dim() == 1 else dest.shape[1]
+    out_dtype = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty((out_rows, H), dtype=out_dtype, device=x.device)
+    _want(out, "out", out_dtype)
+    if scale.numel() < out_rows or out.shape[0] < out_rows or out.shape[1] != H:
+        raise ValueError("scale and out need out_rows rows")
+    if n_valid is not None:
+        _want(n_valid, "n_valid", torch.int32)
+    st = _lib.lib().moe_permute_scaled(_p(x), _DT[x.dtype], T, H, _p(dest), width, _p(scale),
+                                       _p(out), _DT[out_dtype], out_rows, _p(n_valid), _p(d_err),
+                                       _stream())
+    check("moe_permute_scaled", st)
+    return out
+
+
+def row_dot(a: torch.Tensor, b: torch.Tensor, rows: torch.Tensor, *,
+            out: Optional[torch.Tensor] = None, n_valid: Optional[torch.Tensor] = None,
+            d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_row_dot: out[t, q] = <a[t], b[rows[t, q]]> (float32)."""
+    _want(a, "a")
+    _want(b, "b")
+    if a.dtype not in _DT or b.dtype not in _DT:
+        raise TypeError("a and b must be float32 or bfloat16")
+    _want(rows, "rows", torch.int32)
+    T, H = a.shape
+    if b.shape[1] != H or rows.shape[0] != T:
+        raise ValueError("shapes of a, b and rows disagree")
+    width = 1 if rows.dim() == 1 else rows.shape[1]
+    if out is None:
+        out = torch.empty((T, width), dtype=torch.float32, device=a.device)
+    _want(out, "out", torch.float32)
+    if n_valid is not None:
+        _want(n_valid, "n_valid", torch.int32)
+    st = _lib.lib().moe_row_dot(_p(a), _DT[a.dtype], T, H, _p(b), _DT[b.dtype], b.shape[0],
+                                _p(rows), width, _p(out), _p(n_valid), _p(d_err), _stream())
+    check("moe_row_dot", st)
+    return out

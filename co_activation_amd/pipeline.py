@@ -309,3 +309,71 @@ class ExpertSideStep:
         with _timed(timers, "reply_combine"):
             ops.combine(self.reply, self.layer.plan.token_rows, None, out=self.y, d_err=self.d_err)
         return self
+
+
+class LayerBackward:
+    """Backward mirror of a LayerStep's weighted combine and permute:
+    dz = a(row) * dy scattered to the rows, dw_tj = <dy_t, z[slot_row(t,j)]>,
+    and dx = the unweighted combine of the gradient of the send rows."""
+
+    STAGES = ("grad_rows", "grad_gates", "grad_tokens")
+
+    def __init__(self, layer):
+        self.layer = layer
+        dev = layer.send.device
+        H = layer.send.shape[1]
+        self.dz = torch.empty(layer.cap, H, dtype=layer.z.dtype, device=dev)
+        self.dw = torch.empty(layer.T, layer.k, dtype=torch.float32, device=dev)
+        self.dx = torch.empty(layer.T, H, dtype=layer.x.dtype, device=dev)
+
+    def run(self, dy, dsend, timers: Optional[StageTimers] = None):
+        p = self.layer.plan
+        err = self.layer.d_err
+        with _timed(timers, "grad_rows"):
+            ops.permute_scaled(dy, p.token_rows, p.row_weight, self.layer.cap, out=self.dz,
+                               d_err=err)
+        with _timed(timers, "grad_gates"):
+            ops.row_dot(dy, self.layer.z, p.slot_row, out=self.dw, d_err=err)
+        with _timed(timers, "grad_tokens"):
+            ops.combine(dsend, p.token_rows, None, out=self.dx, d_err=err)
+        return self
+
+
+class ExpertSideBackward:
+    """Backward mirror of an ExpertSideStep: the reply combine's gradient is
+    dy copied to every reply row of its token; each expert output row gets
+    its gate times its reply row's gradient; the gate gradients are
+    dw_tj = <dy_t, expert_out[erow(t,j)]>; the expert inputs' gradients are
+    summed back into send rows and the send rows' back into tokens."""
+
+    STAGES = ("grad_replies", "grad_expert_out", "grad_gates", "grad_send", "grad_tokens")
+
+    def __init__(self, side):
+        self.side = side
+        dev = side.y.device
+        H = side.y.shape[1]
+        dt = side.y.dtype
+        self.d_reply = torch.empty(side.cap, H, dtype=dt, device=dev)
+        self.d_expert_out = torch.empty(side.T * side.k, H, dtype=dt, device=dev)
+        self.dw = torch.empty(side.T, side.k, dtype=torch.float32, device=dev)
+        self.d_send = torch.empty(side.cap, H, dtype=dt, device=dev)
+        self.dx = torch.empty(side.T, H, dtype=dt, device=dev)
+
+    def run(self, dy, expert_out, d_expert_in, timers: Optional[StageTimers] = None):
+        s = self.side
+        lp = s.layer.plan
+        err = s.d_err
+        n = s.n_rows()
+        with _timed(timers, "grad_replies"):
+            ops.permute(dy, lp.token_rows, s.cap, out=self.d_reply, d_err=err)
+        with _timed(timers, "grad_expert_out"):
+            ops.permute_scaled(self.d_reply, s.plan["row_dest"], s.plan["erow_weight"],
+                               s.T * s.k, out=self.d_expert_out, n_valid=n, d_err=err)
+        with _timed(timers, "grad_gates"):
+            ops.row_dot(dy, expert_out, s.plan["erow"], out=self.dw, d_err=err)
+        with _timed(timers, "grad_send"):
+            ops.combine(d_expert_in, s.plan["row_dest"], None, out=self.d_send, n_valid=n,
+                        d_err=err)
+        with _timed(timers, "grad_tokens"):
+            ops.combine(self.d_send, lp.token_rows, None, out=self.dx, d_err=err)
+        return self

@@ -11,7 +11,8 @@
  *   4. combines the returned rows back to token order with the gate weights,
  *   5. predicts each token's next-layer rank and orders tokens by it (token
  *      shuffling),
- *   6. lays the received rows out per expert on the destination side.
+ *   6. lays the received rows out per expert on the destination side,
+ *   7. runs the backward mirror (scaled scatter, gate gradients).
  * The ranks of the expert-parallel group are logical: each (source rank,
  * destination rank) block of the send buffer stands for one all-to-all
  * message.
@@ -265,6 +266,33 @@ int moe_expert_plan(const int32_t* topk, const float* gates, int64_t T, int k, i
                     int32_t* erow, int32_t* expert_first, int32_t* expert_count,
                     int32_t* rank_offsets, float* erow_weight, int32_t* erow_slot,
                     int32_t* row_dest, int32_t* d_err, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward mirror.  The all-to-alls run again in the backward pass with the
+ * data flowing back ([EC] abstract; [CE] footnote 3: inverse all-to-alls of
+ * the dispatch, routed-probability dispatch and combine).  For the weighted
+ * combine y_t = sum_q a(row_q) z[row_q]:
+ *   dL/dz[row] = a(row) * dL/dy_t          -> moe_permute_scaled
+ *   dL/dw_tj   = <dL/dy_t, z[slot_row(t,j)]> -> moe_row_dot
+ * and the adjoint of moe_permute is the unweighted moe_combine.
+ *
+ * moe_permute_scaled:  out[dest[t*width+q]] = scale[dest] * x[t] for every
+ *   dest >= 0, the product formed in fp32 and rounded once to out_dtype.
+ *   x [T*H] of x_dtype; dest [T*width] int32; scale [out_rows] float (indexed
+ *   by the destination row); out [out_rows*H] of out_dtype (untargeted rows
+ *   untouched); n_valid as for moe_permute.  H*sizeof must be a multiple of
+ *   16 bytes for both types (8 elements when a bf16 side is involved),
+ *   buffers 16-byte aligned.  d_err bits: ROW_RANGE.
+ * moe_row_dot:  out[t*width+q] = <a[t], b[rows[t*width+q]]> summed in fp32
+ *   in a fixed order (0 where the row is < 0).  a [T*H], b [b_rows*H],
+ *   out [T*width] float.  Same row-size rules.  d_err bits: ROW_RANGE.
+ * ---------------------------------------------------------------------- */
+int moe_permute_scaled(const void* x, int x_dtype, int64_t T, int64_t H, const int32_t* dest,
+                       int width, const float* scale, void* out, int out_dtype, int64_t out_rows,
+                       const int32_t* n_valid, int32_t* d_err, void* stream);
+int moe_row_dot(const void* a, int a_dtype, int64_t T, int64_t H, const void* b, int b_dtype,
+                int64_t b_rows, const int32_t* rows, int width, float* out,
+                const int32_t* n_valid, int32_t* d_err, void* stream);
 
 #ifdef __cplusplus
 }

@@ -108,6 +108,16 @@ def test_permute_combine_shuffle_reject(built_lib):
     n = ctypes.c_size_t()
     assert L.moe_expert_plan_workspace_size(65536, 256, ctypes.byref(n)) == 0
     assert n.value >= 256 * 256 * 4
+    ps = L.moe_permute_scaled
+    assert ps(FAKE, 2, 8, 64, FAKE, 1, FAKE, FAKE, 1, 8, NULL, NULL, NULL) == -3
+    assert ps(FAKE, 1, 8, 64, FAKE, 9, FAKE, FAKE, 1, 8, NULL, NULL, NULL) == -2
+    assert ps(FAKE, 1, 8, 64, FAKE, 1, NULL, FAKE, 1, 8, NULL, NULL, NULL) == -1
+    assert ps(FAKE, 1, 8, 60, FAKE, 1, FAKE, FAKE, 1, 8, NULL, NULL, NULL) == -4
+    rd = L.moe_row_dot
+    assert rd(FAKE, 1, 8, 64, FAKE, 5, 8, FAKE, 1, FAKE, NULL, NULL, NULL) == -3
+    assert rd(FAKE, 1, 8, 64, FAKE, 1, 8, FAKE, 0, FAKE, NULL, NULL, NULL) == -2
+    assert rd(FAKE, 1, 8, 64, FAKE, 1, 8, NULL, 1, FAKE, NULL, NULL, NULL) == -1
+    assert rd(FAKE, 0, 8, 4, FAKE, 1, 8, FAKE, 1, FAKE, NULL, NULL, NULL) == -4  # bf16 side, H=4
     sp = L.moe_shuffle_predict
     assert sp(FAKE, 8, 2, 8, FAKE, 8, FAKE, 65, FAKE, FAKE, NULL, FAKE, NULL, FAKE, 1 << 20, NULL) == -2
     assert sp(FAKE, 8, 2, 8, NULL, 8, FAKE, 4, FAKE, FAKE, NULL, FAKE, NULL, FAKE, 1 << 20, NULL) == -1
