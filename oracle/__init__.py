@@ -27,4 +27,7 @@ from .coact import (  # noqa: F401
     moe_output,
     permute_scaled,
     row_dot,
+    ema_update,
+    colocated_coactivation,
+    place_experts,
 )

@@ -573,3 +573,82 @@ def row_dot(a: np.ndarray, a_dtype: str, b: np.ndarray, b_dtype: str,
             if rows[t, q] >= 0:
                 out[t, q] = float(np.dot(af[t], bf[rows[t, q]]))
     return out.astype(np.float32)
+
+
+# ------------------------------------------------- EMA statistics, placement
+
+def ema_update(state: np.ndarray, x: np.ndarray, beta: float) -> np.ndarray:
+    """Exponential moving average of per-step statistics ([CB] Stage 1: the
+    planner works from EMAs of co-selection counts and expert loads; the
+    decay is not given -- reading: a caller parameter).  float32 state;
+    new = beta * state + (1 - beta) * x, each product and the sum rounded to
+    float32 in that order."""
+    b = np.float32(beta)
+    ob = np.float32(np.float32(1.0) - b)
+    s = np.asarray(state, dtype=np.float32)
+    xv = np.asarray(x).astype(np.float32)
+    return (s * b + xv * ob).astype(np.float32)
+
+
+def colocated_coactivation(C: np.ndarray, expert_rank: np.ndarray) -> float:
+    """Sum of C[i][j] over unordered pairs i < j placed on the same rank:
+    the co-activation a placement keeps inside ranks."""
+    E = len(expert_rank)
+    tot = 0.0
+    for i in range(E):
+        for j in range(i + 1, E):
+            if int(expert_rank[i]) == int(expert_rank[j]):
+                tot += float(C[i][j])
+    return tot
+
+
+def place_experts(C: np.ndarray, load: np.ndarray, G: int, eps: float) -> np.ndarray:
+    """Co-activation placement ([EC] abstract: experts often selected
+    together go on the same GPU; [CB] Stage 1: maximise co-activation kept
+    inside ranks under a workload limit).  The pages give no algorithm;
+    reading -- an affinity greedy:
+
+    * every rank holds exactly E/G experts; the workload limit is
+      L = (1 + eps) * sum(load) / G;
+    * experts are taken in descending total co-activation sum_{f != e} C[e][f]
+      (ties: lower id);
+    * each goes to the rank with room whose already-placed experts have the
+      largest summed co-activation with it, among ranks whose load stays
+      within L if there are any (else among all ranks with room); ties go to
+      the lower load, then the lower rank.
+    Sums are float64 over float32 inputs, in ascending expert order."""
+    C = np.asarray(C, dtype=np.float32)
+    load = np.asarray(load, dtype=np.float32)
+    E = C.shape[0]
+    if E % G != 0:
+        raise OracleInputError("E must be divisible by G")
+    cap = E // G
+    limit = (1.0 + eps) * sum(float(v) for v in load) / G
+    total = []
+    for e in range(E):
+        s = 0.0
+        for f in range(E):
+            if f != e:
+                s += float(C[e][f])
+        total.append(s)
+    order = sorted(range(E), key=lambda e: (-total[e], e))
+    rank = [-1] * E
+    members = [[] for _ in range(G)]
+    rload = [0.0] * G
+    for e in order:
+        open_ranks = [r for r in range(G) if len(members[r]) < cap]
+        within = [r for r in open_ranks if rload[r] + float(load[e]) <= limit]
+        cands = within if within else open_ranks
+        best = None
+        for r in cands:
+            aff = 0.0
+            for f in sorted(members[r]):
+                aff += float(C[e][f])
+            key = (-aff, rload[r], r)
+            if best is None or key < best[0]:
+                best = (key, r)
+        r = best[1]
+        rank[e] = r
+        members[r].append(e)
+        rload[r] += float(load[e])
+    return np.array(rank, dtype=np.int32)

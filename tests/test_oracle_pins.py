@@ -620,3 +620,72 @@ def test_permute_scaled_and_row_dot_small():
                                1, "bf16")
     exact = (1.0 + 2 ** -7) * (1.0 + 2 ** -8)
     assert ob[0, 0] == oracle.bf16_round(np.array([exact], np.float32))[0]
+
+
+# ------------------------------------------------------------ EMA, placement
+
+def test_ema_closed_form():
+    """A constant input x from a zero state gives x * (1 - beta^n)."""
+    s = np.zeros(5, np.float32)
+    x = np.array([0, 1, 7, 100, 12345], np.int32)
+    for n in range(1, 40):
+        s = oracle.ema_update(s, x, 0.9)
+        want = x.astype(np.float64) * (1.0 - 0.9 ** n)
+        assert np.allclose(s, want, rtol=1e-5, atol=1e-6)
+    s1 = oracle.ema_update(np.full(3, 5.0, np.float32), np.array([5, 5, 5]), 0.37)
+    assert np.allclose(s1, 5.0, rtol=1e-6)
+
+
+def test_placement_recovers_planted_clusters():
+    """Clusters of E/G experts that are co-selected only among themselves
+    land one cluster per rank."""
+    rng = np.random.default_rng(50)
+    for E, G in [(8, 2), (64, 8), (128, 32), (256, 64)]:
+        cap = E // G
+        perm = rng.permutation(E)
+        C = np.zeros((E, E), np.float32)
+        for c in range(G):
+            mem = perm[c * cap:(c + 1) * cap]
+            for i in mem:
+                for j in mem:
+                    if i != j:
+                        C[i, j] = rng.uniform(1, 10)
+        C = np.maximum(C, C.T)
+        load = rng.uniform(0.5, 1.5, size=E).astype(np.float32)
+        er = oracle.place_experts(C, load, G, 0.5)
+        assert (np.bincount(er, minlength=G) == cap).all()
+        for c in range(G):
+            mem = perm[c * cap:(c + 1) * cap]
+            assert len(set(er[mem].tolist())) == 1
+
+
+def test_placement_capacity_load_and_pairs():
+    """Every rank gets E/G experts; with a feasible workload limit no rank
+    exceeds it; on workload 2's planted pairs the placement keeps at least
+    as much co-activation inside ranks as the contiguous split and removes
+    dispatched rows."""
+    w = make(2, T=8192, with_x=False)
+    st = oracle.coact_stats(w.topk, w.E)
+    C = st["pair_count"].astype(np.float32)
+    np.fill_diagonal(C, 0)
+    load = st["expert_count"].astype(np.float32)
+    er = oracle.place_experts(C, load, w.G, 0.25)
+    assert (np.bincount(er, minlength=w.G) == w.E // w.G).all()
+    loads = np.bincount(er, weights=load, minlength=w.G)
+    assert loads.max() <= 1.25 * load.sum() / w.G + 1e-3
+    kept = oracle.colocated_coactivation(C, er)
+    assert kept >= oracle.colocated_coactivation(C, uniform_contiguous(w.E, w.G))
+    n_planned = oracle.dispatch_plan(w.topk, None, er, w.G, w.ranks_per_node)["N"]
+    n_uniform = oracle.dispatch_plan(w.topk, None, uniform_contiguous(w.E, w.G), w.G,
+                                     w.ranks_per_node)["N"]
+    assert n_planned < n_uniform
+
+
+def test_placement_tiny_exhaustive_optimum():
+    """On 4 experts / 2 ranks with one heavy pair per rank, the greedy reaches
+    the exhaustive optimum of co-located co-activation."""
+    C = np.array([[0, 9, 1, 0], [9, 0, 0, 2], [1, 0, 0, 8], [0, 2, 8, 0]], np.float32)
+    er = oracle.place_experts(C, np.ones(4, np.float32), 2, 0.0)
+    best = max(oracle.colocated_coactivation(C, np.array(p)) for p in
+               itertools.product(range(2), repeat=4) if sorted(p).count(0) == 2)
+    assert oracle.colocated_coactivation(C, er) == best == 17.0
