@@ -118,6 +118,37 @@ def expert_side(step, w, steps: int, device_normal) -> dict:
     return out
 
 
+def placement_planner(w) -> dict:
+    """Co-activation placement for the benchmark's dispatched layer: one
+    step of statistics folded into the moving averages, a plan, and the
+    rows the dispatch needs under it versus the contiguous split."""
+    import numpy as np
+    import torch
+
+    from co_activation_amd import ops
+    from co_activation_amd.placement import PlacementPlanner
+
+    topk = w.topk2 if w.cfg == 5 else w.topk
+    dev = "cuda"
+    tk = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).to(dev)
+    planner = PlacementPlanner(w.E, w.G, beta=0.9, eps=0.1, period=1, device=dev)
+    st = ops.coact_stats(tk, w.E)
+    planner.observe(st)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    er = planner.plan()
+    plan_ms = 1e3 * (time.perf_counter() - t0)
+    rows = {}
+    for name, p in (("contiguous", np.arange(w.E) // (w.E // w.G)), ("planned", er)):
+        pl = ops.dispatch_plan(tk, None, torch.from_numpy(np.ascontiguousarray(p, dtype=np.int32))
+                               .to(dev), w.G, w.ranks_per_node)
+        c = pl.counters.cpu().numpy()
+        rows[name] = {"rows": int(c[0]), "local_assign": int(c[3]), "cross_node_V": int(c[5])}
+    return {"layer": "layer 2" if w.cfg == 5 else "layer", "beta": 0.9, "eps": 0.1,
+            "plan_host_ms": plan_ms, "dispatch": rows,
+            "rows_removed_frac": 1.0 - rows["planned"]["rows"] / rows["contiguous"]["rows"]}
+
+
 def cpu_baseline(w, sample_tokens: int) -> dict:
     """The CPU oracle on the first `sample_tokens` tokens of the same
     workload, single-threaded; rows/s of the same step definition."""
@@ -296,6 +327,7 @@ def main() -> int:
     }
     if not args.no_expert_side:
         line["expert_side"] = expert_side(step, w, args.steps, device_normal)
+        line["placement"] = placement_planner(w)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     print(json.dumps(line), flush=True)

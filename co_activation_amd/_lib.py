@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_dispatch_plan", "moe_permute", "moe_combine",
     "moe_shuffle_predict_workspace_size", "moe_shuffle_predict",
     "moe_expert_plan_workspace_size", "moe_expert_plan",
-    "moe_permute_scaled", "moe_row_dot",
+    "moe_permute_scaled", "moe_row_dot", "moe_ema_update", "moe_place_experts",
 )
 
 _lib = None
@@ -72,6 +72,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.moe_row_dot.argtypes = [P, c_int, c_int64, c_int64, P, c_int, c_int64, P, c_int, P, P, P,
                                 P]
     lib.moe_row_dot.restype = c_int
+    lib.moe_ema_update.argtypes = [P, P, c_int64, ctypes.c_float, P]
+    lib.moe_ema_update.restype = c_int
+    lib.moe_place_experts.argtypes = [P, P, c_int, c_int, ctypes.c_double, P]
+    lib.moe_place_experts.restype = c_int
 
 
 def lib() -> ctypes.CDLL:

@@ -215,3 +215,31 @@ extern "C" int moe_coact_stats(const int32_t* topk, int64_t T, int k, int E,
   }
   return MOE_OK;
 }
+
+namespace moe {
+namespace {
+
+// state[i] = beta * state[i] + (1 - beta) * x[i]; the two products and the
+// sum are rounded separately (no fused multiply-add), in that order.
+__global__ void ema_kernel(float* __restrict__ state, const int32_t* __restrict__ x, int64_t n,
+                           float beta, float one_minus_beta) {
+#pragma clang fp contract(off)
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n; i += stride)
+    state[i] = state[i] * beta + static_cast<float>(x[i]) * one_minus_beta;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_ema_update(float* state, const int32_t* x, int64_t n, float beta,
+                              void* stream) {
+  if (n < 0 || !(beta >= 0.f && beta <= 1.f)) return MOE_ERR_SHAPE;
+  if (n == 0) return MOE_OK;
+  if (state == nullptr || x == nullptr) return MOE_ERR_NULL;
+  const float omb = 1.f - beta;
+  moe::ema_kernel<<<moe::grid_for(n), 256, 0, static_cast<hipStream_t>(stream)>>>(state, x, n, beta,
+                                                                                  omb);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

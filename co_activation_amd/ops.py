@@ -340,3 +340,32 @@ def row_dot(a: torch.Tensor, b: torch.Tensor, rows: torch.Tensor, *,
                                 _p(rows), width, _p(out), _p(n_valid), _p(d_err), _stream())
     check("moe_row_dot", st)
     return out
+
+
+# ----------------------------------------------------------------- placement
+
+def ema_update(state: torch.Tensor, x: torch.Tensor, beta: float) -> torch.Tensor:
+    """moe_ema_update: state = beta * state + (1 - beta) * x, in place."""
+    _want(state, "state", torch.float32)
+    _want(x, "x", torch.int32)
+    if state.numel() != x.numel():
+        raise ValueError("state and x must have the same size")
+    check("moe_ema_update", _lib.lib().moe_ema_update(_p(state), _p(x), state.numel(), float(beta),
+                                                      _stream()))
+    return state
+
+
+def place_experts(coact, load, G: int, eps: float):
+    """moe_place_experts on host arrays (numpy float32 [E,E] and [E]);
+    returns a numpy int32 [E] placement."""
+    import numpy as np
+
+    C = np.ascontiguousarray(coact, dtype=np.float32)
+    w = np.ascontiguousarray(load, dtype=np.float32)
+    E = w.shape[0]
+    if C.shape != (E, E):
+        raise ValueError("coact must be [E, E]")
+    out = np.empty(E, dtype=np.int32)
+    check("moe_place_experts", _lib.lib().moe_place_experts(C.ctypes.data, w.ctypes.data, E, G,
+                                                            float(eps), out.ctypes.data))
+    return out

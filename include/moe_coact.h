@@ -12,7 +12,9 @@
  *   5. predicts each token's next-layer rank and orders tokens by it (token
  *      shuffling),
  *   6. lays the received rows out per expert on the destination side,
- *   7. runs the backward mirror (scaled scatter, gate gradients).
+ *   7. runs the backward mirror (scaled scatter, gate gradients),
+ *   8. keeps moving averages of the statistics and plans a co-activation
+ *      placement from them.
  * The ranks of the expert-parallel group are logical: each (source rank,
  * destination rank) block of the send buffer stands for one all-to-all
  * message.
@@ -293,6 +295,29 @@ int moe_permute_scaled(const void* x, int x_dtype, int64_t T, int64_t H, const i
 int moe_row_dot(const void* a, int a_dtype, int64_t T, int64_t H, const void* b, int b_dtype,
                 int64_t b_rows, const int32_t* rows, int width, float* out,
                 const int32_t* n_valid, int32_t* d_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Statistics over steps and placement ("Cobalt: Leveraging Expert
+ * Co-activation for Efficient Distributed MoE Training", Stage 1: the layout
+ * is re-planned periodically from moving averages of co-selection counts
+ * and expert loads; [EC] abstract: experts often selected together go on
+ * the same GPU).
+ *
+ * moe_ema_update:  state[i] = beta * state[i] + (1 - beta) * x[i] for
+ *   i < n, each product and the sum rounded to float separately.  state
+ *   [n] float (device, in/out), x [n] int32 (device), 0 <= beta <= 1.
+ * moe_place_experts (HOST pointers, runs on the host, synchronous):
+ *   coact [E*E] float (co-selection weights, diagonal ignored), load [E]
+ *   float, eps >= 0, expert_rank [E] int32 out.  Every rank receives E/G
+ *   experts (E % G == 0).  Ranks are filled one at a time, in order; each
+ *   step adds the unplaced expert most co-selected with the rank's experts
+ *   so far (ties: larger total co-activation, then lower id), preferring
+ *   experts that keep the rank's load within (1 + eps) * sum(load) / G.
+ *   Double-precision sums in ascending expert order.
+ * ---------------------------------------------------------------------- */
+int moe_ema_update(float* state, const int32_t* x, int64_t n, float beta, void* stream);
+int moe_place_experts(const float* coact /* host */, const float* load /* host */, int E, int G,
+                      double eps, int32_t* expert_rank /* host */);
 
 #ifdef __cplusplus
 }

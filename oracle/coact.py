@@ -606,16 +606,16 @@ def place_experts(C: np.ndarray, load: np.ndarray, G: int, eps: float) -> np.nda
     """Co-activation placement ([EC] abstract: experts often selected
     together go on the same GPU; [CB] Stage 1: maximise co-activation kept
     inside ranks under a workload limit).  The pages give no algorithm;
-    reading -- an affinity greedy:
+    reading -- grow one rank at a time:
 
     * every rank holds exactly E/G experts; the workload limit is
       L = (1 + eps) * sum(load) / G;
-    * experts are taken in descending total co-activation sum_{f != e} C[e][f]
-      (ties: lower id);
-    * each goes to the rank with room whose already-placed experts have the
-      largest summed co-activation with it, among ranks whose load stays
-      within L if there are any (else among all ranks with room); ties go to
-      the lower load, then the lower rank.
+    * ranks are filled in order 0..G-1; each step adds to the current rank
+      the unplaced expert with the largest summed co-activation with the
+      rank's experts so far, ties broken by the larger total co-activation
+      sum_{f != e} C[e][f], then the lower id (so an empty rank is seeded
+      with the most co-activated expert left); candidates whose load keeps
+      the rank within L are preferred when there are any.
     Sums are float64 over float32 inputs, in ascending expert order."""
     C = np.asarray(C, dtype=np.float32)
     load = np.asarray(load, dtype=np.float32)
@@ -626,29 +626,29 @@ def place_experts(C: np.ndarray, load: np.ndarray, G: int, eps: float) -> np.nda
     limit = (1.0 + eps) * sum(float(v) for v in load) / G
     total = []
     for e in range(E):
-        s = 0.0
+        t = 0.0
         for f in range(E):
             if f != e:
-                s += float(C[e][f])
-        total.append(s)
-    order = sorted(range(E), key=lambda e: (-total[e], e))
+                t += float(C[e][f])
+        total.append(t)
     rank = [-1] * E
-    members = [[] for _ in range(G)]
-    rload = [0.0] * G
-    for e in order:
-        open_ranks = [r for r in range(G) if len(members[r]) < cap]
-        within = [r for r in open_ranks if rload[r] + float(load[e]) <= limit]
-        cands = within if within else open_ranks
-        best = None
-        for r in cands:
-            aff = 0.0
-            for f in sorted(members[r]):
-                aff += float(C[e][f])
-            key = (-aff, rload[r], r)
-            if best is None or key < best[0]:
-                best = (key, r)
-        r = best[1]
-        rank[e] = r
-        members[r].append(e)
-        rload[r] += float(load[e])
+    for r in range(G):
+        members = []
+        rload = 0.0
+        while len(members) < cap:
+            cands = [e for e in range(E) if rank[e] < 0]
+            fits = [e for e in cands if rload + float(load[e]) <= limit]
+            pool = fits if fits else cands
+            best = None
+            for e in pool:
+                aff = 0.0
+                for f in sorted(members):
+                    aff += float(C[e][f])
+                key = (-aff, -total[e], e)
+                if best is None or key < best[0]:
+                    best = (key, e)
+            e = best[1]
+            rank[e] = r
+            members.append(e)
+            rload += float(load[e])
     return np.array(rank, dtype=np.int32)
