@@ -30,4 +30,5 @@ from .coact import (  # noqa: F401
     ema_update,
     colocated_coactivation,
     place_experts,
+    shuffle_balanced,
 )

@@ -652,3 +652,42 @@ def place_experts(C: np.ndarray, load: np.ndarray, G: int, eps: float) -> np.nda
             members.append(e)
             rload += float(load[e])
     return np.array(rank, dtype=np.int32)
+
+
+def shuffle_balanced(topk: np.ndarray, transition: np.ndarray, expert_rank_next: np.ndarray,
+                     G: int) -> dict:
+    """Token shuffle with equal shards: every rank receives exactly T/G
+    tokens, as the reduce-scatter that carries the shuffle ([EC] abstract)
+    hands each rank a fixed share.
+
+    Reading (the pages do not say how a full rank is handled): tokens are
+    taken in token order; each takes the highest-scoring rank (score_t[r] as
+    in shuffle_predict, ties to the lower rank) that still has room.  The new
+    order is stable, as in shuffle_predict."""
+    topk = np.asarray(topk)
+    T = topk.shape[0]
+    if T % G != 0:
+        raise OracleInputError("equal shards need T divisible by G")
+    cap = T // G
+    M = shuffle_predict(topk, transition, expert_rank_next, G)["rank_score"]
+    taken = [0] * G
+    pred = np.empty(T, dtype=np.int64)
+    for t in range(T):
+        score = np.zeros(G, dtype=np.int64)
+        for i in topk[t]:
+            score += M[int(i)]
+        prefs = sorted(range(G), key=lambda r: (-int(score[r]), r))
+        for r in prefs:
+            if taken[r] < cap:
+                pred[t] = r
+                taken[r] += 1
+                break
+    fill = [r * cap for r in range(G)]
+    dest_pos = np.empty(T, dtype=np.int64)
+    perm = np.empty(T, dtype=np.int64)
+    for t in range(T):
+        dest_pos[t] = fill[pred[t]]
+        perm[fill[pred[t]]] = t
+        fill[pred[t]] += 1
+    return {"pred_rank": pred, "dest_pos": dest_pos, "perm": perm,
+            "shard_offsets": np.arange(G + 1, dtype=np.int64) * cap}

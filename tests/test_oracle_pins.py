@@ -689,3 +689,75 @@ def test_placement_tiny_exhaustive_optimum():
     best = max(oracle.colocated_coactivation(C, np.array(p)) for p in
                itertools.product(range(2), repeat=4) if sorted(p).count(0) == 2)
     assert oracle.colocated_coactivation(C, er) == best == 17.0
+
+
+# ------------------------------------------------------------ balanced shuffle
+
+def _deferred_acceptance(score, G, cap):
+    """Tokens propose down their preference lists; each rank keeps its cap
+    lowest-index proposers and rejects the rest, until nobody is rejected.
+    With the same token priority at every rank this gives the same matching
+    as taking tokens in order (written here independently of the oracle)."""
+    T = score.shape[0]
+    prefs = [sorted(range(G), key=lambda r: (-int(score[t, r]), r)) for t in range(T)]
+    nxt = [0] * T
+    held = {r: [] for r in range(G)}
+    free = list(range(T))
+    while free:
+        for t in free:
+            held[prefs[t][nxt[t]]].append(t)
+            nxt[t] += 1
+        free = []
+        for r in range(G):
+            held[r].sort()
+            free += held[r][cap:]
+            held[r] = held[r][:cap]
+    out = np.empty(T, np.int64)
+    for r in range(G):
+        for t in held[r]:
+            out[t] = r
+    return out
+
+
+def test_balanced_shuffle_matches_deferred_acceptance():
+    rng = np.random.default_rng(80)
+    for trial in range(40):
+        G = int(rng.integers(1, 6))
+        T = G * int(rng.integers(1, 12))
+        E = int(rng.integers(2, 7))
+        k = int(rng.integers(1, E + 1))
+        topk = _random_routing(rng, T, E, k)
+        X = rng.integers(0, 3, size=(E, E))
+        er2 = rng.integers(0, G, size=E).astype(np.int32)
+        sh = oracle.shuffle_balanced(topk, X, er2, G)
+        M = oracle.shuffle_predict(topk, X, er2, G)["rank_score"]
+        score = np.stack([M[topk[t]].sum(axis=0) for t in range(T)]) if T else np.zeros((0, G))
+        assert sh["pred_rank"].tolist() == _deferred_acceptance(score, G, T // G).tolist()
+        assert (np.bincount(sh["pred_rank"], minlength=G) == T // G).all()
+        order = sorted(range(T), key=lambda t: (int(sh["pred_rank"][t]), t))
+        assert sh["perm"].tolist() == order
+
+
+def test_balanced_shuffle_equals_free_shuffle_when_balanced():
+    """If every rank is predicted by exactly T/G tokens, the capacity never
+    binds and the balanced shuffle is the unconstrained one."""
+    topk = np.array([[0], [1], [2], [3], [0], [1], [2], [3]], np.int32)
+    X = np.eye(4, dtype=np.int64) * 5
+    er2 = np.array([0, 1, 2, 3], np.int32)
+    a = oracle.shuffle_predict(topk, X, er2, 4)
+    b = oracle.shuffle_balanced(topk, X, er2, 4)
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert a[key].tolist() == b[key].tolist()
+
+
+def test_balanced_shuffle_local_share():
+    """Equal shards still keep more next-layer assignments local than the
+    1/G baseline, though fewer than the unconstrained shuffle can."""
+    w = make(5, T=4096, with_x=False)
+    st = oracle.coact_stats(w.topk, w.E, w.topk2, w.E)
+    sh = oracle.shuffle_balanced(w.topk, st["transition"], w.expert_rank2, w.G)
+    perm = sh["perm"]
+    p = oracle.dispatch_plan(w.topk2[perm], None, w.expert_rank2, w.G, w.ranks_per_node,
+                             src_offsets=sh["shard_offsets"])
+    share = p["counters"][3] / (w.T * w.k)
+    assert share > 0.125 + 0.05
