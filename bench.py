@@ -149,6 +149,38 @@ def placement_planner(w) -> dict:
             "rows_removed_frac": 1.0 - rows["planned"]["rows"] / rows["contiguous"]["rows"]}
 
 
+def shuffle_modes(w, x, z, steps: int) -> dict:
+    """The two-layer step with the free shuffle (shards sized by the
+    prediction) and with equal shards: shuffle time, layer-2 local share and
+    the largest shard, per mode."""
+    import numpy as np
+    import torch
+
+    from co_activation_amd.pipeline import StageTimers, TwoLayerStep
+
+    dev = "cuda"
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    out = {}
+    for name, bal in (("free", False), ("balanced", True)):
+        st = TwoLayerStep(i32(w.topk), i32(w.topk2), torch.from_numpy(w.gates2).to(dev),
+                          i32(w.expert_rank2), x, z, w.G, w.ranks_per_node, E1=w.E, balanced=bal)
+        st.run()
+        timers = StageTimers(("shuffle_predict",), steps)
+        for _ in range(steps):
+            st.run(timers)
+        torch.cuda.synchronize()
+        c = st.plan.counters.cpu().numpy()
+        off = st.shuffle["shard_offsets"].cpu().numpy()
+        out[name] = {"shuffle_predict_us": 1e3 * timers.mean_ms()["shuffle_predict"],
+                     "local_share": float(c[3]) / (w.T * w.k),
+                     "largest_shard": int(np.diff(off).max()), "rows": int(c[0])}
+        del st
+    return out
+
+
 def cpu_baseline(w, sample_tokens: int) -> dict:
     """The CPU oracle on the first `sample_tokens` tokens of the same
     workload, single-threaded; rows/s of the same step definition."""
@@ -328,6 +360,8 @@ def main() -> int:
     if not args.no_expert_side:
         line["expert_side"] = expert_side(step, w, args.steps, device_normal)
         line["placement"] = placement_planner(w)
+        if w.cfg == 5:
+            line["shuffle_modes"] = shuffle_modes(w, x, z, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
     print(json.dumps(line), flush=True)

@@ -35,6 +35,7 @@ EXPORTS = (
     "moe_shuffle_predict_workspace_size", "moe_shuffle_predict",
     "moe_expert_plan_workspace_size", "moe_expert_plan",
     "moe_permute_scaled", "moe_row_dot", "moe_ema_update", "moe_place_experts",
+    "moe_shuffle_balanced_workspace_size", "moe_shuffle_balanced",
 )
 
 _lib = None
@@ -61,6 +62,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.moe_shuffle_predict.argtypes = [P, c_int64, c_int, c_int, P, c_int, P, c_int, P, P, P, P,
                                         P, P, c_size_t, P]
     lib.moe_shuffle_predict.restype = c_int
+    lib.moe_shuffle_balanced_workspace_size.argtypes = [c_int64, c_int, c_int, POINTER(c_size_t)]
+    lib.moe_shuffle_balanced_workspace_size.restype = c_int
+    lib.moe_shuffle_balanced.argtypes = [P, c_int64, c_int, c_int, P, c_int, P, c_int, P, P, P, P,
+                                         P, P, c_size_t, P]
+    lib.moe_shuffle_balanced.restype = c_int
     lib.moe_expert_plan_workspace_size.argtypes = [c_int64, c_int, POINTER(c_size_t)]
     lib.moe_expert_plan_workspace_size.restype = c_int
     lib.moe_expert_plan.argtypes = [P, P, c_int64, c_int, c_int, P, c_int, P, c_int64, P, P, P, P,

@@ -128,6 +128,262 @@ __global__ __launch_bounds__(kPredThreads) void predict_kernel(
 }  // namespace
 }  // namespace moe
 
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Capacity-balanced shuffle: every rank receives exactly C = T/G tokens.
+// Tokens in order take their best-scoring rank that still has room.  With
+// the index f_r of the token that fills rank r (its C-th taker), token t's
+// choice is its best rank with f_r >= t, independently of the other tokens;
+// so the fill indices are found as a fixed point: start from "never full",
+// assign every token, set f_r to the index of r's C-th taker, repeat.  The
+// rank that fills first is exact after one round, the next after two, and
+// so on: at most G rounds, stopping early once the f_r stop changing.
+
+constexpr int kBalTile = 256;
+
+// Best available rank of token t (score descending, lower rank on ties);
+// -1 if none is available.
+__device__ __forceinline__ int best_available(const int64_t* __restrict__ score_row, int G,
+                                              const int* fill, int t) {
+  int best = -1;
+  long long bs = 0;
+  for (int r = 0; r < G; ++r) {
+    if (fill[r] < t) continue;
+    const long long sc = score_row[r];
+    if (best < 0 || sc > bs) {
+      best = r;
+      bs = sc;
+    }
+  }
+  return best;
+}
+
+// scores[t][r] = sum_{i in D_t} M[i][r]; block 0 also resets the fill
+// indices to "never full" and the convergence flag.
+__global__ __launch_bounds__(kBalTile) void balanced_scores_kernel(
+    const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
+    int64_t* __restrict__ scores, int32_t* __restrict__ fill, int32_t* __restrict__ flag,
+    int32_t* d_err) {
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = INT32_MAX;
+    if (threadIdx.x == 0) *flag = 0;
+  }
+  const int t = blockIdx.x * kBalTile + threadIdx.x;
+  if (t >= T) return;
+  int e[MOE_MAX_K];
+  int errbits = 0;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_K; ++j) {
+    e[j] = -1;
+    if (j < k) {
+      const int v = topk[static_cast<int64_t>(t) * k + j];
+      if (v >= 0 && v < E)
+        e[j] = v;
+      else
+        errbits |= MOE_DERR_EXPERT_RANGE;
+    }
+  }
+  for (int r = 0; r < G; ++r) {
+    long long sc = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j)
+      if (e[j] >= 0) sc += M[static_cast<int64_t>(e[j]) * G + r];
+    scores[static_cast<int64_t>(t) * G + r] = sc;
+  }
+  report(d_err, errbits);
+}
+
+// One round, part 1: every token's choice under the current fill indices,
+// counted per (tile, rank) with wave ballots.
+__global__ __launch_bounds__(kBalTile) void balanced_assign_kernel(
+    const int64_t* __restrict__ scores, int T, int G, const int32_t* __restrict__ fill_g,
+    const int32_t* __restrict__ flag, int32_t* __restrict__ tile_cnt) {
+  __shared__ int fill[MOE_MAX_G];
+  __shared__ int s_cnt[kBalTile / kWave][kWave];
+  if (*flag) return;
+  if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = fill_g[threadIdx.x];
+  __syncthreads();
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int t = blockIdx.x * kBalTile + threadIdx.x;
+  const int a = t < T ? best_available(scores + static_cast<int64_t>(t) * G, G, fill, t) : -1;
+  int mine = 0;
+  for (int r = 0; r < G; ++r) {
+    const uint64_t b = ballot(a == r);
+    if (lane == r) mine = __popcll(b);
+  }
+  if (lane < G) s_cnt[wave][lane] = mine;
+  __syncthreads();
+  if (threadIdx.x < static_cast<unsigned>(G)) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kBalTile / kWave; ++w) c += s_cnt[w][threadIdx.x];
+    tile_cnt[static_cast<int64_t>(blockIdx.x) * G + threadIdx.x] = c;
+  }
+}
+
+constexpr int kBalUpdThreads = 1024;
+
+// One round, part 2 (one block): for each rank, the tile where its takers
+// reach C, then the exact C-th taker inside that tile; new fill indices, or
+// the convergence flag when none changed.
+__global__ __launch_bounds__(kBalUpdThreads) void balanced_update_kernel(
+    const int64_t* __restrict__ scores, int T, int G, int cap, int NT,
+    const int32_t* __restrict__ tile_cnt, int32_t* __restrict__ fill_g, int32_t* __restrict__ flag) {
+  __shared__ int fill[MOE_MAX_G];
+  __shared__ int nfill[MOE_MAX_G];
+  if (*flag) return;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = fill_g[threadIdx.x];
+  __syncthreads();
+  for (int r = wave; r < G; r += kBalUpdThreads / kWave) {
+    // tile where the running count of r's takers reaches cap
+    int carry = 0, hit_tile = -1, need = 0;
+    for (int base = 0; base < NT && hit_tile < 0; base += kWave) {
+      const int j = base + lane;
+      const int v = j < NT ? tile_cnt[static_cast<int64_t>(j) * G + r] : 0;
+      const int incl = wave_incl_scan(v) + carry;
+      const uint64_t b = ballot(j < NT && incl >= cap);
+      if (b) {
+        const int first = __ffsll(static_cast<long long>(b)) - 1;
+        hit_tile = base + first;
+        need = cap - (__shfl(incl, first, kWave) - __shfl(v, first, kWave));
+      }
+      carry = __shfl(incl, kWave - 1, kWave);
+    }
+    int nf = INT32_MAX;
+    if (hit_tile >= 0) {
+      // the need-th taker of r inside tile hit_tile
+      int seen = 0;
+      for (int c = 0; c < kBalTile; c += kWave) {
+        const int t = hit_tile * kBalTile + c + lane;
+        const int a = t < T ? best_available(scores + static_cast<int64_t>(t) * G, G, fill, t) : -1;
+        const uint64_t b = ballot(a == r);
+        const int cnt = __popcll(b);
+        if (seen + cnt >= need) {
+          // position need - seen (1-based) among the set bits of b
+          uint64_t m = b;
+          for (int q = 1; q < need - seen; ++q) m &= m - 1;
+          nf = hit_tile * kBalTile + c + (__ffsll(static_cast<long long>(m)) - 1);
+          break;
+        }
+        seen += cnt;
+      }
+    }
+    if (lane == 0) nfill[r] = nf;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bool same = true;
+    for (int r = 0; r < G; ++r) same = same && (nfill[r] == fill[r]);
+    if (same) *flag = 1;
+  }
+  if (threadIdx.x < static_cast<unsigned>(G)) fill_g[threadIdx.x] = nfill[threadIdx.x];
+}
+
+__global__ __launch_bounds__(kBalTile) void balanced_final_kernel(
+    const int64_t* __restrict__ scores, int T, int G, const int32_t* __restrict__ fill_g,
+    int32_t* __restrict__ pred) {
+  __shared__ int fill[MOE_MAX_G];
+  if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = fill_g[threadIdx.x];
+  __syncthreads();
+  const int t = blockIdx.x * kBalTile + threadIdx.x;
+  if (t >= T) return;
+  const int a = best_available(scores + static_cast<int64_t>(t) * G, G, fill, t);
+  pred[t] = a < 0 ? 0 : a;
+}
+
+struct BalancedWs {
+  ShuffleWs base;
+  int64_t* scores;
+  int32_t* fill;
+  int32_t* flag;
+  int32_t* tile_cnt;
+  size_t bytes;
+};
+
+BalancedWs balanced_layout(void* base, int64_t T, int E, int G) {
+  BalancedWs w{};
+  w.base = shuffle_layout(base, T, E, G);
+  char* p = static_cast<char*>(base);
+  size_t off = w.base.bytes;
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + off : nullptr;
+    off += align256(bytes);
+    return q;
+  };
+  const int64_t nt = (T + kBalTile - 1) / kBalTile;
+  w.scores = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * (T > 0 ? T : 1) * G));
+  w.fill = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * G));
+  w.flag = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
+  w.tile_cnt = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (nt > 0 ? nt : 1) * G));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_shuffle_balanced_workspace_size(int64_t T, int E, int G, size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return MOE_ERR_NULL;
+  if (T < 0 || E < 1 || E > MOE_MAX_E || G < 1 || G > MOE_MAX_G) return MOE_ERR_SHAPE;
+  *ws_bytes = moe::balanced_layout(nullptr, T, E, G).bytes;
+  return MOE_OK;
+}
+
+extern "C" int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E,
+                                    const int32_t* transition, int E_next,
+                                    const int32_t* expert_rank_next, int G, int32_t* pred_rank,
+                                    int32_t* dest_pos, int32_t* perm, int32_t* shard_offsets,
+                                    int32_t* d_err, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_K || E < 1 || E > MOE_MAX_E || E_next < 1 ||
+      E_next > MOE_MAX_E || G < 1 || G > MOE_MAX_G ||
+      T * static_cast<int64_t>(k) >= (int64_t{1} << 31) || T % G != 0)
+    return MOE_ERR_SHAPE;
+  if (transition == nullptr || expert_rank_next == nullptr || shard_offsets == nullptr ||
+      ws == nullptr)
+    return MOE_ERR_NULL;
+  if (T > 0 && (topk == nullptr || pred_rank == nullptr || dest_pos == nullptr))
+    return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return MOE_ERR_ALIGN;
+  const moe::BalancedWs w = moe::balanced_layout(ws, T, E, G);
+  if (ws_bytes < w.bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int Ti = static_cast<int>(T);
+  const int NT = static_cast<int>((T + moe::kBalTile - 1) / moe::kBalTile);
+  const int blocks = NT > 0 ? NT : 1;
+
+  moe::rank_score_kernel<<<E, moe::kScoreThreads, 0, s>>>(transition, E_next, expert_rank_next, G,
+                                                          Ti, w.base.M, w.base.identity,
+                                                          w.base.src1, d_err);
+  MOE_CHECK_LAUNCH();
+  moe::balanced_scores_kernel<<<blocks, moe::kBalTile, 0, s>>>(topk, Ti, k, E, w.base.M, G,
+                                                               w.scores, w.fill, w.flag, d_err);
+  MOE_CHECK_LAUNCH();
+  if (Ti > 0) {
+    for (int round = 0; round < G; ++round) {
+      moe::balanced_assign_kernel<<<NT, moe::kBalTile, 0, s>>>(w.scores, Ti, G, w.fill, w.flag,
+                                                               w.tile_cnt);
+      MOE_CHECK_LAUNCH();
+      moe::balanced_update_kernel<<<1, moe::kBalUpdThreads, 0, s>>>(w.scores, Ti, G, Ti / G, NT,
+                                                                    w.tile_cnt, w.fill, w.flag);
+      MOE_CHECK_LAUNCH();
+    }
+    moe::balanced_final_kernel<<<NT, moe::kBalTile, 0, s>>>(w.scores, Ti, G, w.fill, pred_rank);
+    MOE_CHECK_LAUNCH();
+  }
+  moe::PlanArgs a{pred_rank,      nullptr,        Ti,        1,
+                  G,              w.base.identity, G,        G,
+                  w.base.src1,    T,              w.base.send_counts, w.base.send_offsets,
+                  perm ? perm : w.base.perm_scratch, nullptr, dest_pos,
+                  nullptr,        w.base.counters, d_err,    w.base.plan_ws,
+                  shard_offsets};
+  return moe::launch_plan(a, s);
+}
+
 extern "C" int moe_shuffle_predict_workspace_size(int64_t T, int E, int G, size_t* ws_bytes) {
   if (ws_bytes == nullptr) return MOE_ERR_NULL;
   if (T < 0 || E < 1 || E > MOE_MAX_E || G < 1 || G > MOE_MAX_G) return MOE_ERR_SHAPE;

@@ -206,19 +206,19 @@ def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tens
 
 # ----------------------------------------------------------------- shuffle
 
-def shuffle_workspace_bytes(T: int, E: int, G: int) -> int:
+def shuffle_workspace_bytes(T: int, E: int, G: int, balanced: bool = False) -> int:
     n = ctypes.c_size_t()
-    check("moe_shuffle_predict_workspace_size",
-          _lib.lib().moe_shuffle_predict_workspace_size(T, E, G, ctypes.byref(n)))
+    fn = "moe_shuffle_balanced_workspace_size" if balanced else "moe_shuffle_predict_workspace_size"
+    check(fn, getattr(_lib.lib(), fn)(T, E, G, ctypes.byref(n)))
     return n.value
 
 
 def shuffle_predict(topk: torch.Tensor, transition: torch.Tensor, expert_rank_next: torch.Tensor,
-                    G: int, *, with_perm: bool = True, out: Optional[dict] = None,
-                    ws: Optional[torch.Tensor] = None,
+                    G: int, *, balanced: bool = False, with_perm: bool = True,
+                    out: Optional[dict] = None, ws: Optional[torch.Tensor] = None,
                     d_err: Optional[torch.Tensor] = None) -> dict:
-    """moe_shuffle_predict: pred_rank [T], dest_pos [T], perm [T],
-    shard_offsets [G+1]."""
+    """moe_shuffle_predict (or moe_shuffle_balanced with balanced=True):
+    pred_rank [T], dest_pos [T], perm [T], shard_offsets [G+1]."""
     _want(topk, "topk", torch.int32)
     T, k = topk.shape
     E, E2 = transition.shape
@@ -231,15 +231,15 @@ def shuffle_predict(topk: torch.Tensor, transition: torch.Tensor, expert_rank_ne
         "perm": _alloc(out, "perm", (T,), torch.int32, dev) if with_perm else None,
         "shard_offsets": _alloc(out, "shard_offsets", (G + 1,), torch.int32, dev),
     }
-    need = shuffle_workspace_bytes(T, E, G)
-    if ws is None:
+    need = shuffle_workspace_bytes(T, E, G, balanced)
+    if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _want(ws, "ws", torch.uint8)
-    st = _lib.lib().moe_shuffle_predict(
-        _p(topk), T, k, E, _p(transition), E2, _p(expert_rank_next), G, _p(res["pred_rank"]),
-        _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(d_err), _p(ws),
-        ws.numel(), _stream())
-    check("moe_shuffle_predict", st)
+    fn = _lib.lib().moe_shuffle_balanced if balanced else _lib.lib().moe_shuffle_predict
+    st = fn(_p(topk), T, k, E, _p(transition), E2, _p(expert_rank_next), G, _p(res["pred_rank"]),
+            _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(d_err), _p(ws),
+            ws.numel(), _stream())
+    check("moe_shuffle_balanced" if balanced else "moe_shuffle_predict", st)
     return res
 
 

@@ -176,8 +176,10 @@ class TwoLayerStep:
     """Layer-1 statistics with transitions, shuffle prediction, the shuffle,
     and the layer-2 deduplicated dispatch and combine."""
 
-    def __init__(self, topk1, topk2, gates2, expert_rank2, x, z, G, ranks_per_node, E1=None):
+    def __init__(self, topk1, topk2, gates2, expert_rank2, x, z, G, ranks_per_node, E1=None,
+                 balanced=False):
         dev = topk1.device
+        self.balanced = balanced
         self.T, self.k1 = topk1.shape
         self.k2 = topk2.shape[1]
         self.E1 = E1 if E1 is not None else expert_rank2.numel()
@@ -199,8 +201,8 @@ class TwoLayerStep:
             "perm": torch.empty(T, dtype=torch.int32, device=dev),
             "shard_offsets": torch.empty(G + 1, dtype=torch.int32, device=dev),
         }
-        self.shuffle_ws = torch.empty(ops.shuffle_workspace_bytes(T, E1, G), dtype=torch.uint8,
-                                      device=dev)
+        self.shuffle_ws = torch.empty(ops.shuffle_workspace_bytes(T, E1, G, balanced),
+                                      dtype=torch.uint8, device=dev)
         self.x_s = torch.empty_like(x)
         self.topk2_s = torch.empty_like(topk2)
         self.gates2_s = torch.empty_like(gates2)
@@ -221,7 +223,8 @@ class TwoLayerStep:
                                     d_err=self.d_err)
         with _timed(timers, "shuffle_predict"):
             self.shuffle = ops.shuffle_predict(self.topk1, stats["transition"], self.expert_rank2,
-                                               self.G, out=self.shuffle_out, ws=self.shuffle_ws,
+                                               self.G, balanced=self.balanced,
+                                               out=self.shuffle_out, ws=self.shuffle_ws,
                                                d_err=self.d_err)
         dest = self.shuffle["dest_pos"]
         with _timed(timers, "shuffle_permute"):

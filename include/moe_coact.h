@@ -231,6 +231,22 @@ int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E, const int3
                         int32_t* d_err, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_shuffle_balanced -- token shuffling with equal shards: every rank
+ * receives exactly T/G tokens (T % G == 0), as the reduce-scatter that
+ * carries the shuffle hands each rank a fixed share ([EC] abstract).
+ * Tokens in order take their highest-scoring rank (the scores of
+ * moe_shuffle_predict, lower rank on ties) that still has room.  Arguments,
+ * outputs and workspace rules as for moe_shuffle_predict, with
+ * moe_shuffle_balanced_workspace_size(); pred_rank receives the assigned
+ * rank and shard_offsets = [0, T/G, 2T/G, ..., T].
+ * ---------------------------------------------------------------------- */
+int moe_shuffle_balanced_workspace_size(int64_t T, int E, int G, size_t* ws_bytes /* host */);
+int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E, const int32_t* transition,
+                         int E_next, const int32_t* expert_rank_next, int G, int32_t* pred_rank,
+                         int32_t* dest_pos, int32_t* perm, int32_t* shard_offsets,
+                         int32_t* d_err, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_expert_plan -- destination-side layout for the expert computation.
  *
  * Every assignment (t, j) -- expert e = D_t[j] on rank r = expert_rank[e] --

@@ -73,20 +73,22 @@ def test_layer_fullsize(cfg, placement):
     _check_samples(step, ref, lambda t: w.x[t], w.gates, w.dtype, np.random.default_rng(cfg))
 
 
-def test_two_layer_fullsize():
+@pytest.mark.parametrize("balanced", [False, True])
+def test_two_layer_fullsize(balanced):
     w = make(5)
-    say("fullsize two-layer", w.T, w.H)
+    say("fullsize two-layer", w.T, w.H, "balanced" if balanced else "free")
     cap = w.T * min(w.k, w.G)
     z = device_normal(cap, w.H, w.dtype, seed=1)
     step = TwoLayerStep(i32(w.topk), i32(w.topk2), dev(w.gates2), i32(w.expert_rank2),
-                        x_tensor(w), z, w.G, w.ranks_per_node, E1=w.E)
+                        x_tensor(w), z, w.G, w.ranks_per_node, E1=w.E, balanced=balanced)
     step.run()
     torch.cuda.synchronize()
     assert int(step.d_err.item()) == 0
     st = oracle.coact_stats(w.topk, w.E, w.topk2, w.E)
     for key in ("expert_count", "pair_count", "ochiai", "transition"):
         assert_equal(host(step.stats_out[key]), st[key], key)
-    sh = oracle.shuffle_predict(w.topk, st["transition"], w.expert_rank2, w.G)
+    sh = (oracle.shuffle_balanced if balanced else oracle.shuffle_predict)(
+        w.topk, st["transition"], w.expert_rank2, w.G)
     for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
         assert_equal(host(step.shuffle[key]), sh[key], key)
     perm = sh["perm"]

@@ -442,3 +442,42 @@ def test_permute_word_rows(words, width):
             if dest[t, q] >= 0:
                 want[dest[t, q]] = rows[t]
     assert_equal(host(out), want, "word rows")
+
+
+# ------------------------------------------------------------------ balanced shuffle
+
+@pytest.mark.parametrize("E,E2,k,G,T,seed", [(64, 64, 2, 8, 4096, 0), (256, 256, 8, 64, 2048, 1),
+                                             (16, 40, 3, 5, 1000, 2), (8, 8, 1, 3, 300, 3),
+                                             (8, 8, 2, 1, 64, 4), (32, 32, 2, 4, 4, 5)])
+def test_balanced_shuffle_parity(E, E2, k, G, T, seed):
+    """Random small-integer transitions (many ties), every shape path."""
+    rng = np.random.default_rng(seed)
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    X = rng.integers(0, 3, size=(E, E2)).astype(np.int32)
+    er2 = rng.integers(0, G, size=E2).astype(np.int32)
+    say("balanced shuffle", E, E2, k, G, T)
+    err = _err()
+    sh = ops.shuffle_predict(i32(topk), i32(X), i32(er2), G, balanced=True, d_err=err)
+    _no_errors(err)
+    ref = oracle.shuffle_balanced(topk, X, er2, G)
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert_equal(host(sh[key]), ref[key], key)
+
+
+def test_balanced_two_layer_step():
+    w = make(5, T=4104, H=256)
+    say("balanced two-layer step")
+    cap = w.T * min(w.k, w.G)
+    Z = expert_outputs(cap, w.H, "bf16", seed=1)
+    step = TwoLayerStep(i32(w.topk), i32(w.topk2), dev(w.gates2), i32(w.expert_rank2),
+                        x_tensor(w), dev(Z), w.G, w.ranks_per_node, E1=w.E, balanced=True)
+    step.run()
+    _no_errors(step.d_err)
+    st = oracle.coact_stats(w.topk, w.E, w.topk2, w.E)
+    sh = oracle.shuffle_balanced(w.topk, st["transition"], w.expert_rank2, w.G)
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert_equal(host(step.shuffle[key]), sh[key], key)
+    perm = sh["perm"]
+    ref = oracle.dispatch_plan(w.topk2[perm], w.gates2[perm], w.expert_rank2, w.G,
+                               w.ranks_per_node, src_offsets=sh["shard_offsets"])
+    _check_plan(step.plan, ref, w.T, w.k)
