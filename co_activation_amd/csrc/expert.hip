@@ -14,9 +14,10 @@
 //           popcounts give per-(tile, expert) counts.  Also fills row_dest
 //           with -1.
 //   scan  : one block; per expert the exclusive prefix over tiles; expert
-//           blocks placed in (rank, id) order; per-tile bases.
-//   write : same tiles and columns; a slot's position in its expert block is
-//           the popcount of its column below its token.
+//           blocks placed in (rank, id) order.
+//   write : same tiles and columns; a slot's row is its expert's first row
+//           plus the tile's prefix plus the popcount of its column below its
+//           token.
 #include "common.hpp"
 
 namespace moe {
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(kExTile) void expert_count_kernel(
     int c = 0;
 #pragma unroll
     for (int w = 0; w < kExWords; ++w) c += __popcll(cols[e][w]);
-    tile_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+    tile_cnt[static_cast<int64_t>(e) * gridDim.x + blockIdx.x] = c;
   }
 }
 
@@ -97,7 +98,8 @@ __global__ __launch_bounds__(kExScanThreads) void expert_scan_kernel(
     int32_t* __restrict__ rank_offsets) {
   __shared__ int s_count[MOE_MAX_E];
   __shared__ int s_rank[MOE_MAX_E];
-  __shared__ int s_first[MOE_MAX_E];
+  __shared__ int s_rtot[MOE_MAX_G + 1];
+  __shared__ int s_roff[MOE_MAX_G + 1];
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
@@ -105,46 +107,78 @@ __global__ __launch_bounds__(kExScanThreads) void expert_scan_kernel(
     const int r = expert_rank[e];
     s_rank[e] = (r >= 0 && r < G) ? r : G;  // unplaced experts sort last, hold no rows
   }
-  // Per expert: exclusive prefix of its tile counts, and its total.
+  // Per expert: exclusive prefix of its tile counts, and its total.  The
+  // loads of every chunk of the wave's next expert are issued before its
+  // scan (kPre chunks of 64 tiles at once), so latencies overlap.
+  constexpr int kPre = 8;
   for (int e = wave; e < E; e += kExScanWaves) {
+    int pre[kPre];
+#pragma unroll
+    for (int c = 0; c < kPre; ++c) {
+      const int j = c * kWave + lane;
+      pre[c] = j < NT ? tile_cnt[static_cast<int64_t>(e) * NT + j] : 0;
+    }
     int carry = 0;
-    for (int base = 0; base < NT; base += kWave) {
+#pragma unroll
+    for (int c = 0; c < kPre; ++c) {
+      if (c * kWave >= NT) break;
+      const int j = c * kWave + lane;
+      const int incl = wave_incl_scan(pre[c]) + carry;
+      if (j < NT) tile_cnt[static_cast<int64_t>(e) * NT + j] = incl - pre[c];
+      carry = __shfl(incl, kWave - 1, kWave);
+    }
+    for (int base = kPre * kWave; base < NT; base += kWave) {
       const int j = base + lane;
-      const int v = j < NT ? tile_cnt[static_cast<int64_t>(j) * E + e] : 0;
+      const int v = j < NT ? tile_cnt[static_cast<int64_t>(e) * NT + j] : 0;
       const int incl = wave_incl_scan(v) + carry;
-      if (j < NT) tile_cnt[static_cast<int64_t>(j) * E + e] = incl - v;
+      if (j < NT) tile_cnt[static_cast<int64_t>(e) * NT + j] = incl - v;
       carry = __shfl(incl, kWave - 1, kWave);
     }
     if (lane == 0) s_count[e] = carry;
   }
   __syncthreads();
-  // Expert blocks in (rank, id) order.
-  for (int e = tid; e < E; e += kExScanThreads) {
-    const int re = s_rank[e];
-    int first = 0;
-    for (int f = 0; f < E; ++f) {
-      const int rf = s_rank[f];
-      if (rf < re || (rf == re && f < e)) first += s_count[f];
-    }
-    s_first[e] = first;
-    expert_first[e] = first;
-    expert_count[e] = s_count[e];
-  }
-  for (int r = tid; r <= G; r += kExScanThreads) {
-    int off = 0;
-    for (int f = 0; f < E; ++f)
-      if (s_rank[f] < r) off += s_count[f];
-    rank_offsets[r] = off;
+  // Expert blocks in (rank, id) order: rank totals by LDS atomics, a scan
+  // over ranks, then each expert's offset inside its rank as the sum of the
+  // counts of lower-id experts of the same rank (tpe threads per expert).
+  if (tid <= G) s_rtot[tid] = 0;
+  __syncthreads();
+  for (int e = tid; e < E; e += kExScanThreads)
+    if (s_rank[e] < G) atomicAdd(&s_rtot[s_rank[e]], s_count[e]);
+  __syncthreads();
+  if (wave == 0) {
+    const int v = lane < G ? s_rtot[lane] : 0;
+    const int incl = wave_incl_scan(v);
+    if (lane < G) s_roff[lane] = incl - v;
+    if (lane == 0) s_roff[G] = __shfl(incl, kWave - 1, kWave);
   }
   __syncthreads();
-  for (int64_t idx = tid; idx < static_cast<int64_t>(NT) * E; idx += kExScanThreads)
-    tile_cnt[idx] += s_first[idx % E];
+  int tpe = kExScanThreads / E;
+  tpe = tpe >= 64 ? 64 : (tpe >= 32 ? 32 : (tpe >= 16 ? 16 : (tpe >= 8 ? 8 : (tpe >= 4 ? 4 : (tpe >= 2 ? 2 : 1)))));
+  for (int base = 0; base < E * tpe; base += kExScanThreads) {
+    const int g = base + tid;
+    const int e = g / tpe, sub = g % tpe;
+    int part = 0;
+    if (e < E) {
+      const int re = s_rank[e];
+      for (int f = sub; f < e; f += tpe)
+        if (s_rank[f] == re) part += s_count[f];
+    }
+    for (int d = tpe >> 1; d >= 1; d >>= 1) part += __shfl_xor(part, d, kWave);
+    if (e < E && sub == 0) {
+      const int re = s_rank[e];
+      const int first = (re < G ? s_roff[re] : s_roff[G]) + part;
+      expert_first[e] = first;
+      expert_count[e] = s_count[e];
+    }
+  }
+  for (int r = tid; r <= G; r += kExScanThreads) rank_offsets[r] = s_roff[r];
 }
 
 __global__ __launch_bounds__(kExTile) void expert_write_kernel(
     const int32_t* __restrict__ topk, const float* __restrict__ gates, int T, int k, int E,
     const int32_t* __restrict__ expert_rank, int G, const int32_t* __restrict__ tile_base,
-    const int32_t* __restrict__ slot_row, int64_t send_rows, int32_t* __restrict__ erow,
+    const int32_t* __restrict__ expert_first, const int32_t* __restrict__ slot_row,
+    int64_t send_rows, int32_t* __restrict__ erow,
     float* __restrict__ erow_weight, int32_t* __restrict__ erow_slot,
     int32_t* __restrict__ row_dest, int32_t* d_err) {
   __shared__ uint64_t cols[MOE_MAX_E][kExWords];
@@ -167,7 +201,7 @@ __global__ __launch_bounds__(kExTile) void expert_write_kernel(
     const int e = ex[j];
     int pos = __popcll(cols[e][word] & below);
     for (int w = 0; w < word; ++w) pos += __popcll(cols[e][w]);
-    const int row = tile_base[static_cast<int64_t>(blockIdx.x) * E + e] + pos;
+    const int row = expert_first[e] + tile_base[static_cast<int64_t>(e) * gridDim.x + blockIdx.x] + pos;
     erow[slot] = row;
     if (erow_weight != nullptr) erow_weight[row] = gates != nullptr ? gates[slot] : 0.f;
     if (erow_slot != nullptr) erow_slot[row] = static_cast<int32_t>(slot);
@@ -228,8 +262,9 @@ extern "C" int moe_expert_plan(const int32_t* topk, const float* gates, int64_t 
   MOE_CHECK_LAUNCH();
   if (NT > 0) {
     moe::expert_write_kernel<<<NT, moe::kExTile, 0, s>>>(topk, gates, Ti, k, E, expert_rank, G,
-                                                          tile_cnt, slot_row, send_rows, erow,
-                                                          erow_weight, erow_slot, row_dest, d_err);
+                                                          tile_cnt, expert_first, slot_row,
+                                                          send_rows, erow, erow_weight, erow_slot,
+                                                          row_dest, d_err);
     MOE_CHECK_LAUNCH();
   }
   return MOE_OK;

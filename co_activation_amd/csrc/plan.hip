@@ -15,8 +15,8 @@
 //           order independent.
 //   scan  : one block; per rank a segmented scan over the tiles of each
 //           source rank (rank r's tiles are walked by one wave 64 at a time),
-//           then an exclusive scan of S[s][r] in (s, r) order; turns the
-//           per-tile counts into each tile's first row per rank.
+//           then an exclusive scan of S[s][r] in (s, r) order; per tile it
+//           leaves the prefix inside its (s, r) block.
 //   write : one block per tile; the same ballots give each token's position
 //           inside its wave, LDS gives the wave's offset inside the tile.
 #include "plan.hpp"
@@ -79,7 +79,8 @@ __device__ __forceinline__ bool block_tile(const int32_t* off, int T, int G, int
 __global__ __launch_bounds__(kPlanTile) void plan_count_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int32_t* __restrict__ expert_rank,
     int G, int ranks_per_node, const int32_t* __restrict__ src_offsets,
-    int32_t* __restrict__ tile_cnt, int32_t* __restrict__ tile_stats, int32_t* d_err) {
+    int32_t* __restrict__ tile_cnt, int64_t stride, int32_t* __restrict__ tile_stats,
+    int32_t* d_err) {
   __shared__ int s_cnt[kPlanTile / kWave][kWave];
   __shared__ int s_stat[kPlanTile / kWave][4];
   const int lane = lane_id();
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kPlanTile) void plan_count_kernel(
     int c = 0;
 #pragma unroll
     for (int w = 0; w < kPlanTile / kWave; ++w) c += s_cnt[w][threadIdx.x];
-    tile_cnt[static_cast<int64_t>(j) * G + threadIdx.x] = c;
+    tile_cnt[static_cast<int64_t>(threadIdx.x) * stride + j] = c;
   }
   if (threadIdx.x < 4) {
     int c = 0;
@@ -170,7 +171,7 @@ __device__ __forceinline__ int shard_of_tile(int j, const int* incl, int G) {
 
 __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
     const int32_t* __restrict__ src_offsets, int T, int k, int G, int32_t* __restrict__ tile_cnt,
-    const int32_t* __restrict__ tile_stats, int64_t row_capacity, int32_t* __restrict__ send_counts,
+    int64_t stride, const int32_t* __restrict__ tile_stats, int64_t row_capacity, int32_t* __restrict__ send_counts,
     int32_t* __restrict__ send_offsets, int64_t* __restrict__ counters,
     int32_t* __restrict__ first_offsets, int32_t* d_err) {
   __shared__ int s_incl[kWave];
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
 #pragma unroll
     for (int c = 0; c < kPrefetch; ++c) {
       const int j = c * kWave + lane;
-      pre[c] = j < NT ? tile_cnt[static_cast<int64_t>(j) * G + r] : 0;
+      pre[c] = j < NT ? tile_cnt[static_cast<int64_t>(r) * stride + j] : 0;
     }
     int carry = 0;
     for (int base = 0, c = 0; base < NT; base += kWave, ++c) {
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
         for (int q = 0; q < kPrefetch; ++q)
           if (q == c) v = pre[q];
       } else if (in) {
-        v = tile_cnt[static_cast<int64_t>(j) * G + r];
+        v = tile_cnt[static_cast<int64_t>(r) * stride + j];
       }
       const int s = in ? shard_of_tile(j, s_incl, G) : 0;
       const bool head = in && s_first[s] == j;
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
         }
       }
       if (!flag) val += carry;
-      if (in) tile_cnt[static_cast<int64_t>(j) * G + r] = val - v;
+      if (in) tile_cnt[static_cast<int64_t>(r) * stride + j] = val - v;
       if (last) s_S[s * G + r] = val;
       carry = __shfl(val, kWave - 1, kWave);
     }
@@ -281,13 +282,6 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
   __syncthreads();
   if (first_offsets != nullptr && tid <= G) first_offsets[tid] = tid < n ? s_S[tid] : total_rows;
 
-  // Each tile's first row per destination rank.
-  for (int idx = tid; idx < NT * G; idx += kScanThreads) {
-    const int j = idx / G;
-    const int r = idx - j * G;
-    tile_cnt[idx] += s_S[shard_of_tile(j, s_incl, G) * G + r];
-  }
-
   // Counters.
   long long c[4] = {0, 0, 0, 0};
   for (int j = tid; j < NT; j += kScanThreads) {
@@ -317,7 +311,9 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
 __global__ __launch_bounds__(kPlanTile) void plan_write_kernel(
     const int32_t* __restrict__ topk, const float* __restrict__ gates, int T, int k, int E,
     const int32_t* __restrict__ expert_rank, int G, const int32_t* __restrict__ src_offsets,
-    const int32_t* __restrict__ tile_base, int64_t row_capacity, int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ tile_base, int64_t stride,
+    const int32_t* __restrict__ send_offsets, int64_t row_capacity,
+    int32_t* __restrict__ row_token,
     float* __restrict__ row_weight, int32_t* __restrict__ token_rows,
     int32_t* __restrict__ slot_row, int32_t* d_err) {
   __shared__ int s_cnt[kPlanTile / kWave][kWave];
@@ -355,10 +351,11 @@ __global__ __launch_bounds__(kPlanTile) void plan_write_kernel(
   }
   if (lane < G) s_cnt[wave][lane] = mine;
   __syncthreads();
-  // First row of (this wave, rank = lane).
+  // First row of (this wave, rank = lane): the (s, r) block's offset, the
+  // tile's prefix inside the block, the earlier waves of the tile.
   int mybase = 0;
   if (lane < G) {
-    mybase = tile_base[static_cast<int64_t>(blockIdx.x) * G + lane];
+    mybase = send_offsets[s * G + lane] + tile_base[static_cast<int64_t>(lane) * stride + blockIdx.x];
     for (int w2 = 0; w2 < wave; ++w2) mybase += s_cnt[w2][lane];
   }
 
@@ -407,18 +404,19 @@ int launch_plan(const PlanArgs& a, hipStream_t stream) {
   int32_t* tile_stats = tile_cnt + nt * a.G;
   if (nt > 0) {
     plan_count_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(kPlanTile), 0, stream>>>(
-        a.topk, a.T, a.k, a.E, a.expert_rank, a.G, a.ranks_per_node, a.src_offsets, tile_cnt,
+        a.topk, a.T, a.k, a.E, a.expert_rank, a.G, a.ranks_per_node, a.src_offsets, tile_cnt, nt,
         tile_stats, a.d_err);
     MOE_CHECK_LAUNCH();
   }
   plan_scan_kernel<<<dim3(1), dim3(kScanThreads), 0, stream>>>(
-      a.src_offsets, a.T, a.k, a.G, tile_cnt, tile_stats, a.row_capacity, a.send_counts,
+      a.src_offsets, a.T, a.k, a.G, tile_cnt, nt, tile_stats, a.row_capacity, a.send_counts,
       a.send_offsets, a.counters, a.first_offsets, a.d_err);
   MOE_CHECK_LAUNCH();
   if (nt > 0) {
     plan_write_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(kPlanTile), 0, stream>>>(
-        a.topk, a.gates, a.T, a.k, a.E, a.expert_rank, a.G, a.src_offsets, tile_cnt,
-        a.row_capacity, a.row_token, a.row_weight, a.token_rows, a.slot_row, a.d_err);
+        a.topk, a.gates, a.T, a.k, a.E, a.expert_rank, a.G, a.src_offsets, tile_cnt, nt,
+        a.send_offsets, a.row_capacity, a.row_token, a.row_weight, a.token_rows, a.slot_row,
+        a.d_err);
     MOE_CHECK_LAUNCH();
   }
   return MOE_OK;
