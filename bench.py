@@ -100,7 +100,7 @@ def expert_side(step, w, steps: int, device_normal) -> dict:
     torch.cuda.synchronize()
     if int(side.d_err.item()) != 0:
         return {"error": f"device data errors {int(side.d_err.item())}"}
-    ms = timers.mean_ms()
+    ms = timers.median_ms()
     N = int(step.plan.counters[0].item())
     k = side.k
     TK, rb, T = side.T * k, w.row_bytes, side.T
@@ -174,7 +174,7 @@ def shuffle_modes(w, x, z, steps: int) -> dict:
         torch.cuda.synchronize()
         c = st.plan.counters.cpu().numpy()
         off = st.shuffle["shard_offsets"].cpu().numpy()
-        out[name] = {"shuffle_predict_us": 1e3 * timers.mean_ms()["shuffle_predict"],
+        out[name] = {"shuffle_predict_us": 1e3 * timers.median_ms()["shuffle_predict"],
                      "local_share": float(c[3]) / (w.T * w.k),
                      "largest_shard": int(np.diff(off).max()), "rows": int(c[0])}
         del st
@@ -297,7 +297,7 @@ def main() -> int:
     for _ in range(args.steps):
         step.run(stages)
     torch.cuda.synchronize()
-    stage_ms = stages.mean_ms()
+    stage_ms = stages.median_ms()
     dom = max(("permute", "combine") + (("shuffle_permute",) if w.cfg == 5 else ()),
               key=lambda n: stage_ms[n])
 
@@ -315,7 +315,8 @@ def main() -> int:
     wall = time.perf_counter() - wall0
     gpu_ms = e_start.elapsed_time(e_end)
     ms_per_step = gpu_ms / args.steps
-    dom_ms = statistics.mean(timers.durations_ms(dom))
+    dom_all = timers.durations_ms(dom)
+    dom_ms = statistics.mean(dom_all)
 
     counters = step.plan.counters.cpu().numpy()
     N = int(counters[0])
@@ -346,13 +347,14 @@ def main() -> int:
                    "logical_ranks": w.G, "dispatched_rows": N},
         "permute_combine_gbps": pc_gbs,
         "permute_combine_pct_of_hbm_peak": 100.0 * pc_gbs / HBM_PEAK_GBS,
-        "stage_us": {n: 1e3 * v for n, v in stage_ms.items()},
+        "stage_us_median": {n: 1e3 * v for n, v in stage_ms.items()},
         "counters": {"rows": N, "assignments": int(counters[1]), "local_rows": int(counters[2]),
                      "local_assign": int(counters[3]), "node_rows": int(counters[4]),
                      "cross_node_V": int(counters[5]), "max_recv_rows": int(counters[6])},
         "copy_probe_gbps": copy_gbs,
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": 1e3 * dom_ms,
+                     "kernel_us_median": 1e3 * statistics.median(dom_all),
                      "algorithmic_bytes": kernels[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic(w.cfg, dom)},

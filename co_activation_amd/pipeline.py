@@ -90,6 +90,11 @@ class StageTimers:
     def mean_ms(self):
         return {n: sum(self.durations_ms(n)) / self.used[n] for n in self.pairs if self.used[n]}
 
+    def median_ms(self):
+        import statistics
+
+        return {n: statistics.median(self.durations_ms(n)) for n in self.pairs if self.used[n]}
+
     def __del__(self):
         try:
             h = _Hip.get()
