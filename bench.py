@@ -292,10 +292,11 @@ def main() -> int:
         print(json.dumps({"error": f"device data errors {int(step.d_err.item())}"}))
         return 1
 
-    # Stage breakdown (events around every stage), outside the timed region.
+    # Stage breakdown (events around every stage, all on one stream so that
+    # each stage is timed alone), outside the timed region.
     stages = StageTimers(step.STAGES, args.steps)
     for _ in range(args.steps):
-        step.run(stages)
+        step.run(stages, overlap=False)
     torch.cuda.synchronize()
     stage_ms = stages.median_ms()
     dom = max(("permute", "combine") + (("shuffle_permute",) if w.cfg == 5 else ()),
@@ -348,6 +349,8 @@ def main() -> int:
         "permute_combine_gbps": pc_gbs,
         "permute_combine_pct_of_hbm_peak": 100.0 * pc_gbs / HBM_PEAK_GBS,
         "stage_us_median": {n: 1e3 * v for n, v in stage_ms.items()},
+        "stage_overlap": ("second stream: statistics beside plan/permute/combine" if w.cfg != 5 else
+                          "second stream: routing move and layer-2 plan beside the token move"),
         "counters": {"rows": N, "assignments": int(counters[1]), "local_rows": int(counters[2]),
                      "local_assign": int(counters[3]), "node_rows": int(counters[4]),
                      "cross_node_V": int(counters[5]), "max_recv_rows": int(counters[6])},

@@ -1,4 +1,4 @@
-"""One step of the dispatch path, as a sequence of C-ABI calls on one stream.
+"""One step of the dispatch path, as a sequence of C-ABI calls.
 
 Single layer (workloads 1-4):
     stats(topk) -> plan(topk, gates, placement) -> permute(x) -> combine(z)
@@ -9,6 +9,13 @@ its next-layer experts):
     -> permute x, topk2, gates2 to the new order (one row per token)
     -> plan(topk2', gates2', placement2, src_offsets = shard_offsets)
     -> permute(x') -> combine(z)
+
+Latency-bound stages that nothing on the bandwidth-bound chain waits for run
+on a second stream, overlapped with it: in one layer the statistics run
+beside plan, permute and combine; with the shuffle, the move of the routing
+and the layer-2 plan run beside the move of the token rows (the plan needs
+only the routing).  ``run(..., overlap=False)`` keeps everything on one
+stream, which is how per-stage times are taken.
 
 All buffers are allocated once in the constructor; ``run`` only enqueues
 kernels (no allocation, no host synchronisation).  ``z`` stands for the
@@ -41,23 +48,89 @@ class _Hip:
             h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                               ctypes.c_void_p]
             h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            h.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
             cls._h = h
         return cls._h
+
+
+# hipEventCreateWithFlags flags.  Fork/join events only order two streams
+# of one device, so a device-scope release is enough; timing events skip the
+# system-scope fence, which otherwise adds a cache writeback to every record
+# (a few microseconds of idle GPU per event after a kernel that wrote much).
+_EVENT_DISABLE_TIMING = 0x2
+_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+_EVENT_RELEASE_TO_DEVICE = 0x40000000
+_FORK_EVENT_FLAGS = _EVENT_DISABLE_TIMING | _EVENT_RELEASE_TO_DEVICE
+_TIMER_EVENT_FLAGS = _EVENT_DISABLE_SYSTEM_FENCE
+
+
+class _Fork:
+    """A second stream (default priority) with fork and join events: work
+    enqueued on it between ``fork`` and ``join`` runs beside the current
+    stream's work and is complete before anything the current stream
+    enqueues after ``join``."""
+
+    def __init__(self, device):
+        self.stream = torch.cuda.Stream(device=device)
+        self._side = ctypes.c_void_p(self.stream.cuda_stream)
+        h = _Hip.get()
+        self._ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+        for e in self._ev:
+            if h.hipEventCreateWithFlags(ctypes.byref(e), _FORK_EVENT_FLAGS):
+                raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def fork(self):
+        h = _Hip.get()
+        cur = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if h.hipEventRecord(self._ev[0], cur) or h.hipStreamWaitEvent(self._side, self._ev[0], 0):
+            raise RuntimeError("fork: hipEventRecord/hipStreamWaitEvent failed")
+        return torch.cuda.stream(self.stream)
+
+    def join(self):
+        h = _Hip.get()
+        cur = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if h.hipEventRecord(self._ev[1], self._side) or h.hipStreamWaitEvent(cur, self._ev[1], 0):
+            raise RuntimeError("join: hipEventRecord/hipStreamWaitEvent failed")
+
+    def __del__(self):
+        try:
+            h = _Hip.get()
+            for e in self._ev:
+                h.hipEventDestroy(e)
+        except Exception:
+            pass
+
+
+class _Inline:
+    """Stands in for a _Fork when everything stays on the current stream."""
+
+    def fork(self):
+        import contextlib
+
+        return contextlib.nullcontext()
+
+    def join(self):
+        pass
+
+
+_INLINE = _Inline()
 
 
 class StageTimers:
     """HIP event pairs per stage, created up front so that a timed loop only
     records events on the stream the stage's kernels run on."""
 
-    def __init__(self, names, steps):
+    def __init__(self, names, steps, flags=None):
+        if flags is None:
+            flags = _TIMER_EVENT_FLAGS
         h = _Hip.get()
         self.pairs = {}
         for n in names:
             lst = []
             for _ in range(steps):
                 a, b = ctypes.c_void_p(), ctypes.c_void_p()
-                if h.hipEventCreateWithFlags(ctypes.byref(a), 0) or \
-                        h.hipEventCreateWithFlags(ctypes.byref(b), 0):
+                if h.hipEventCreateWithFlags(ctypes.byref(a), flags) or \
+                        h.hipEventCreateWithFlags(ctypes.byref(b), flags):
                     raise RuntimeError("hipEventCreateWithFlags failed")
                 lst.append((a, b))
             self.pairs[n] = lst
@@ -147,6 +220,7 @@ class LayerStep:
         self.send = torch.empty((self.cap,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
         self.y = torch.empty((self.T, x.shape[1]), dtype=self.out_dtype, device=dev)
         self.plan = None
+        self._fork = _Fork(dev)
 
     @staticmethod
     def _plan_buffers(T, k, G, cap, dev):
@@ -162,8 +236,9 @@ class LayerStep:
 
     STAGES = ("stats", "plan", "permute", "combine")
 
-    def run(self, timers: Optional[StageTimers] = None):
-        with _timed(timers, "stats"):
+    def run(self, timers: Optional[StageTimers] = None, overlap: bool = True):
+        fork = self._fork if overlap else _INLINE
+        with fork.fork(), _timed(timers, "stats"):
             ops.coact_stats(self.topk, self.E, out=self.stats_out, d_err=self.d_err)
         with _timed(timers, "plan"):
             self.plan = ops.dispatch_plan(self.topk, self.gates, self.expert_rank, self.G, self.Rn,
@@ -174,6 +249,7 @@ class LayerStep:
         with _timed(timers, "combine"):
             ops.combine(self.z, self.plan.token_rows, self.plan.row_weight,
                         out_dtype=self.out_dtype, out=self.y, d_err=self.d_err)
+        fork.join()
         return self
 
 
@@ -218,11 +294,13 @@ class TwoLayerStep:
         self.y = torch.empty((T, x.shape[1]), dtype=x.dtype, device=dev)
         self.plan = None
         self.shuffle = None
+        self._fork = _Fork(dev)
 
     STAGES = ("stats", "shuffle_predict", "shuffle_permute", "shuffle_routing", "plan", "permute",
               "combine")
 
-    def run(self, timers: Optional[StageTimers] = None):
+    def run(self, timers: Optional[StageTimers] = None, overlap: bool = True):
+        fork = self._fork if overlap else _INLINE
         with _timed(timers, "stats"):
             stats = ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
                                     d_err=self.d_err)
@@ -232,15 +310,18 @@ class TwoLayerStep:
                                                out=self.shuffle_out, ws=self.shuffle_ws,
                                                d_err=self.d_err)
         dest = self.shuffle["dest_pos"]
+        with fork.fork():
+            with _timed(timers, "shuffle_routing"):
+                ops.permute(self.topk2, dest, self.T, out=self.topk2_s, d_err=self.d_err)
+                ops.permute(self.gates2, dest, self.T, out=self.gates2_s, d_err=self.d_err)
+            with _timed(timers, "plan"):
+                self.plan = ops.dispatch_plan(self.topk2_s, self.gates2_s, self.expert_rank2,
+                                              self.G, self.Rn, self.shuffle["shard_offsets"],
+                                              out=self.plan_out, ws=self.plan_ws,
+                                              d_err=self.d_err)
         with _timed(timers, "shuffle_permute"):
             ops.permute(self.x, dest, self.T, out=self.x_s, d_err=self.d_err)
-        with _timed(timers, "shuffle_routing"):
-            ops.permute(self.topk2, dest, self.T, out=self.topk2_s, d_err=self.d_err)
-            ops.permute(self.gates2, dest, self.T, out=self.gates2_s, d_err=self.d_err)
-        with _timed(timers, "plan"):
-            self.plan = ops.dispatch_plan(self.topk2_s, self.gates2_s, self.expert_rank2, self.G,
-                                          self.Rn, self.shuffle["shard_offsets"],
-                                          out=self.plan_out, ws=self.plan_ws, d_err=self.d_err)
+        fork.join()
         with _timed(timers, "permute"):
             ops.permute(self.x_s, self.plan.token_rows, self.cap, out=self.send, d_err=self.d_err)
         with _timed(timers, "combine"):

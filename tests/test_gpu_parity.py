@@ -326,6 +326,38 @@ def test_two_layer_step_parity():
     assert c[3] / (w.T * w.k) > ref["local_share_before"]
 
 
+@pytest.mark.parametrize("two_layer", [False, True])
+def test_overlapped_steps_match_serial(two_layer):
+    """Steps that run latency-bound stages on a second stream give, after
+    several back-to-back steps, exactly what one single-stream step gives."""
+    if two_layer:
+        w = make(5, T=8192, H=1024)
+        mk = lambda: TwoLayerStep(i32(w.topk), i32(w.topk2), dev(w.gates2), i32(w.expert_rank2),
+                                  x_tensor(w), dev(Z), w.G, w.ranks_per_node, E1=w.E)
+    else:
+        w = make(4, T=2048, H=1024)
+        mk = lambda: LayerStep(i32(w.topk), dev(w.gates), i32(w.expert_rank), x_tensor(w), dev(Z),
+                               w.G, w.ranks_per_node)
+    say("overlapped vs serial steps", "two-layer" if two_layer else "one layer")
+    cap = w.T * min(w.k, w.G)
+    Z = expert_outputs(cap, w.H, "bf16", seed=1)
+    ser = mk().run(overlap=False)
+    ovl = mk()
+    for _ in range(6):
+        ovl.run()
+    torch.cuda.synchronize()
+    _no_errors(ovl.d_err)
+    N = int(host(ser.plan.counters)[0])
+    for key, a in ser.stats_out.items():
+        assert_equal(host(ovl.stats_out[key]), host(a), key)
+    for a, b, name in ((ovl.plan.token_rows, ser.plan.token_rows, "token_rows"),
+                       (ovl.plan.send_offsets, ser.plan.send_offsets, "send_offsets"),
+                       (ovl.plan.counters, ser.plan.counters, "counters"),
+                       (ovl.y, ser.y, "y")):
+        assert_equal(host(a), host(b), name)
+    assert_equal(host(ovl.send)[:N], host(ser.send)[:N], "send")
+
+
 # ------------------------------------------------------------------ determinism
 
 def test_determinism():
