@@ -8,8 +8,9 @@ import pytest
 import torch
 
 import oracle
-from co_activation_amd.pipeline import LayerStep, TwoLayerStep
-from gpu_util import assert_equal, check_combine, dev, host, i32, say, x_tensor
+from co_activation_amd.pipeline import (ExpertSideBackward, ExpertSideStep, LayerStep,
+                                        TwoLayerStep)
+from gpu_util import assert_equal, bf16_ulps, check_combine, dev, host, i32, say, x_tensor
 from workloads import make
 from workloads.gen import device_normal
 
@@ -106,3 +107,147 @@ def test_two_layer_fullsize(balanced):
     share_after = ref["counters"][3] / (w.T * w.k)
     say("local share before/after shuffle", share_before, share_after)
     assert share_after > share_before
+
+
+def _check_sum(got, ref32, scale, dt, what):
+    """A sum of several terms: fp32 within 1e-5 of the terms' magnitude; bf16
+    within 1 ulp of the oracle's fp32 value rounded once, or within the fp32
+    bound where the terms cancel."""
+    if dt == "bf16":
+        d = bf16_ulps(got, oracle.bf16_round(ref32))
+        near = np.abs(oracle.bf16_to_f32(got).astype(np.float64) - ref32) <= 1e-5 * scale
+        ok = (d <= 1) | near
+    else:
+        ok = np.abs(got.astype(np.float64) - ref32) <= 1e-5 * scale + 1e-30
+    assert ok.all(), f"{what}: {np.count_nonzero(~ok)} elements out of tolerance"
+
+
+def _f64(a, dt):
+    return oracle.bf16_to_f32(a).astype(np.float64) if dt == "bf16" else a.astype(np.float64)
+
+
+@pytest.mark.parametrize("cfg", [5, 4])
+def test_expert_side_fullsize(cfg):
+    """Destination side and its backward at full size, after the step the
+    benchmark times (the two-layer step of workload 5, the layer of workload
+    4): the expert layout in full, and expansion, reply rows, reply combine
+    and every backward output on a seeded sample of tokens, each computed by
+    the oracle on that sample."""
+    w = make(cfg)
+    dt = w.dtype
+    say("fullsize expert side", cfg, w.T, w.H)
+    cap = w.T * min(w.k, w.G)
+    z = device_normal(cap, w.H, dt, seed=1)
+    if cfg == 5:
+        step = TwoLayerStep(i32(w.topk), i32(w.topk2), dev(w.gates2), i32(w.expert_rank2),
+                            x_tensor(w), z, w.G, w.ranks_per_node, E1=w.E)
+    else:
+        step = LayerStep(i32(w.topk), dev(w.gates), i32(w.expert_rank), x_tensor(w), z, w.G,
+                         w.ranks_per_node)
+    step.run()
+    side = ExpertSideStep(step)
+    side.dispatch()
+    y_expert = device_normal(w.T * w.k, w.H, dt, seed=2)
+    dy = device_normal(w.T, w.H, dt, seed=3)
+    d_in = device_normal(w.T * w.k, w.H, dt, seed=4)
+    side.reply_and_combine(y_expert)
+    bw = ExpertSideBackward(side).run(dy, y_expert, d_in)
+    torch.cuda.synchronize()
+    assert int(step.d_err.item()) == 0
+
+    if cfg == 5:
+        st = oracle.coact_stats(w.topk, w.E, w.topk2, w.E)
+        sh = oracle.shuffle_predict(w.topk, st["transition"], w.expert_rank2, w.G)
+        perm, er, src = sh["perm"], w.expert_rank2, sh["shard_offsets"]
+        topk_s, gates_s = w.topk2[perm], w.gates2[perm]
+    else:
+        perm, er, src = np.arange(w.T), w.expert_rank, None
+        topk_s, gates_s = w.topk, w.gates
+    rp = oracle.dispatch_plan(topk_s, gates_s, er, w.G, w.ranks_per_node, src_offsets=src)
+    ref = oracle.expert_plan(topk_s, gates_s, er, w.G, rp["slot_row"], rp["N"])
+    for key in ("erow", "expert_first", "expert_count", "rank_offsets", "erow_slot"):
+        assert_equal(host(side.plan[key]), ref[key], key)
+    assert_equal(host(side.plan["erow_weight"]).view(np.uint32),
+                 ref["erow_weight"].view(np.uint32), "erow_weight")
+    rd = host(side.plan["row_dest"])
+    N = int(rp["N"])
+    assert_equal(rd[:N], ref["row_dest"], "row_dest")
+    assert (rd[N:] == -1).all()
+
+    # a sample of tokens; every row they touch, in compact numbering
+    rng = np.random.default_rng(55)
+    toks = np.sort(rng.choice(w.T, size=SAMPLES, replace=False))
+    S, k = toks.size, w.k
+    erows = ref["erow"][toks]                               # [S, k] expert rows
+    erow_c = np.arange(S * k).reshape(S, k)                 # compact expert rows
+    srows = rp["slot_row"][toks]                            # [S, k] send rows
+    uniq, inv = np.unique(srows, return_inverse=True)
+    slot_c = inv.reshape(S, k)                              # compact send rows
+    trows = rp["token_rows"][toks]
+    trows_c = np.where(trows >= 0, np.searchsorted(uniq, np.maximum(trows, 0)), -1)
+    rd_c = np.full((uniq.size, k), -1, np.int64)            # compact row_dest
+    pos = {int(e): i for i, e in enumerate(erows.reshape(-1))}
+    for i, r in enumerate(uniq):
+        for q in range(k):
+            if ref["row_dest"][r, q] >= 0:
+                rd_c[i, q] = pos[int(ref["row_dest"][r, q])]
+    sel_e = torch.from_numpy(erows.reshape(-1)).cuda()
+    sel_s = torch.from_numpy(uniq).cuda()
+    sel_t = torch.from_numpy(toks).cuda()
+
+    # expansion: each expert row is its token's (shuffled) row
+    assert_equal(host(side.expert_in[sel_e]), np.repeat(w.x[perm[toks]], k, axis=0), "expanded")
+    # reply rows
+    Y = host(y_expert[sel_e])
+    Yf = _f64(Y, dt)
+    Zref = oracle.partial_combine(Y, dt, erow_c, gates_s[toks], slot_c, uniq.size, "f32")
+    scale = np.zeros((uniq.size, w.H))
+    for s_ in range(S):
+        for j in range(k):
+            scale[slot_c[s_, j]] += abs(float(gates_s[toks[s_], j])) * np.abs(Yf[erow_c[s_, j]])
+    Z = host(side.reply[sel_s])
+    _check_sum(Z, Zref.astype(np.float64), scale, dt, "reply rows")
+    # reply combine
+    Zf = _f64(Z, dt)
+    yref = oracle.combine_unweighted(Z, dt, trows_c, "f32").astype(np.float64)
+    sc = np.zeros((S, w.H))
+    for q in range(k):
+        m = trows_c[:, q] >= 0
+        sc[m] += np.abs(Zf[trows_c[m, q]])
+    _check_sum(host(side.y[sel_t]), yref, sc, dt, "reply combine")
+
+    # backward: reply-row gradients are copies of dy
+    DY = host(dy[sel_t])
+    tok_of_row = np.empty(uniq.size, np.int64)
+    for s_ in range(S):
+        tok_of_row[slot_c[s_]] = s_
+    dR = host(bw.d_reply[sel_s])
+    assert_equal(dR, DY[tok_of_row], "reply-row gradients")
+    # expert-output gradients: gate times the reply-row gradient, rounded once
+    want = oracle.permute_scaled(dR, dt, rd_c, ref["erow_weight"][erows.reshape(-1)], S * k, dt)
+    assert_equal(host(bw.d_expert_out[sel_e]), want, "expert-output gradients")
+    # gate gradients
+    dw = host(bw.dw[sel_t]).astype(np.float64)
+    dref = oracle.row_dot(DY, dt, Y, dt, erow_c).astype(np.float64)
+    DYf = _f64(DY, dt)
+    dsc = np.array([[float(np.sum(np.abs(DYf[s_] * Yf[erow_c[s_, j]]))) for j in range(k)]
+                    for s_ in range(S)])
+    assert (np.abs(dw - dref) <= 1e-5 * dsc + 1e-30).all(), "gate gradients"
+    # send-row gradients: sum of the expert-input gradients of the row
+    DI = host(d_in[sel_e])
+    DIf = _f64(DI, dt)
+    sref = oracle.combine_unweighted(DI, dt, rd_c, "f32").astype(np.float64)
+    ssc = np.zeros((uniq.size, w.H))
+    for q in range(k):
+        m = rd_c[:, q] >= 0
+        ssc[m] += np.abs(DIf[rd_c[m, q]])
+    dS = host(bw.d_send[sel_s])
+    _check_sum(dS, sref, ssc, dt, "send-row gradients")
+    # token gradients
+    dSf = _f64(dS, dt)
+    xref = oracle.combine_unweighted(dS, dt, trows_c, "f32").astype(np.float64)
+    xsc = np.zeros((S, w.H))
+    for q in range(k):
+        m = trows_c[:, q] >= 0
+        xsc[m] += np.abs(dSf[trows_c[m, q]])
+    _check_sum(host(bw.dx[sel_t]), xref, xsc, dt, "token gradients")
