@@ -455,9 +455,10 @@ def expert_plan(topk: np.ndarray, gates: Optional[np.ndarray], expert_rank: np.n
     carries its gate).
 
     Outputs: erow [T, k] (expert row of each slot), expert_first[e] and
-    expert_count[e], rank_offsets [G+1], erow_weight / erow_slot per expert
-    row (gate and t*k + j), and row_dest [n_send_rows, k]: for send row
-    (t, r), the expert rows of t's slots on r in ascending slot order, then -1.
+    expert_count[e], rank_offsets [G+1], erow_weight / erow_slot / erow_src
+    per expert row (gate, t*k + j, and the send row the slot was dispatched
+    in), and row_dest [n_send_rows, k]: for send row (t, r), the expert rows
+    of t's slots on r in ascending slot order, then -1.
     """
     topk = np.asarray(topk)
     expert_rank = np.asarray(expert_rank)
@@ -470,9 +471,11 @@ def expert_plan(topk: np.ndarray, gates: Optional[np.ndarray], expert_rank: np.n
     erow = np.full((T, k), -1, dtype=np.int64)
     erow_weight = np.zeros(T * k, dtype=np.float32)
     erow_slot = np.full(T * k, -1, dtype=np.int64)
+    erow_src = np.full(T * k, -1, dtype=np.int64)
     for i, (r, e, t, j) in enumerate(keys):
         erow[t, j] = i
         erow_slot[i] = t * k + j
+        erow_src[i] = int(slot_row[t, j])
         if gates is not None:
             erow_weight[i] = np.float32(gates[t, j])
     expert_count = np.zeros(E, dtype=np.int64)
@@ -498,7 +501,7 @@ def expert_plan(topk: np.ndarray, gates: Optional[np.ndarray], expert_rank: np.n
             used[i] = q + 1
     return {"erow": erow, "expert_first": expert_first, "expert_count": expert_count,
             "rank_offsets": rank_offsets, "erow_weight": erow_weight, "erow_slot": erow_slot,
-            "row_dest": row_dest}
+            "erow_src": erow_src, "row_dest": row_dest}
 
 
 def partial_combine(Y: np.ndarray, y_dtype: str, erow: np.ndarray, gates: np.ndarray,

@@ -464,6 +464,9 @@ def test_expert_plan_hand_example():
     assert ep["rank_offsets"].tolist() == [0, 3, 4]
     assert ep["erow_slot"].tolist() == [2, 0, 3, 1]
     assert ep["erow_weight"].tolist() == [0.5, 0.75, 0.5, 0.25]
+    # send rows (s, r, t): (0,0,0) (0,1,0) (1,0,1); token 1 has both experts on rank 0
+    assert plan["row_token"].tolist() == [0, 0, 1]
+    assert ep["erow_src"].tolist() == [2, 0, 2, 1]
 
 
 def test_expert_plan_bruteforce_and_counts():
@@ -490,12 +493,15 @@ def test_expert_plan_bruteforce_and_counts():
         for r in range(G):
             assert ep["rank_offsets"][r + 1] - ep["rank_offsets"][r] == \
                 sum(int(st["expert_count"][e]) for e in range(E) if er[e] == r)
-        # each send row lists exactly the expert rows of its token's slots on its rank
+        # each send row lists exactly the expert rows of its token's slots on its rank,
+        # and each expert row names that send row as its source
         for t in range(T):
             for j in range(k):
                 i = plan["slot_row"][t, j]
                 on_r = [ep["erow"][t, jj] for jj in range(k) if plan["slot_row"][t, jj] == i]
                 assert ep["row_dest"][i].tolist() == on_r + [-1] * (k - len(on_r))
+                assert ep["erow_src"][ep["erow"][t, j]] == i
+                assert plan["row_token"][i] == t
 
 
 def test_expert_side_reproduces_moe_output():
@@ -517,6 +523,8 @@ def test_expert_side_reproduces_moe_output():
                 erows[ep["row_dest"][i, q]] = send[i]
     tok = ep["erow_slot"] // w.k
     assert np.array_equal(erows, w.x[tok])
+    # the same expansion as a gather by source row
+    assert np.array_equal(oracle.permute_rows(send, ep["erow_src"]), erows)
     # experts: scale each row by its expert's constant (float32, rounded to bf16)
     e_of_row = w.topk.reshape(-1)[ep["erow_slot"]]
     Y = oracle.bf16_round((oracle.bf16_to_f32(erows) * c[e_of_row][:, None]).astype(np.float32))
