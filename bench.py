@@ -104,7 +104,8 @@ def expert_side(step, w, steps: int, device_normal) -> dict:
     N = int(step.plan.counters[0].item())
     k = side.k
     TK, rb, T = side.T * k, w.row_bytes, side.T
-    bytes_ = {"expand": N * rb + TK * rb + 4 * N * k,
+    # each received row read once, each expert row written once, one index per expert row
+    bytes_ = {"expand": N * rb + TK * rb + 4 * TK,
               "partial_combine": TK * rb + 4 * TK + N * rb + 4 * N * k,
               "reply_combine": N * rb + T * rb + 4 * T * k,
               "grad_replies": T * rb + N * rb + 4 * T * k,

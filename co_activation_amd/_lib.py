@@ -35,7 +35,7 @@ EXPORTS = (
     "moe_shuffle_predict_workspace_size", "moe_shuffle_predict",
     "moe_expert_plan_workspace_size", "moe_expert_plan",
     "moe_permute_scaled", "moe_row_dot", "moe_ema_update", "moe_place_experts",
-    "moe_shuffle_balanced_workspace_size", "moe_shuffle_balanced",
+    "moe_shuffle_balanced_workspace_size", "moe_shuffle_balanced", "moe_gather",
 )
 
 _lib = None
@@ -54,6 +54,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.moe_dispatch_plan.restype = c_int
     lib.moe_permute.argtypes = [P, c_int64, c_int64, P, c_int, P, c_int64, P, P, P]
     lib.moe_permute.restype = c_int
+    lib.moe_gather.argtypes = [P, c_int64, c_int64, P, c_int64, P, P, P, P]
+    lib.moe_gather.restype = c_int
     lib.moe_combine.argtypes = [P, c_int, c_int64, c_int64, P, c_int, P, c_int64, P, c_int, P, P,
                                 P]
     lib.moe_combine.restype = c_int
@@ -70,7 +72,7 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.moe_expert_plan_workspace_size.argtypes = [c_int64, c_int, POINTER(c_size_t)]
     lib.moe_expert_plan_workspace_size.restype = c_int
     lib.moe_expert_plan.argtypes = [P, P, c_int64, c_int, c_int, P, c_int, P, c_int64, P, P, P, P,
-                                    P, P, P, P, P, c_size_t, P]
+                                    P, P, P, P, P, P, c_size_t, P]
     lib.moe_expert_plan.restype = c_int
     lib.moe_permute_scaled.argtypes = [P, c_int, c_int64, c_int64, P, c_int, P, P, c_int, c_int64,
                                        P, P, P]

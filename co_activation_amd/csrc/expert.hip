@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kExTile) void expert_write_kernel(
     const int32_t* __restrict__ expert_first, const int32_t* __restrict__ slot_row,
     int64_t send_rows, int32_t* __restrict__ erow,
     float* __restrict__ erow_weight, int32_t* __restrict__ erow_slot,
-    int32_t* __restrict__ row_dest, int32_t* d_err) {
+    int32_t* __restrict__ erow_src, int32_t* __restrict__ row_dest, int32_t* d_err) {
   __shared__ uint64_t cols[MOE_MAX_E][kExWords];
   int ex[MOE_MAX_K], rk[MOE_MAX_K];
   build_columns(topk, T, k, E, expert_rank, G, cols, ex, rk);
@@ -210,10 +210,12 @@ __global__ __launch_bounds__(kExTile) void expert_write_kernel(
 #pragma unroll
     for (int jj = 0; jj < j; ++jj) q += (rk[jj] == rk[j]);
     const int i = slot_row[slot];
-    if (i >= 0 && i < send_rows)
+    const bool ok = i >= 0 && i < send_rows;
+    if (ok)
       row_dest[static_cast<int64_t>(i) * k + q] = row;
     else
       errbits |= MOE_DERR_ROW_RANGE;
+    if (erow_src != nullptr) erow_src[row] = ok ? i : -1;
   }
   report(d_err, errbits);
 }
@@ -233,8 +235,8 @@ extern "C" int moe_expert_plan(const int32_t* topk, const float* gates, int64_t 
                                const int32_t* expert_rank, int G, const int32_t* slot_row,
                                int64_t send_rows, int32_t* erow, int32_t* expert_first,
                                int32_t* expert_count, int32_t* rank_offsets, float* erow_weight,
-                               int32_t* erow_slot, int32_t* row_dest, int32_t* d_err, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               int32_t* erow_slot, int32_t* erow_src, int32_t* row_dest,
+                               int32_t* d_err, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || k < 1 || k > MOE_MAX_K || E < 1 || E > MOE_MAX_E || G < 1 || G > MOE_MAX_G ||
       send_rows < 0 || T * static_cast<int64_t>(k) >= (int64_t{1} << 31) ||
       send_rows * static_cast<int64_t>(k) >= (int64_t{1} << 31))
@@ -264,7 +266,7 @@ extern "C" int moe_expert_plan(const int32_t* topk, const float* gates, int64_t 
     moe::expert_write_kernel<<<NT, moe::kExTile, 0, s>>>(topk, gates, Ti, k, E, expert_rank, G,
                                                           tile_cnt, expert_first, slot_row,
                                                           send_rows, erow, erow_weight, erow_slot,
-                                                          row_dest, d_err);
+                                                          erow_src, row_dest, d_err);
     MOE_CHECK_LAUNCH();
   }
   return MOE_OK;

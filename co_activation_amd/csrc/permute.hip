@@ -1,14 +1,19 @@
 // Row scatter into rank-contiguous send buffers: the dispatched hidden
 // states of "Training Communication-Efficient Mixture-of-Experts Language
 // Models with Layer Re-Configuration" (footnote 3), sent once per destination
-// rank as in "Expert Coupling in MoE Pretraining ..." (abstract); the same
-// kernel moves tokens for the token shuffle.
+// rank as in "Expert Coupling in MoE Pretraining ..." (abstract).
 //
 // Token-major: a group of threads owns one token, reads its row once and
 // writes it to each of its (<= 8) destination rows.  The destination list is
 // uniform per token and lives in scalar registers; every store instruction of
 // a wave writes 64 x 16 contiguous bytes.  HBM-bound: algorithmic bytes per
 // token are row_bytes * (1 + destinations) + 4 * width.
+//
+// Row gather (moe_gather): the destination-ordered form for maps in which
+// every output row has exactly one source -- the token shuffle's move into
+// the predicted order and the expansion of received rows into expert rows.
+// Output rows are written in order (one dense write front), sources are
+// gathered; on MI355X this beats the scatter form for such maps.
 #include "common.hpp"
 
 namespace moe {
@@ -158,8 +163,111 @@ int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* des
   return MOE_OK;
 }
 
+// ------------------------------------------------------------ row gather
+
+// TPT threads own one output row: out[i] = x[src[i]].  A negative source
+// leaves the row untouched; a source past x_rows is reported and skipped.
+template <typename V, int TPT, int U>
+__global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void gather_kernel(
+    const V* __restrict__ x, int64_t x_rows, int64_t vec_per_row, const int32_t* __restrict__ src,
+    int n_rows, V* __restrict__ out, const int32_t* __restrict__ n_valid, int32_t* d_err) {
+  constexpr int kBlock = TPT < kPermThreads ? kPermThreads : TPT;
+  constexpr int kRows = kBlock / TPT;
+  const int sub = kRows == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / TPT);
+  const int i = blockIdx.x * kRows + sub;
+  if (i >= n_rows || (n_valid != nullptr && i >= *n_valid)) return;
+  const int l = kRows == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x % TPT);
+  const int s = __builtin_amdgcn_readfirstlane(src[i]);
+  if (s < 0) return;
+  if (s >= x_rows) {
+    if (l == 0) report(d_err, MOE_DERR_ROW_RANGE);
+    return;
+  }
+  const V* a = x + static_cast<int64_t>(s) * vec_per_row;
+  V* b = out + static_cast<int64_t>(i) * vec_per_row;
+  for (int64_t c0 = l; c0 < vec_per_row; c0 += TPT * U) {
+    V v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * TPT;
+      if (c < vec_per_row) v[u] = load_row<false>(a + c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * TPT;
+      if (c < vec_per_row) __builtin_nontemporal_store(v[u], b + c);
+    }
+  }
+}
+
+// Rows narrower than one wave's width of vectors: one thread per
+// (output row, vector).
+template <typename V>
+__global__ __launch_bounds__(kPermThreads) void gather_flat_kernel(
+    const V* __restrict__ x, int64_t x_rows, int vec_per_row, const int32_t* __restrict__ src,
+    int n_rows, V* __restrict__ out, const int32_t* __restrict__ n_valid, int32_t* d_err) {
+  const int limit = n_valid != nullptr ? min(n_rows, max(*n_valid, 0)) : n_rows;
+  const int64_t n = static_cast<int64_t>(limit) * vec_per_row;
+  int errbits = 0;
+  for (int64_t q = blockIdx.x * static_cast<int64_t>(kPermThreads) + threadIdx.x; q < n;
+       q += static_cast<int64_t>(gridDim.x) * kPermThreads) {
+    const int i = static_cast<int>(q / vec_per_row);
+    const int c = static_cast<int>(q - static_cast<int64_t>(i) * vec_per_row);
+    const int s = src[i];
+    if (s >= 0 && s < x_rows)
+      __builtin_nontemporal_store(x[static_cast<int64_t>(s) * vec_per_row + c], out + q);
+    else if (s >= x_rows)
+      errbits = MOE_DERR_ROW_RANGE;
+  }
+  report(d_err, errbits);
+}
+
+// Launch shape by row size R (vectors): one thread per (row, vector) below
+// 64; a wave per row below 256 (4 vectors per lane per pass); 512 threads
+// per row above (measured best for 8 KiB and 14 KiB rows).
+template <typename V>
+int launch_gather(const void* x, int64_t x_rows, int64_t vec_per_row, const int32_t* src,
+                  int n_rows, void* out, const int32_t* n_valid, int32_t* d_err, hipStream_t s) {
+  const V* xv = static_cast<const V*>(x);
+  V* ov = static_cast<V*>(out);
+  if (vec_per_row < kWave) {
+    const int64_t n = static_cast<int64_t>(n_rows) * vec_per_row;
+    int64_t blocks = (n + kPermThreads - 1) / kPermThreads;
+    if (blocks > 8192) blocks = 8192;
+    gather_flat_kernel<V><<<static_cast<unsigned>(blocks), kPermThreads, 0, s>>>(
+        xv, x_rows, static_cast<int>(vec_per_row), src, n_rows, ov, n_valid, d_err);
+  } else if (vec_per_row < 256) {
+    constexpr int kRows = kPermThreads / 64;
+    gather_kernel<V, 64, 4><<<static_cast<unsigned>((n_rows + kRows - 1) / kRows), kPermThreads,
+                              0, s>>>(xv, x_rows, vec_per_row, src, n_rows, ov, n_valid, d_err);
+  } else {
+    gather_kernel<V, 512, 1><<<static_cast<unsigned>(n_rows), 512, 0, s>>>(
+        xv, x_rows, vec_per_row, src, n_rows, ov, n_valid, d_err);
+  }
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
+
+extern "C" int moe_gather(const void* x, int64_t x_rows, int64_t row_bytes, const int32_t* src,
+                          int64_t n_rows, void* out, const int32_t* n_valid, int32_t* d_err,
+                          void* stream) {
+  if (x_rows < 0 || row_bytes <= 0 || n_rows < 0 || n_rows >= (int64_t{1} << 31) ||
+      x_rows >= (int64_t{1} << 31))
+    return MOE_ERR_SHAPE;
+  if (n_rows == 0) return MOE_OK;
+  if (src == nullptr || out == nullptr || (x == nullptr && x_rows > 0)) return MOE_ERR_NULL;
+  const auto xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(out);
+  if (row_bytes % 4 != 0 || xa % 4 != 0 || oa % 4 != 0) return MOE_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = static_cast<int>(n_rows);
+  if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0)
+    return moe::launch_gather<moe::u32x4>(x, x_rows, row_bytes / 16, src, n, out, n_valid, d_err,
+                                          s);
+  return moe::launch_gather<uint32_t>(x, x_rows, row_bytes / 4, src, n, out, n_valid, d_err, s);
+}
 
 extern "C" int moe_permute(const void* x, int64_t T, int64_t row_bytes, const int32_t* dest,
                            int width, void* out, int64_t out_rows, const int32_t* n_valid,

@@ -11,6 +11,7 @@ tensor of one element); ``raise_on_errors`` reads it back.
 from __future__ import annotations
 
 import ctypes
+import math
 from typing import NamedTuple, Optional
 
 import torch
@@ -177,6 +178,31 @@ def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
     return out
 
 
+def gather(x: torch.Tensor, src: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+           n_valid: Optional[torch.Tensor] = None,
+           d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_gather: out[i] = x[src[i]] (bit copy; rows with src < 0 are left
+    as they are).  src is [n] int32; out has n rows shaped like x's rows."""
+    _want(x, "x")
+    _want(src, "src", torch.int32)
+    if src.dim() != 1:
+        raise ValueError("src must be one-dimensional")
+    n = src.shape[0]
+    row_shape = tuple(x.shape[1:])
+    row_bytes = x.element_size() * math.prod(row_shape)
+    if out is None:
+        out = torch.empty((n,) + row_shape, dtype=x.dtype, device=x.device)
+    _want(out, "out", x.dtype)
+    if tuple(out.shape[1:]) != row_shape or out.shape[0] < n:
+        raise ValueError("out must have n rows shaped like x's rows")
+    if n_valid is not None:
+        _want(n_valid, "n_valid", torch.int32)
+    st = _lib.lib().moe_gather(_p(x), x.shape[0], row_bytes, _p(src), n, _p(out), _p(n_valid),
+                               _p(d_err), _stream())
+    check("moe_gather", st)
+    return out
+
+
 # ----------------------------------------------------------------- combine
 
 def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tensor] = None, *,
@@ -257,8 +283,8 @@ def expert_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank: 
                 out: Optional[dict] = None, ws: Optional[torch.Tensor] = None,
                 d_err: Optional[torch.Tensor] = None) -> dict:
     """moe_expert_plan: erow [T,k], expert_first [E], expert_count [E],
-    rank_offsets [G+1], erow_weight [T*k], erow_slot [T*k], row_dest
-    [send_rows, k]."""
+    rank_offsets [G+1], erow_weight [T*k], erow_slot [T*k], erow_src [T*k],
+    row_dest [send_rows, k]."""
     _want(topk, "topk", torch.int32)
     T, k = topk.shape
     E = expert_rank.numel()
@@ -274,6 +300,7 @@ def expert_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank: 
         "rank_offsets": _alloc(out, "rank_offsets", (G + 1,), torch.int32, dev),
         "erow_weight": _alloc(out, "erow_weight", (T * k,), torch.float32, dev),
         "erow_slot": _alloc(out, "erow_slot", (T * k,), torch.int32, dev) if with_slots else None,
+        "erow_src": _alloc(out, "erow_src", (T * k,), torch.int32, dev),
         "row_dest": _alloc(out, "row_dest", (send_rows, k), torch.int32, dev),
     }
     need = expert_workspace_bytes(T, E)
@@ -283,8 +310,8 @@ def expert_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank: 
     st = _lib.lib().moe_expert_plan(
         _p(topk), _p(gates), T, k, E, _p(expert_rank), G, _p(slot_row), send_rows, _p(res["erow"]),
         _p(res["expert_first"]), _p(res["expert_count"]), _p(res["rank_offsets"]),
-        _p(res["erow_weight"]), _p(res["erow_slot"]), _p(res["row_dest"]), _p(d_err), _p(ws),
-        ws.numel(), _stream())
+        _p(res["erow_weight"]), _p(res["erow_slot"]), _p(res["erow_src"]), _p(res["row_dest"]),
+        _p(d_err), _p(ws), ws.numel(), _stream())
     check("moe_expert_plan", st)
     return res
 

@@ -6,7 +6,7 @@ Two layers with token shuffling (workload 5, "Expert Coupling in MoE
 Pretraining ..." abstract: shuffle each token to the rank predicted to hold
 its next-layer experts):
     stats(topk1, topk2) -> shuffle_predict(topk1, transition, placement2)
-    -> permute x, topk2, gates2 to the new order (one row per token)
+    -> gather x, topk2, gates2 into the new order (one row per token)
     -> plan(topk2', gates2', placement2, src_offsets = shard_offsets)
     -> permute(x') -> combine(z)
 
@@ -309,18 +309,18 @@ class TwoLayerStep:
                                                self.G, balanced=self.balanced,
                                                out=self.shuffle_out, ws=self.shuffle_ws,
                                                d_err=self.d_err)
-        dest = self.shuffle["dest_pos"]
+        perm = self.shuffle["perm"]
         with fork.fork():
             with _timed(timers, "shuffle_routing"):
-                ops.permute(self.topk2, dest, self.T, out=self.topk2_s, d_err=self.d_err)
-                ops.permute(self.gates2, dest, self.T, out=self.gates2_s, d_err=self.d_err)
+                ops.gather(self.topk2, perm, out=self.topk2_s, d_err=self.d_err)
+                ops.gather(self.gates2, perm, out=self.gates2_s, d_err=self.d_err)
             with _timed(timers, "plan"):
                 self.plan = ops.dispatch_plan(self.topk2_s, self.gates2_s, self.expert_rank2,
                                               self.G, self.Rn, self.shuffle["shard_offsets"],
                                               out=self.plan_out, ws=self.plan_ws,
                                               d_err=self.d_err)
         with _timed(timers, "shuffle_permute"):
-            ops.permute(self.x, dest, self.T, out=self.x_s, d_err=self.d_err)
+            ops.gather(self.x, perm, out=self.x_s, d_err=self.d_err)
         fork.join()
         with _timed(timers, "permute"):
             ops.permute(self.x_s, self.plan.token_rows, self.cap, out=self.send, d_err=self.d_err)
@@ -363,6 +363,7 @@ class ExpertSideStep:
             "rank_offsets": torch.empty(self.G + 1, dtype=torch.int32, device=dev),
             "erow_weight": torch.empty(self.T * self.k, dtype=torch.float32, device=dev),
             "erow_slot": torch.empty(self.T * self.k, dtype=torch.int32, device=dev),
+            "erow_src": torch.empty(self.T * self.k, dtype=torch.int32, device=dev),
             "row_dest": torch.empty(self.cap, self.k, dtype=torch.int32, device=dev),
         }
         self.ws = torch.empty(ops.expert_workspace_bytes(self.T, self.E), dtype=torch.uint8,
@@ -386,8 +387,8 @@ class ExpertSideStep:
                                         lp.slot_row, self.cap, out=self.out, ws=self.ws,
                                         d_err=self.d_err)
         with _timed(timers, "expand"):
-            ops.permute(self.layer.send, self.plan["row_dest"], self.T * self.k,
-                        out=self.expert_in, n_valid=self.n_rows(), d_err=self.d_err)
+            ops.gather(self.layer.send, self.plan["erow_src"], out=self.expert_in,
+                       d_err=self.d_err)
         return self
 
     def reply_and_combine(self, expert_out, timers: Optional[StageTimers] = None):

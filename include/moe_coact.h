@@ -182,6 +182,25 @@ int moe_permute(const void* x, int64_t T, int64_t row_bytes, const int32_t* dest
                 void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_gather -- row gather, the destination-ordered form of moe_permute for
+ * maps in which every output row has one source: the token shuffle of [EC]
+ * abstract (out = x[perm]) and the expansion of received rows into expert
+ * rows (out[i] = send[erow_src[i]], see moe_expert_plan).
+ *
+ *   out[i] = x[src[i]]   for i < n_rows (and i < *n_valid when given), src >= 0
+ * Rows are copied bit for bit.
+ *   x          [x_rows * row_bytes] bytes
+ *   src        [n_rows] int32: source row of each output row (-1 = leave the
+ *              output row untouched)
+ *   out        [n_rows * row_bytes] bytes
+ *   n_valid    int32 device word or NULL, as for moe_permute
+ * Same row-size and alignment rules as moe_permute; n_rows, x_rows < 2^31.
+ * d_err bits: ROW_RANGE (src >= x_rows; that row is skipped).
+ * ---------------------------------------------------------------------- */
+int moe_gather(const void* x, int64_t x_rows, int64_t row_bytes, const int32_t* src,
+               int64_t n_rows, void* out, const int32_t* n_valid, int32_t* d_err, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_combine -- weighted combine back to token order (the hidden-state
  * combine of [CE] footnote 3 over the deduplicated rows of [EC] abstract).
  *
@@ -266,12 +285,15 @@ int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E, const int
  *   rank_offsets  [G+1] int32 out: first expert row of each rank
  *   erow_weight   [T*k] float out or NULL: the gate carried by each expert row
  *   erow_slot     [T*k] int32 out or NULL: t*k + j of each expert row
+ *   erow_src      [T*k] int32 out or NULL: the send row each expert row is
+ *                 expanded from (slot_row of its slot; -1 if out of range)
  *   row_dest      [send_rows*k] int32 out: for send row (t, r), the expert
  *                 rows of t's slots on r in ascending slot order, then -1
  *                 (all -1 for rows no slot maps to)
  *   ws, ws_bytes  workspace of moe_expert_plan_workspace_size() bytes
- * With these, moe_permute(send, send_rows, row_bytes, row_dest, k, ...)
- * expands the received rows into expert rows, and moe_combine(expert_out,
+ * With these, moe_gather(send, send_rows, row_bytes, erow_src, T*k, ...)
+ * (or, equivalently, moe_permute(send, send_rows, row_bytes, row_dest, k,
+ * ...)) expands the received rows into expert rows, and moe_combine(expert_out,
  * ..., row_dest, k, erow_weight, send_rows, reply, ...) forms each (t, r)
  * reply row sum_{j on r} w_tj * expert_out[erow(t, j)]; the final
  * moe_combine of the replies is then unweighted.
@@ -283,7 +305,8 @@ int moe_expert_plan(const int32_t* topk, const float* gates, int64_t T, int k, i
                     const int32_t* expert_rank, int G, const int32_t* slot_row, int64_t send_rows,
                     int32_t* erow, int32_t* expert_first, int32_t* expert_count,
                     int32_t* rank_offsets, float* erow_weight, int32_t* erow_slot,
-                    int32_t* row_dest, int32_t* d_err, void* ws, size_t ws_bytes, void* stream);
+                    int32_t* erow_src, int32_t* row_dest, int32_t* d_err, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward mirror.  The all-to-alls run again in the backward pass with the

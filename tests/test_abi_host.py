@@ -92,19 +92,28 @@ def test_permute_combine_shuffle_reject(built_lib):
     assert L.moe_permute(FAKE + 2, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -4
     assert L.moe_permute(NULL, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -1
     assert L.moe_permute(NULL, 0, 16, NULL, 1, NULL, 0, NULL, NULL, NULL) == 0   # empty: no-op
+    g = L.moe_gather
+    assert g(FAKE, 8, 0, FAKE, 8, FAKE, NULL, NULL, NULL) == -2     # row_bytes
+    assert g(FAKE, -1, 16, FAKE, 8, FAKE, NULL, NULL, NULL) == -2   # x_rows
+    assert g(FAKE, 8, 16, FAKE, 1 << 31, FAKE, NULL, NULL, NULL) == -2
+    assert g(FAKE, 8, 6, FAKE, 8, FAKE, NULL, NULL, NULL) == -4     # not whole words
+    assert g(FAKE, 8, 16, FAKE, 8, FAKE + 2, NULL, NULL, NULL) == -4
+    assert g(FAKE, 8, 16, NULL, 8, FAKE, NULL, NULL, NULL) == -1    # src
+    assert g(NULL, 8, 16, FAKE, 8, FAKE, NULL, NULL, NULL) == -1    # x
+    assert g(NULL, 0, 16, NULL, 0, NULL, NULL, NULL, NULL) == 0     # empty: no-op
     assert L.moe_combine(FAKE, 7, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -3
     assert L.moe_combine(FAKE, 1, 8, 60, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -4  # 120 B
     assert L.moe_combine(FAKE, 1, 8, 64, FAKE, 0, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -2
     assert L.moe_combine(FAKE, 1, 8, 64, NULL, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -1
     assert L.moe_combine(FAKE + 8, 1, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -4
     ep = L.moe_expert_plan
-    args = [FAKE, NULL, 64, 2, 8, FAKE, 4, FAKE, 128, FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE,
-            NULL, FAKE, 1 << 20, NULL]
+    args = [FAKE, NULL, 64, 2, 8, FAKE, 4, FAKE, 128, FAKE, FAKE, FAKE, FAKE, NULL, NULL, NULL,
+            FAKE, NULL, FAKE, 1 << 20, NULL]
     assert ep(*args[:3], 9, *args[4:]) == -2                       # k > 8
     assert ep(*args[:6], 65, *args[7:]) == -2                      # G > 64
     assert ep(*args[:7], NULL, *args[8:]) == -1                    # slot_row
-    assert ep(*args[:15], NULL, *args[16:]) == -1                  # row_dest
-    assert ep(*args[:18], 16, NULL) == -5                          # workspace
+    assert ep(*args[:16], NULL, *args[17:]) == -1                  # row_dest
+    assert ep(*args[:19], 16, NULL) == -5                          # workspace
     n = ctypes.c_size_t()
     assert L.moe_expert_plan_workspace_size(65536, 256, ctypes.byref(n)) == 0
     assert n.value >= 256 * 256 * 4

@@ -26,7 +26,7 @@ def _no_errors(err):
 
 
 def _check_expert_plan(ep, ref, cap):
-    for key in ("erow", "expert_first", "expert_count", "rank_offsets", "erow_slot"):
+    for key in ("erow", "expert_first", "expert_count", "rank_offsets", "erow_slot", "erow_src"):
         assert_equal(host(ep[key]), ref[key], key)
     assert_equal(host(ep["erow_weight"]).view(np.uint32), ref["erow_weight"].view(np.uint32),
                  "erow_weight")

@@ -165,7 +165,7 @@ def test_expert_side_fullsize(cfg):
         topk_s, gates_s = w.topk, w.gates
     rp = oracle.dispatch_plan(topk_s, gates_s, er, w.G, w.ranks_per_node, src_offsets=src)
     ref = oracle.expert_plan(topk_s, gates_s, er, w.G, rp["slot_row"], rp["N"])
-    for key in ("erow", "expert_first", "expert_count", "rank_offsets", "erow_slot"):
+    for key in ("erow", "expert_first", "expert_count", "rank_offsets", "erow_slot", "erow_src"):
         assert_equal(host(side.plan[key]), ref[key], key)
     assert_equal(host(side.plan["erow_weight"]).view(np.uint32),
                  ref["erow_weight"].view(np.uint32), "erow_weight")

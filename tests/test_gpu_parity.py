@@ -195,6 +195,67 @@ def test_permute_narrow_rows_and_untouched():
     assert (got[~targeted] == -7).all()
 
 
+GATHER_CASES = [(3000, 2500, 8192, 0.1), (1001, 1001, 14336, 0.0), (777, 900, 512, 0.2),
+                (1500, 64, 1024, 0.0), (613, 400, 2064, 0.05), (5000, 4000, 8, 0.1),
+                (300, 300, 4, 0.0), (200, 150, 48, 0.3), (1, 1, 16384, 0.0)]
+
+
+@pytest.mark.parametrize("n,x_rows,row_bytes,neg", GATHER_CASES)
+def test_gather_parity(n, x_rows, row_bytes, neg):
+    """out[i] = x[src[i]] bit for bit over every launch shape (word rows,
+    flat, wave per row, 512 threads per row with a ragged second pass);
+    rows with a negative source stay as they were."""
+    rng = np.random.default_rng(n + row_bytes)
+    words = row_bytes // 4
+    x = rng.integers(-2**31, 2**31 - 1, size=(x_rows, words), dtype=np.int64).astype(np.int32)
+    src = rng.integers(0, x_rows, size=n).astype(np.int32)
+    src[rng.random(n) < neg] = -1
+    say("gather", n, x_rows, row_bytes)
+    err = _err()
+    out = torch.full((n, words), -7, dtype=torch.int32, device="cuda")
+    ops.gather(i32(x), i32(src), out=out, d_err=err)
+    _no_errors(err)
+    got = host(out)
+    ok = src >= 0
+    assert_equal(got[ok], oracle.permute_rows(x, src[ok]), "gathered rows")
+    assert (got[~ok] == -7).all()
+
+
+def test_gather_is_the_inverse_scatter():
+    """Gathering by a permutation equals scattering by its inverse: the
+    shuffle's move in either form (bf16 rows of 4096 elements)."""
+    w = make(5, T=2056, H=4096)
+    rng = np.random.default_rng(14)
+    perm = rng.permutation(w.T).astype(np.int32)
+    dest = np.argsort(perm).astype(np.int32)
+    say("gather vs scatter")
+    err = _err()
+    x = x_tensor(w)
+    a = ops.gather(x, i32(perm), d_err=err)
+    b = ops.permute(x, i32(dest), w.T, d_err=err)
+    _no_errors(err)
+    assert_equal(host(a), oracle.permute_rows(w.x, perm), "gather")
+    assert_equal(host(a), host(b), "gather vs scatter")
+
+
+def test_gather_n_valid_and_row_range():
+    rng = np.random.default_rng(15)
+    x = torch.from_numpy(rng.standard_normal((64, 32)).astype(np.float32)).cuda()
+    src = i32(rng.integers(0, 64, size=50))
+    out = torch.full((50, 32), -1.0, device="cuda")
+    ops.gather(x, src, out=out, n_valid=i32([20]))
+    torch.cuda.synchronize()
+    assert torch.equal(out[:20], x[src[:20].long()]) and (out[20:] == -1).all()
+    say("gather row range")
+    err = _err()
+    bad = i32([0, 1, 64, 3])        # 64 is past the 64 source rows
+    out2 = torch.full((4, 32), -1.0, device="cuda")
+    ops.gather(x, bad, out=out2, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 32
+    assert torch.equal(out2[[0, 1, 3]], x[[0, 1, 3]]) and (out2[2] == -1).all()
+
+
 # ------------------------------------------------------------------ combine
 
 COMBINE_CASES = [(1, 2048, 128, "f32", "f32"), (1, 2048, 128, "f32", "bf16"),
