@@ -12,10 +12,11 @@ its next-layer experts):
 
 Latency-bound stages that nothing on the bandwidth-bound chain waits for run
 on a second stream, overlapped with it: in one layer the statistics run
-beside plan, permute and combine; with the shuffle, the move of the routing
-and the layer-2 plan run beside the move of the token rows (the plan needs
-only the routing).  ``run(..., overlap=False)`` keeps everything on one
-stream, which is how per-stage times are taken.
+beside plan, permute and combine; with the shuffle, the move of the routing,
+the layer-2 plan and the layer-1 pair counts and Ochiai run beside the move
+of the token rows (the plan needs only the routing; the prediction before it
+needs only the transitions).  ``run(..., overlap=False)`` keeps everything on
+one stream, which is how per-stage times are taken.
 
 All buffers are allocated once in the constructor; ``run`` only enqueues
 kernels (no allocation, no host synchronisation).  ``z`` stands for the
@@ -295,17 +296,26 @@ class TwoLayerStep:
         self.plan = None
         self.shuffle = None
         self._fork = _Fork(dev)
+        self._counts_tmp = torch.empty(E1, dtype=torch.int32, device=dev)
 
     STAGES = ("stats", "shuffle_predict", "shuffle_permute", "shuffle_routing", "plan", "permute",
               "combine")
 
     def run(self, timers: Optional[StageTimers] = None, overlap: bool = True):
         fork = self._fork if overlap else _INLINE
+        st = self.stats_out
         with _timed(timers, "stats"):
-            stats = ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
-                                    d_err=self.d_err)
+            if overlap:
+                # The prediction needs only the transitions; the pair counts
+                # and Ochiai are computed on the second stream below.
+                ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, pairs=False,
+                                out={"expert_count": self._counts_tmp,
+                                     "transition": st["transition"]}, d_err=self.d_err)
+            else:
+                ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=st,
+                                d_err=self.d_err)
         with _timed(timers, "shuffle_predict"):
-            self.shuffle = ops.shuffle_predict(self.topk1, stats["transition"], self.expert_rank2,
+            self.shuffle = ops.shuffle_predict(self.topk1, st["transition"], self.expert_rank2,
                                                self.G, balanced=self.balanced,
                                                out=self.shuffle_out, ws=self.shuffle_ws,
                                                d_err=self.d_err)
@@ -319,6 +329,10 @@ class TwoLayerStep:
                                               self.G, self.Rn, self.shuffle["shard_offsets"],
                                               out=self.plan_out, ws=self.plan_ws,
                                               d_err=self.d_err)
+            if overlap:
+                ops.coact_stats(self.topk1, self.E1, out={k: st[k] for k in
+                                                          ("expert_count", "pair_count", "ochiai")},
+                                d_err=self.d_err)
         with _timed(timers, "shuffle_permute"):
             ops.gather(self.x, perm, out=self.x_s, d_err=self.d_err)
         fork.join()
