@@ -26,6 +26,7 @@ from .coact import (  # noqa: F401
     partial_combine,
     moe_output,
     permute_scaled,
+    gather_scaled,
     row_dot,
     ema_update,
     colocated_coactivation,
