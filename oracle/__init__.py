@@ -26,7 +26,6 @@ from .coact import (  # noqa: F401
     partial_combine,
     moe_output,
     permute_scaled,
-    gather_scaled,
     row_dot,
     ema_update,
     colocated_coactivation,

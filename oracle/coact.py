@@ -561,23 +561,6 @@ def permute_scaled(x: np.ndarray, x_dtype: str, dest: np.ndarray, scale: np.ndar
     return bf16_round(o32) if out_dtype == "bf16" else o32
 
 
-def gather_scaled(x: np.ndarray, x_dtype: str, src: np.ndarray, scale: np.ndarray,
-                  out_dtype: str) -> np.ndarray:
-    """out[i] = scale[i] * x[src[i]], the product formed exactly (float64) and
-    rounded once to float32, then to bf16 for a bf16 output; rows with
-    src[i] < 0 stay zero.  The same gradient as permute_scaled, indexed by
-    output row: each expert row's gradient is its gate times the gradient of
-    the send row it was expanded from."""
-    xf = _as_f64(x, x_dtype)
-    src = np.asarray(src, dtype=np.int64)
-    out = np.zeros((src.shape[0], xf.shape[1]), dtype=np.float64)
-    for i in range(src.shape[0]):
-        if src[i] >= 0:
-            out[i] = float(np.float32(scale[i])) * xf[src[i]]
-    o32 = out.astype(np.float32)
-    return bf16_round(o32) if out_dtype == "bf16" else o32
-
-
 def row_dot(a: np.ndarray, a_dtype: str, b: np.ndarray, b_dtype: str,
             rows: np.ndarray) -> np.ndarray:
     """out[t, q] = <a[t], b[rows[t, q]]> (0 where rows[t, q] < 0), summed in

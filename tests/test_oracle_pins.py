@@ -630,33 +630,6 @@ def test_permute_scaled_and_row_dot_small():
     assert ob[0, 0] == oracle.bf16_round(np.array([exact], np.float32))[0]
 
 
-def test_gather_scaled_is_the_scaled_scatter_by_source():
-    """Indexing the scaled scatter by output row: building each source row's
-    list of output rows from src and scattering gives the same rows bit for
-    bit (bf16 and fp32), and a hand case shows the single rounding."""
-    rng = np.random.default_rng(24)
-    for xd, od in (("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32"), ("f32", "bf16")):
-        n_x, n, H = 40, 90, 24
-        x = rng.standard_normal((n_x, H)).astype(np.float32)
-        xin = oracle.bf16_round(x) if xd == "bf16" else x
-        src = rng.integers(0, n_x, size=n)
-        src[rng.random(n) < 0.2] = -1
-        scale = rng.standard_normal(n).astype(np.float32)
-        lists = [[i for i in range(n) if src[i] == t] for t in range(n_x)]
-        width = max(1, max(len(v) for v in lists))
-        dest = np.full((n_x, width), -1, np.int64)
-        for t, v in enumerate(lists):
-            dest[t, :len(v)] = v
-        a = oracle.gather_scaled(xin, xd, src, scale, od)
-        b = oracle.permute_scaled(xin, xd, dest, scale, n, od)
-        assert np.array_equal(a, b)
-    xb = oracle.bf16_round(np.array([[1.0 + 2 ** -7]], np.float32))
-    g = oracle.gather_scaled(xb, "bf16", np.array([0]), np.array([1.0 + 2 ** -8], np.float32),
-                             "bf16")
-    exact = (1.0 + 2 ** -7) * (1.0 + 2 ** -8)
-    assert g[0, 0] == oracle.bf16_round(np.array([exact], np.float32))[0]
-
-
 # ------------------------------------------------------------ EMA, placement
 
 def test_ema_closed_form():
