@@ -195,6 +195,54 @@ def test_permute_narrow_rows_and_untouched():
     assert (got[~targeted] == -7).all()
 
 
+@pytest.mark.parametrize("row_bytes,width", [(8192, 6), (14336, 8), (6400, 3), (16384, 4)])
+def test_permute_fanout_paths(row_bytes, width):
+    """Wide rows with more than two destinations, through the fan-out launch
+    (6-8 KiB rows) and the plain one (14-16 KiB rows): scattered -1 entries,
+    a device row count, and a destination past the output (reported,
+    skipped, nothing else written wrong)."""
+    rng = np.random.default_rng(row_bytes + width)
+    T = 700
+    words = row_bytes // 4
+    x = rng.integers(-2**31, 2**31 - 1, size=(T, words), dtype=np.int64).astype(np.int32)
+    out_rows = T * width + 5
+    dest = rng.permutation(out_rows)[:T * width].reshape(T, width).astype(np.int32)
+    dest[rng.random((T, width)) < 0.3] = -1
+    say("permute fan-out", row_bytes, width)
+    err = _err()
+    out = torch.full((out_rows, words), -7, dtype=torch.int32, device="cuda")
+    ops.permute(i32(x), i32(dest), out_rows, out=out, d_err=err)
+    _no_errors(err)
+    got = host(out)
+    want = np.full((out_rows, words), -7, np.int32)
+    for t in range(T):
+        for q in range(width):
+            if dest[t, q] >= 0:
+                want[dest[t, q]] = x[t]
+    assert_equal(got, want, "fan-out rows")
+    # device row count: tokens past it move nothing
+    out2 = torch.full((out_rows, words), -7, dtype=torch.int32, device="cuda")
+    ops.permute(i32(x), i32(dest), out_rows, out=out2, n_valid=i32([123]), d_err=err)
+    _no_errors(err)
+    want2 = np.full((out_rows, words), -7, np.int32)
+    for t in range(123):
+        for q in range(width):
+            if dest[t, q] >= 0:
+                want2[dest[t, q]] = x[t]
+    assert_equal(host(out2), want2, "fan-out rows, device count")
+    # one destination past the output: reported and skipped
+    bad = dest.copy()
+    bad[5, width - 1] = out_rows
+    out3 = torch.full((out_rows, words), -7, dtype=torch.int32, device="cuda")
+    ops.permute(i32(x), i32(bad), out_rows, out=out3, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 32
+    want3 = want.copy()
+    if dest[5, width - 1] >= 0:
+        want3[dest[5, width - 1]] = -7
+    assert_equal(host(out3), want3, "fan-out rows with a bad destination")
+
+
 GATHER_CASES = [(3000, 2500, 8192, 0.1), (1001, 1001, 14336, 0.0), (777, 900, 512, 0.2),
                 (1500, 64, 1024, 0.0), (613, 400, 2064, 0.05), (5000, 4000, 8, 0.1),
                 (300, 300, 4, 0.0), (200, 150, 48, 0.3), (1, 1, 16384, 0.0)]
