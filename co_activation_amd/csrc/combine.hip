@@ -41,25 +41,32 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   const int64_t zvec = groups * (ZBF16 ? EPL / 8 : EPL / 4);
   const int64_t yvec = groups * (YBF16 ? EPL / 8 : EPL / 4);
 
+  // The token's rows, then their weights: every load of a kind is issued
+  // before any is used, so the prologue costs two memory latencies.
   int rid[MOE_MAX_K];
   float a[MOE_MAX_K];
   int errbits = 0;
 #pragma unroll
+  for (int q = 0; q < MOE_MAX_K; ++q)
+    rid[q] = q < k ? __builtin_amdgcn_readfirstlane(rows[static_cast<int64_t>(t) * k + q]) : -1;
+#pragma unroll
   for (int q = 0; q < MOE_MAX_K; ++q) {
-    rid[q] = -1;
-    a[q] = 0.f;
-    if (q < k) {
-      const int r = __builtin_amdgcn_readfirstlane(rows[static_cast<int64_t>(t) * k + q]);
-      if (r >= 0 && r < z_rows) {
-        rid[q] = r;
-        if (weight != nullptr)
-          a[q] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(weight[r])));
-        else
-          a[q] = 1.f;
-      } else if (r >= z_rows) {
-        errbits = MOE_DERR_ROW_RANGE;
-      }
+    if (rid[q] >= z_rows) {
+      errbits = MOE_DERR_ROW_RANGE;
+      rid[q] = -1;
     }
+  }
+  if (weight != nullptr && z_rows > 0) {
+    // One load per slot, absent rows reading row 0's weight (unused).
+    float wv[MOE_MAX_K];
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_K; ++q) wv[q] = weight[rid[q] < 0 ? 0 : rid[q]];
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_K; ++q)
+      a[q] = rid[q] < 0 ? 0.f : __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wv[q])));
+  } else {
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_K; ++q) a[q] = rid[q] < 0 ? 0.f : 1.f;
   }
   if (chunk == 0 && lane == 0) report(d_err, errbits);
 
@@ -93,6 +100,16 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   }
 }
 
+// Tokens with many rows (k >= 6 slots and at least 6 rows of z per output
+// row, so that most slots are in use -- not so for the expert side's reply
+// rows, whose k slots hold one or two rows): blocks reserve this much LDS
+// (unused) so that at most six are resident per CU (160 KB of LDS), which
+// keeps fewer rows streaming at once.  Measured on MI355X inside the
+// one-layer step: 8 KiB rows with k = 6 combine in 481 instead of 505 us,
+// 14 KiB rows with k = 8 in 623 instead of 667 us; with one or two rows per
+// output row the cap costs 8-14%.
+constexpr unsigned kCombLdsManyRows = 24 * 1024;
+
 template <bool ZBF16, bool YBF16, int EPL>
 int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k, const float* w,
            int64_t T, void* y, const int32_t* n_valid, int32_t* d_err, hipStream_t s) {
@@ -102,7 +119,8 @@ int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k,
   constexpr int kItemsPerBlock = kCombThreads / kWave;
   const int64_t blocks = (items + kItemsPerBlock - 1) / kItemsPerBlock;
   if (blocks > INT32_MAX) return MOE_ERR_SHAPE;
-  combine_kernel<ZBF16, YBF16, EPL><<<static_cast<unsigned>(blocks), kCombThreads, 0, s>>>(
+  const unsigned lds = (k >= 6 && z_rows >= 6 * T) ? kCombLdsManyRows : 0;
+  combine_kernel<ZBF16, YBF16, EPL><<<static_cast<unsigned>(blocks), kCombThreads, lds, s>>>(
       static_cast<const u32x4*>(z), z_rows, groups, chunks, rows, k, w, static_cast<int>(T),
       static_cast<u32x4*>(y), n_valid, d_err);
   MOE_CHECK_LAUNCH();
