@@ -227,7 +227,8 @@ def main() -> int:
     import torch
 
     import co_activation_amd
-    from co_activation_amd.pipeline import ExpertSideStep, LayerStep, StageTimers, TwoLayerStep
+    from co_activation_amd.pipeline import (ExpertSideStep, GraphStep, LayerStep, StageTimers,
+                                            TwoLayerStep)
     from workloads import make
     from workloads.gen import device_normal
 
@@ -320,6 +321,20 @@ def main() -> int:
     dom_all = timers.durations_ms(dom)
     dom_ms = statistics.mean(dom_all)
 
+    # The same step captured once as a HIP graph and replayed (outside the
+    # timed region above): the host enqueues one launch per step.
+    graph = GraphStep(step)
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graph
+
     counters = step.plan.counters.cpu().numpy()
     N = int(counters[0])
     T, k = w.T, w.k
@@ -357,6 +372,8 @@ def main() -> int:
                      "cross_node_V": int(counters[5]), "max_recv_rows": int(counters[6])},
         "copy_probe_gbps": copy_gbs,
         "wall_s_timed": wall,
+        "graph_replay": {"ms_per_step": graph_ms,
+                         "dispatched_rows_per_s": int(counters[0]) / (graph_ms * 1e-3)},
         "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": 1e3 * dom_ms,
                      "kernel_us_median": 1e3 * statistics.median(dom_all),
                      "algorithmic_bytes": kernels[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -481,3 +481,31 @@ class ExpertSideBackward:
         with _timed(timers, "grad_tokens"):
             ops.combine(self.d_send, lp.token_rows, None, out=self.dx, d_err=err)
         return self
+
+
+class GraphStep:
+    """A step captured once as a HIP graph and replayed: the whole dispatch
+    path of a step (both streams, every kernel) is enqueued by one launch,
+    so the host does no per-kernel work.  ``step`` is a LayerStep or
+    TwoLayerStep whose buffers the graph reads and writes in place; the
+    captured kernels keep the launch shapes and pointers of capture time.
+    Nothing in the path allocates, synchronises or clears memory with a
+    runtime memset, so the capture is complete."""
+
+    def __init__(self, step):
+        self.step = step
+        # one eager run on a side stream first (settles lazy initialisation)
+        warm = torch.cuda.Stream()
+        warm.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(warm):
+            step.run()
+        torch.cuda.current_stream().wait_stream(warm)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            step.run()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()
+        return self.step

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from co_activation_amd import ops
-from co_activation_amd.pipeline import LayerStep, TwoLayerStep
+from co_activation_amd.pipeline import GraphStep, LayerStep, TwoLayerStep
 from gpu_util import (assert_equal, check_combine, dev, f32_ulps, host, i32, say, x_tensor)
 from workloads import make, expert_outputs
 
@@ -433,6 +433,46 @@ def test_two_layer_step_parity():
                   "two-layer combine")
     c = host(step.plan.counters)
     assert c[3] / (w.T * w.k) > ref["local_share_before"]
+
+
+@pytest.mark.parametrize("two_layer", [False, True])
+def test_graph_replays_match_eager(two_layer):
+    """A step captured as a HIP graph: every replay, with eager work and
+    synchronisations between replays and the outputs cleared before each,
+    gives exactly what an eager single-stream step gives."""
+    if two_layer:
+        w = make(5, T=8192, H=1024)
+        mk = lambda: TwoLayerStep(i32(w.topk), i32(w.topk2), dev(w.gates2), i32(w.expert_rank2),
+                                  x_tensor(w), dev(Z), w.G, w.ranks_per_node, E1=w.E)
+    else:
+        w = make(3, T=4096, H=1024)
+        mk = lambda: LayerStep(i32(w.topk), dev(w.gates), i32(w.expert_rank), x_tensor(w), dev(Z),
+                               w.G, w.ranks_per_node)
+    say("graph replay", "two-layer" if two_layer else "one layer")
+    cap = w.T * min(w.k, w.G)
+    Z = expert_outputs(cap, w.H, "bf16", seed=1)
+    ref = mk().run(overlap=False)
+    torch.cuda.synchronize()
+    N = int(host(ref.plan.counters)[0])
+    want = {k: host(v) for k, v in ref.stats_out.items()}
+    want.update(token_rows=host(ref.plan.token_rows), counters=host(ref.plan.counters),
+                send=host(ref.send)[:N], y=host(ref.y))
+    g = GraphStep(mk())
+    st = g.step
+    for rep in range(4):
+        ref.run()                      # eager work between replays
+        torch.cuda.synchronize()
+        for t in (st.y, st.send, st.plan.token_rows, st.plan.counters, *st.stats_out.values()):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _no_errors(st.d_err)
+        got = {k: host(v) for k, v in st.stats_out.items()}
+        got.update(token_rows=host(st.plan.token_rows), counters=host(st.plan.counters),
+                   send=host(st.send)[:N], y=host(st.y))
+        for k in want:
+            assert_equal(got[k], want[k], f"replay {rep}: {k}")
 
 
 @pytest.mark.parametrize("two_layer", [False, True])
