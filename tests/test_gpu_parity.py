@@ -107,6 +107,28 @@ def test_plan_parity(cfg, T, placement):
     _check_plan(plan, ref, w.T, w.k)
 
 
+@pytest.mark.parametrize("G,rn", [(64, 8), (32, 4)])
+def test_plan_large_tile_count(G, rn):
+    """Many tiles on many ranks: 65 536 tokens on 64 ranks and 147 456 on
+    32, over uneven shards (the scan walks several chunks of 64 tiles per
+    rank), compared in full."""
+    T = 65536 if G == 64 else 147456
+    rng = np.random.default_rng(G)
+    E, k = 128, 4
+    topk = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    gates = rng.random((T, k)).astype(np.float32)
+    er = rng.integers(0, G, size=E).astype(np.int32)
+    cuts = np.sort(rng.integers(0, T + 1, size=G - 1))
+    src = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+    say("plan, large tile count", T, G)
+    err = _err()
+    plan = ops.dispatch_plan(i32(topk), dev(gates), i32(er), G, rn, src_offsets=i32(src),
+                             d_err=err)
+    _no_errors(err)
+    ref = oracle.dispatch_plan(topk, gates, er, G, rn, src_offsets=src)
+    _check_plan(plan, ref, T, k)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_plan_uneven_shards(seed):
     """Explicit source offsets: uneven, empty shards, a shard of one token."""
