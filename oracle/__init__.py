@@ -22,6 +22,7 @@ from .coact import (  # noqa: F401
     bf16_to_f32,
     shuffle_predict,
     two_layer_pipeline,
+    shuffle_dispatch,
     expert_plan,
     partial_combine,
     moe_output,
