@@ -259,7 +259,8 @@ def main() -> int:
                             i32(w.expert_rank2), x, z, w.G, w.ranks_per_node, E1=w.E)
         workload = (f"two MoE layers with token shuffle: T={w.T} H={w.H} bf16 E={w.E} k={w.k} "
                     f"G={w.G} (1 node of {w.ranks_per_node}); layer-1 stats+transitions, shuffle "
-                    f"predict+permute, layer-2 dedup plan, permute, combine")
+                    f"predict, layer-2 dedup plan, shuffle move fused with the layer-2 permute, "
+                    f"combine")
     else:
         er = w.expert_rank if args.placement == "main" else w.alt_expert_rank
         cap = w.T * min(w.k, w.G)
@@ -301,8 +302,8 @@ def main() -> int:
         step.run(stages, overlap=False)
     torch.cuda.synchronize()
     stage_ms = stages.median_ms()
-    dom = max(("permute", "combine") + (("shuffle_permute",) if w.cfg == 5 else ()),
-              key=lambda n: stage_ms[n])
+    moves = ("shuffle_dispatch",) if "shuffle_dispatch" in stage_ms else ("permute",)
+    dom = max(moves + ("combine",), key=lambda n: stage_ms[n])
 
     # Timed region: K steps; events only around the dominant kernel.
     timers = StageTimers((dom,), args.steps)
@@ -341,10 +342,12 @@ def main() -> int:
     rb = w.row_bytes
     bytes_perm = (T + N) * rb + 4 * T * k
     bytes_comb = N * rb + T * rb + 4 * T * k + 4 * N
-    pc_gbs = (bytes_perm + bytes_comb) / ((stage_ms["permute"] + stage_ms["combine"]) * 1e-3) / 1e9
     kernels = {"permute": bytes_perm, "combine": bytes_comb}
-    if w.cfg == 5:
-        kernels["shuffle_permute"] = 2 * T * rb + 4 * T
+    # the shuffle's move fused with the layer-2 permute: each row read once,
+    # written to its shuffled place and its send rows; dest_pos and token_rows
+    kernels["shuffle_dispatch"] = (2 * T + N) * rb + 4 * T + 4 * T * k
+    mv = moves[0]
+    pc_gbs = (kernels[mv] + bytes_comb) / ((stage_ms[mv] + stage_ms["combine"]) * 1e-3) / 1e9
     achieved = kernels[dom] / (dom_ms * 1e-3) / 1e9
 
     line = {

@@ -36,6 +36,7 @@ EXPORTS = (
     "moe_expert_plan_workspace_size", "moe_expert_plan",
     "moe_permute_scaled", "moe_row_dot", "moe_ema_update", "moe_place_experts",
     "moe_shuffle_balanced_workspace_size", "moe_shuffle_balanced", "moe_gather",
+    "moe_shuffle_dispatch",
 )
 
 _lib = None
@@ -56,6 +57,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.moe_permute.restype = c_int
     lib.moe_gather.argtypes = [P, c_int64, c_int64, P, c_int64, P, P, P, P]
     lib.moe_gather.restype = c_int
+    lib.moe_shuffle_dispatch.argtypes = [P, c_int64, c_int64, P, P, c_int, P, P, c_int64, P, P]
+    lib.moe_shuffle_dispatch.restype = c_int
     lib.moe_combine.argtypes = [P, c_int, c_int64, c_int64, P, c_int, P, c_int64, P, c_int, P, P,
                                 P]
     lib.moe_combine.restype = c_int

@@ -308,8 +308,114 @@ int launch_gather(const void* x, int64_t x_rows, int64_t vec_per_row, const int3
   return MOE_OK;
 }
 
+// ------------------------------------------------- shuffle + dispatch
+
+// The token shuffle's move and the next layer's dispatch in one pass: token
+// t's row is read once and written to its shuffled position p = dest_pos[t]
+// and to the send rows token_rows[p][*] of that position.  TPT threads own a
+// token (the same layout as the permute).
+template <typename V, int TPT, int U>
+__global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void shuffle_dispatch_kernel(
+    const V* __restrict__ x, int T, int64_t vec_per_row, const int32_t* __restrict__ dest_pos,
+    const int32_t* __restrict__ token_rows, int k, V* __restrict__ x_out, V* __restrict__ send,
+    int64_t send_rows, int32_t* d_err) {
+  constexpr int kBlock = TPT < kPermThreads ? kPermThreads : TPT;
+  constexpr int kTokens = kBlock / TPT;
+  const int sub = kTokens == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / TPT);
+  const int t = blockIdx.x * kTokens + sub;
+  if (t >= T) return;
+  const int l = kTokens == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x % TPT);
+  const int p = __builtin_amdgcn_readfirstlane(dest_pos[t]);
+  if (p < 0 || p >= T) {
+    if (l == 0) report(d_err, MOE_DERR_ROW_RANGE);
+    return;
+  }
+  int drow[MOE_MAX_K];
+#pragma unroll
+  for (int q = 0; q < MOE_MAX_K; ++q)
+    drow[q] = q < k ? __builtin_amdgcn_readfirstlane(token_rows[static_cast<int64_t>(p) * k + q])
+                    : -1;
+  int errbits = 0;
+  const V* src = x + static_cast<int64_t>(t) * vec_per_row;
+  V* xo = x_out + static_cast<int64_t>(p) * vec_per_row;
+  for (int64_t c0 = l; c0 < vec_per_row; c0 += TPT * U) {
+    V v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * TPT;
+      if (c < vec_per_row) v[u] = load_row<false>(src + c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * TPT;
+      if (c < vec_per_row) __builtin_nontemporal_store(v[u], xo + c);
+    }
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_K; ++q) {
+      if (q >= k) break;
+      if (drow[q] < 0) continue;
+      if (drow[q] >= send_rows) {
+        errbits = MOE_DERR_ROW_RANGE;
+        continue;
+      }
+      V* dst = send + static_cast<int64_t>(drow[q]) * vec_per_row;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * TPT;
+        if (c < vec_per_row) __builtin_nontemporal_store(v[u], dst + c);
+      }
+    }
+  }
+  if (l == 0) report(d_err, errbits);
+}
+
+// Launch shape by row size R (vectors): a wave per token below 256 (four
+// vectors per lane per pass), else 512 threads per token.
+template <typename V>
+int launch_shuffle_dispatch(const void* x, int T, int64_t vec_per_row, const int32_t* dest_pos,
+                            const int32_t* token_rows, int k, void* x_out, void* send,
+                            int64_t send_rows, int32_t* d_err, hipStream_t s) {
+  const V* xv = static_cast<const V*>(x);
+  if (vec_per_row < 256) {
+    constexpr int kTokens = kPermThreads / 64;
+    shuffle_dispatch_kernel<V, 64, 4><<<static_cast<unsigned>((T + kTokens - 1) / kTokens),
+                                        kPermThreads, 0, s>>>(
+        xv, T, vec_per_row, dest_pos, token_rows, k, static_cast<V*>(x_out),
+        static_cast<V*>(send), send_rows, d_err);
+  } else {
+    shuffle_dispatch_kernel<V, 512, 1><<<static_cast<unsigned>(T), 512, 0, s>>>(
+        xv, T, vec_per_row, dest_pos, token_rows, k, static_cast<V*>(x_out),
+        static_cast<V*>(send), send_rows, d_err);
+  }
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
+
+extern "C" int moe_shuffle_dispatch(const void* x, int64_t T, int64_t row_bytes,
+                                    const int32_t* dest_pos, const int32_t* token_rows, int k,
+                                    void* x_out, void* send, int64_t send_rows, int32_t* d_err,
+                                    void* stream) {
+  if (T < 0 || row_bytes <= 0 || k < 1 || k > MOE_MAX_K || send_rows < 0 ||
+      T * static_cast<int64_t>(k) >= (int64_t{1} << 31))
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || dest_pos == nullptr || token_rows == nullptr || x_out == nullptr ||
+      (send == nullptr && send_rows > 0))
+    return MOE_ERR_NULL;
+  const auto xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(x_out),
+             sa = reinterpret_cast<uintptr_t>(send);
+  if (row_bytes % 4 != 0 || xa % 4 != 0 || oa % 4 != 0 || sa % 4 != 0) return MOE_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int Ti = static_cast<int>(T);
+  if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0 && sa % 16 == 0)
+    return moe::launch_shuffle_dispatch<moe::u32x4>(x, Ti, row_bytes / 16, dest_pos, token_rows, k,
+                                                    x_out, send, send_rows, d_err, s);
+  return moe::launch_shuffle_dispatch<uint32_t>(x, Ti, row_bytes / 4, dest_pos, token_rows, k,
+                                                x_out, send, send_rows, d_err, s);
+}
 
 extern "C" int moe_gather(const void* x, int64_t x_rows, int64_t row_bytes, const int32_t* src,
                           int64_t n_rows, void* out, const int32_t* n_valid, int32_t* d_err,

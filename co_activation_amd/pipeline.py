@@ -256,12 +256,19 @@ class LayerStep:
 
 class TwoLayerStep:
     """Layer-1 statistics with transitions, shuffle prediction, the shuffle,
-    and the layer-2 deduplicated dispatch and combine."""
+    and the layer-2 deduplicated dispatch and combine.
+
+    fused=True (the default): the move of the token rows into the shuffled
+    order and the layer-2 permute are one pass (moe_shuffle_dispatch), which
+    reads each row once; the layer-2 plan, which needs only the shuffled
+    routing, runs before it.  fused=False: the move and the permute are
+    separate passes, the plan overlapping the move on a second stream."""
 
     def __init__(self, topk1, topk2, gates2, expert_rank2, x, z, G, ranks_per_node, E1=None,
-                 balanced=False):
+                 balanced=False, fused=True):
         dev = topk1.device
         self.balanced = balanced
+        self.fused = fused
         self.T, self.k1 = topk1.shape
         self.k2 = topk2.shape[1]
         self.E1 = E1 if E1 is not None else expert_rank2.numel()
@@ -298,10 +305,18 @@ class TwoLayerStep:
         self._fork = _Fork(dev)
         self._counts_tmp = torch.empty(E1, dtype=torch.int32, device=dev)
 
-    STAGES = ("stats", "shuffle_predict", "shuffle_permute", "shuffle_routing", "plan", "permute",
-              "combine")
+    STAGES_FUSED = ("stats", "shuffle_predict", "shuffle_routing", "plan", "shuffle_dispatch",
+                    "combine")
+    STAGES_SPLIT = ("stats", "shuffle_predict", "shuffle_permute", "shuffle_routing", "plan",
+                    "permute", "combine")
+
+    @property
+    def STAGES(self):
+        return self.STAGES_FUSED if self.fused else self.STAGES_SPLIT
 
     def run(self, timers: Optional[StageTimers] = None, overlap: bool = True):
+        if self.fused:
+            return self._run_fused(timers)
         fork = self._fork if overlap else _INLINE
         st = self.stats_out
         with _timed(timers, "stats"):
@@ -338,6 +353,34 @@ class TwoLayerStep:
         fork.join()
         with _timed(timers, "permute"):
             ops.permute(self.x_s, self.plan.token_rows, self.cap, out=self.send, d_err=self.d_err)
+        with _timed(timers, "combine"):
+            ops.combine(self.z, self.plan.token_rows, self.plan.row_weight, out=self.y,
+                        d_err=self.d_err)
+        return self
+
+    def _run_fused(self, timers):
+        """One stream: statistics, prediction, the routing move and the
+        layer-2 plan, then the token rows moved and dispatched in one pass,
+        then the combine."""
+        with _timed(timers, "stats"):
+            ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
+                            d_err=self.d_err)
+        with _timed(timers, "shuffle_predict"):
+            self.shuffle = ops.shuffle_predict(self.topk1, self.stats_out["transition"],
+                                               self.expert_rank2, self.G, balanced=self.balanced,
+                                               out=self.shuffle_out, ws=self.shuffle_ws,
+                                               d_err=self.d_err)
+        perm = self.shuffle["perm"]
+        with _timed(timers, "shuffle_routing"):
+            ops.gather(self.topk2, perm, out=self.topk2_s, d_err=self.d_err)
+            ops.gather(self.gates2, perm, out=self.gates2_s, d_err=self.d_err)
+        with _timed(timers, "plan"):
+            self.plan = ops.dispatch_plan(self.topk2_s, self.gates2_s, self.expert_rank2, self.G,
+                                          self.Rn, self.shuffle["shard_offsets"],
+                                          out=self.plan_out, ws=self.plan_ws, d_err=self.d_err)
+        with _timed(timers, "shuffle_dispatch"):
+            ops.shuffle_dispatch(self.x, self.shuffle["dest_pos"], self.plan.token_rows, self.cap,
+                                 x_out=self.x_s, send=self.send, d_err=self.d_err)
         with _timed(timers, "combine"):
             ops.combine(self.z, self.plan.token_rows, self.plan.row_weight, out=self.y,
                         d_err=self.d_err)

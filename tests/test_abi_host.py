@@ -92,6 +92,12 @@ def test_permute_combine_shuffle_reject(built_lib):
     assert L.moe_permute(FAKE + 2, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -4
     assert L.moe_permute(NULL, 8, 16, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -1
     assert L.moe_permute(NULL, 0, 16, NULL, 1, NULL, 0, NULL, NULL, NULL) == 0   # empty: no-op
+    sdp = L.moe_shuffle_dispatch
+    assert sdp(FAKE, 8, 16, FAKE, FAKE, 9, FAKE, FAKE, 16, NULL, NULL) == -2   # k > 8
+    assert sdp(FAKE, 8, 0, FAKE, FAKE, 2, FAKE, FAKE, 16, NULL, NULL) == -2    # row_bytes
+    assert sdp(FAKE, 8, 16, NULL, FAKE, 2, FAKE, FAKE, 16, NULL, NULL) == -1   # dest_pos
+    assert sdp(FAKE, 8, 6, FAKE, FAKE, 2, FAKE, FAKE, 16, NULL, NULL) == -4    # not whole words
+    assert sdp(NULL, 0, 16, NULL, NULL, 2, NULL, NULL, 0, NULL, NULL) == 0     # empty: no-op
     g = L.moe_gather
     assert g(FAKE, 8, 0, FAKE, 8, FAKE, NULL, NULL, NULL) == -2     # row_bytes
     assert g(FAKE, -1, 16, FAKE, 8, FAKE, NULL, NULL, NULL) == -2   # x_rows

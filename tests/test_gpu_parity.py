@@ -265,6 +265,65 @@ def test_permute_fanout_paths(row_bytes, width):
     assert_equal(host(out3), want3, "fan-out rows with a bad destination")
 
 
+@pytest.mark.parametrize("row_bytes,k", [(8192, 2), (14336, 8), (1024, 3), (48, 1), (8, 2), (12, 4)])
+def test_shuffle_dispatch_parity(row_bytes, k):
+    """The shuffle's move fused with the next layer's permute, bit for bit
+    against the oracle over every launch shape (16-byte and 4-byte rows);
+    rows no position targets stay as they were."""
+    rng = np.random.default_rng(row_bytes + k)
+    T = 777
+    words = row_bytes // 4
+    x = rng.integers(-2**31, 2**31 - 1, size=(T, words), dtype=np.int64).astype(np.int32)
+    dest_pos = rng.permutation(T).astype(np.int32)
+    send_rows = T * k + 9
+    token_rows = rng.permutation(send_rows)[:T * k].reshape(T, k).astype(np.int32)
+    token_rows[rng.random((T, k)) < 0.3] = -1
+    say("shuffle dispatch", row_bytes, k)
+    err = _err()
+    xo = torch.full((T, words), -5, dtype=torch.int32, device="cuda")
+    sd = torch.full((send_rows, words), -7, dtype=torch.int32, device="cuda")
+    ops.shuffle_dispatch(i32(x), i32(dest_pos), i32(token_rows), send_rows, x_out=xo, send=sd,
+                         d_err=err)
+    _no_errors(err)
+    want_x, want_s = oracle.shuffle_dispatch(x, dest_pos, token_rows, send_rows)
+    assert_equal(host(xo), want_x, "shuffled rows")
+    got = host(sd)
+    hit = np.isin(np.arange(send_rows), token_rows[token_rows >= 0])
+    assert_equal(got[hit], want_s[hit], "send rows")
+    assert (got[~hit] == -7).all()
+
+
+def test_shuffle_dispatch_errors():
+    """A position outside [0, T) or a send row past the buffer is reported
+    and that copy skipped; nothing else changes."""
+    T, k, words = 64, 2, 4
+    rng = np.random.default_rng(77)
+    x = rng.integers(0, 1000, size=(T, words)).astype(np.int32)
+    dest_pos = np.arange(T, dtype=np.int32)
+    token_rows = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    bad_pos = dest_pos.copy()
+    bad_pos[3] = T
+    say("shuffle dispatch errors")
+    for dp, tr in ((bad_pos, token_rows), (dest_pos, np.where(token_rows == 10, T * k, token_rows))):
+        err = _err()
+        xo = torch.full((T, words), -5, dtype=torch.int32, device="cuda")
+        sd = torch.full((T * k, words), -7, dtype=torch.int32, device="cuda")
+        ops.shuffle_dispatch(i32(x), i32(dp), i32(tr.astype(np.int32)), T * k, x_out=xo, send=sd,
+                             d_err=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 32
+        gx, gs = host(xo), host(sd)
+        if dp is bad_pos:
+            keep = np.arange(T) != 3
+            assert_equal(gx[keep], x[keep], "moved rows")
+            assert (gx[3] == -5).all() and (gs[6:8] == -7).all()
+        else:
+            assert_equal(gx, x, "moved rows")
+            assert (gs[10] == -7).all()
+            assert_equal(np.delete(gs, 10, axis=0), np.delete(np.repeat(x, k, axis=0), 10, axis=0),
+                         "send rows")
+
+
 GATHER_CASES = [(3000, 2500, 8192, 0.1), (1001, 1001, 14336, 0.0), (777, 900, 512, 0.2),
                 (1500, 64, 1024, 0.0), (613, 400, 2064, 0.05), (5000, 4000, 8, 0.1),
                 (300, 300, 4, 0.0), (200, 150, 48, 0.3), (1, 1, 16384, 0.0)]
@@ -431,13 +490,14 @@ def test_layer_step_parity():
     assert_equal(host(step.stats_out["pair_count"]), st["pair_count"], "pairs")
 
 
-def test_two_layer_step_parity():
+@pytest.mark.parametrize("fused", [True, False])
+def test_two_layer_step_parity(fused):
     w = make(5, T=4104, H=256)
-    say("two-layer step cfg5")
+    say("two-layer step cfg5", "fused" if fused else "split")
     cap = w.T * min(w.k, w.G)
     Z = expert_outputs(cap, w.H, "bf16", seed=1)
     step = TwoLayerStep(i32(w.topk), i32(w.topk2), dev(w.gates2), i32(w.expert_rank2),
-                        x_tensor(w), dev(Z), w.G, w.ranks_per_node, E1=w.E)
+                        x_tensor(w), dev(Z), w.G, w.ranks_per_node, E1=w.E, fused=fused)
     step.run()
     _no_errors(step.d_err)
     ref = oracle.two_layer_pipeline(w.topk, w.topk2, w.gates2, w.x, w.expert_rank2, w.E, w.E,
@@ -500,11 +560,14 @@ def test_graph_replays_match_eager(two_layer):
 @pytest.mark.parametrize("two_layer", [False, True])
 def test_overlapped_steps_match_serial(two_layer):
     """Steps that run latency-bound stages on a second stream give, after
-    several back-to-back steps, exactly what one single-stream step gives."""
+    several back-to-back steps, exactly what one single-stream step gives
+    (the two-layer step in its separate-pass form, whose layer-2 plan
+    overlaps the token move)."""
     if two_layer:
         w = make(5, T=8192, H=1024)
         mk = lambda: TwoLayerStep(i32(w.topk), i32(w.topk2), dev(w.gates2), i32(w.expert_rank2),
-                                  x_tensor(w), dev(Z), w.G, w.ranks_per_node, E1=w.E)
+                                  x_tensor(w), dev(Z), w.G, w.ranks_per_node, E1=w.E,
+                                  fused=False)
     else:
         w = make(4, T=2048, H=1024)
         mk = lambda: LayerStep(i32(w.topk), dev(w.gates), i32(w.expert_rank), x_tensor(w), dev(Z),
