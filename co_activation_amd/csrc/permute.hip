@@ -310,23 +310,24 @@ int launch_gather(const void* x, int64_t x_rows, int64_t vec_per_row, const int3
 
 // ------------------------------------------------- shuffle + dispatch
 
-// The token shuffle's move and the next layer's dispatch in one pass: token
-// t's row is read once and written to its shuffled position p = dest_pos[t]
-// and to the send rows token_rows[p][*] of that position.  TPT threads own a
-// token (the same layout as the permute).
+// The token shuffle's move and the next layer's dispatch in one pass, in
+// the shuffled order: TPT threads own position p, read the row of token
+// t = perm[p] once and write it to x_out[p] and to the send rows
+// token_rows[p][*].  Writes stay in few dense streams (x_out in order, the
+// send rows of one source rank's positions in G blocks); the reads gather.
 template <typename V, int TPT, int U>
 __global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void shuffle_dispatch_kernel(
-    const V* __restrict__ x, int T, int64_t vec_per_row, const int32_t* __restrict__ dest_pos,
+    const V* __restrict__ x, int T, int64_t vec_per_row, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ token_rows, int k, V* __restrict__ x_out, V* __restrict__ send,
     int64_t send_rows, int32_t* d_err) {
   constexpr int kBlock = TPT < kPermThreads ? kPermThreads : TPT;
   constexpr int kTokens = kBlock / TPT;
   const int sub = kTokens == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / TPT);
-  const int t = blockIdx.x * kTokens + sub;
-  if (t >= T) return;
+  const int p = blockIdx.x * kTokens + sub;
+  if (p >= T) return;
   const int l = kTokens == 1 ? static_cast<int>(threadIdx.x) : static_cast<int>(threadIdx.x % TPT);
-  const int p = __builtin_amdgcn_readfirstlane(dest_pos[t]);
-  if (p < 0 || p >= T) {
+  const int t = __builtin_amdgcn_readfirstlane(perm[p]);
+  if (t < 0 || t >= T) {
     if (l == 0) report(d_err, MOE_DERR_ROW_RANGE);
     return;
   }
@@ -369,10 +370,10 @@ __global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void shuff
   if (l == 0) report(d_err, errbits);
 }
 
-// Launch shape by row size R (vectors): a wave per token below 256 (four
-// vectors per lane per pass), else 512 threads per token.
+// Launch shape by row size R (vectors): a wave per position below 256 (four
+// vectors per lane per pass), else 512 threads per position.
 template <typename V>
-int launch_shuffle_dispatch(const void* x, int T, int64_t vec_per_row, const int32_t* dest_pos,
+int launch_shuffle_dispatch(const void* x, int T, int64_t vec_per_row, const int32_t* perm,
                             const int32_t* token_rows, int k, void* x_out, void* send,
                             int64_t send_rows, int32_t* d_err, hipStream_t s) {
   const V* xv = static_cast<const V*>(x);
@@ -380,11 +381,11 @@ int launch_shuffle_dispatch(const void* x, int T, int64_t vec_per_row, const int
     constexpr int kTokens = kPermThreads / 64;
     shuffle_dispatch_kernel<V, 64, 4><<<static_cast<unsigned>((T + kTokens - 1) / kTokens),
                                         kPermThreads, 0, s>>>(
-        xv, T, vec_per_row, dest_pos, token_rows, k, static_cast<V*>(x_out),
+        xv, T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
         static_cast<V*>(send), send_rows, d_err);
   } else {
     shuffle_dispatch_kernel<V, 512, 1><<<static_cast<unsigned>(T), 512, 0, s>>>(
-        xv, T, vec_per_row, dest_pos, token_rows, k, static_cast<V*>(x_out),
+        xv, T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
         static_cast<V*>(send), send_rows, d_err);
   }
   MOE_CHECK_LAUNCH();
@@ -395,14 +396,14 @@ int launch_shuffle_dispatch(const void* x, int T, int64_t vec_per_row, const int
 }  // namespace moe
 
 extern "C" int moe_shuffle_dispatch(const void* x, int64_t T, int64_t row_bytes,
-                                    const int32_t* dest_pos, const int32_t* token_rows, int k,
+                                    const int32_t* perm, const int32_t* token_rows, int k,
                                     void* x_out, void* send, int64_t send_rows, int32_t* d_err,
                                     void* stream) {
   if (T < 0 || row_bytes <= 0 || k < 1 || k > MOE_MAX_K || send_rows < 0 ||
       T * static_cast<int64_t>(k) >= (int64_t{1} << 31))
     return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
-  if (x == nullptr || dest_pos == nullptr || token_rows == nullptr || x_out == nullptr ||
+  if (x == nullptr || perm == nullptr || token_rows == nullptr || x_out == nullptr ||
       (send == nullptr && send_rows > 0))
     return MOE_ERR_NULL;
   const auto xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(x_out),
@@ -411,9 +412,9 @@ extern "C" int moe_shuffle_dispatch(const void* x, int64_t T, int64_t row_bytes,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Ti = static_cast<int>(T);
   if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0 && sa % 16 == 0)
-    return moe::launch_shuffle_dispatch<moe::u32x4>(x, Ti, row_bytes / 16, dest_pos, token_rows, k,
+    return moe::launch_shuffle_dispatch<moe::u32x4>(x, Ti, row_bytes / 16, perm, token_rows, k,
                                                     x_out, send, send_rows, d_err, s);
-  return moe::launch_shuffle_dispatch<uint32_t>(x, Ti, row_bytes / 4, dest_pos, token_rows, k,
+  return moe::launch_shuffle_dispatch<uint32_t>(x, Ti, row_bytes / 4, perm, token_rows, k,
                                                 x_out, send, send_rows, d_err, s);
 }
 

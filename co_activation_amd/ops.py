@@ -178,19 +178,19 @@ def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
     return out
 
 
-def shuffle_dispatch(x: torch.Tensor, dest_pos: torch.Tensor, token_rows: torch.Tensor,
+def shuffle_dispatch(x: torch.Tensor, perm: torch.Tensor, token_rows: torch.Tensor,
                      send_rows: int, *, x_out: Optional[torch.Tensor] = None,
                      send: Optional[torch.Tensor] = None,
                      d_err: Optional[torch.Tensor] = None) -> tuple:
-    """moe_shuffle_dispatch: x_out[dest_pos[t]] = x[t] and
-    send[token_rows[dest_pos[t], q]] = x[t] (bit copies); token_rows [T, k]
-    is indexed by shuffled position.  Returns (x_out, send)."""
+    """moe_shuffle_dispatch: x_out[p] = x[perm[p]] and
+    send[token_rows[p, q]] = x[perm[p]] (bit copies); token_rows [T, k] is
+    indexed by shuffled position.  Returns (x_out, send)."""
     _want(x, "x")
-    _want(dest_pos, "dest_pos", torch.int32)
+    _want(perm, "perm", torch.int32)
     _want(token_rows, "token_rows", torch.int32)
     T = x.shape[0]
-    if dest_pos.numel() != T or token_rows.dim() != 2 or token_rows.shape[0] != T:
-        raise ValueError("dest_pos and token_rows need one entry / row per token")
+    if perm.numel() != T or token_rows.dim() != 2 or token_rows.shape[0] != T:
+        raise ValueError("perm and token_rows need one entry / row per position")
     k = token_rows.shape[1]
     row_shape = tuple(x.shape[1:])
     row_bytes = x.element_size() * math.prod(row_shape)
@@ -202,7 +202,7 @@ def shuffle_dispatch(x: torch.Tensor, dest_pos: torch.Tensor, token_rows: torch.
     _want(send, "send", x.dtype)
     if x_out.shape != x.shape or tuple(send.shape[1:]) != row_shape or send.shape[0] < send_rows:
         raise ValueError("x_out must match x; send needs send_rows rows shaped like x's rows")
-    st = _lib.lib().moe_shuffle_dispatch(_p(x), T, row_bytes, _p(dest_pos), _p(token_rows), k,
+    st = _lib.lib().moe_shuffle_dispatch(_p(x), T, row_bytes, _p(perm), _p(token_rows), k,
                                          _p(x_out), _p(send), send_rows, _p(d_err), _stream())
     check("moe_shuffle_dispatch", st)
     return x_out, send

@@ -379,7 +379,7 @@ class TwoLayerStep:
                                           self.Rn, self.shuffle["shard_offsets"],
                                           out=self.plan_out, ws=self.plan_ws, d_err=self.d_err)
         with _timed(timers, "shuffle_dispatch"):
-            ops.shuffle_dispatch(self.x, self.shuffle["dest_pos"], self.plan.token_rows, self.cap,
+            ops.shuffle_dispatch(self.x, perm, self.plan.token_rows, self.cap,
                                  x_out=self.x_s, send=self.send, d_err=self.d_err)
         with _timed(timers, "combine"):
             ops.combine(self.z, self.plan.token_rows, self.plan.row_weight, out=self.y,

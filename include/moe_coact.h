@@ -185,21 +185,22 @@ int moe_permute(const void* x, int64_t T, int64_t row_bytes, const int32_t* dest
  * moe_shuffle_dispatch -- the token shuffle's move and the next layer's
  * dispatch in one pass ([EC] abstract: tokens are shuffled to the rank
  * predicted to hold their next-layer experts and dispatched from there):
- *   x_out[dest_pos[t]] = x[t]
- *   send[token_rows[dest_pos[t]*k + q]] = x[t]   for q < k, entry >= 0
- * i.e. moe_permute(x, dest_pos) followed by moe_permute(x_out, token_rows),
- * reading each row once.  token_rows is the next layer's plan over the
- * shuffled order (moe_dispatch_plan on the shuffled routing with the
- * shuffle's shard_offsets).
+ *   x_out[p] = x[perm[p]]
+ *   send[token_rows[p*k + q]] = x[perm[p]]   for q < k, entry >= 0
+ * i.e. the shuffle's move (moe_gather(x, perm)) followed by
+ * moe_permute(x_out, token_rows), reading each row once.  token_rows is the
+ * next layer's plan over the shuffled order (moe_dispatch_plan on the
+ * shuffled routing with the shuffle's shard_offsets).
  *   x          [T * row_bytes] bytes
- *   dest_pos   [T] int32: a permutation of [0, T) (moe_shuffle_predict)
+ *   perm       [T] int32: the token at each shuffled position
+ *              (moe_shuffle_predict's perm)
  *   token_rows [T*k] int32, by shuffled position
  *   x_out      [T * row_bytes] bytes, send [send_rows * row_bytes] bytes
  * Same row-size and alignment rules as moe_permute; k in 1..8.
- * d_err bits: ROW_RANGE (a dest_pos outside [0, T) or a send row >=
- * send_rows; that copy is skipped).
+ * d_err bits: ROW_RANGE (a perm entry outside [0, T) -- that position is
+ * skipped -- or a send row >= send_rows -- that copy is skipped).
  * ---------------------------------------------------------------------- */
-int moe_shuffle_dispatch(const void* x, int64_t T, int64_t row_bytes, const int32_t* dest_pos,
+int moe_shuffle_dispatch(const void* x, int64_t T, int64_t row_bytes, const int32_t* perm,
                          const int32_t* token_rows, int k, void* x_out, void* send,
                          int64_t send_rows, int32_t* d_err, void* stream);
 

@@ -439,26 +439,26 @@ def two_layer_pipeline(topk1: np.ndarray, topk2: np.ndarray, gates2: np.ndarray,
             "local_share_after": plan["counters"][3] / (T * k2)}
 
 
-def shuffle_dispatch(x: np.ndarray, dest_pos: np.ndarray, token_rows: np.ndarray,
+def shuffle_dispatch(x: np.ndarray, perm: np.ndarray, token_rows: np.ndarray,
                      n_send_rows: int) -> tuple:
     """The shuffle's token move and the next layer's dispatch in one pass:
-    token t goes to position dest_pos[t] of the shuffled order, and its row
-    is also written to every send row the next layer's plan gives that
-    position (token_rows is indexed by shuffled position).  Returns
-    (x_shuffled, send); send rows no position targets stay zero.  Written
-    from the definitions: x_s[dest_pos[t]] = x[t], send[token_rows[dest_pos[t], q]] = x[t]."""
+    shuffled position p holds token perm[p], and that row is also written to
+    every send row the next layer's plan gives position p (token_rows is
+    indexed by shuffled position).  Returns (x_shuffled, send); send rows no
+    position targets stay zero.  Written from the definitions:
+    x_s[p] = x[perm[p]], send[token_rows[p, q]] = x[perm[p]]."""
     x = np.asarray(x)
-    dest_pos = np.asarray(dest_pos, dtype=np.int64)
+    perm = np.asarray(perm, dtype=np.int64)
     token_rows = np.asarray(token_rows, dtype=np.int64)
     x_s = np.zeros_like(x)
     send = np.zeros((n_send_rows,) + x.shape[1:], dtype=x.dtype)
-    for t in range(x.shape[0]):
-        p = int(dest_pos[t])
-        x_s[p] = x[t]
+    for p in range(x.shape[0]):
+        row = x[int(perm[p])]
+        x_s[p] = row
         for q in range(token_rows.shape[1]):
             r = int(token_rows[p, q])
             if r >= 0:
-                send[r] = x[t]
+                send[r] = row
     return x_s, send
 
 

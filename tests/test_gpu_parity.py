@@ -274,7 +274,7 @@ def test_shuffle_dispatch_parity(row_bytes, k):
     T = 777
     words = row_bytes // 4
     x = rng.integers(-2**31, 2**31 - 1, size=(T, words), dtype=np.int64).astype(np.int32)
-    dest_pos = rng.permutation(T).astype(np.int32)
+    perm = rng.permutation(T).astype(np.int32)
     send_rows = T * k + 9
     token_rows = rng.permutation(send_rows)[:T * k].reshape(T, k).astype(np.int32)
     token_rows[rng.random((T, k)) < 0.3] = -1
@@ -282,10 +282,10 @@ def test_shuffle_dispatch_parity(row_bytes, k):
     err = _err()
     xo = torch.full((T, words), -5, dtype=torch.int32, device="cuda")
     sd = torch.full((send_rows, words), -7, dtype=torch.int32, device="cuda")
-    ops.shuffle_dispatch(i32(x), i32(dest_pos), i32(token_rows), send_rows, x_out=xo, send=sd,
+    ops.shuffle_dispatch(i32(x), i32(perm), i32(token_rows), send_rows, x_out=xo, send=sd,
                          d_err=err)
     _no_errors(err)
-    want_x, want_s = oracle.shuffle_dispatch(x, dest_pos, token_rows, send_rows)
+    want_x, want_s = oracle.shuffle_dispatch(x, perm, token_rows, send_rows)
     assert_equal(host(xo), want_x, "shuffled rows")
     got = host(sd)
     hit = np.isin(np.arange(send_rows), token_rows[token_rows >= 0])
@@ -294,17 +294,17 @@ def test_shuffle_dispatch_parity(row_bytes, k):
 
 
 def test_shuffle_dispatch_errors():
-    """A position outside [0, T) or a send row past the buffer is reported
-    and that copy skipped; nothing else changes."""
+    """A token index outside [0, T) or a send row past the buffer is
+    reported and that copy skipped; nothing else changes."""
     T, k, words = 64, 2, 4
     rng = np.random.default_rng(77)
     x = rng.integers(0, 1000, size=(T, words)).astype(np.int32)
-    dest_pos = np.arange(T, dtype=np.int32)
+    perm = np.arange(T, dtype=np.int32)
     token_rows = np.arange(T * k, dtype=np.int32).reshape(T, k)
-    bad_pos = dest_pos.copy()
+    bad_pos = perm.copy()
     bad_pos[3] = T
     say("shuffle dispatch errors")
-    for dp, tr in ((bad_pos, token_rows), (dest_pos, np.where(token_rows == 10, T * k, token_rows))):
+    for dp, tr in ((bad_pos, token_rows), (perm, np.where(token_rows == 10, T * k, token_rows))):
         err = _err()
         xo = torch.full((T, words), -5, dtype=torch.int32, device="cuda")
         sd = torch.full((T * k, words), -7, dtype=torch.int32, device="cuda")

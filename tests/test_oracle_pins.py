@@ -449,22 +449,22 @@ def test_two_layer_shuffle_raises_local_share():
 
 
 def test_shuffle_dispatch_is_move_then_permute():
-    """One pass (move each token to its shuffled position and to its
-    next-layer send rows) equals the two steps it replaces: the shuffle's
-    move, then the permute of the shuffled rows by the plan."""
+    """One pass (each shuffled position takes its token's row and writes it
+    to the next layer's send rows) equals the two steps it replaces: the
+    shuffle's move, then the permute of the shuffled rows by the plan."""
     w = make(5, T=1032, H=16)
     res = oracle.two_layer_pipeline(w.topk, w.topk2, w.gates2, w.x, w.expert_rank2, w.E, w.E,
                                     w.G, w.ranks_per_node)
     plan = res["plan"]
     N = int(plan["N"])
-    x_s, send = oracle.shuffle_dispatch(w.x, res["shuffle"]["dest_pos"], plan["token_rows"], N)
+    x_s, send = oracle.shuffle_dispatch(w.x, res["shuffle"]["perm"], plan["token_rows"], N)
     assert np.array_equal(x_s, res["x_shuffled"])
     assert np.array_equal(send, res["send"])
     # a hand case: 3 tokens, shuffled order (2, 0, 1), rows by shuffled position
     x = np.array([[1], [2], [3]], np.int32)
-    dest_pos = np.array([1, 2, 0])
+    perm = np.array([2, 0, 1])
     token_rows = np.array([[0, 3], [1, -1], [2, 4]])
-    xs, sd = oracle.shuffle_dispatch(x, dest_pos, token_rows, 5)
+    xs, sd = oracle.shuffle_dispatch(x, perm, token_rows, 5)
     assert xs[:, 0].tolist() == [3, 1, 2]
     assert sd[:, 0].tolist() == [3, 1, 2, 3, 2]
 
