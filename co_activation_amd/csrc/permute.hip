@@ -14,6 +14,11 @@
 // the predicted order and the expansion of received rows into expert rows.
 // Output rows are written in order (one dense write front), sources are
 // gathered; on MI355X this beats the scatter form for such maps.
+//
+// Shuffle dispatch (moe_shuffle_dispatch): the token shuffle's move and the
+// next layer's permute in one pass, in the shuffled order, reading each row
+// once ("Expert Coupling in MoE Pretraining ...", abstract: tokens are moved
+// to the rank predicted to hold their next-layer experts, then dispatched).
 #include "common.hpp"
 
 namespace moe {
