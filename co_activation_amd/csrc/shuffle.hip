@@ -195,20 +195,28 @@ __global__ __launch_bounds__(kBalTile) void balanced_scores_kernel(
   report(d_err, errbits);
 }
 
-// One round, part 1: every token's choice under the current fill indices,
-// counted per (tile, rank) with wave ballots.
+// One round, part 1: every token's choice under the current fill indices
+// (stored in pred, so that the round which finds the fixed point leaves the
+// final assignment there), counted per (tile, rank) with wave ballots.
+// Tokens before the smallest fill index choose freely in every round, so
+// after the first round their tiles are skipped (counts and choices stand).
 __global__ __launch_bounds__(kBalTile) void balanced_assign_kernel(
     const int64_t* __restrict__ scores, int T, int G, const int32_t* __restrict__ fill_g,
-    const int32_t* __restrict__ flag, int32_t* __restrict__ tile_cnt) {
+    const int32_t* __restrict__ flag, int32_t* __restrict__ tile_cnt,
+    int32_t* __restrict__ pred) {
   __shared__ int fill[MOE_MAX_G];
   __shared__ int s_cnt[kBalTile / kWave][kWave];
   if (*flag) return;
   if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = fill_g[threadIdx.x];
   __syncthreads();
+  int min_fill = INT32_MAX;
+  for (int r = 0; r < G; ++r) min_fill = min(min_fill, fill[r]);
+  if (min_fill != INT32_MAX && (blockIdx.x + 1) * kBalTile <= min_fill) return;
   const int lane = lane_id();
   const int wave = wave_id();
   const int t = blockIdx.x * kBalTile + threadIdx.x;
   const int a = t < T ? best_available(scores + static_cast<int64_t>(t) * G, G, fill, t) : -1;
+  if (t < T) pred[t] = a < 0 ? 0 : a;
   int mine = 0;
   for (int r = 0; r < G; ++r) {
     const uint64_t b = ballot(a == r);
@@ -227,10 +235,10 @@ __global__ __launch_bounds__(kBalTile) void balanced_assign_kernel(
 constexpr int kBalUpdThreads = 1024;
 
 // One round, part 2 (one block): for each rank, the tile where its takers
-// reach C, then the exact C-th taker inside that tile; new fill indices, or
-// the convergence flag when none changed.
+// reach C, then the exact C-th taker inside that tile (from the choices part
+// 1 stored); new fill indices, or the convergence flag when none changed.
 __global__ __launch_bounds__(kBalUpdThreads) void balanced_update_kernel(
-    const int64_t* __restrict__ scores, int T, int G, int cap, int NT,
+    const int32_t* __restrict__ choice, int T, int G, int cap, int NT,
     const int32_t* __restrict__ tile_cnt, int32_t* __restrict__ fill_g, int32_t* __restrict__ flag) {
   __shared__ int fill[MOE_MAX_G];
   __shared__ int nfill[MOE_MAX_G];
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(kBalUpdThreads) void balanced_update_kernel(
       int seen = 0;
       for (int c = 0; c < kBalTile; c += kWave) {
         const int t = hit_tile * kBalTile + c + lane;
-        const int a = t < T ? best_available(scores + static_cast<int64_t>(t) * G, G, fill, t) : -1;
+        const int a = t < T ? choice[t] : -1;
         const uint64_t b = ballot(a == r);
         const int cnt = __popcll(b);
         if (seen + cnt >= need) {
@@ -284,10 +292,14 @@ __global__ __launch_bounds__(kBalUpdThreads) void balanced_update_kernel(
   if (threadIdx.x < static_cast<unsigned>(G)) fill_g[threadIdx.x] = nfill[threadIdx.x];
 }
 
+// Only when the rounds ended without confirming the fixed point (the last
+// round computed its choices with fill indices that then changed): the
+// choices under the final fill indices.
 __global__ __launch_bounds__(kBalTile) void balanced_final_kernel(
     const int64_t* __restrict__ scores, int T, int G, const int32_t* __restrict__ fill_g,
-    int32_t* __restrict__ pred) {
+    const int32_t* __restrict__ flag, int32_t* __restrict__ pred) {
   __shared__ int fill[MOE_MAX_G];
+  if (*flag) return;
   if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = fill_g[threadIdx.x];
   __syncthreads();
   const int t = blockIdx.x * kBalTile + threadIdx.x;
@@ -366,13 +378,14 @@ extern "C" int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E
   if (Ti > 0) {
     for (int round = 0; round < G; ++round) {
       moe::balanced_assign_kernel<<<NT, moe::kBalTile, 0, s>>>(w.scores, Ti, G, w.fill, w.flag,
-                                                               w.tile_cnt);
+                                                               w.tile_cnt, pred_rank);
       MOE_CHECK_LAUNCH();
-      moe::balanced_update_kernel<<<1, moe::kBalUpdThreads, 0, s>>>(w.scores, Ti, G, Ti / G, NT,
+      moe::balanced_update_kernel<<<1, moe::kBalUpdThreads, 0, s>>>(pred_rank, Ti, G, Ti / G, NT,
                                                                     w.tile_cnt, w.fill, w.flag);
       MOE_CHECK_LAUNCH();
     }
-    moe::balanced_final_kernel<<<NT, moe::kBalTile, 0, s>>>(w.scores, Ti, G, w.fill, pred_rank);
+    moe::balanced_final_kernel<<<NT, moe::kBalTile, 0, s>>>(w.scores, Ti, G, w.fill, w.flag,
+                                                            pred_rank);
     MOE_CHECK_LAUNCH();
   }
   moe::PlanArgs a{pred_rank,      nullptr,        Ti,        1,
