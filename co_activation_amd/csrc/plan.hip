@@ -153,9 +153,6 @@ __global__ __launch_bounds__(kPlanTile) void plan_count_kernel(
   }
 }
 
-constexpr int kScanThreads = 1024;
-constexpr int kScanWaves = kScanThreads / kWave;
-
 // Smallest s in [0, G) with incl[s] > j (the source rank of tile j).
 __device__ __forceinline__ int shard_of_tile(int j, const int* incl, int G) {
   int lo = 0, hi = G - 1;
@@ -169,11 +166,17 @@ __device__ __forceinline__ int shard_of_tile(int j, const int* incl, int G) {
   return lo;
 }
 
+// kScanThreads is 256 for up to 16 ranks and 1024 above: a four-wave block
+// finds room on a CU that a bandwidth-bound kernel on another stream keeps
+// full far sooner than a sixteen-wave one.
+template <int kScanThreads>
 __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
     const int32_t* __restrict__ src_offsets, int T, int k, int G, int32_t* __restrict__ tile_cnt,
     int64_t stride, const int32_t* __restrict__ tile_stats, int64_t row_capacity, int32_t* __restrict__ send_counts,
     int32_t* __restrict__ send_offsets, int64_t* __restrict__ counters,
     int32_t* __restrict__ first_offsets, int32_t* d_err) {
+  constexpr int kScanWaves = kScanThreads / kWave;
+  constexpr int kPer = MOE_MAX_G * MOE_MAX_G / kScanThreads;  // S entries per thread
   __shared__ int s_incl[kWave];
   __shared__ int s_first[kWave];
   __shared__ int s_S[MOE_MAX_G * MOE_MAX_G];
@@ -248,13 +251,13 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
     if (lane == 0) s_maxrecv = col;
   }
 
-  // Exclusive scan of S in (s, r) order: four entries per thread.
+  // Exclusive scan of S in (s, r) order: kPer consecutive entries per thread.
   const int n = G * G;
-  const int i0 = tid * 4;
-  int v[4];
+  const int i0 = tid * kPer;
+  int v[kPer];
   int local = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kPer; ++q) {
     v[q] = (i0 + q < n) ? s_S[i0 + q] : 0;
     local += v[q];
   }
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
   int run = (wave ? s_part[wave - 1] : 0) + winc - local;
   const int total_rows = s_part[kScanWaves - 1];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < kPer; ++q) {
     if (i0 + q < n) {
       send_counts[i0 + q] = v[q];
       send_offsets[i0 + q] = run;
@@ -408,9 +411,14 @@ int launch_plan(const PlanArgs& a, hipStream_t stream) {
         tile_stats, a.d_err);
     MOE_CHECK_LAUNCH();
   }
-  plan_scan_kernel<<<dim3(1), dim3(kScanThreads), 0, stream>>>(
-      a.src_offsets, a.T, a.k, a.G, tile_cnt, nt, tile_stats, a.row_capacity, a.send_counts,
-      a.send_offsets, a.counters, a.first_offsets, a.d_err);
+  if (a.G <= 16)
+    plan_scan_kernel<256><<<dim3(1), dim3(256), 0, stream>>>(
+        a.src_offsets, a.T, a.k, a.G, tile_cnt, nt, tile_stats, a.row_capacity, a.send_counts,
+        a.send_offsets, a.counters, a.first_offsets, a.d_err);
+  else
+    plan_scan_kernel<1024><<<dim3(1), dim3(1024), 0, stream>>>(
+        a.src_offsets, a.T, a.k, a.G, tile_cnt, nt, tile_stats, a.row_capacity, a.send_counts,
+        a.send_offsets, a.counters, a.first_offsets, a.d_err);
   MOE_CHECK_LAUNCH();
   if (nt > 0) {
     plan_write_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(kPlanTile), 0, stream>>>(

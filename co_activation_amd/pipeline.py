@@ -237,19 +237,55 @@ class LayerStep:
 
     STAGES = ("stats", "plan", "permute", "combine")
 
-    def run(self, timers: Optional[StageTimers] = None, overlap: bool = True):
-        fork = self._fork if overlap else _INLINE
-        with fork.fork(), _timed(timers, "stats"):
+    @property
+    def plan_beside(self):
+        """Where a Pipeline runs this step's plan phase: beside the combine,
+        unless the combine reserves LDS to cap its residency (k >= 6 with a
+        row per slot, as the expert side returns), which leaves no room on
+        the CUs for the statistics histogram and the plan scan; then beside
+        the whole move."""
+        return "move" if self.k >= 6 and self.z.shape[0] >= 6 * self.T else "combine"
+
+    def _stats(self, timers):
+        with _timed(timers, "stats"):
             ops.coact_stats(self.topk, self.E, out=self.stats_out, d_err=self.d_err)
+
+    def _plan(self, timers):
         with _timed(timers, "plan"):
             self.plan = ops.dispatch_plan(self.topk, self.gates, self.expert_rank, self.G, self.Rn,
                                           self.src_offsets, out=self.plan_out, ws=self.plan_ws,
                                           d_err=self.d_err)
+
+    def plan_phase(self, timers: Optional[StageTimers] = None):
+        """Everything that reads only the routing: statistics and plan."""
+        self._stats(timers)
+        self._plan(timers)
+        return self
+
+    def dispatch_phase(self, timers: Optional[StageTimers] = None):
+        """The send rows, which need the plan: the permute."""
         with _timed(timers, "permute"):
             ops.permute(self.x, self.plan.token_rows, self.cap, out=self.send, d_err=self.d_err)
+        return self
+
+    def combine_phase(self, timers: Optional[StageTimers] = None):
+        """The returned rows back in token order: the combine."""
         with _timed(timers, "combine"):
             ops.combine(self.z, self.plan.token_rows, self.plan.row_weight,
                         out_dtype=self.out_dtype, out=self.y, d_err=self.d_err)
+        return self
+
+    def move_phase(self, timers: Optional[StageTimers] = None):
+        """The row traffic, which needs the plan: permute and combine."""
+        self.dispatch_phase(timers)
+        return self.combine_phase(timers)
+
+    def run(self, timers: Optional[StageTimers] = None, overlap: bool = True):
+        fork = self._fork if overlap else _INLINE
+        with fork.fork():
+            self._stats(timers)
+        self._plan(timers)
+        self.move_phase(timers)
         fork.join()
         return self
 
@@ -314,6 +350,11 @@ class TwoLayerStep:
     def STAGES(self):
         return self.STAGES_FUSED if self.fused else self.STAGES_SPLIT
 
+    @property
+    def plan_beside(self):
+        """Where a Pipeline runs this step's plan phase (see LayerStep)."""
+        return "move" if self.k2 >= 6 and self.z.shape[0] >= 6 * self.T else "combine"
+
     def run(self, timers: Optional[StageTimers] = None, overlap: bool = True):
         if self.fused:
             return self._run_fused(timers)
@@ -358,10 +399,9 @@ class TwoLayerStep:
                         d_err=self.d_err)
         return self
 
-    def _run_fused(self, timers):
-        """One stream: statistics, prediction, the routing move and the
-        layer-2 plan, then the token rows moved and dispatched in one pass,
-        then the combine."""
+    def plan_phase(self, timers: Optional[StageTimers] = None):
+        """Everything that reads only the routing: statistics, prediction,
+        the routing move and the layer-2 plan."""
         with _timed(timers, "stats"):
             ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
                             d_err=self.d_err)
@@ -378,13 +418,43 @@ class TwoLayerStep:
             self.plan = ops.dispatch_plan(self.topk2_s, self.gates2_s, self.expert_rank2, self.G,
                                           self.Rn, self.shuffle["shard_offsets"],
                                           out=self.plan_out, ws=self.plan_ws, d_err=self.d_err)
-        with _timed(timers, "shuffle_dispatch"):
-            ops.shuffle_dispatch(self.x, perm, self.plan.token_rows, self.cap,
-                                 x_out=self.x_s, send=self.send, d_err=self.d_err)
+        return self
+
+    def dispatch_phase(self, timers: Optional[StageTimers] = None):
+        """The token rows moved to their shuffled places and dispatched into
+        the layer-2 send rows: one pass when fused, a gather and a permute
+        otherwise."""
+        perm = self.shuffle["perm"]
+        if self.fused:
+            with _timed(timers, "shuffle_dispatch"):
+                ops.shuffle_dispatch(self.x, perm, self.plan.token_rows, self.cap,
+                                     x_out=self.x_s, send=self.send, d_err=self.d_err)
+        else:
+            with _timed(timers, "shuffle_permute"):
+                ops.gather(self.x, perm, out=self.x_s, d_err=self.d_err)
+            with _timed(timers, "permute"):
+                ops.permute(self.x_s, self.plan.token_rows, self.cap, out=self.send,
+                            d_err=self.d_err)
+        return self
+
+    def combine_phase(self, timers: Optional[StageTimers] = None):
+        """The returned rows back in (shuffled) token order: the combine."""
         with _timed(timers, "combine"):
             ops.combine(self.z, self.plan.token_rows, self.plan.row_weight, out=self.y,
                         d_err=self.d_err)
         return self
+
+    def move_phase(self, timers: Optional[StageTimers] = None):
+        """The row traffic, which needs the plan: dispatch, then combine."""
+        self.dispatch_phase(timers)
+        return self.combine_phase(timers)
+
+    def _run_fused(self, timers):
+        """One stream: statistics, prediction, the routing move and the
+        layer-2 plan, then the token rows moved and dispatched in one pass,
+        then the combine."""
+        self.plan_phase(timers)
+        return self.move_phase(timers)
 
 
 class ExpertSideStep:
@@ -552,3 +622,111 @@ class GraphStep:
     def replay(self):
         self.graph.replay()
         return self.step
+
+
+class Pipeline:
+    """Independent batches through a ring of steps, the routing-only phase
+    of one batch overlapped with the row traffic of the batch before.
+
+    Each step (LayerStep or TwoLayerStep, at least two, on one device) owns
+    its buffers; batch i runs on step i mod m.  Its ``plan_phase``
+    (statistics, prediction, plan: short latency-bound kernels) runs on a
+    second stream; its ``dispatch_phase`` and ``combine_phase`` (the
+    bandwidth-bound kernels) run on the current stream once that plan is
+    complete.  Where the plan phase runs depends on ``beside``:
+
+    - "combine": it starts once batch i-1 has dispatched, so it runs beside
+      batch i-1's combine and the dispatch, the heaviest kernel, never shares
+      the GPU with it.  Needs a combine that leaves room on the CUs for the
+      plan kernels.
+    - "move": it starts once batch i-m, the last user of the step's buffers,
+      has combined, so it runs beside batch i-1's dispatch (and combine).
+
+    The default is the steps' ``plan_beside``.  Every batch runs its whole
+    path and gets the results it would get alone.
+
+    ``prepare(step, i)``, if given, is called with the second stream current
+    just before batch i's plan phase is enqueued, after the step's previous
+    batch has left its buffers: the place to write batch i's inputs into the
+    step.  ``collect(step, i)`` is called with the current stream current just
+    after batch i's combine: the place to read its outputs.  Work that the
+    caller enqueued on the current stream before ``run`` is complete before
+    any batch starts, and everything ``run`` enqueues is ordered before what
+    the caller enqueues on the current stream afterwards."""
+
+    def __init__(self, steps, beside: Optional[str] = None):
+        if len(steps) < 2:
+            raise ValueError("a pipeline needs at least two steps (one per batch in flight)")
+        dev = steps[0].d_err.device
+        if any(st.d_err.device != dev for st in steps):
+            raise ValueError("all steps of a pipeline must be on one device")
+        if len({id(st) for st in steps}) != len(steps):
+            raise ValueError("each step may appear once in a pipeline")
+        self.beside = beside if beside is not None else steps[0].plan_beside
+        if self.beside not in ("combine", "move"):
+            raise ValueError("beside must be 'combine' or 'move'")
+        self.steps = list(steps)
+        self.side = torch.cuda.Stream(device=dev)
+        self._side = ctypes.c_void_p(self.side.cuda_stream)
+        h = _Hip.get()
+        self._start = ctypes.c_void_p()       # current stream at the start of run
+        self._planned = ctypes.c_void_p()     # side stream after a plan phase
+        self._dispatched = ctypes.c_void_p()  # current stream after a dispatch phase
+        self._done = [ctypes.c_void_p() for _ in steps]  # after each step's combine
+        for e in self._events():
+            if h.hipEventCreateWithFlags(ctypes.byref(e), _FORK_EVENT_FLAGS):
+                raise RuntimeError("hipEventCreateWithFlags failed")
+        self._next = 0
+
+    def _events(self):
+        return [self._start, self._planned, self._dispatched] + self._done
+
+    def run(self, batches: int, timers: Optional[StageTimers] = None, prepare=None,
+            collect=None):
+        """Runs ``batches`` batches; returns the step that ran the last one."""
+        h = _Hip.get()
+        main = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        m = len(self.steps)
+        # The first batches of a call wait for everything before the call.
+        if h.hipEventRecord(self._start, main) or h.hipStreamWaitEvent(self._side, self._start, 0):
+            raise RuntimeError("pipeline: hipEventRecord/hipStreamWaitEvent failed")
+        by_combine = self.beside == "combine"
+        last = None
+        for i in range(batches):
+            j = self._next % m
+            st = self.steps[j]
+            with torch.cuda.stream(self.side):
+                if by_combine:
+                    # batch i-1 has dispatched: every earlier batch, the last
+                    # user of this step's buffers included, has combined
+                    ev = self._dispatched if i > 0 else None
+                else:
+                    # batch i-m, the last user of this step's buffers
+                    ev = self._done[j] if i >= m else None
+                if ev is not None and h.hipStreamWaitEvent(self._side, ev, 0):
+                    raise RuntimeError("pipeline: hipStreamWaitEvent failed")
+                if prepare is not None:
+                    prepare(st, i)
+                st.plan_phase(timers)
+            if h.hipEventRecord(self._planned, self._side) or \
+                    h.hipStreamWaitEvent(main, self._planned, 0):
+                raise RuntimeError("pipeline: hipEventRecord/hipStreamWaitEvent failed")
+            st.dispatch_phase(timers)
+            if by_combine and h.hipEventRecord(self._dispatched, main):
+                raise RuntimeError("pipeline: hipEventRecord failed")
+            st.combine_phase(timers)
+            if collect is not None:
+                collect(st, i)
+            if not by_combine and h.hipEventRecord(self._done[j], main):
+                raise RuntimeError("pipeline: hipEventRecord failed")
+            self._next += 1
+            last = st
+        return last
+
+    def __del__(self):
+        try:
+            h = _Hip.get()
+            for e in self._events():
+                h.hipEventDestroy(e)
+        except Exception:
+            pass
