@@ -197,47 +197,59 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
   __syncthreads();
 
   // Per destination rank r: exclusive prefix of the tile counts within each
-  // source rank (segments), and the segment totals S[s][r].  The first
-  // kPrefetch chunks of 64 tiles are loaded before any is scanned, so their
-  // load latencies overlap.
+  // source rank (segments), and the segment totals S[s][r].  A wave takes
+  // kGroup ranks at a time; the first kPrefetch chunks of 64 tiles of each
+  // are loaded before any is scanned, so their load latencies overlap.
   constexpr int kPrefetch = 8;
-  for (int r = wave; r < G; r += kScanWaves) {
-    int pre[kPrefetch];
+  constexpr int kGroup = 4;
+  for (int r0 = wave; r0 < G; r0 += kScanWaves * kGroup) {
+    int pre[kGroup][kPrefetch];
 #pragma unroll
-    for (int c = 0; c < kPrefetch; ++c) {
-      const int j = c * kWave + lane;
-      pre[c] = j < NT ? tile_cnt[static_cast<int64_t>(r) * stride + j] : 0;
+    for (int g = 0; g < kGroup; ++g) {
+      const int r = r0 + g * kScanWaves;
+#pragma unroll
+      for (int c = 0; c < kPrefetch; ++c) {
+        const int j = c * kWave + lane;
+        pre[g][c] = (r < G && j < NT) ? tile_cnt[static_cast<int64_t>(r) * stride + j] : 0;
+      }
     }
-    int carry = 0;
+    int carry[kGroup];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) carry[g] = 0;
     for (int base = 0, c = 0; base < NT; base += kWave, ++c) {
       const int j = base + lane;
       const bool in = j < NT;
-      int v = 0;
-      if (c < kPrefetch) {
-#pragma unroll
-        for (int q = 0; q < kPrefetch; ++q)
-          if (q == c) v = pre[q];
-      } else if (in) {
-        v = tile_cnt[static_cast<int64_t>(r) * stride + j];
-      }
       const int s = in ? shard_of_tile(j, s_incl, G) : 0;
       const bool head = in && s_first[s] == j;
       const bool last = in && j + 1 == s_incl[s];
-      int val = v;
-      int flag = head ? 1 : 0;
 #pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const int uv = __shfl_up(val, d, kWave);
-        const int uf = __shfl_up(flag, d, kWave);
-        if (lane >= d) {
-          if (!flag) val += uv;
-          flag |= uf;
+      for (int g = 0; g < kGroup; ++g) {
+        const int r = r0 + g * kScanWaves;  // uniform across the wave
+        if (r >= G) break;
+        int v = 0;
+        if (c < kPrefetch) {
+#pragma unroll
+          for (int q = 0; q < kPrefetch; ++q)
+            if (q == c) v = pre[g][q];
+        } else if (in) {
+          v = tile_cnt[static_cast<int64_t>(r) * stride + j];
         }
+        int val = v;
+        int flag = head ? 1 : 0;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+          const int uv = __shfl_up(val, d, kWave);
+          const int uf = __shfl_up(flag, d, kWave);
+          if (lane >= d) {
+            if (!flag) val += uv;
+            flag |= uf;
+          }
+        }
+        if (!flag) val += carry[g];
+        if (in) tile_cnt[static_cast<int64_t>(r) * stride + j] = val - v;
+        if (last) s_S[s * G + r] = val;
+        carry[g] = __shfl(val, kWave - 1, kWave);
       }
-      if (!flag) val += carry;
-      if (in) tile_cnt[static_cast<int64_t>(r) * stride + j] = val - v;
-      if (last) s_S[s * G + r] = val;
-      carry = __shfl(val, kWave - 1, kWave);
     }
   }
   __syncthreads();
