@@ -306,12 +306,20 @@ def main() -> int:
             return 1
 
     # Stage breakdown (events around every stage, all on one stream so that
-    # each stage is timed alone), outside the timed region.
+    # each stage is timed alone), outside the timed region.  Before each step
+    # a 512 MiB read evicts the step's data from L2 and the 256 MB Infinity
+    # Cache, so every stage starts cold.  (A write would leave dirty lines
+    # whose write-back the next stage would pay for.)
+    flush = torch.ones(512 << 18, dtype=torch.int32, device=dev)
     stages = StageTimers(step.STAGES, args.steps)
     for _ in range(args.steps):
+        flush.sum()
         step.run(stages, overlap=False)
     torch.cuda.synchronize()
+    del flush
     stage_ms = stages.median_ms()
+    stage_min = {n: min(stages.durations_ms(n)) for n in stage_ms}
+    stage_p90 = {n: float(np.percentile(stages.durations_ms(n), 90)) for n in stage_ms}
     moves = ("shuffle_dispatch",) if "shuffle_dispatch" in stage_ms else ("permute",)
     dom = max(moves + ("combine",), key=lambda n: stage_ms[n])
 
@@ -395,6 +403,8 @@ def main() -> int:
         "permute_combine_gbps": pc_gbs,
         "permute_combine_pct_of_hbm_peak": 100.0 * pc_gbs / HBM_PEAK_GBS,
         "stage_us_median": {n: 1e3 * v for n, v in stage_ms.items()},
+        "stage_us_min": {n: 1e3 * v for n, v in stage_min.items()},
+        "stage_us_p90": {n: 1e3 * v for n, v in stage_p90.items()},
         "schedule": ("two batches in flight: each batch's " +
                      ("statistics and plan" if w.cfg != 5 else
                       "statistics, shuffle prediction, routing move and layer-2 plan") +
