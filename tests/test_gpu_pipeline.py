@@ -36,6 +36,15 @@ def _step(two_layer, inp, w0):
                      w0.ranks_per_node)
 
 
+def _bits(t):
+    """The tensor's bit patterns, so that equality is bitwise."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32)
+    return t
+
+
 def _outputs(st, two_layer):
     out = {"y": st.y, "send": st.send}
     out.update({"stats." + k: v for k, v in st.stats_out.items()})
@@ -104,3 +113,60 @@ def test_pipeline_rejects_bad_rings():
         Pipeline([a, a])
     with pytest.raises(ValueError):
         Pipeline([a, _step(False, inp, w)], beside="dispatch")
+
+
+@pytest.mark.parametrize("cfg", [5, 3])
+def test_pipeline_fullsize_matches_single_steps(cfg):
+    """The benchmark's timed configuration at full size: batches through a
+    two-step pipeline (the plan beside the combine for workload 5, beside
+    the whole move for workload 3), two routings and four row sets
+    alternating, each batch equal on the device, bit for bit, to one step
+    run alone on it."""
+    from workloads.gen import device_normal
+
+    two_layer = cfg == 5
+    n = 4
+    ws = [make(cfg, seed=s, with_x=False) for s in range(2)]
+    w0 = ws[0]
+    T, H = w0.T, w0.H
+    cap = T * min(w0.k, w0.G)
+    say("pipeline fullsize", cfg, f"T={T}", f"H={H}", f"batches={n}")
+    batches = []
+    for b in range(n):
+        w = ws[b % 2]
+        x = device_normal(T, H, w0.dtype, seed=20 + b)
+        z = device_normal(cap, H, w0.dtype, seed=30 + b)
+        if two_layer:
+            batches.append({"topk1": i32(w.topk), "topk2": i32(w.topk2), "gates2": dev(w.gates2),
+                            "x": x, "z": z})
+        else:
+            batches.append({"topk": i32(w.topk), "gates": dev(w.gates), "x": x, "z": z})
+    steps = [_step(two_layer, batches[0], w0) for _ in range(2)]
+    pipe = Pipeline(steps)
+    assert pipe.beside == ("combine" if two_layer else "move")
+    got = {}
+
+    def prepare(st, i):
+        for name, v in batches[i].items():
+            getattr(st, name).copy_(v)
+
+    def collect(st, i):
+        got[i] = {key: v.clone() for key, v in _outputs(st, two_layer).items()}
+
+    pipe.run(n, prepare=prepare, collect=collect)
+    torch.cuda.synchronize()
+    for st in steps:
+        assert int(st.d_err.item()) == 0
+    del steps, pipe
+    for b in range(n):
+        ref = _step(two_layer, batches[b], w0).run(overlap=False)
+        torch.cuda.synchronize()
+        assert int(ref.d_err.item()) == 0
+        N = int(ref.plan.counters[0].item())
+        for key, want in _outputs(ref, two_layer).items():
+            a = got[b][key]
+            if key in ("send", "plan.row_token", "plan.row_weight"):
+                a, want = a[:N], want[:N]
+            assert torch.equal(_bits(a), _bits(want)), f"batch {b}: {key}"
+        del ref, got[b]
+        torch.cuda.empty_cache()
