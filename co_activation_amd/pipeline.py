@@ -1,26 +1,33 @@
-"""One step of the dispatch path, as a sequence of C-ABI calls.
+"""The dispatch path as sequences of C-ABI calls: steps, and a pipeline of
+steps.
 
-Single layer (workloads 1-4):
+Single layer (workloads 1-4), ``LayerStep``:
     stats(topk) -> plan(topk, gates, placement) -> permute(x) -> combine(z)
 Two layers with token shuffling (workload 5, "Expert Coupling in MoE
 Pretraining ..." abstract: shuffle each token to the rank predicted to hold
-its next-layer experts):
+its next-layer experts), ``TwoLayerStep``:
     stats(topk1, topk2) -> shuffle_predict(topk1, transition, placement2)
-    -> gather x, topk2, gates2 into the new order (one row per token)
+    -> move topk2, gates2 into the new order
     -> plan(topk2', gates2', placement2, src_offsets = shard_offsets)
-    -> permute(x') -> combine(z)
+    -> x moved into the new order and dispatched into the layer-2 send rows
+       in one pass (shuffle_dispatch; or a gather then a permute)
+    -> combine(z)
 
-Latency-bound stages that nothing on the bandwidth-bound chain waits for run
-on a second stream, overlapped with it: in one layer the statistics run
-beside plan, permute and combine; with the shuffle, the move of the routing,
-the layer-2 plan and the layer-1 pair counts and Ochiai run beside the move
-of the token rows (the plan needs only the routing; the prediction before it
-needs only the transitions).  ``run(..., overlap=False)`` keeps everything on
-one stream, which is how per-stage times are taken.
+Each step splits into ``plan_phase`` (everything that reads only the
+routing), ``dispatch_phase`` and ``combine_phase`` (the row traffic).
+``run`` runs one step; latency-bound stages that the bandwidth-bound chain
+does not wait for run on a second stream beside it (the statistics of one
+layer; the routing move, layer-2 plan and pair statistics beside the token
+move of the separate-pass two-layer step).  ``run(..., overlap=False)``
+keeps everything on one stream, which is how per-stage times are taken.
+``Pipeline`` runs a stream of independent batches over a ring of steps,
+each batch's plan phase beside the previous batch's row traffic;
+``GraphStep`` captures one step as a HIP graph.
 
-All buffers are allocated once in the constructor; ``run`` only enqueues
+All buffers are allocated once in the constructors; ``run`` only enqueues
 kernels (no allocation, no host synchronisation).  ``z`` stands for the
-expert side's returned rows (one per send row).
+expert side's returned rows (one per send row); ``ExpertSideStep`` and the
+backward steps cover the destination side and the gradients.
 """
 
 from __future__ import annotations
