@@ -400,6 +400,7 @@ def main() -> int:
         "data": "synthetic (seeded router logits, N(0,1) rows)",
         "config": {"workload": workload, "tokens": T, "hidden": w.H, "experts": w.E, "top_k": k,
                    "logical_ranks": w.G, "dispatched_rows": N},
+        "dispatched_rows_per_s_of_move_kernel": N / (stage_ms[mv] * 1e-3),
         "permute_combine_gbps": pc_gbs,
         "permute_combine_pct_of_hbm_peak": 100.0 * pc_gbs / HBM_PEAK_GBS,
         "stage_us_median": {n: 1e3 * v for n, v in stage_ms.items()},
