@@ -143,33 +143,12 @@ namespace {
 
 constexpr int kBalTile = 256;
 
-// Best available rank of token t (score descending, lower rank on ties);
-// -1 if none is available.
-__device__ __forceinline__ int best_available(const int64_t* __restrict__ score_row, int G,
-                                              const int* fill, int t) {
-  int best = -1;
-  long long bs = 0;
-  for (int r = 0; r < G; ++r) {
-    if (fill[r] < t) continue;
-    const long long sc = score_row[r];
-    if (best < 0 || sc > bs) {
-      best = r;
-      bs = sc;
-    }
-  }
-  return best;
-}
-
-// scores[t][r] = sum_{i in D_t} M[i][r]; block 0 also resets the fill
-// indices to "never full" and the convergence flag.
+// scores[t][r] = sum_{i in D_t} M[i][r]; block 0 also resets the
+// convergence flag.
 __global__ __launch_bounds__(kBalTile) void balanced_scores_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
-    int64_t* __restrict__ scores, int32_t* __restrict__ fill, int32_t* __restrict__ flag,
-    int32_t* d_err) {
-  if (blockIdx.x == 0) {
-    if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = INT32_MAX;
-    if (threadIdx.x == 0) *flag = 0;
-  }
+    int64_t* __restrict__ scores, int32_t* __restrict__ flag, int32_t* d_err) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *flag = 0;
   const int t = blockIdx.x * kBalTile + threadIdx.x;
   if (t >= T) return;
   int e[MOE_MAX_K];
@@ -195,125 +174,178 @@ __global__ __launch_bounds__(kBalTile) void balanced_scores_kernel(
   report(d_err, errbits);
 }
 
-// One round, part 1: every token's choice under the current fill indices
-// (stored in pred, so that the round which finds the fixed point leaves the
-// final assignment there), counted per (tile, rank) with wave ballots.
-// Tokens before the smallest fill index choose freely in every round, so
-// after the first round their tiles are skipped (counts and choices stand).
-__global__ __launch_bounds__(kBalTile) void balanced_assign_kernel(
-    const int64_t* __restrict__ scores, int T, int G, const int32_t* __restrict__ fill_g,
-    const int32_t* __restrict__ flag, int32_t* __restrict__ tile_cnt,
-    int32_t* __restrict__ pred) {
-  __shared__ int fill[MOE_MAX_G];
-  __shared__ int s_cnt[kBalTile / kWave][kWave];
-  if (*flag) return;
-  if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = fill_g[threadIdx.x];
-  __syncthreads();
-  int min_fill = INT32_MAX;
-  for (int r = 0; r < G; ++r) min_fill = min(min_fill, fill[r]);
-  if (min_fill != INT32_MAX && (blockIdx.x + 1) * kBalTile <= min_fill) return;
+constexpr int kBalWaves = kBalTile / kWave;
+constexpr int kScorePre = 8;  // ranks whose scores a round kernel loads up front
+
+// The fill index of every rank under one round's choices, into fill[] (LDS):
+// for rank r, the tile where the running count of r's takers reaches cap,
+// then the need-th taker inside that tile from the tile's taker masks (one
+// 64-bit ballot per wave); "never full" when r has fewer than cap takers.
+// The waves of the block take the ranks in turn.
+__device__ void balanced_fill(const int32_t* __restrict__ tile_cnt,
+                              const uint64_t* __restrict__ tile_mask, int NT, int G, int cap,
+                              int* fill) {
+  // A wave takes kGroup ranks at a time; their first kPre chunks of 64 tile
+  // counts are loaded together before any is scanned.
+  constexpr int kGroup = 2;
+  constexpr int kPre = 4;
   const int lane = lane_id();
   const int wave = wave_id();
+  for (int r0 = wave; r0 < G; r0 += kBalWaves * kGroup) {
+    int pre[kGroup][kPre];
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int r = r0 + g * kBalWaves;
+#pragma unroll
+      for (int c = 0; c < kPre; ++c) {
+        const int j = c * kWave + lane;
+        pre[g][c] = (r < G && j < NT) ? tile_cnt[static_cast<int64_t>(j) * G + r] : 0;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      const int r = r0 + g * kBalWaves;  // uniform across the wave
+      if (r >= G) break;
+      int carry = 0, hit = -1, need = 0;
+      for (int base = 0, c = 0; base < NT && hit < 0; base += kWave, ++c) {
+        const int j = base + lane;
+        int v = 0;
+        if (c < kPre) {
+#pragma unroll
+          for (int q = 0; q < kPre; ++q)
+            if (q == c) v = pre[g][q];
+        } else if (j < NT) {
+          v = tile_cnt[static_cast<int64_t>(j) * G + r];
+        }
+        const int incl = wave_incl_scan(v) + carry;
+        const uint64_t b = ballot(j < NT && incl >= cap);
+        if (b) {
+          const int first = __ffsll(static_cast<long long>(b)) - 1;
+          hit = base + first;
+          need = cap - (__shfl(incl, first, kWave) - __shfl(v, first, kWave));
+        }
+        carry = __shfl(incl, kWave - 1, kWave);
+      }
+      int nf = INT32_MAX;
+      if (hit >= 0) {
+        const uint64_t* m = tile_mask + (static_cast<int64_t>(hit) * G + r) * kBalWaves;
+        uint64_t words[kBalWaves];
+#pragma unroll
+        for (int w = 0; w < kBalWaves; ++w) words[w] = m[w];
+        int seen = 0;
+#pragma unroll
+        for (int w = 0; w < kBalWaves; ++w) {
+          uint64_t bits = words[w];
+          const int cnt = __popcll(bits);
+          if (nf == INT32_MAX && seen + cnt >= need) {
+            for (int q = 1; q < need - seen; ++q) bits &= bits - 1;
+            nf = hit * kBalTile + w * kWave + (__ffsll(static_cast<long long>(bits)) - 1);
+          }
+          seen += cnt;
+        }
+      }
+      if (lane == 0) fill[r] = nf;
+    }
+  }
+}
+
+// One round, one launch.  Every block first finds this round's fill indices
+// from the previous round's per-tile counts and taker masks (the same in
+// every block, so no block waits for another); if they equal the previous
+// round's, the previous choices (in pred) are the fixed point and the round
+// does nothing.  Otherwise every token takes its best rank with a fill index
+// >= t, stored in pred, and the tile's counts and taker masks go to this
+// round's half of the double buffers.  From round 2 on, tiles that end
+// before the smallest fill index are skipped: those tokens choose freely in
+// every round, and both halves already hold their counts and masks.
+__global__ __launch_bounds__(kBalTile) void balanced_round_kernel(
+    const int64_t* __restrict__ scores, int T, int G, int cap, int NT, int round,
+    int32_t* __restrict__ tile_cnt, uint64_t* __restrict__ tile_mask,
+    int32_t* __restrict__ fill_hist, int32_t* __restrict__ flag, int32_t* __restrict__ pred) {
+  __shared__ int fill[MOE_MAX_G];
+  __shared__ int s_cnt[kBalWaves][kWave];
+  __shared__ int s_diff;
+  if (round > 0 && *flag) return;
+  const int cur = round & 1, prev = cur ^ 1;
+  const int64_t half = static_cast<int64_t>(NT) * G;
   const int t = blockIdx.x * kBalTile + threadIdx.x;
-  const int a = t < T ? best_available(scores + static_cast<int64_t>(t) * G, G, fill, t) : -1;
-  if (t < T) pred[t] = a < 0 ? 0 : a;
+  // Loads that do not depend on this round's fill indices go first, so their
+  // latency overlaps the fill computation: the token's scores (up to
+  // kScorePre ranks) and the previous round's fill index of rank threadIdx.x.
+  long long sc[kScorePre];
+#pragma unroll
+  for (int r = 0; r < kScorePre; ++r)
+    sc[r] = (t < T && r < G) ? scores[static_cast<int64_t>(t) * G + r] : 0;
+  const int old_fill = (round > 0 && threadIdx.x < static_cast<unsigned>(G))
+                           ? fill_hist[prev * G + threadIdx.x] : 0;
+  if (threadIdx.x == 0) s_diff = 0;
+  if (round == 0) {
+    if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = INT32_MAX;
+  } else {
+    balanced_fill(tile_cnt + prev * half, tile_mask + prev * half * kBalWaves, NT, G, cap, fill);
+  }
+  __syncthreads();
+  if (round > 0) {
+    if (threadIdx.x < static_cast<unsigned>(G) && fill[threadIdx.x] != old_fill) s_diff = 1;
+    __syncthreads();
+    if (!s_diff) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) *flag = 1;
+      return;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < static_cast<unsigned>(G))
+    fill_hist[cur * G + threadIdx.x] = fill[threadIdx.x];
+  if (round >= 2) {
+    int min_fill = INT32_MAX;
+    for (int r = 0; r < G; ++r) min_fill = min(min_fill, fill[r]);
+    if (min_fill != INT32_MAX && (blockIdx.x + 1) * kBalTile <= min_fill) return;
+  }
+  const int lane = lane_id();
+  const int wave = wave_id();
+  // best rank with a fill index >= t: score descending, lower rank on ties
+  int a = -1;
+  if (t < T) {
+    long long bs = 0;
+    for (int r = 0; r < G; ++r) {
+      if (fill[r] < t) continue;
+      long long v = 0;
+#pragma unroll
+      for (int q = 0; q < kScorePre; ++q)
+        if (q == r) v = sc[q];
+      if (r >= kScorePre) v = scores[static_cast<int64_t>(t) * G + r];
+      if (a < 0 || v > bs) {
+        a = r;
+        bs = v;
+      }
+    }
+    pred[t] = a < 0 ? 0 : a;
+  }
+  uint64_t* mask = tile_mask + (cur * half + static_cast<int64_t>(blockIdx.x) * G) * kBalWaves;
   int mine = 0;
   for (int r = 0; r < G; ++r) {
     const uint64_t b = ballot(a == r);
-    if (lane == r) mine = __popcll(b);
+    if (lane == r) {
+      mine = __popcll(b);
+      mask[static_cast<int64_t>(r) * kBalWaves + wave] = b;
+    }
   }
   if (lane < G) s_cnt[wave][lane] = mine;
   __syncthreads();
   if (threadIdx.x < static_cast<unsigned>(G)) {
     int c = 0;
 #pragma unroll
-    for (int w = 0; w < kBalTile / kWave; ++w) c += s_cnt[w][threadIdx.x];
-    tile_cnt[static_cast<int64_t>(blockIdx.x) * G + threadIdx.x] = c;
+    for (int w = 0; w < kBalWaves; ++w) c += s_cnt[w][threadIdx.x];
+    tile_cnt[cur * half + static_cast<int64_t>(blockIdx.x) * G + threadIdx.x] = c;
   }
-}
-
-constexpr int kBalUpdThreads = 1024;
-
-// One round, part 2 (one block): for each rank, the tile where its takers
-// reach C, then the exact C-th taker inside that tile (from the choices part
-// 1 stored); new fill indices, or the convergence flag when none changed.
-__global__ __launch_bounds__(kBalUpdThreads) void balanced_update_kernel(
-    const int32_t* __restrict__ choice, int T, int G, int cap, int NT,
-    const int32_t* __restrict__ tile_cnt, int32_t* __restrict__ fill_g, int32_t* __restrict__ flag) {
-  __shared__ int fill[MOE_MAX_G];
-  __shared__ int nfill[MOE_MAX_G];
-  if (*flag) return;
-  const int lane = lane_id();
-  const int wave = wave_id();
-  if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = fill_g[threadIdx.x];
-  __syncthreads();
-  for (int r = wave; r < G; r += kBalUpdThreads / kWave) {
-    // tile where the running count of r's takers reaches cap
-    int carry = 0, hit_tile = -1, need = 0;
-    for (int base = 0; base < NT && hit_tile < 0; base += kWave) {
-      const int j = base + lane;
-      const int v = j < NT ? tile_cnt[static_cast<int64_t>(j) * G + r] : 0;
-      const int incl = wave_incl_scan(v) + carry;
-      const uint64_t b = ballot(j < NT && incl >= cap);
-      if (b) {
-        const int first = __ffsll(static_cast<long long>(b)) - 1;
-        hit_tile = base + first;
-        need = cap - (__shfl(incl, first, kWave) - __shfl(v, first, kWave));
-      }
-      carry = __shfl(incl, kWave - 1, kWave);
-    }
-    int nf = INT32_MAX;
-    if (hit_tile >= 0) {
-      // the need-th taker of r inside tile hit_tile
-      int seen = 0;
-      for (int c = 0; c < kBalTile; c += kWave) {
-        const int t = hit_tile * kBalTile + c + lane;
-        const int a = t < T ? choice[t] : -1;
-        const uint64_t b = ballot(a == r);
-        const int cnt = __popcll(b);
-        if (seen + cnt >= need) {
-          // position need - seen (1-based) among the set bits of b
-          uint64_t m = b;
-          for (int q = 1; q < need - seen; ++q) m &= m - 1;
-          nf = hit_tile * kBalTile + c + (__ffsll(static_cast<long long>(m)) - 1);
-          break;
-        }
-        seen += cnt;
-      }
-    }
-    if (lane == 0) nfill[r] = nf;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    bool same = true;
-    for (int r = 0; r < G; ++r) same = same && (nfill[r] == fill[r]);
-    if (same) *flag = 1;
-  }
-  if (threadIdx.x < static_cast<unsigned>(G)) fill_g[threadIdx.x] = nfill[threadIdx.x];
-}
-
-// Only when the rounds ended without confirming the fixed point (the last
-// round computed its choices with fill indices that then changed): the
-// choices under the final fill indices.
-__global__ __launch_bounds__(kBalTile) void balanced_final_kernel(
-    const int64_t* __restrict__ scores, int T, int G, const int32_t* __restrict__ fill_g,
-    const int32_t* __restrict__ flag, int32_t* __restrict__ pred) {
-  __shared__ int fill[MOE_MAX_G];
-  if (*flag) return;
-  if (threadIdx.x < static_cast<unsigned>(G)) fill[threadIdx.x] = fill_g[threadIdx.x];
-  __syncthreads();
-  const int t = blockIdx.x * kBalTile + threadIdx.x;
-  if (t >= T) return;
-  const int a = best_available(scores + static_cast<int64_t>(t) * G, G, fill, t);
-  pred[t] = a < 0 ? 0 : a;
 }
 
 struct BalancedWs {
   ShuffleWs base;
   int64_t* scores;
-  int32_t* fill;
+  int32_t* fill_hist;  // [2][G]: the fill indices of the last two rounds
   int32_t* flag;
-  int32_t* tile_cnt;
+  int32_t* tile_cnt;   // [2][NT][G]
+  uint64_t* tile_mask; // [2][NT][G][waves per tile]
   size_t bytes;
 };
 
@@ -328,10 +360,12 @@ BalancedWs balanced_layout(void* base, int64_t T, int E, int G) {
     return q;
   };
   const int64_t nt = (T + kBalTile - 1) / kBalTile;
+  const int64_t ntc = nt > 0 ? nt : 1;
   w.scores = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * (T > 0 ? T : 1) * G));
-  w.fill = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * G));
+  w.fill_hist = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 2 * G));
   w.flag = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
-  w.tile_cnt = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (nt > 0 ? nt : 1) * G));
+  w.tile_cnt = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 2 * ntc * G));
+  w.tile_mask = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 2 * ntc * G * kBalWaves));
   w.bytes = off;
   return w;
 }
@@ -373,20 +407,17 @@ extern "C" int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E
                                                           w.base.src1, d_err);
   MOE_CHECK_LAUNCH();
   moe::balanced_scores_kernel<<<blocks, moe::kBalTile, 0, s>>>(topk, Ti, k, E, w.base.M, G,
-                                                               w.scores, w.fill, w.flag, d_err);
+                                                               w.scores, w.flag, d_err);
   MOE_CHECK_LAUNCH();
   if (Ti > 0) {
-    for (int round = 0; round < G; ++round) {
-      moe::balanced_assign_kernel<<<NT, moe::kBalTile, 0, s>>>(w.scores, Ti, G, w.fill, w.flag,
-                                                               w.tile_cnt, pred_rank);
-      MOE_CHECK_LAUNCH();
-      moe::balanced_update_kernel<<<1, moe::kBalUpdThreads, 0, s>>>(pred_rank, Ti, G, Ti / G, NT,
-                                                                    w.tile_cnt, w.fill, w.flag);
+    // Round i's fill indices have the first i ranks to fill exact, so round
+    // G assigns with the fixed point (rounds stop early once it is seen).
+    for (int round = 0; round <= G; ++round) {
+      moe::balanced_round_kernel<<<NT, moe::kBalTile, 0, s>>>(
+          w.scores, Ti, G, Ti / G, NT, round, w.tile_cnt, w.tile_mask, w.fill_hist, w.flag,
+          pred_rank);
       MOE_CHECK_LAUNCH();
     }
-    moe::balanced_final_kernel<<<NT, moe::kBalTile, 0, s>>>(w.scores, Ti, G, w.fill, w.flag,
-                                                            pred_rank);
-    MOE_CHECK_LAUNCH();
   }
   moe::PlanArgs a{pred_rank,      nullptr,        Ti,        1,
                   G,              w.base.identity, G,        G,
