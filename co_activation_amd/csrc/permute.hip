@@ -168,6 +168,47 @@ __global__ __launch_bounds__(kPermThreads) void permute_flat_kernel(
   report(d_err, errbits);
 }
 
+// Wide rows (more than 512 vectors): a row is split into parts of
+// kSplitVec vectors, and one wave (block) moves one part of one token to
+// every destination; block (t, part) covers [part, part + 1) * kSplitVec.
+// Measured on MI355X for 14 KiB rows with 8 destinations: 5% faster than a
+// 256-thread block per token (two-KiB pieces per wave beat one-KiB pieces
+// and four-KiB blocks); for 8 KiB and narrower rows it was slower.
+constexpr int kSplitVec = 128;
+
+template <typename V>
+__global__ __launch_bounds__(kWave) void permute_split_kernel(
+    const V* __restrict__ x, int T, int64_t vec_per_row, int parts,
+    const int32_t* __restrict__ dest, int width, V* __restrict__ out, int64_t out_rows,
+    const int32_t* __restrict__ n_valid, int32_t* d_err) {
+  const int t = static_cast<int>(blockIdx.x / parts);
+  const int part = static_cast<int>(blockIdx.x % parts);
+  if (t >= T || (n_valid != nullptr && t >= *n_valid)) return;
+  const int64_t c_lo = static_cast<int64_t>(part) * kSplitVec;
+  const int64_t c_hi = c_lo + kSplitVec < vec_per_row ? c_lo + kSplitVec : vec_per_row;
+  int drow[MOE_MAX_K];
+#pragma unroll
+  for (int q = 0; q < MOE_MAX_K; ++q)
+    drow[q] = q < width ? __builtin_amdgcn_readfirstlane(dest[static_cast<int64_t>(t) * width + q])
+                        : -1;
+  int errbits = 0;
+  const V* src = x + static_cast<int64_t>(t) * vec_per_row;
+  for (int64_t c = c_lo + threadIdx.x; c < c_hi; c += kWave) {
+    const V v = load_row<false>(src + c);
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_K; ++q) {
+      if (q >= width) break;
+      if (drow[q] < 0) continue;
+      if (drow[q] >= out_rows) {
+        errbits = MOE_DERR_ROW_RANGE;
+        continue;
+      }
+      __builtin_nontemporal_store(v, out + static_cast<int64_t>(drow[q]) * vec_per_row + c);
+    }
+  }
+  if (threadIdx.x == 0) report(d_err, errbits);
+}
+
 template <typename V, int TPT, int U>
 void launch_rows(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
                  void* out, int64_t out_rows, const int32_t* n_valid, int32_t* d_err,
@@ -201,6 +242,7 @@ constexpr unsigned kFanoutLds = 64 * 1024;
 //                          token with two vectors each
 //   384 < R <= 512 and at most 2 destinations
 //                          512 threads per token, one vector each
+//   R > 512                one wave per 128-vector part of a row
 //   otherwise              256 threads per token, one vector per pass
 template <typename V>
 int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
@@ -221,6 +263,11 @@ int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* des
         n_valid, d_err);
   } else if (vec_per_row > 384 && vec_per_row <= 512 && width <= 2) {
     launch_rows<V, 512, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
+  } else if (vec_per_row > 512) {
+    const int64_t parts = (vec_per_row + kSplitVec - 1) / kSplitVec;
+    permute_split_kernel<V><<<static_cast<unsigned>(static_cast<int64_t>(T) * parts), kWave, 0, s>>>(
+        static_cast<const V*>(x), T, vec_per_row, static_cast<int>(parts), dest, width,
+        static_cast<V*>(out), out_rows, n_valid, d_err);
   } else {
     launch_rows<V, 256, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
   }
