@@ -217,12 +217,14 @@ def test_permute_narrow_rows_and_untouched():
     assert (got[~targeted] == -7).all()
 
 
-@pytest.mark.parametrize("row_bytes,width", [(8192, 6), (14336, 8), (6400, 3), (16384, 4)])
+@pytest.mark.parametrize("row_bytes,width", [(8192, 6), (14336, 8), (6400, 3), (16384, 4),
+                                             (8464, 5)])
 def test_permute_fanout_paths(row_bytes, width):
     """Wide rows with more than two destinations, through the fan-out launch
-    (6-8 KiB rows) and the plain one (14-16 KiB rows): scattered -1 entries,
-    a device row count, and a destination past the output (reported,
-    skipped, nothing else written wrong)."""
+    (6-8 KiB rows) and the split one (rows over 8 KiB, one wave per 2 KiB
+    part; 8464 bytes leave a ragged last part): scattered -1 entries, a
+    device row count, and a destination past the output (reported, skipped,
+    nothing else written wrong)."""
     rng = np.random.default_rng(row_bytes + width)
     T = 700
     words = row_bytes // 4
