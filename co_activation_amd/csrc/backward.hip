@@ -154,7 +154,7 @@ int launch_scaled(const void* x, int64_t T, int64_t H, const int32_t* dest, int 
   const int64_t groups = H / EPL;
   const int chunks = static_cast<int>((groups + kBwChunk - 1) / kBwChunk);
   const int64_t blocks = (T * chunks + kBwThreads / kWave - 1) / (kBwThreads / kWave);
-  if (blocks > INT32_MAX) return MOE_ERR_SHAPE;
+  if (!grid_ok(blocks, kBwThreads)) return MOE_ERR_SHAPE;
   permute_scaled_kernel<XBF16, OBF16, EPL><<<static_cast<unsigned>(blocks), kBwThreads, 0, s>>>(
       static_cast<const u32x4*>(x), groups, chunks, dest, width, scale, static_cast<int>(T),
       static_cast<u32x4*>(out), out_rows, n_valid, d_err);
@@ -166,6 +166,7 @@ template <bool ABF16, bool BBF16, int EPL>
 int launch_dot(const void* a, const void* b, int64_t b_rows, int64_t T, int64_t H,
                const int32_t* rows, int width, float* out, const int32_t* n_valid,
                int32_t* d_err, hipStream_t s) {
+  if (!grid_ok(T, kBwThreads)) return MOE_ERR_SHAPE;
   row_dot_kernel<ABF16, BBF16, EPL><<<static_cast<unsigned>(T), kBwThreads, 0, s>>>(
       static_cast<const u32x4*>(a), static_cast<const u32x4*>(b), H / EPL, b_rows, rows, width,
       static_cast<int>(T), out, n_valid, d_err);

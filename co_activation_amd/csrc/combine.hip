@@ -118,7 +118,7 @@ int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k,
   const int64_t items = T * chunks;
   constexpr int kItemsPerBlock = kCombThreads / kWave;
   const int64_t blocks = (items + kItemsPerBlock - 1) / kItemsPerBlock;
-  if (blocks > INT32_MAX) return MOE_ERR_SHAPE;
+  if (!grid_ok(blocks, kCombThreads)) return MOE_ERR_SHAPE;
   const unsigned lds = (k >= 6 && z_rows >= 6 * T) ? kCombLdsManyRows : 0;
   combine_kernel<ZBF16, YBF16, EPL><<<static_cast<unsigned>(blocks), kCombThreads, lds, s>>>(
       static_cast<const u32x4*>(z), z_rows, groups, chunks, rows, k, w, static_cast<int>(T),

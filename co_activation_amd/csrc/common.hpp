@@ -10,6 +10,13 @@ namespace moe {
 
 constexpr int kWave = 64;
 
+// One launch holds fewer than 2^32 work-items: the dispatch packet counts a
+// grid's work-items in 32 bits.  Launchers whose grid grows with rows times
+// row width check this and refuse larger inputs with MOE_ERR_SHAPE.
+inline bool grid_ok(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks <= INT32_MAX && blocks * threads < (int64_t{1} << 32);
+}
+
 // Launch-status check used right after every kernel launch.
 #define MOE_CHECK_LAUNCH()                                  \
   do {                                                      \

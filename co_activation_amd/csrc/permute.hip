@@ -210,12 +210,14 @@ __global__ __launch_bounds__(kWave) void permute_split_kernel(
 }
 
 template <typename V, int TPT, int U>
-void launch_rows(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
-                 void* out, int64_t out_rows, const int32_t* n_valid, int32_t* d_err,
-                 hipStream_t s) {
+int launch_rows(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
+                void* out, int64_t out_rows, const int32_t* n_valid, int32_t* d_err,
+                hipStream_t s) {
   constexpr int kBlock = TPT < kPermThreads ? kPermThreads : TPT;
   constexpr int kTokens = kBlock / TPT;
-  const unsigned blocks = static_cast<unsigned>((T + kTokens - 1) / kTokens);
+  const int64_t nb = (static_cast<int64_t>(T) + kTokens - 1) / kTokens;
+  if (!grid_ok(nb, kBlock)) return MOE_ERR_SHAPE;
+  const unsigned blocks = static_cast<unsigned>(nb);
   if (width == 1)
     permute_kernel<V, TPT, U, true><<<blocks, kBlock, 0, s>>>(
         static_cast<const V*>(x), T, vec_per_row, dest, width, static_cast<V*>(out), out_rows,
@@ -224,6 +226,7 @@ void launch_rows(const void* x, int T, int64_t vec_per_row, const int32_t* dest,
     permute_kernel<V, TPT, U, false><<<blocks, kBlock, 0, s>>>(
         static_cast<const V*>(x), T, vec_per_row, dest, width, static_cast<V*>(out), out_rows,
         n_valid, d_err);
+  return MOE_OK;
 }
 
 // Blocks of a fan-out launch reserve this much LDS (unused) so that at most
@@ -256,20 +259,28 @@ int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* des
         static_cast<const V*>(x), T, static_cast<int>(vec_per_row), dest, width,
         static_cast<V*>(out), out_rows, n_valid, d_err);
   } else if (vec_per_row < 256) {
-    launch_rows<V, 64, 4>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
+    const int rc = launch_rows<V, 64, 4>(x, T, vec_per_row, dest, width, out, out_rows, n_valid,
+                                         d_err, s);
+    if (rc != MOE_OK) return rc;
   } else if (vec_per_row > 384 && vec_per_row <= 512 && width > 2) {
+    if (!grid_ok(T, 256)) return MOE_ERR_SHAPE;
     permute_fanout_kernel<V, 256, 2><<<static_cast<unsigned>(T), 256, kFanoutLds, s>>>(
         static_cast<const V*>(x), T, vec_per_row, dest, width, static_cast<V*>(out), out_rows,
         n_valid, d_err);
   } else if (vec_per_row > 384 && vec_per_row <= 512 && width <= 2) {
-    launch_rows<V, 512, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
+    const int rc = launch_rows<V, 512, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid,
+                                          d_err, s);
+    if (rc != MOE_OK) return rc;
   } else if (vec_per_row > 512) {
     const int64_t parts = (vec_per_row + kSplitVec - 1) / kSplitVec;
+    if (parts > INT32_MAX || !grid_ok(static_cast<int64_t>(T) * parts, kWave)) return MOE_ERR_SHAPE;
     permute_split_kernel<V><<<static_cast<unsigned>(static_cast<int64_t>(T) * parts), kWave, 0, s>>>(
         static_cast<const V*>(x), T, vec_per_row, static_cast<int>(parts), dest, width,
         static_cast<V*>(out), out_rows, n_valid, d_err);
   } else {
-    launch_rows<V, 256, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
+    const int rc = launch_rows<V, 256, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid,
+                                          d_err, s);
+    if (rc != MOE_OK) return rc;
   }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
@@ -350,9 +361,12 @@ int launch_gather(const void* x, int64_t x_rows, int64_t vec_per_row, const int3
         xv, x_rows, static_cast<int>(vec_per_row), src, n_rows, ov, n_valid, d_err);
   } else if (vec_per_row < 256) {
     constexpr int kRows = kPermThreads / 64;
-    gather_kernel<V, 64, 4><<<static_cast<unsigned>((n_rows + kRows - 1) / kRows), kPermThreads,
-                              0, s>>>(xv, x_rows, vec_per_row, src, n_rows, ov, n_valid, d_err);
+    const int64_t nb = (static_cast<int64_t>(n_rows) + kRows - 1) / kRows;
+    if (!grid_ok(nb, kPermThreads)) return MOE_ERR_SHAPE;
+    gather_kernel<V, 64, 4><<<static_cast<unsigned>(nb), kPermThreads, 0, s>>>(
+        xv, x_rows, vec_per_row, src, n_rows, ov, n_valid, d_err);
   } else {
+    if (!grid_ok(n_rows, 512)) return MOE_ERR_SHAPE;
     gather_kernel<V, 512, 1><<<static_cast<unsigned>(n_rows), 512, 0, s>>>(
         xv, x_rows, vec_per_row, src, n_rows, ov, n_valid, d_err);
   }
@@ -431,11 +445,13 @@ int launch_shuffle_dispatch(const void* x, int T, int64_t vec_per_row, const int
   const V* xv = static_cast<const V*>(x);
   if (vec_per_row < 256) {
     constexpr int kTokens = kPermThreads / 64;
-    shuffle_dispatch_kernel<V, 64, 4><<<static_cast<unsigned>((T + kTokens - 1) / kTokens),
-                                        kPermThreads, 0, s>>>(
+    const int64_t nb = (static_cast<int64_t>(T) + kTokens - 1) / kTokens;
+    if (!grid_ok(nb, kPermThreads)) return MOE_ERR_SHAPE;
+    shuffle_dispatch_kernel<V, 64, 4><<<static_cast<unsigned>(nb), kPermThreads, 0, s>>>(
         xv, T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
         static_cast<V*>(send), send_rows, d_err);
   } else {
+    if (!grid_ok(T, 512)) return MOE_ERR_SHAPE;
     shuffle_dispatch_kernel<V, 512, 1><<<static_cast<unsigned>(T), 512, 0, s>>>(
         xv, T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
         static_cast<V*>(send), send_rows, d_err);

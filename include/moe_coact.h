@@ -75,7 +75,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 #define MOE_DERR_SRC_OFFSETS 16  /* src_offsets not nondecreasing from 0 to T            */
 #define MOE_DERR_ROW_RANGE 32    /* permute/combine: a row index >= the buffer's rows    */
 
-/* Limits checked on the host. */
+/* Limits checked on the host.  Besides these, the row-moving calls
+   (moe_permute, moe_gather, moe_shuffle_dispatch, moe_combine,
+   moe_permute_scaled, moe_row_dot) return MOE_ERR_SHAPE, launching nothing,
+   when one launch would need 2^32 or more work-items (the dispatch packet
+   counts them in 32 bits): roughly when rows times 16-byte row vectors
+   reach 2^32, i.e. inputs of several tens of GB. */
 #define MOE_MAX_K 8      /* experts per token           */
 #define MOE_MAX_E 256    /* experts per layer           */
 #define MOE_MAX_G 64     /* logical ranks in the group  */

@@ -107,6 +107,14 @@ def test_permute_combine_shuffle_reject(built_lib):
     assert g(FAKE, 8, 16, NULL, 8, FAKE, NULL, NULL, NULL) == -1    # src
     assert g(NULL, 8, 16, FAKE, 8, FAKE, NULL, NULL, NULL) == -1    # x
     assert g(NULL, 0, 16, NULL, 0, NULL, NULL, NULL, NULL) == 0     # empty: no-op
+    # launches of 2^32 or more work-items are refused before anything runs
+    big = 1 << 24
+    assert L.moe_permute(FAKE, big, 4096, FAKE, 1, FAKE, big, NULL, NULL, NULL) == -2
+    assert L.moe_permute(FAKE, big // 2, 16384, FAKE, 2, FAKE, big, NULL, NULL, NULL) == -2
+    assert sdp(FAKE, big // 2, 8192, FAKE, FAKE, 2, FAKE, FAKE, big, NULL, NULL) == -2
+    assert g(FAKE, big, 8192, FAKE, big // 2, FAKE, NULL, NULL, NULL) == -2
+    assert L.moe_combine(FAKE, 1, big, 1 << 20, FAKE, 2, NULL, big // 64, FAKE, 1, NULL, NULL,
+                         NULL) == -2
     assert L.moe_combine(FAKE, 7, 8, 64, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -3
     assert L.moe_combine(FAKE, 1, 8, 60, FAKE, 2, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -4  # 120 B
     assert L.moe_combine(FAKE, 1, 8, 64, FAKE, 0, NULL, 8, FAKE, 1, NULL, NULL, NULL) == -2
