@@ -13,6 +13,7 @@ import torch
 import oracle
 from co_activation_amd import ops
 from co_activation_amd.pipeline import GraphStep, LayerStep, TwoLayerStep
+import gpu_util
 from gpu_util import (assert_equal, check_combine, dev, f32_ulps, host, i32, say, x_tensor)
 from workloads import make, expert_outputs
 
@@ -419,6 +420,53 @@ def test_combine_parity(cfg, T, H, zd, yd):
         m = ref["token_rows"][:, q] >= 0
         scale[m] += np.abs(Zf[ref["token_rows"][m, q]])
     assert (np.abs(host(yu) - refu) <= 1e-5 * scale + 1e-30).all()
+
+
+@pytest.mark.parametrize("yd", ["bf16", "f32"])
+def test_combine_special_values(yd):
+    """Rows holding signed zeros, a subnormal, the bf16 maximum, infinities
+    and NaN, weighted by 1/4, 1/2 or 1: NaN and infinities (with their sign)
+    appear exactly where the oracle has them, sums past the fp32 range
+    overflow on both sides, and every finite element meets the usual bound.
+    With this pool every sum is either exactly representable or at least 3%
+    away from an overflow threshold, far beyond any rounding-order effect.
+    (No zero gates: when two slots share a row the kernel scales the row by
+    their summed gate, while the definition sums the slots; with an infinite
+    row and a zero gate the two differ by 0 * inf.)"""
+    rng = np.random.default_rng(41)
+    T, E, k, G, H = 512, 4, 2, 2, 64
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    er = np.array([0, 0, 1, 1], np.int32)
+    gates = rng.choice(np.array([0.25, 0.5, 1.0], np.float32), size=(T, k))
+    say("combine special values", yd)
+    err = _err()
+    plan = ops.dispatch_plan(i32(topk), dev(gates), i32(er), G, G, d_err=err)
+    ref_plan = oracle.dispatch_plan(topk, gates, er, G, G)
+    N = int(ref_plan["N"])
+    pool = np.array([0x0000, 0x8000, 0x0001, 0x3F80, 0xBF80, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80,
+                     0x7FC0, 0x7E00, 0x4049], np.uint16)
+    Z = rng.choice(pool, size=(T * min(k, G), H)).astype(np.uint16)
+    tdt = torch.bfloat16 if yd == "bf16" else torch.float32
+    y = ops.combine(dev(Z), plan.token_rows, plan.row_weight, out_dtype=tdt, d_err=err)
+    _no_errors(err)
+    got = oracle.bf16_to_f32(host(y)) if yd == "bf16" else host(y)
+    with np.errstate(all="ignore"):  # the reference overflows and makes NaN on purpose
+        ref32 = oracle.combine(Z, "bf16", ref_plan["slot_row"], gates, "f32")
+        ref = oracle.bf16_to_f32(oracle.bf16_round(ref32)) if yd == "bf16" else ref32
+        scale_all = gpu_util.combine_scale(Z, "bf16", ref_plan["slot_row"], gates)
+    assert N > T
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "NaN positions"
+    for sign in (1, -1):
+        assert np.array_equal(got == sign * np.inf, ref == sign * np.inf), f"{sign:+d} infinity"
+    assert np.isnan(ref).any() and np.isinf(ref).any() and np.isfinite(ref).any()
+    fin = np.isfinite(ref)
+    dev_err = np.abs(got[fin].astype(np.float64) - ref32[fin].astype(np.float64))
+    scale = scale_all[fin]
+    if yd == "f32":
+        assert (dev_err <= 1e-5 * scale + 1e-30).all()
+    else:
+        d = gpu_util.bf16_ulps(host(y)[fin], oracle.bf16_round(ref32)[fin])
+        assert ((d <= 1) | (dev_err <= 1e-5 * scale)).all()
 
 
 def test_combine_of_permute_is_identity():
