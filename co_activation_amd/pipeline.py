@@ -50,7 +50,15 @@ class _Hip:
     @classmethod
     def get(cls):
         if cls._h is None:
-            h = ctypes.CDLL("libamdhip64.so.7")
+            h = None
+            for name in ("libamdhip64.so.7", "libamdhip64.so"):
+                try:
+                    h = ctypes.CDLL(name)
+                    break
+                except OSError:
+                    continue
+            if h is None:
+                raise RuntimeError("the HIP runtime library (libamdhip64) could not be loaded")
             h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
