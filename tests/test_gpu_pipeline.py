@@ -6,7 +6,7 @@ those of one step run alone (one stream) on that batch."""
 import pytest
 import torch
 
-from co_activation_amd.pipeline import LayerStep, Pipeline, TwoLayerStep
+from co_activation_amd.pipeline import GraphPipeline, LayerStep, Pipeline, TwoLayerStep
 from gpu_util import assert_equal, dev, host, i32, say
 from workloads import expert_outputs, make
 
@@ -170,3 +170,40 @@ def test_pipeline_fullsize_matches_single_steps(cfg):
             assert torch.equal(_bits(a), _bits(want)), f"batch {b}: {key}"
         del ref, got[b]
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("two_layer", [False, True])
+def test_graph_pipeline_replays_match_single_steps(two_layer):
+    """Four batches of a two-step pipeline captured as one graph and replayed
+    three times, with eager work, synchronisation and cleared outputs in
+    between: after every replay each step's outputs equal those of one step
+    run alone on its inputs, bit for bit."""
+    cfg, T, H = (5, 8192, 1024) if two_layer else (3, 4096, 1024)
+    say("graph pipeline", "two-layer" if two_layer else "one layer", f"T={T}", f"H={H}")
+    ws = [make(cfg, T=T, H=H, seed=s) for s in range(2)]
+    w0 = ws[0]
+    cap = T * min(w0.k, w0.G)
+    batches = [_inputs(two_layer, w, dev(expert_outputs(cap, H, "bf16", seed=10 + s)))
+               for s, w in enumerate(ws)]
+    steps = [_step(two_layer, batches[j], w0) for j in range(2)]
+    gp = GraphPipeline(Pipeline(steps), 4)
+    refs = []
+    for j in range(2):
+        ref = _step(two_layer, batches[j], w0).run(overlap=False)
+        torch.cuda.synchronize()
+        refs.append(ref)
+    for rep in range(3):
+        for st in steps:
+            st.y.zero_()
+            st.send.zero_()
+        torch.cuda.synchronize()
+        gp.replay()
+        torch.cuda.synchronize()
+        for j, (st, ref) in enumerate(zip(steps, refs)):
+            assert int(st.d_err.item()) == 0
+            N = int(ref.plan.counters[0].item())
+            for key, want in _outputs(ref, two_layer).items():
+                a = _outputs(st, two_layer)[key]
+                if key in ("send", "plan.row_token", "plan.row_weight"):
+                    a, want = a[:N], want[:N]
+                assert torch.equal(_bits(a), _bits(want)), f"replay {rep}, step {j}: {key}"
