@@ -414,10 +414,11 @@ __global__ __launch_bounds__(kPlanTile) void plan_write_kernel(
 }  // namespace
 
 int launch_plan(const PlanArgs& a, hipStream_t stream) {
-  const int64_t nt = plan_max_tiles(a.T, a.G);
-  int32_t* tile_cnt = static_cast<int32_t*>(a.ws);
-  int32_t* tile_stats = tile_cnt + nt * a.G;
-  if (nt > 0) {
+  const PlanTiles tiles = plan_tiles(a.ws, a.T, a.G);
+  const int64_t nt = tiles.stride;
+  int32_t* tile_cnt = tiles.cnt;
+  int32_t* tile_stats = tiles.stats;
+  if (nt > 0 && !a.counts_ready) {
     plan_count_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(kPlanTile), 0, stream>>>(
         a.topk, a.T, a.k, a.E, a.expert_rank, a.G, a.ranks_per_node, a.src_offsets, tile_cnt, nt,
         tile_stats, a.d_err);

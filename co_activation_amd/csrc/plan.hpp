@@ -18,6 +18,21 @@ inline size_t plan_workspace_bytes(int64_t T, int G) {
   return (b + 255) & ~static_cast<size_t>(255);
 }
 
+// Where the count kernel leaves its per-tile results in the plan workspace:
+// counts per (rank, tile) at cnt[r * stride + tile], then four counter
+// partials per tile.
+struct PlanTiles {
+  int32_t* cnt;
+  int32_t* stats;
+  int64_t stride;
+};
+
+inline PlanTiles plan_tiles(void* ws, int64_t T, int G) {
+  const int64_t nt = plan_max_tiles(T, G);
+  int32_t* cnt = static_cast<int32_t*>(ws);
+  return PlanTiles{cnt, cnt + nt * G, nt};
+}
+
 struct PlanArgs {
   const int32_t* topk;
   const float* gates;
@@ -38,6 +53,9 @@ struct PlanArgs {
   // Optional: receives send_offsets[0..G] (the row offsets of source rank 0's
   // blocks), i.e. the bucket offsets when the plan serves as a sort.
   int32_t* first_offsets = nullptr;
+  // Set when the per-tile counts are already in the workspace (the token
+  // shuffle's prediction kernel writes them): the count kernel is skipped.
+  bool counts_ready = false;
 };
 
 // Enqueues the three plan kernels; arguments already validated.

@@ -89,40 +89,63 @@ __global__ __launch_bounds__(kScoreThreads) void rank_score_kernel(
   }
 }
 
-constexpr int kPredThreads = 256;
-
-__global__ __launch_bounds__(kPredThreads) void predict_kernel(
+// The prediction and the sort's first plan kernel in one pass.  Each block
+// takes one 256-token tile: per token the k*G score sums and the argmax
+// (ties to the lower rank; an all-zero score gives rank 0), written to
+// pred_rank, the sort's one-slot routing; then the tile's count per rank
+// from wave ballots, stored where the plan's count kernel stores them, with
+// zero counter partials.  The sort continues with the plan's scan and write.
+__global__ __launch_bounds__(kPlanTile) void predict_count_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
-    int32_t* __restrict__ pred_rank, int32_t* d_err) {
-  const int t = blockIdx.x * kPredThreads + threadIdx.x;
-  if (t >= T) return;
-  int e[MOE_MAX_K];
+    int32_t* __restrict__ pred_rank, int32_t* __restrict__ tile_cnt, int64_t stride,
+    int32_t* __restrict__ tile_stats, int32_t* d_err) {
+  __shared__ int s_cnt[kPlanTile / kWave][kWave];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int t = blockIdx.x * kPlanTile + threadIdx.x;
+  int best_r = -1;
   int errbits = 0;
+  if (t < T) {
+    int e[MOE_MAX_K];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_K; ++j) {
-    e[j] = -1;
-    if (j < k) {
-      const int v = topk[static_cast<int64_t>(t) * k + j];
-      if (v >= 0 && v < E)
-        e[j] = v;
-      else
-        errbits |= MOE_DERR_EXPERT_RANGE;
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+      e[j] = -1;
+      if (j < k) {
+        const int v = topk[static_cast<int64_t>(t) * k + j];
+        if (v >= 0 && v < E)
+          e[j] = v;
+        else
+          errbits |= MOE_DERR_EXPERT_RANGE;
+      }
     }
-  }
-  long long best = 0;
-  int best_r = 0;
-  for (int r = 0; r < G; ++r) {
-    long long sc = 0;
+    long long best = 0;
+    for (int r = 0; r < G; ++r) {
+      long long sc = 0;
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_K; ++j)
-      if (e[j] >= 0) sc += M[static_cast<int64_t>(e[j]) * G + r];
-    if (r == 0 || sc > best) {
-      best = sc;
-      best_r = r;
+      for (int j = 0; j < MOE_MAX_K; ++j)
+        if (e[j] >= 0) sc += M[static_cast<int64_t>(e[j]) * G + r];
+      if (r == 0 || sc > best) {
+        best = sc;
+        best_r = r;
+      }
     }
+    pred_rank[t] = best_r;
   }
-  pred_rank[t] = best_r;
   report(d_err, errbits);
+  int mine = 0;
+  for (int r = 0; r < G; ++r) {
+    const uint64_t b = ballot(best_r == r);
+    if (lane == r) mine = __popcll(b);
+  }
+  if (lane < G) s_cnt[wave][lane] = mine;
+  __syncthreads();
+  if (threadIdx.x < static_cast<unsigned>(G)) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanTile / kWave; ++w) c += s_cnt[w][threadIdx.x];
+    tile_cnt[static_cast<int64_t>(threadIdx.x) * stride + blockIdx.x] = c;
+  }
+  if (threadIdx.x < 4) tile_stats[static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x] = 0;
 }
 
 }  // namespace
@@ -458,9 +481,12 @@ extern "C" int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E,
   moe::rank_score_kernel<<<E, moe::kScoreThreads, 0, s>>>(transition, E_next, expert_rank_next, G, Ti,
                                                   w.M, w.identity, w.src1, d_err);
   MOE_CHECK_LAUNCH();
+  // the sort's tiles: one source rank, 256 tokens each, numbered from 0
+  const moe::PlanTiles tiles = moe::plan_tiles(w.plan_ws, T, G);
   if (Ti > 0) {
-    moe::predict_kernel<<<(Ti + moe::kPredThreads - 1) / moe::kPredThreads, moe::kPredThreads, 0,
-                          s>>>(topk, Ti, k, E, w.M, G, pred_rank, d_err);
+    moe::predict_count_kernel<<<(Ti + moe::kPlanTile - 1) / moe::kPlanTile, moe::kPlanTile, 0,
+                                s>>>(topk, Ti, k, E, w.M, G, pred_rank, tiles.cnt, tiles.stride,
+                                     tiles.stats, d_err);
     MOE_CHECK_LAUNCH();
   }
   moe::PlanArgs a{pred_rank,      nullptr,        Ti,        1,
@@ -469,5 +495,6 @@ extern "C" int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E,
                   perm ? perm : w.perm_scratch,   nullptr,   dest_pos,
                   nullptr,        w.counters,     d_err,     w.plan_ws,
                   shard_offsets};
+  a.counts_ready = true;
   return moe::launch_plan(a, s);
 }
