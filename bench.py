@@ -422,7 +422,7 @@ def main() -> int:
         "stage_us_p90": {n: 1e3 * v for n, v in stage_p90.items()},
         "schedule": ("two batches in flight: each batch's " +
                      ("statistics and plan" if w.cfg != 5 else
-                      "statistics, shuffle prediction, routing move and layer-2 plan") +
+                      "statistics, shuffle prediction and layer-2 plan") +
                      " on a second stream beside the previous batch's combine"),
         "counters": {"rows": N, "assignments": int(counters[1]), "local_rows": int(counters[2]),
                      "local_assign": int(counters[3]), "node_rows": int(counters[4]),

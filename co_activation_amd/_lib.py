@@ -36,7 +36,7 @@ EXPORTS = (
     "moe_expert_plan_workspace_size", "moe_expert_plan",
     "moe_permute_scaled", "moe_row_dot", "moe_ema_update", "moe_place_experts",
     "moe_shuffle_balanced_workspace_size", "moe_shuffle_balanced", "moe_gather",
-    "moe_shuffle_dispatch",
+    "moe_shuffle_dispatch", "moe_dispatch_plan_gathered",
 )
 
 _lib = None
@@ -53,6 +53,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.moe_dispatch_plan.argtypes = [P, P, c_int64, c_int, c_int, P, c_int, c_int, P, c_int64,
                                       P, P, P, P, P, P, P, P, P, c_size_t, P]
     lib.moe_dispatch_plan.restype = c_int
+    lib.moe_dispatch_plan_gathered.argtypes = [P, P, P, c_int64, c_int, c_int, P, c_int, c_int, P,
+                                               c_int64, P, P, P, P, P, P, P, P, P, P, P,
+                                               c_size_t, P]
+    lib.moe_dispatch_plan_gathered.restype = c_int
     lib.moe_permute.argtypes = [P, c_int64, c_int64, P, c_int, P, c_int64, P, P, P]
     lib.moe_permute.restype = c_int
     lib.moe_gather.argtypes = [P, c_int64, c_int64, P, c_int64, P, P, P, P]

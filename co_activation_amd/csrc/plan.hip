@@ -76,8 +76,13 @@ __device__ __forceinline__ bool block_tile(const int32_t* off, int T, int G, int
   return true;
 }
 
+// With perm set, position t of the plan holds token perm[t]: its routing
+// is read through perm and copied to topk_out / gates_out (row t), so the
+// gathered routing comes out of this pass.
 __global__ __launch_bounds__(kPlanTile) void plan_count_kernel(
-    const int32_t* __restrict__ topk, int T, int k, int E, const int32_t* __restrict__ expert_rank,
+    const int32_t* __restrict__ topk, const int32_t* __restrict__ perm,
+    const float* __restrict__ gates, int32_t* __restrict__ topk_out,
+    float* __restrict__ gates_out, int T, int k, int E, const int32_t* __restrict__ expert_rank,
     int G, int ranks_per_node, const int32_t* __restrict__ src_offsets,
     int32_t* __restrict__ tile_cnt, int64_t stride, int32_t* __restrict__ tile_stats,
     int32_t* d_err) {
@@ -92,8 +97,24 @@ __global__ __launch_bounds__(kPlanTile) void plan_count_kernel(
   const int t = t0 + static_cast<int>(threadIdx.x);
   uint64_t mask = 0, nodes = 0;
   int local_assign = 0, errbits = 0;
-  if (t < t1) {
-    const int32_t* row = topk + static_cast<int64_t>(t) * k;
+  int src = t;
+  if (t < t1 && perm != nullptr) {
+    src = perm[t];
+    if (src < 0 || src >= T) {
+      errbits |= MOE_DERR_ROW_RANGE;
+      src = -1;
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+      if (j >= k) break;
+      const int64_t i = static_cast<int64_t>(src) * k + j;
+      topk_out[static_cast<int64_t>(t) * k + j] = src >= 0 ? topk[i] : -1;
+      if (gates_out != nullptr)
+        gates_out[static_cast<int64_t>(t) * k + j] = (src >= 0 && gates != nullptr) ? gates[i] : 0.f;
+    }
+  }
+  if (t < t1 && src >= 0) {
+    const int32_t* row = topk + static_cast<int64_t>(src) * k;
     int ex[MOE_MAX_K];
 #pragma unroll
     for (int j = 0; j < MOE_MAX_K; ++j) {
@@ -420,8 +441,8 @@ int launch_plan(const PlanArgs& a, hipStream_t stream) {
   int32_t* tile_stats = tiles.stats;
   if (nt > 0 && !a.counts_ready) {
     plan_count_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(kPlanTile), 0, stream>>>(
-        a.topk, a.T, a.k, a.E, a.expert_rank, a.G, a.ranks_per_node, a.src_offsets, tile_cnt, nt,
-        tile_stats, a.d_err);
+        a.topk, a.perm, a.gates, a.topk_out, a.gates_out, a.T, a.k, a.E, a.expert_rank, a.G,
+        a.ranks_per_node, a.src_offsets, tile_cnt, nt, tile_stats, a.d_err);
     MOE_CHECK_LAUNCH();
   }
   if (a.G <= 16)
@@ -434,8 +455,11 @@ int launch_plan(const PlanArgs& a, hipStream_t stream) {
         a.send_offsets, a.counters, a.first_offsets, a.d_err);
   MOE_CHECK_LAUNCH();
   if (nt > 0) {
+    // with perm, the routing in the plan's order is the count kernel's copy
+    const int32_t* wtopk = a.perm != nullptr ? a.topk_out : a.topk;
+    const float* wgates = a.perm != nullptr ? a.gates_out : a.gates;
     plan_write_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(kPlanTile), 0, stream>>>(
-        a.topk, a.gates, a.T, a.k, a.E, a.expert_rank, a.G, a.src_offsets, tile_cnt, nt,
+        wtopk, wgates, a.T, a.k, a.E, a.expert_rank, a.G, a.src_offsets, tile_cnt, nt,
         a.send_offsets, a.row_capacity, a.row_token, a.row_weight, a.token_rows, a.slot_row,
         a.d_err);
     MOE_CHECK_LAUNCH();
@@ -452,13 +476,15 @@ extern "C" int moe_dispatch_plan_workspace_size(int64_t T, int G, size_t* ws_byt
   return MOE_OK;
 }
 
-extern "C" int moe_dispatch_plan(const int32_t* topk, const float* gates, int64_t T, int k, int E,
-                                 const int32_t* expert_rank, int G, int ranks_per_node,
-                                 const int32_t* src_offsets, int64_t row_capacity,
-                                 int32_t* send_counts, int32_t* send_offsets, int32_t* row_token,
-                                 float* row_weight, int32_t* token_rows, int32_t* slot_row,
-                                 int64_t* counters, int32_t* d_err, void* ws, size_t ws_bytes,
-                                 void* stream) {
+namespace moe {
+namespace {
+
+int plan_entry(const int32_t* topk, const float* gates, const int32_t* perm, int64_t T, int k,
+               int E, const int32_t* expert_rank, int G, int ranks_per_node,
+               const int32_t* src_offsets, int64_t row_capacity, int32_t* send_counts,
+               int32_t* send_offsets, int32_t* row_token, float* row_weight,
+               int32_t* token_rows, int32_t* slot_row, int64_t* counters, int32_t* topk_out,
+               float* gates_out, int32_t* d_err, void* ws, size_t ws_bytes, void* stream) {
   if (k < 1 || k > MOE_MAX_K || E < 1 || E > MOE_MAX_E || G < 1 || G > MOE_MAX_G || T < 0 ||
       ranks_per_node < 1 || G % ranks_per_node != 0 || row_capacity < 0 ||
       row_capacity > INT32_MAX || T * static_cast<int64_t>(k) >= (int64_t{1} << 31))
@@ -470,10 +496,47 @@ extern "C" int moe_dispatch_plan(const int32_t* topk, const float* gates, int64_
   if (T > 0 && (topk == nullptr || token_rows == nullptr)) return MOE_ERR_NULL;
   if (row_capacity > 0 && row_token == nullptr) return MOE_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return MOE_ERR_ALIGN;
-  if (ws_bytes < moe::plan_workspace_bytes(T, G)) return MOE_ERR_WORKSPACE;
-  moe::PlanArgs a{topk,         gates,        static_cast<int>(T), k,         E,
-                  expert_rank,  G,            ranks_per_node,      src_offsets, row_capacity,
-                  send_counts,  send_offsets, row_token,           row_weight, token_rows,
-                  slot_row,     counters,     d_err,               ws};
-  return moe::launch_plan(a, static_cast<hipStream_t>(stream));
+  if (ws_bytes < plan_workspace_bytes(T, G)) return MOE_ERR_WORKSPACE;
+  PlanArgs a{topk,         gates,        static_cast<int>(T), k,         E,
+             expert_rank,  G,            ranks_per_node,      src_offsets, row_capacity,
+             send_counts,  send_offsets, row_token,           row_weight, token_rows,
+             slot_row,     counters,     d_err,               ws};
+  a.perm = perm;
+  a.topk_out = topk_out;
+  a.gates_out = gates_out;
+  return launch_plan(a, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_dispatch_plan(const int32_t* topk, const float* gates, int64_t T, int k, int E,
+                                 const int32_t* expert_rank, int G, int ranks_per_node,
+                                 const int32_t* src_offsets, int64_t row_capacity,
+                                 int32_t* send_counts, int32_t* send_offsets, int32_t* row_token,
+                                 float* row_weight, int32_t* token_rows, int32_t* slot_row,
+                                 int64_t* counters, int32_t* d_err, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  return moe::plan_entry(topk, gates, nullptr, T, k, E, expert_rank, G, ranks_per_node,
+                         src_offsets, row_capacity, send_counts, send_offsets, row_token,
+                         row_weight, token_rows, slot_row, counters, nullptr, nullptr, d_err, ws,
+                         ws_bytes, stream);
+}
+
+extern "C" int moe_dispatch_plan_gathered(
+    const int32_t* topk, const float* gates, const int32_t* perm, int64_t T, int k, int E,
+    const int32_t* expert_rank, int G, int ranks_per_node, const int32_t* src_offsets,
+    int64_t row_capacity, int32_t* send_counts, int32_t* send_offsets, int32_t* row_token,
+    float* row_weight, int32_t* token_rows, int32_t* slot_row, int64_t* counters,
+    int32_t* topk_out, float* gates_out, int32_t* d_err, void* ws, size_t ws_bytes,
+    void* stream) {
+  if (T > 0 && (perm == nullptr || topk_out == nullptr || (gates != nullptr && gates_out == nullptr)))
+    return MOE_ERR_NULL;
+  if (T > 0 && (topk_out == topk || (gates_out != nullptr &&
+                                     static_cast<const void*>(gates_out) == gates)))
+    return MOE_ERR_SHAPE;
+  return moe::plan_entry(topk, gates, perm, T, k, E, expert_rank, G, ranks_per_node, src_offsets,
+                         row_capacity, send_counts, send_offsets, row_token, row_weight,
+                         token_rows, slot_row, counters, topk_out, gates_out, d_err, ws, ws_bytes,
+                         stream);
 }

@@ -56,6 +56,12 @@ struct PlanArgs {
   // Set when the per-tile counts are already in the workspace (the token
   // shuffle's prediction kernel writes them): the count kernel is skipped.
   bool counts_ready = false;
+  // Optional: plan the batch in the order perm (position p holds token
+  // perm[p] of topk / gates); the count kernel then writes that order's
+  // routing to topk_out / gates_out, which the write kernel reads.
+  const int32_t* perm = nullptr;
+  int32_t* topk_out = nullptr;
+  float* gates_out = nullptr;
 };
 
 // Enqueues the three plan kernels; arguments already validated.

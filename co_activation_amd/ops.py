@@ -118,8 +118,15 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
                   row_capacity: Optional[int] = None, with_weights: bool = True,
                   with_slot_row: bool = True, out: Optional[dict] = None,
                   ws: Optional[torch.Tensor] = None,
-                  d_err: Optional[torch.Tensor] = None) -> Plan:
-    """moe_dispatch_plan.  row_capacity defaults to T * min(k, G)."""
+                  d_err: Optional[torch.Tensor] = None, perm: Optional[torch.Tensor] = None,
+                  topk_out: Optional[torch.Tensor] = None,
+                  gates_out: Optional[torch.Tensor] = None) -> Plan:
+    """moe_dispatch_plan.  row_capacity defaults to T * min(k, G).
+
+    With ``perm`` (moe_dispatch_plan_gathered): the plan of the batch in the
+    order perm, position p holding token perm[p]; the routing in that order
+    is written to ``topk_out`` (and ``gates_out`` when gates are given),
+    which the caller provides."""
     _want(topk, "topk", torch.int32)
     T, k = topk.shape
     E = expert_rank.numel()
@@ -141,11 +148,25 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _want(ws, "ws", torch.uint8)
-    st = _lib.lib().moe_dispatch_plan(
-        _p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node, _p(src_offsets), cap,
-        _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(d_err), _p(ws), ws.numel(),
-        _stream())
-    check("moe_dispatch_plan", st)
+    if perm is None:
+        st = _lib.lib().moe_dispatch_plan(
+            _p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node, _p(src_offsets),
+            cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(d_err), _p(ws),
+            ws.numel(), _stream())
+        check("moe_dispatch_plan", st)
+        return Plan(sc, so, rt, rw, tr, sr, cn)
+    _want(perm, "perm", torch.int32, (T,))
+    if topk_out is None or (gates is not None and gates_out is None):
+        raise ValueError("a gathered plan writes the routing in the new order: give topk_out "
+                         "(and gates_out with gates)")
+    _want(topk_out, "topk_out", torch.int32, (T, k))
+    if gates is not None:
+        _want(gates_out, "gates_out", torch.float32, (T, k))
+    st = _lib.lib().moe_dispatch_plan_gathered(
+        _p(topk), _p(gates), _p(perm), T, k, E, _p(expert_rank), G, ranks_per_node,
+        _p(src_offsets), cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn),
+        _p(topk_out), _p(gates_out), _p(d_err), _p(ws), ws.numel(), _stream())
+    check("moe_dispatch_plan_gathered", st)
     return Plan(sc, so, rt, rw, tr, sr, cn)
 
 

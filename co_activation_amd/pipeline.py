@@ -7,8 +7,9 @@ Two layers with token shuffling (workload 5, "Expert Coupling in MoE
 Pretraining ..." abstract: shuffle each token to the rank predicted to hold
 its next-layer experts), ``TwoLayerStep``:
     stats(topk1, topk2) -> shuffle_predict(topk1, transition, placement2)
-    -> move topk2, gates2 into the new order
-    -> plan(topk2', gates2', placement2, src_offsets = shard_offsets)
+    -> plan(topk2, gates2, placement2, src_offsets = shard_offsets) over the
+       new order, reading the routing through perm and writing it out
+       reordered (moe_dispatch_plan_gathered)
     -> x moved into the new order and dispatched into the layer-2 send rows
        in one pass (shuffle_dispatch; or a gather then a permute)
     -> combine(z)
@@ -17,7 +18,7 @@ Each step splits into ``plan_phase`` (everything that reads only the
 routing), ``dispatch_phase`` and ``combine_phase`` (the row traffic).
 ``run`` runs one step; latency-bound stages that the bandwidth-bound chain
 does not wait for run on a second stream beside it (the statistics of one
-layer; the routing move, layer-2 plan and pair statistics beside the token
+layer; the layer-2 plan and the pair statistics beside the token
 move of the separate-pass two-layer step).  ``run(..., overlap=False)``
 keeps everything on one stream, which is how per-stage times are taken.
 ``Pipeline`` runs a stream of independent batches over a ring of steps,
@@ -356,10 +357,8 @@ class TwoLayerStep:
         self._fork = _Fork(dev)
         self._counts_tmp = torch.empty(E1, dtype=torch.int32, device=dev)
 
-    STAGES_FUSED = ("stats", "shuffle_predict", "shuffle_routing", "plan", "shuffle_dispatch",
-                    "combine")
-    STAGES_SPLIT = ("stats", "shuffle_predict", "shuffle_permute", "shuffle_routing", "plan",
-                    "permute", "combine")
+    STAGES_FUSED = ("stats", "shuffle_predict", "plan", "shuffle_dispatch", "combine")
+    STAGES_SPLIT = ("stats", "shuffle_predict", "shuffle_permute", "plan", "permute", "combine")
 
     @property
     def STAGES(self):
@@ -392,14 +391,8 @@ class TwoLayerStep:
                                                d_err=self.d_err)
         perm = self.shuffle["perm"]
         with fork.fork():
-            with _timed(timers, "shuffle_routing"):
-                ops.gather(self.topk2, perm, out=self.topk2_s, d_err=self.d_err)
-                ops.gather(self.gates2, perm, out=self.gates2_s, d_err=self.d_err)
             with _timed(timers, "plan"):
-                self.plan = ops.dispatch_plan(self.topk2_s, self.gates2_s, self.expert_rank2,
-                                              self.G, self.Rn, self.shuffle["shard_offsets"],
-                                              out=self.plan_out, ws=self.plan_ws,
-                                              d_err=self.d_err)
+                self._plan(perm)
             if overlap:
                 ops.coact_stats(self.topk1, self.E1, out={k: st[k] for k in
                                                           ("expert_count", "pair_count", "ochiai")},
@@ -416,7 +409,7 @@ class TwoLayerStep:
 
     def plan_phase(self, timers: Optional[StageTimers] = None):
         """Everything that reads only the routing: statistics, prediction,
-        the routing move and the layer-2 plan."""
+        and the layer-2 plan over the shuffled order."""
         with _timed(timers, "stats"):
             ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
                             d_err=self.d_err)
@@ -425,15 +418,17 @@ class TwoLayerStep:
                                                self.expert_rank2, self.G, balanced=self.balanced,
                                                out=self.shuffle_out, ws=self.shuffle_ws,
                                                d_err=self.d_err)
-        perm = self.shuffle["perm"]
-        with _timed(timers, "shuffle_routing"):
-            ops.gather(self.topk2, perm, out=self.topk2_s, d_err=self.d_err)
-            ops.gather(self.gates2, perm, out=self.gates2_s, d_err=self.d_err)
         with _timed(timers, "plan"):
-            self.plan = ops.dispatch_plan(self.topk2_s, self.gates2_s, self.expert_rank2, self.G,
-                                          self.Rn, self.shuffle["shard_offsets"],
-                                          out=self.plan_out, ws=self.plan_ws, d_err=self.d_err)
+            self._plan(self.shuffle["perm"])
         return self
+
+    def _plan(self, perm):
+        """The layer-2 plan over the shuffled order, reading the routing
+        through perm and leaving it in that order in topk2_s / gates2_s."""
+        self.plan = ops.dispatch_plan(self.topk2, self.gates2, self.expert_rank2, self.G, self.Rn,
+                                      self.shuffle["shard_offsets"], out=self.plan_out,
+                                      ws=self.plan_ws, d_err=self.d_err, perm=perm,
+                                      topk_out=self.topk2_s, gates_out=self.gates2_s)
 
     def dispatch_phase(self, timers: Optional[StageTimers] = None):
         """The token rows moved to their shuffled places and dispatched into
@@ -465,9 +460,8 @@ class TwoLayerStep:
         return self.combine_phase(timers)
 
     def _run_fused(self, timers):
-        """One stream: statistics, prediction, the routing move and the
-        layer-2 plan, then the token rows moved and dispatched in one pass,
-        then the combine."""
+        """One stream: statistics, prediction and the layer-2 plan, then the
+        token rows moved and dispatched in one pass, then the combine."""
         self.plan_phase(timers)
         return self.move_phase(timers)
 

@@ -165,6 +165,36 @@ int moe_dispatch_plan(const int32_t* topk, const float* gates, int64_t T, int k,
                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_dispatch_plan_gathered -- the plan of a shuffled batch.
+ *
+ * [EC] abstract: tokens are shuffled to the rank predicted to hold their
+ * next-layer experts, and the next layer's dispatch starts from there.  This
+ * is moe_dispatch_plan on the routing in the shuffled order -- position p
+ * holds token perm[p], i.e. topk'[p] = topk[perm[p]], gates'[p] =
+ * gates[perm[p]] -- and writes that gathered routing out as well, so the
+ * routing needs no separate move.  Every plan output is indexed by position,
+ * exactly as moe_dispatch_plan(topk', gates', ...) would give it.
+ *
+ *   topk, gates     [T*k] in the original token order (gates may be NULL)
+ *   perm            [T] int32: the token at each position (moe_shuffle_predict's
+ *                   perm); entries outside [0, T) set ROW_RANGE and that
+ *                   position plans no rows (its topk_out row is -1)
+ *   topk_out        [T*k] int32 out: topk'; gates_out [T*k] float out: gates'
+ *                   (required when gates is given); neither may alias its input
+ *   everything else as for moe_dispatch_plan (src_offsets by position, e.g.
+ *   the shuffle's shard_offsets; same workspace size).
+ * d_err bits: as moe_dispatch_plan, plus ROW_RANGE for perm.
+ * ---------------------------------------------------------------------- */
+int moe_dispatch_plan_gathered(const int32_t* topk, const float* gates, const int32_t* perm,
+                               int64_t T, int k, int E, const int32_t* expert_rank, int G,
+                               int ranks_per_node, const int32_t* src_offsets,
+                               int64_t row_capacity, int32_t* send_counts,
+                               int32_t* send_offsets, int32_t* row_token, float* row_weight,
+                               int32_t* token_rows, int32_t* slot_row, int64_t* counters,
+                               int32_t* topk_out, float* gates_out, int32_t* d_err, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_permute -- row scatter into send buffers (the dispatched hidden
  * states of [CE] footnote 3; also the token shuffle of [EC] abstract).
  *

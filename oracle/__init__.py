@@ -14,6 +14,7 @@ from .coact import (  # noqa: F401
     coact_stats,
     ochiai,
     dispatch_plan,
+    dispatch_plan_gathered,
     permute_rows,
     scatter_rows,
     combine,

@@ -410,6 +410,24 @@ def shuffle_predict(topk: np.ndarray, transition: np.ndarray, expert_rank_next: 
             "shard_offsets": shard_offsets, "rank_score": M}
 
 
+def dispatch_plan_gathered(topk: np.ndarray, gates: Optional[np.ndarray], perm: np.ndarray,
+                           expert_rank: np.ndarray, G: int, ranks_per_node: int,
+                           src_offsets=None) -> dict:
+    """The plan of a shuffled batch ([EC] abstract: tokens move to the rank
+    predicted for their next-layer experts, and that layer dispatches from
+    there): position p holds token perm[p], so the routing in the new order
+    is topk[perm], gates[perm], and the plan is dispatch_plan on it.  Returns
+    the plan with the gathered routing under "topk_out" / "gates_out"."""
+    perm = np.asarray(perm, dtype=np.int64)
+    topk_s = np.asarray(topk)[perm]
+    gates_s = None if gates is None else np.asarray(gates)[perm]
+    out = dict(dispatch_plan(topk_s, gates_s, expert_rank, G, ranks_per_node,
+                             src_offsets=src_offsets))
+    out["topk_out"] = topk_s
+    out["gates_out"] = gates_s
+    return out
+
+
 def two_layer_pipeline(topk1: np.ndarray, topk2: np.ndarray, gates2: np.ndarray,
                        x: np.ndarray, expert_rank2: np.ndarray, E: int, E2: int,
                        G: int, ranks_per_node: int) -> dict:

@@ -84,6 +84,28 @@ def test_plan_rejects(built_lib):
     assert _plan(L, wsb=16) == -5        # workspace too small
 
 
+def test_gathered_plan_rejects(built_lib):
+    L = built_lib
+    f = L.moe_dispatch_plan_gathered
+    # topk, gates, perm, T, k, E, er, G, Rn, src, cap, sc, so, rt, rw, tr, sr, cn,
+    # topk_out, gates_out, d_err, ws, ws_bytes, stream
+    base = [FAKE, FAKE, FAKE, 64, 2, 8, FAKE, 4, 4, NULL, 128, FAKE, FAKE, FAKE, FAKE, FAKE, NULL,
+            FAKE, FAKE + 4096, FAKE + 8192, NULL, FAKE, 1 << 20, NULL]
+    def call(**kw):
+        a = list(base)
+        idx = {"perm": 2, "T": 3, "k": 4, "topk_out": 18, "gates_out": 19, "ws_bytes": 22}
+        for key, v in kw.items():
+            a[idx[key]] = v
+        return f(*a)
+    assert call(perm=NULL) == -1                  # no order
+    assert call(topk_out=NULL) == -1              # nowhere to put the routing
+    assert call(gates_out=NULL) == -1             # gates given, no gates_out
+    assert call(topk_out=FAKE) == -2              # in place
+    assert call(gates_out=FAKE) == -2             # in place
+    assert call(k=9) == -2
+    assert call(ws_bytes=16) == -5
+
+
 def test_permute_combine_shuffle_reject(built_lib):
     L = built_lib
     assert L.moe_permute(FAKE, 8, 0, FAKE, 1, FAKE, 8, NULL, NULL, NULL) == -2

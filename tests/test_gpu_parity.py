@@ -469,6 +469,54 @@ def test_combine_special_values(yd):
         assert ((d <= 1) | (dev_err <= 1e-5 * scale)).all()
 
 
+@pytest.mark.parametrize("cfg,T", [(5, 4096), (3, 2560), (4, 1313)])
+def test_gathered_plan_parity(cfg, T):
+    """moe_dispatch_plan_gathered against the oracle: random orders, shards
+    of uneven length (as a shuffle leaves them, some empty), ragged tiles;
+    every plan output and the gathered routing bit for bit.  Then a position
+    whose perm entry is out of range: ROW_RANGE, no rows for it, and every
+    other position planned as before."""
+    w = make(cfg, T=T, H=64)
+    rng = np.random.default_rng(cfg * 1000 + T)
+    G = w.G
+    cuts = np.sort(rng.integers(0, T + 1, size=G - 1))
+    cuts[: G // 4] = 0
+    src = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+    perm = rng.permutation(T).astype(np.int32)
+    say("gathered plan", cfg, T)
+    err = _err()
+    topk_out = torch.empty(T, w.k, dtype=torch.int32, device="cuda")
+    gates_out = torch.empty(T, w.k, dtype=torch.float32, device="cuda")
+    plan = ops.dispatch_plan(i32(w.topk), dev(w.gates), i32(w.expert_rank), G, w.ranks_per_node,
+                             i32(src), d_err=err, perm=i32(perm), topk_out=topk_out,
+                             gates_out=gates_out)
+    _no_errors(err)
+    ref = oracle.dispatch_plan_gathered(w.topk, w.gates, perm, w.expert_rank, G,
+                                        w.ranks_per_node, src_offsets=src)
+    N = int(ref["N"])
+    assert_equal(host(topk_out), ref["topk_out"], "topk_out")
+    assert_equal(host(gates_out).view(np.uint32), ref["gates_out"].view(np.uint32), "gates_out")
+    assert_equal(host(plan.counters), ref["counters"], "counters")
+    assert_equal(host(plan.send_offsets), ref["send_offsets"], "send_offsets")
+    assert_equal(host(plan.row_token)[:N], ref["row_token"], "row_token")
+    assert_equal(host(plan.row_weight)[:N].view(np.uint32), ref["row_weight"].view(np.uint32),
+                 "row_weight")
+    assert_equal(host(plan.token_rows), ref["token_rows"], "token_rows")
+    assert_equal(host(plan.slot_row), ref["slot_row"], "slot_row")
+    # one out-of-range entry
+    bad = perm.copy()
+    bad[T // 2] = T + 5
+    err2 = _err()
+    ops.dispatch_plan(i32(w.topk), dev(w.gates), i32(w.expert_rank), G, w.ranks_per_node,
+                      i32(src), d_err=err2, perm=i32(bad), topk_out=topk_out, gates_out=gates_out)
+    torch.cuda.synchronize()
+    assert int(err2.item()) == 32
+    got_tr = host(topk_out)
+    assert (got_tr[T // 2] == -1).all()
+    keep = np.arange(T) != T // 2
+    assert_equal(got_tr[keep], w.topk[bad[keep]], "topk_out around the bad entry")
+
+
 def test_combine_of_permute_is_identity():
     """permute then weighted combine returns x bit-exact in bf16 (gates sum
     to 1 within 2^-10), and the unweighted combine gives |R_t| * x exactly."""

@@ -791,3 +791,33 @@ def test_balanced_shuffle_local_share():
                              src_offsets=sh["shard_offsets"])
     share = p["counters"][3] / (w.T * w.k)
     assert share > 0.125 + 0.05
+
+
+def test_gathered_plan_pins():
+    """The plan of a shuffled batch: the identity order gives the plain plan;
+    reversing two tokens on two ranks gives the hand-worked reversed rows;
+    and the gathered routing is exactly the rows of topk in perm's order."""
+    rng = np.random.default_rng(77)
+    T, E, k, G = 96, 8, 2, 4
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    gates = rng.random((T, k)).astype(np.float32)
+    er = (np.arange(E) // 2).astype(np.int32)
+    ident = oracle.dispatch_plan_gathered(topk, gates, np.arange(T), er, G, G)
+    plain = oracle.dispatch_plan(topk, gates, er, G, G)
+    for key in ("row_token", "token_rows", "slot_row", "send_offsets", "counters"):
+        assert np.array_equal(ident[key], plain[key]), key
+    assert np.array_equal(ident["row_weight"].view(np.uint32), plain["row_weight"].view(np.uint32))
+    # hand case: token 0 -> experts {0} (rank 0), token 1 -> experts {2} (rank 1); one source
+    # rank; perm = [1, 0] puts token 1 first, so rank 0's single row carries position 1
+    t2 = np.array([[0], [2]], np.int32)
+    g2 = np.array([[0.25], [0.75]], np.float32)
+    er2 = np.array([0, 0, 1, 1], np.int32)
+    hp = oracle.dispatch_plan_gathered(t2, g2, np.array([1, 0]), er2, 2, 2,
+                                       src_offsets=np.array([0, 2, 2]))
+    assert hp["topk_out"].tolist() == [[2], [0]]
+    assert hp["row_token"].tolist() == [1, 0]          # rank 0: position 1; rank 1: position 0
+    assert hp["token_rows"].tolist() == [[1], [0]]
+    assert np.allclose(hp["row_weight"], [0.25, 0.75])
+    perm = rng.permutation(T)
+    gp = oracle.dispatch_plan_gathered(topk, gates, perm, er, G, G)
+    assert np.array_equal(gp["topk_out"], topk[perm]) and np.array_equal(gp["gates_out"], gates[perm])
