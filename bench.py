@@ -4,13 +4,16 @@
 One step = one pass of the whole path over one batch:
   workload 5 (default; two MoE layers, T=65536, H=4096 bf16, E=64, k=2, G=8):
     layer-1 co-activation stats (+ transitions) -> shuffle prediction ->
-    shuffle of x / layer-2 routing -> layer-2 dedup plan -> permute -> combine
+    layer-2 dedup plan over the shuffled order -> the token rows moved to
+    their shuffled places and into the layer-2 send rows in one pass ->
+    combine
   workloads 1-4: stats -> plan -> permute -> combine of one layer.
 Inputs are seeded synthetic routings already resident in HBM when timing
-starts.  The timed region runs K batches with two in flight: each batch's
+starts.  The timed region runs K batches (default 200, so that filling the
+pipeline costs about 1 us per batch) with two in flight: each batch's
 routing-only phase (statistics, prediction, plan) runs on a second stream
-beside the previous batch's combine; the same K batches run one after
-another are reported beside it.  Prints ONE JSON line.  The metric is
+beside the previous batch's combine (workload 5) or its whole move (k >= 6);
+the same K batches run one after another are reported beside it.  Prints ONE JSON line.  The metric is
 dispatched rows per second of the whole step; permute+combine HBM GB/s and
 the dominant kernel's roofline fraction ride along, with the CPU oracle timed
 on a bounded sample.
@@ -32,7 +35,7 @@ HBM_PEAK_GBS = 8000.0
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--placement", default="main", choices=["main", "alt"])
