@@ -1,10 +1,10 @@
 """torch-facing wrappers of the C ABI (argument marshalling only).
 
 Every function takes device tensors, checks dtype / contiguity / device /
-shape, passes raw pointers and ``torch.cuda.current_stream()`` to the
-library, and returns the output tensors.  All compute happens in the HIP
-kernels; outputs may be preallocated through ``out=`` to keep allocations out
-of a timed loop.  Device-side data errors are OR-ed into ``d_err`` (an int32
+shape, passes raw pointers and ``torch.cuda.current_stream()`` (which must
+be on the tensors' device) to the library, and returns the output tensors.
+All compute happens in the HIP kernels; outputs may be preallocated through
+``out=`` to keep allocations out of a timed loop.  Device-side data errors are OR-ed into ``d_err`` (an int32
 tensor of one element); ``raise_on_errors`` reads it back.
 """
 
@@ -22,8 +22,15 @@ from ._lib import MOE_BF16, MOE_F32, check
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 
 
-def _stream() -> int:
-    return torch.cuda.current_stream().cuda_stream
+def _stream(ref: torch.Tensor) -> int:
+    """The current stream, which must belong to the device holding ``ref``:
+    the kernels run on the stream's device and would otherwise be handed
+    another device's pointers."""
+    s = torch.cuda.current_stream()
+    if ref.device != s.device:
+        raise ValueError(f"tensors are on {ref.device} but the current device is {s.device}; "
+                         "call under torch.cuda.device(...)")
+    return s.cuda_stream
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -89,7 +96,7 @@ def coact_stats(topk: torch.Tensor, E: int, topk_next: Optional[torch.Tensor] = 
     st = _lib.lib().moe_coact_stats(
         _p(topk), T, k, E, _p(topk_next), k2, E_next or 0, _p(res["expert_count"]),
         _p(res.get("pair_count")), _p(res.get("ochiai")), _p(res.get("transition")), _p(d_err),
-        _stream())
+        _stream(topk))
     check("moe_coact_stats", st)
     return res
 
@@ -152,7 +159,7 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
         st = _lib.lib().moe_dispatch_plan(
             _p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node, _p(src_offsets),
             cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(d_err), _p(ws),
-            ws.numel(), _stream())
+            ws.numel(), _stream(topk))
         check("moe_dispatch_plan", st)
         return Plan(sc, so, rt, rw, tr, sr, cn)
     _want(perm, "perm", torch.int32, (T,))
@@ -165,7 +172,7 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
     st = _lib.lib().moe_dispatch_plan_gathered(
         _p(topk), _p(gates), _p(perm), T, k, E, _p(expert_rank), G, ranks_per_node,
         _p(src_offsets), cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn),
-        _p(topk_out), _p(gates_out), _p(d_err), _p(ws), ws.numel(), _stream())
+        _p(topk_out), _p(gates_out), _p(d_err), _p(ws), ws.numel(), _stream(topk))
     check("moe_dispatch_plan_gathered", st)
     return Plan(sc, so, rt, rw, tr, sr, cn)
 
@@ -194,7 +201,7 @@ def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
     st = _lib.lib().moe_permute(_p(x), T, row_bytes, _p(dest), width, _p(out), out_rows,
-                                _p(n_valid), _p(d_err), _stream())
+                                _p(n_valid), _p(d_err), _stream(x))
     check("moe_permute", st)
     return out
 
@@ -224,7 +231,7 @@ def shuffle_dispatch(x: torch.Tensor, perm: torch.Tensor, token_rows: torch.Tens
     if x_out.shape != x.shape or tuple(send.shape[1:]) != row_shape or send.shape[0] < send_rows:
         raise ValueError("x_out must match x; send needs send_rows rows shaped like x's rows")
     st = _lib.lib().moe_shuffle_dispatch(_p(x), T, row_bytes, _p(perm), _p(token_rows), k,
-                                         _p(x_out), _p(send), send_rows, _p(d_err), _stream())
+                                         _p(x_out), _p(send), send_rows, _p(d_err), _stream(x))
     check("moe_shuffle_dispatch", st)
     return x_out, send
 
@@ -249,7 +256,7 @@ def gather(x: torch.Tensor, src: torch.Tensor, *, out: Optional[torch.Tensor] = 
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
     st = _lib.lib().moe_gather(_p(x), x.shape[0], row_bytes, _p(src), n, _p(out), _p(n_valid),
-                               _p(d_err), _stream())
+                               _p(d_err), _stream(x))
     check("moe_gather", st)
     return out
 
@@ -276,7 +283,7 @@ def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tens
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
     st = _lib.lib().moe_combine(_p(z), _DT[z.dtype], z.shape[0], H, _p(rows), k, _p(row_weight),
-                                T, _p(out), _DT[out_dtype], _p(n_valid), _p(d_err), _stream())
+                                T, _p(out), _DT[out_dtype], _p(n_valid), _p(d_err), _stream(z))
     check("moe_combine", st)
     return out
 
@@ -315,7 +322,7 @@ def shuffle_predict(topk: torch.Tensor, transition: torch.Tensor, expert_rank_ne
     fn = _lib.lib().moe_shuffle_balanced if balanced else _lib.lib().moe_shuffle_predict
     st = fn(_p(topk), T, k, E, _p(transition), E2, _p(expert_rank_next), G, _p(res["pred_rank"]),
             _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(d_err), _p(ws),
-            ws.numel(), _stream())
+            ws.numel(), _stream(topk))
     check("moe_shuffle_balanced" if balanced else "moe_shuffle_predict", st)
     return res
 
@@ -362,7 +369,7 @@ def expert_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank: 
         _p(topk), _p(gates), T, k, E, _p(expert_rank), G, _p(slot_row), send_rows, _p(res["erow"]),
         _p(res["expert_first"]), _p(res["expert_count"]), _p(res["rank_offsets"]),
         _p(res["erow_weight"]), _p(res["erow_slot"]), _p(res["erow_src"]), _p(res["row_dest"]),
-        _p(d_err), _p(ws), ws.numel(), _stream())
+        _p(d_err), _p(ws), ws.numel(), _stream(topk))
     check("moe_expert_plan", st)
     return res
 
@@ -391,7 +398,7 @@ def permute_scaled(x: torch.Tensor, dest: torch.Tensor, scale: torch.Tensor, out
         _want(n_valid, "n_valid", torch.int32)
     st = _lib.lib().moe_permute_scaled(_p(x), _DT[x.dtype], T, H, _p(dest), width, _p(scale),
                                        _p(out), _DT[out_dtype], out_rows, _p(n_valid), _p(d_err),
-                                       _stream())
+                                       _stream(x))
     check("moe_permute_scaled", st)
     return out
 
@@ -415,7 +422,7 @@ def row_dot(a: torch.Tensor, b: torch.Tensor, rows: torch.Tensor, *,
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
     st = _lib.lib().moe_row_dot(_p(a), _DT[a.dtype], T, H, _p(b), _DT[b.dtype], b.shape[0],
-                                _p(rows), width, _p(out), _p(n_valid), _p(d_err), _stream())
+                                _p(rows), width, _p(out), _p(n_valid), _p(d_err), _stream(a))
     check("moe_row_dot", st)
     return out
 
@@ -429,7 +436,7 @@ def ema_update(state: torch.Tensor, x: torch.Tensor, beta: float) -> torch.Tenso
     if state.numel() != x.numel():
         raise ValueError("state and x must have the same size")
     check("moe_ema_update", _lib.lib().moe_ema_update(_p(state), _p(x), state.numel(), float(beta),
-                                                      _stream()))
+                                                      _stream(state)))
     return state
 
 

@@ -176,3 +176,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_binding_rejects_a_stream_of_another_device(monkeypatch):
+    """The binding hands the kernels the current stream; tensors on another
+    device than that stream's are refused before any call."""
+    import types
+
+    import torch
+
+    from co_activation_amd import ops
+
+    cur = types.SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=0x1234)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda *a, **kw: cur)
+    assert ops._stream(types.SimpleNamespace(device=torch.device("cuda", 1))) == 0x1234
+    with pytest.raises(ValueError, match="current device"):
+        ops._stream(types.SimpleNamespace(device=torch.device("cuda", 0)))

@@ -517,6 +517,29 @@ def test_gathered_plan_parity(cfg, T):
     assert_equal(got_tr[keep], w.topk[bad[keep]], "topk_out around the bad entry")
 
 
+def test_gathered_plan_without_gates():
+    """A gathered plan with no gates (an unweighted dispatch): the routing
+    alone is gathered, row weights are 0, and everything else matches the
+    oracle bit for bit; equal shards (src_offsets NULL), a ragged last tile."""
+    w = make(3, T=32 * 37, H=64)
+    T, G = w.T, w.G
+    perm = np.random.default_rng(5).permutation(T).astype(np.int32)
+    say("gathered plan without gates", T, G)
+    err = _err()
+    topk_out = torch.empty(T, w.k, dtype=torch.int32, device="cuda")
+    plan = ops.dispatch_plan(i32(w.topk), None, i32(w.expert_rank), G, w.ranks_per_node,
+                             d_err=err, perm=i32(perm), topk_out=topk_out)
+    _no_errors(err)
+    ref = oracle.dispatch_plan_gathered(w.topk, None, perm, w.expert_rank, G, w.ranks_per_node)
+    N = int(ref["N"])
+    assert_equal(host(topk_out), ref["topk_out"], "topk_out")
+    assert_equal(host(plan.counters), ref["counters"], "counters")
+    assert_equal(host(plan.row_token)[:N], ref["row_token"], "row_token")
+    assert (host(plan.row_weight)[:N] == 0).all()
+    assert_equal(host(plan.token_rows), ref["token_rows"], "token_rows")
+    assert_equal(host(plan.slot_row), ref["slot_row"], "slot_row")
+
+
 def test_combine_of_permute_is_identity():
     """permute then weighted combine returns x bit-exact in bf16 (gates sum
     to 1 within 2^-10), and the unweighted combine gives |R_t| * x exactly."""
