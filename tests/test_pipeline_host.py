@@ -73,6 +73,8 @@ class _Rec:
 
 
 class _FakeStep:
+    DISPATCH_LAST = "dispatch"
+
     def __init__(self, rec, name, beside):
         self.rec, self.name, self.plan_beside = rec, name, beside
         self.d_err = torch.zeros(1, dtype=torch.int32)
@@ -82,7 +84,8 @@ class _FakeStep:
         self.rec.enqueue(("plan", self.batch, self.name))
 
     def dispatch_phase(self, timers=None):
-        self.rec.enqueue(("dispatch", self.batch, self.name))
+        with pl._timed(timers, "dispatch"):
+            self.rec.enqueue(("dispatch", self.batch, self.name))
 
     def combine_phase(self, timers=None):
         self.rec.enqueue(("combine", self.batch, self.name))
@@ -98,9 +101,10 @@ def rec(monkeypatch):
     return r
 
 
-def _run(rec, m, beside, calls):
+def _run(rec, m, beside, calls, timed=False):
     steps = [_FakeStep(rec, f"s{j}", beside) for j in range(m)]
     pipe = pl.Pipeline(steps)
+    timers = pl.StageTimers(("dispatch",), sum(calls)) if timed else None
     assert pipe.beside == beside
     rec.enqueue(("inputs", -1, "caller"))
     batch = 0
@@ -114,10 +118,10 @@ def _run(rec, m, beside, calls):
         def collect(st, i, first=first):
             rec.enqueue(("collect", first + i, st.name))
 
-        pipe.run(n, prepare=prepare, collect=collect)
+        pipe.run(n, timers, prepare=prepare, collect=collect)
         batch += n
     rec.enqueue(("after", -1, "caller"))
-    return steps, batch
+    return steps, batch, pipe
 
 
 def _op(rec, kind, b):
@@ -127,8 +131,13 @@ def _op(rec, kind, b):
 @pytest.mark.parametrize("beside", ["combine", "move"])
 @pytest.mark.parametrize("m", [2, 3])
 @pytest.mark.parametrize("calls", [(7,), (3, 4), (1, 1, 5)])
-def test_pipeline_orders_every_dependency(rec, beside, m, calls):
-    steps, n = _run(rec, m, beside, calls)
+@pytest.mark.parametrize("timed", [False, True])
+def test_pipeline_orders_every_dependency(rec, beside, m, calls, timed):
+    """With the dispatch timed, the side stream waits on the timer's end
+    event instead of a record of the pipeline's own: same ordering."""
+    steps, n, pipe = _run(rec, m, beside, calls, timed)
+    if timed:
+        assert pipe._dispatched.value not in rec.events, "the timer's event was not used"
     hb = rec.hb
     inputs, after = _op(rec, "inputs", -1), _op(rec, "after", -1)
     for b in range(n):
