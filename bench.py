@@ -13,10 +13,11 @@ starts.  The timed region runs K batches (default 200, so that filling the
 pipeline costs about 1 us per batch) with two in flight: each batch's
 routing-only phase (statistics, prediction, plan) runs on a second stream
 beside the previous batch's combine (workload 5) or its whole move (k >= 6);
-the same K batches run one after another are reported beside it.  Prints ONE JSON line.  The metric is
-dispatched rows per second of the whole step; permute+combine HBM GB/s and
-the dominant kernel's roofline fraction ride along, with the CPU oracle timed
-on a bounded sample.
+the same K batches run one after another are reported beside it.  Prints ONE
+JSON line.  Its value is dispatched rows per second of the whole step (every
+stage, batches back to back); permute+combine HBM GB/s with its share of peak
+(the metric's second half) and the dominant kernel's roofline fraction ride
+along, with the CPU oracle timed on a bounded sample.
 """
 
 from __future__ import annotations
@@ -403,7 +404,7 @@ def main() -> int:
     achieved_alone = kernels[dom] / (stage_ms[dom] * 1e-3) / 1e9
 
     line = {
-        "metric": "dispatched rows/s (whole step) and permute+combine HBM GB/s at 1 MI355X",
+        "metric": "dispatched rows/s and permute+combine HBM GB/s (% of peak) at 1 MI355X",
         "value": N / (ms_per_step * 1e-3),
         "unit": "dispatched rows/s",
         "n_gpus": 1,
