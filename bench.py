@@ -227,8 +227,9 @@ def main() -> int:
     args = _args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU "
-                                   "exchange is not part of this build", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the engine models "
+                                   "the expert-parallel group inside one GPU and has no "
+                                   "multi-GPU exchange", "n_gpus": args.gpus}))
         return 2
 
     import numpy as np
