@@ -26,11 +26,12 @@ def _stream(ref: torch.Tensor) -> int:
     """The current stream, which must belong to the device holding ``ref``:
     the kernels run on the stream's device and would otherwise be handed
     another device's pointers."""
-    s = torch.cuda.current_stream()
-    if ref.device != s.device:
-        raise ValueError(f"tensors are on {ref.device} but the current device is {s.device}; "
+    idx = ref.device.index
+    cur = torch.cuda.current_device()
+    if idx != cur:
+        raise ValueError(f"tensors are on {ref.device} but the current device is cuda:{cur}; "
                          "call under torch.cuda.device(...)")
-    return s.cuda_stream
+    return torch.cuda.current_stream(idx).cuda_stream
 
 
 def _p(t: Optional[torch.Tensor]):

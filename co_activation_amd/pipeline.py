@@ -33,6 +33,7 @@ backward steps cover the destination side and the gradients.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from typing import Optional
 
@@ -122,9 +123,7 @@ class _Inline:
     """Stands in for a _Fork when everything stays on the current stream."""
 
     def fork(self):
-        import contextlib
-
-        return contextlib.nullcontext()
+        return _NULL_CTX
 
     def join(self):
         pass
@@ -204,19 +203,28 @@ class StageTimers:
             pass
 
 
+class _Timed:
+    """Records a stage's event pair around a block."""
+
+    __slots__ = ("timers", "name", "pair")
+
+    def __init__(self, timers, name):
+        self.timers, self.name, self.pair = timers, name, None
+
+    def __enter__(self):
+        self.pair = self.timers.begin(self.name)
+
+    def __exit__(self, *exc):
+        self.timers.end(self.name, self.pair)
+
+
+_NULL_CTX = contextlib.nullcontext()
+
+
 def _timed(timers, name):
-    """Records the stage's event pair around a block when timers are given."""
-
-    class _Ctx:
-        def __enter__(self):
-            if timers is not None:
-                self.pair = timers.begin(name)
-
-        def __exit__(self, *exc):
-            if timers is not None:
-                timers.end(name, self.pair)
-
-    return _Ctx()
+    """The stage's event pair around a block when timers are given (the
+    untimed path builds nothing: it runs on every stage of every step)."""
+    return _NULL_CTX if timers is None else _Timed(timers, name)
 
 
 class LayerStep:
@@ -708,7 +716,8 @@ class Pipeline:
             collect=None):
         """Runs ``batches`` batches; returns the step that ran the last one."""
         h = _Hip.get()
-        main = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        main_stream = torch.cuda.current_stream()
+        main = ctypes.c_void_p(main_stream.cuda_stream)
         m = len(self.steps)
         # The first batches of a call wait for everything before the call.
         if h.hipEventRecord(self._start, main) or h.hipStreamWaitEvent(self._side, self._start, 0):
@@ -719,7 +728,11 @@ class Pipeline:
         for i in range(batches):
             j = self._next % m
             st = self.steps[j]
-            with torch.cuda.stream(self.side):
+            # the side stream current for the plan phase (set_stream, not
+            # the stream context manager: a few microseconds of host time
+            # less per batch, which is what paces small layers)
+            torch.cuda.set_stream(self.side)
+            try:
                 if by_combine:
                     # batch i-1 has dispatched: every earlier batch, the last
                     # user of this step's buffers included, has combined
@@ -732,6 +745,8 @@ class Pipeline:
                 if prepare is not None:
                     prepare(st, i)
                 st.plan_phase(timers)
+            finally:
+                torch.cuda.set_stream(main_stream)
             if h.hipEventRecord(self._planned, self._side) or \
                     h.hipStreamWaitEvent(main, self._planned, 0):
                 raise RuntimeError("pipeline: hipEventRecord/hipStreamWaitEvent failed")

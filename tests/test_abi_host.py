@@ -187,8 +187,9 @@ def test_binding_rejects_a_stream_of_another_device(monkeypatch):
 
     from co_activation_amd import ops
 
-    cur = types.SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=0x1234)
-    monkeypatch.setattr(torch.cuda, "current_stream", lambda *a, **kw: cur)
+    streams = {1: types.SimpleNamespace(cuda_stream=0x1234)}
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 1)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda idx=None: streams[idx])
     assert ops._stream(types.SimpleNamespace(device=torch.device("cuda", 1))) == 0x1234
     with pytest.raises(ValueError, match="current device"):
         ops._stream(types.SimpleNamespace(device=torch.device("cuda", 0)))

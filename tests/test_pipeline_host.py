@@ -32,6 +32,9 @@ class _Rec:
     def current_stream(self):
         return type("S", (), {"cuda_stream": self.current})()
 
+    def set_stream(self, s):
+        self.current = s.cuda_stream
+
     @contextlib.contextmanager
     def stream(self, s):
         prev, self.current = self.current, s.cuda_stream
@@ -98,6 +101,7 @@ def rec(monkeypatch):
     monkeypatch.setattr(pl.torch.cuda, "Stream", r.new_stream)
     monkeypatch.setattr(pl.torch.cuda, "current_stream", r.current_stream)
     monkeypatch.setattr(pl.torch.cuda, "stream", r.stream)
+    monkeypatch.setattr(pl.torch.cuda, "set_stream", r.set_stream)
     return r
 
 
