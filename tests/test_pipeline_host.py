@@ -180,3 +180,18 @@ def test_pipeline_rejects_bad_arguments(rec):
     c.d_err = torch.zeros(1, dtype=torch.int32, device="meta")
     with pytest.raises(ValueError):
         pl.Pipeline([a, c])
+
+
+def test_pipeline_restores_the_current_stream_on_error(rec):
+    """A plan phase that raises leaves the caller's stream current."""
+    a, b = _FakeStep(rec, "a", "combine"), _FakeStep(rec, "b", "combine")
+
+    def boom(timers=None):
+        raise RuntimeError("plan failed")
+
+    b.plan_phase = boom
+    pipe = pl.Pipeline([a, b])
+    caller = rec.current
+    with pytest.raises(RuntimeError, match="plan failed"):
+        pipe.run(3)
+    assert rec.current == caller
