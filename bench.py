@@ -200,6 +200,11 @@ def cpu_baseline(w, sample_tokens: int) -> dict:
 
     Ts = max(w.G, (min(sample_tokens, w.T) // w.G) * w.G)
     sl = slice(0, Ts)
+    try:  # keep any BLAS call the oracle makes on one thread, as reported
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except ImportError:
+        limit = None
     t0 = time.perf_counter()
     if w.cfg == 5:
         res = oracle.two_layer_pipeline(w.topk[sl], w.topk2[sl], w.gates2[sl], w.x[sl],
@@ -217,6 +222,8 @@ def cpu_baseline(w, sample_tokens: int) -> dict:
     oracle.combine(Z, w.dtype, plan["slot_row"], gates, w.dtype)
     t2 = time.perf_counter()
     secs = (t_mid - t0) + (t2 - t1)
+    if limit is not None:
+        limit.restore_original_limits()
     return {"value": N / secs, "unit": "dispatched rows/s", "cores": 1, "kind": "oracle",
             "sample": f"first {Ts} of {w.T} tokens of the same workload (full H={w.H}); "
                       f"{N} rows; {secs:.1f} s single-threaded numpy on {_cpu_model()} "
