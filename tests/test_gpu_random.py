@@ -1,7 +1,8 @@
 """Seeded random shapes through every row-level entry point, against the CPU
 oracle: routings of 1-8 experts out of 1-256, placements on 1-64 ranks with
 any node size, uneven (sometimes empty) source shards, token counts from 0 up
-to ten tiles with ragged ends, bf16 and fp32 rows of many widths.  Integer
+to ten tiles with ragged ends, bf16 and fp32 rows of many widths; the next
+layer planned over the shuffled order and dispatched in one pass.  Integer
 results and moved rows are compared bit for bit, the combine to the usual
 bound."""
 
@@ -112,6 +113,31 @@ def test_random_shapes(seed):
     ref_sh = oracle.shuffle_predict(topk, ref_st["transition"], er2, G)
     for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
         assert_equal(host(sh[key]), ref_sh[key], "free " + key)
+    # the next layer planned over the shuffled order (routing read through
+    # perm), and the token rows moved and dispatched in one pass
+    gates2 = rng.random((T, k2)).astype(np.float32)
+    cap2 = max(T * min(k2, G), 1)
+    t2_out = torch.empty((T, k2), dtype=torch.int32, device="cuda")
+    g2_out = torch.empty((T, k2), dtype=torch.float32, device="cuda")
+    plan2 = ops.dispatch_plan(i32(topk2), dev(gates2), i32(er2), G, rn,
+                              src_offsets=sh["shard_offsets"], row_capacity=cap2, d_err=err,
+                              perm=sh["perm"], topk_out=t2_out, gates_out=g2_out)
+    ref2 = oracle.dispatch_plan_gathered(topk2, gates2, ref_sh["perm"], er2, G, rn,
+                                         src_offsets=ref_sh["shard_offsets"])
+    N2 = int(ref2["N"])
+    assert_equal(host(t2_out), ref2["topk_out"], "gathered topk")
+    assert_equal(host(g2_out).view(np.uint32), ref2["gates_out"].view(np.uint32), "gathered gates")
+    assert_equal(host(plan2.counters), ref2["counters"], "gathered counters")
+    assert_equal(host(plan2.row_token)[:N2], ref2["row_token"], "gathered row_token")
+    assert_equal(host(plan2.row_weight)[:N2].view(np.uint32), ref2["row_weight"].view(np.uint32),
+                 "gathered row_weight")
+    assert_equal(host(plan2.token_rows), ref2["token_rows"], "gathered token_rows")
+    if T:
+        x_s, send2 = ops.shuffle_dispatch(xt, sh["perm"], plan2.token_rows, cap2, d_err=err)
+        torch.cuda.synchronize()
+        want_x, want_s = oracle.shuffle_dispatch(x, ref_sh["perm"], ref2["token_rows"], cap2)
+        assert_equal(host(x_s), want_x, "shuffled rows")
+        assert_equal(host(send2)[:N2], want_s[:N2], "shuffle-dispatched send rows")
     if T % G == 0:
         sb = ops.shuffle_predict(i32(topk), st["transition"], i32(er2), G, balanced=True,
                                  d_err=err)
