@@ -1,0 +1,115 @@
+"""The dispatch plan far beyond the benchmark's sizes: 2^25 tokens with k = 8
+on 64 ranks (2^28 slots, up to 2^28 rows; row indices and offsets need 28
+bits).  Too large for the oracle's loops, so the plan is checked against
+properties that fix it completely at any size -- the counters and the
+per-(source, destination) counts from the tokens' destination masks; every
+token's rows in the segments of its source rank and its destination ranks,
+ascending; the tokens of each segment ascending; every slot's row -- and the
+row weights against the definition on a sample of tokens."""
+
+import numpy as np
+import pytest
+import torch
+
+from co_activation_amd import ops
+from gpu_util import host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(built_lib):
+    assert torch.cuda.is_available()
+    return built_lib
+
+
+def test_plan_at_2_pow_28_slots():
+    T, k, E, G, rn = 1 << 25, 8, 256, 64, 8
+    rng = np.random.default_rng(7)
+    # k distinct experts per token: base + j * step (mod E) with an odd step
+    base = rng.integers(0, E, size=T, dtype=np.int32)
+    step = (2 * rng.integers(0, E // 2, size=T, dtype=np.int32) + 1).astype(np.int32)
+    j = np.arange(k, dtype=np.int32)
+    topk = (base[:, None] + step[:, None] * j[None, :]) % E
+    del base, step
+    er = (rng.permutation(E) % G).astype(np.int32)
+    gates = rng.random((T, k), dtype=np.float32)
+    say("plan at 2^28 slots", T, k, G)
+
+    err = ops.new_error_word()
+    plan = ops.dispatch_plan(torch.from_numpy(topk).cuda(), torch.from_numpy(gates).cuda(),
+                             torch.from_numpy(er).cuda(), G, rn, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, ops.decode_errors(int(err.item()))
+
+    # destination masks, sources, counts
+    ranks = er[topk]
+    del topk
+    mask = np.zeros(T, np.uint64)
+    for jj in range(k):
+        mask |= np.left_shift(np.uint64(1), ranks[:, jj].astype(np.uint64))
+    cnt = np.bitwise_count(mask).astype(np.int64)
+    N = int(cnt.sum())
+    src = np.arange(T, dtype=np.int64) // (T // G)
+    bits = np.unpackbits(mask.view(np.uint8).reshape(T, 8), axis=1, bitorder="little")
+    S = bits.reshape(G, T // G, 64).sum(axis=1, dtype=np.int64)
+    recv_max = int(bits.sum(axis=0, dtype=np.int64).max())
+    local_rows = int(bits[np.arange(T), src].sum(dtype=np.int64))
+    del bits
+    nodes = np.zeros(T, np.uint64)
+    for jj in range(k):
+        nodes |= np.left_shift(np.uint64(1), (ranks[:, jj] // rn).astype(np.uint64))
+    node_rows = int(np.bitwise_count(nodes).sum(dtype=np.int64))
+    own = np.left_shift(np.uint64(1), (src // rn).astype(np.uint64))
+    V = int(np.bitwise_count(nodes & ~own).sum(dtype=np.int64))
+    del nodes, own
+    local_assign = int((ranks == src[:, None]).sum(dtype=np.int64))
+    want_counters = np.array([N, T * k, local_rows, local_assign, node_rows, V, recv_max, 0],
+                             np.int64)
+    np.testing.assert_array_equal(host(plan.counters), want_counters, "counters")
+    np.testing.assert_array_equal(host(plan.send_counts), S, "send_counts")
+    offsets = np.concatenate([[0], np.cumsum(S.ravel())])
+    np.testing.assert_array_equal(host(plan.send_offsets), offsets, "send_offsets")
+
+    # every token's rows: a prefix of its k slots, in the segments (s_t, r)
+    # of its destination ranks r in ascending order, each row naming it
+    tr = host(plan.token_rows)
+    valid = tr >= 0
+    assert (valid[:, :-1] >= valid[:, 1:]).all(), "rows not a prefix of the slots"
+    np.testing.assert_array_equal(valid.sum(axis=1), cnt, "rows per token")
+    rows = tr[valid].astype(np.int64)
+    del tr, valid
+    rt = host(plan.row_token)[:N]
+    np.testing.assert_array_equal(rt[rows], np.repeat(np.arange(T, dtype=np.int32), cnt),
+                                  "row_token of each token's rows")
+    sr = np.sort(ranks, axis=1)
+    first = np.ones_like(sr, dtype=bool)
+    first[:, 1:] = sr[:, 1:] != sr[:, :-1]
+    want_seg = np.repeat(src, cnt) * G + sr[first]
+    got_seg = np.searchsorted(offsets, rows, side="right") - 1
+    np.testing.assert_array_equal(got_seg, want_seg, "segment of each row")
+    del sr, first, want_seg, got_seg, rows
+    # tokens ascending inside each segment
+    seg_of_row = np.repeat(np.arange(G * G), S.ravel())
+    same = seg_of_row[1:] == seg_of_row[:-1]
+    assert (np.diff(rt.astype(np.int64))[same] > 0).all(), "tokens out of order in a segment"
+    del seg_of_row, same
+
+    # every slot's row: in segment (s_t, rank of the slot), naming the token
+    sl = host(plan.slot_row).astype(np.int64)
+    np.testing.assert_array_equal(rt[sl], np.broadcast_to(np.arange(T, dtype=np.int32)[:, None],
+                                                          (T, k)), "row_token of slot rows")
+    got = np.searchsorted(offsets, sl.ravel(), side="right") - 1
+    np.testing.assert_array_equal(got, (src[:, None] * G + ranks).ravel(), "segment of slot rows")
+    del got
+
+    # row weights on a sample of tokens: the gates of the token's slots on
+    # that rank, summed in fp32 in slot order
+    rw = host(plan.row_weight)[:N]
+    for t in rng.choice(T, size=2048, replace=False):
+        for jj in range(k):
+            acc = np.float32(0)
+            for i in range(k):
+                if ranks[t, i] == ranks[t, jj]:
+                    acc = np.float32(acc + gates[t, i])
+            assert rw[sl[t, jj]].view(np.uint32) == acc.view(np.uint32), (t, jj)
