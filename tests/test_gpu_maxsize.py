@@ -1,11 +1,15 @@
-"""The dispatch plan far beyond the benchmark's sizes: 2^25 tokens with k = 8
-on 64 ranks (2^28 slots, up to 2^28 rows; row indices and offsets need 28
-bits).  Too large for the oracle's loops, so the plan is checked against
-properties that fix it completely at any size -- the counters and the
-per-(source, destination) counts from the tokens' destination masks; every
-token's rows in the segments of its source rank and its destination ranks,
-ascending; the tokens of each segment ascending; every slot's row -- and the
-row weights against the definition on a sample of tokens."""
+"""Sizes far beyond the benchmark's, too large for the oracle's loops, so
+checked against properties that fix the results at any size.
+
+The plan at 2^25 tokens with k = 8 on 64 ranks (2^28 slots, up to 2^28 rows):
+the counters and the per-(source, destination) counts from the tokens'
+destination masks; every token's rows in the segments of its source rank and
+its destination ranks, ascending; the tokens of each segment ascending; every
+slot's row; the row weights against the definition on a sample of tokens.
+
+Permute and combine with row indices past 2^31 16-byte vectors (a 40 GiB
+send buffer): combine(permute(x)) = x exactly when each token's gates sum to
+one, and sampled send rows equal their tokens' rows."""
 
 import numpy as np
 import pytest
@@ -113,3 +117,40 @@ def test_plan_at_2_pow_28_slots():
                 if ranks[t, i] == ranks[t, jj]:
                     acc = np.float32(acc + gates[t, i])
             assert rw[sl[t, jj]].view(np.uint32) == acc.view(np.uint32), (t, jj)
+
+
+def test_rows_beyond_2_pow_31_vectors():
+    """Permute then combine with row indices past 2^31 16-byte vectors
+    (2.6 M tokens of 8 KiB bf16 rows, a 40 GiB send buffer): every address
+    is formed in 64 bits.  With each token's gates summing to 1 the combine
+    of the permuted rows returns x exactly (fp32 error far below half a bf16
+    ulp), checked on every token; send rows are checked against their tokens'
+    rows on the last 4096 rows and 4096 random ones."""
+    from workloads.gen import device_normal
+
+    T, H, E, k, G, rn = (1 << 21) + (1 << 19), 4096, 64, 2, 8, 8
+    rng = np.random.default_rng(11)
+    base = rng.integers(0, E, size=T, dtype=np.int32)
+    step = 2 * rng.integers(0, E // 2, size=T, dtype=np.int32) + 1
+    topk = np.stack([base, (base + step) % E], axis=1).astype(np.int32)
+    er = (np.arange(E) // (E // G)).astype(np.int32)
+    g = rng.random((T, k), dtype=np.float32) + np.float32(0.1)
+    gates = (g / g.sum(axis=1, keepdims=True)).astype(np.float32)
+    cap = T * min(k, G)
+    say("rows beyond 2^31 vectors", T, H, cap)
+    x = device_normal(T, H, "bf16", seed=3)
+    err = ops.new_error_word()
+    plan = ops.dispatch_plan(torch.from_numpy(topk).cuda(), torch.from_numpy(gates).cuda(),
+                             torch.from_numpy(er).cuda(), G, rn, d_err=err)
+    N = int(plan.counters[0].item())
+    assert N * (H // 8) > (1 << 31) + (1 << 28), "the largest rows must lie past 2^31 vectors"
+    send = ops.permute(x, plan.token_rows, cap, d_err=err)
+    y = ops.combine(send, plan.token_rows, plan.row_weight, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, ops.decode_errors(int(err.item()))
+    assert torch.equal(y.view(torch.int16), x.view(torch.int16)), "combine(permute(x)) != x"
+    del y
+    idx = torch.cat([torch.arange(N - 4096, N, device="cuda"),
+                     torch.randint(0, N, (4096,), device="cuda")])
+    tok = plan.row_token[:N].long()[idx]
+    assert torch.equal(send[idx].view(torch.int16), x[tok].view(torch.int16)), "send rows"
