@@ -9,7 +9,8 @@ slot's row; the row weights against the definition on a sample of tokens.
 
 Permute and combine with row indices past 2^31 16-byte vectors (a 40 GiB
 send buffer): combine(permute(x)) = x exactly when each token's gates sum to
-one, and sampled send rows equal their tokens' rows."""
+one, and sampled send rows equal their tokens' rows; then the one-pass
+shuffle dispatch into the same buffer under a random order."""
 
 import numpy as np
 import pytest
@@ -154,3 +155,18 @@ def test_rows_beyond_2_pow_31_vectors():
                      torch.randint(0, N, (4096,), device="cuda")])
     tok = plan.row_token[:N].long()[idx]
     assert torch.equal(send[idx].view(torch.int16), x[tok].view(torch.int16)), "send rows"
+    # the one-pass shuffle dispatch at the same size, into the same buffer:
+    # x_s[p] = x[perm[p]] everywhere, send[token_rows[p, q]] = x[perm[p]] sampled
+    perm = torch.randperm(T, device="cuda", dtype=torch.int64)
+    x_s, send = ops.shuffle_dispatch(x, perm.int(), plan.token_rows, cap, send=send, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, ops.decode_errors(int(err.item()))
+    assert torch.equal(x_s.view(torch.int16), x[perm].view(torch.int16)), "shuffled rows"
+    del x_s
+    pos = torch.cat([torch.arange(T - 2048, T, device="cuda"),
+                     torch.randint(0, T, (2048,), device="cuda")])
+    tr = plan.token_rows.long()[pos]
+    for q in range(k):
+        ok = tr[:, q] >= 0
+        assert torch.equal(send[tr[ok, q]].view(torch.int16),
+                           x[perm[pos[ok]]].view(torch.int16)), f"shuffle-dispatched rows, slot {q}"
