@@ -35,8 +35,12 @@
  *     long as their buffers differ.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued on it and the call returns without synchronising.
- *   - The return value is a moe_status.  A negative status means the
- *     arguments were rejected on the host and NOTHING was enqueued.
+ *   - The return value is a moe_status.  A negative status other than
+ *     MOE_ERR_HIP means the arguments were rejected on the host and NOTHING
+ *     was enqueued.  MOE_ERR_HIP means the HIP runtime reported an error
+ *     right after one of the call's kernel launches (hipGetLastError, which
+ *     also returns an error an earlier HIP call on this thread left behind);
+ *     kernels of the call launched before it may still run.
  *   - Errors that depend on device data set bits (MOE_DERR_*) in *d_err with
  *     an atomic OR.  d_err is an int32 device word that the caller zeroes;
  *     it may be NULL (then such errors go unreported).  When a bit is set the
