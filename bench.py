@@ -432,10 +432,13 @@ def main() -> int:
         "stage_us_median": {n: 1e3 * v for n, v in stage_ms.items()},
         "stage_us_min": {n: 1e3 * v for n, v in stage_min.items()},
         "stage_us_p90": {n: 1e3 * v for n, v in stage_p90.items()},
+        "stage_gbps": {n: b / (stage_ms[n] * 1e-3) / 1e9
+                       for n, b in ((mv, kernels[mv]), ("combine", bytes_comb))},
         "schedule": ("two batches in flight: each batch's " +
                      ("statistics and plan" if w.cfg != 5 else
                       "statistics, shuffle prediction and layer-2 plan") +
-                     " on a second stream beside the previous batch's combine"),
+                     " on a second stream beside the previous batch's " +
+                     ("combine" if pipe.beside == "combine" else "permute and combine")),
         "counters": {"rows": N, "assignments": int(counters[1]), "local_rows": int(counters[2]),
                      "local_assign": int(counters[3]), "node_rows": int(counters[4]),
                      "cross_node_V": int(counters[5]), "max_recv_rows": int(counters[6])},
