@@ -36,8 +36,9 @@ EXPORTS = (
     "moe_expert_plan_workspace_size", "moe_expert_plan",
     "moe_permute_scaled", "moe_row_dot", "moe_ema_update", "moe_place_experts",
     "moe_shuffle_balanced_workspace_size", "moe_shuffle_balanced", "moe_gather",
-    "moe_shuffle_dispatch", "moe_dispatch_plan_gathered",
+    "moe_shuffle_dispatch", "moe_dispatch_plan_gathered", "moe_dispatch_plan_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 4 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -57,6 +58,9 @@ def _declare(lib: ctypes.CDLL) -> None:
                                                c_int64, P, P, P, P, P, P, P, P, P, P, P,
                                                c_size_t, P]
     lib.moe_dispatch_plan_gathered.restype = c_int
+    lib.moe_dispatch_plan_noalloc.argtypes = [P, P, c_int64, c_int, c_int, P, c_int, c_int, P,
+                                              c_int64, P, P, P, P, P, P, P, P, P]
+    lib.moe_dispatch_plan_noalloc.restype = c_int
     lib.moe_permute.argtypes = [P, c_int64, c_int64, P, c_int, P, c_int64, P, P, P]
     lib.moe_permute.restype = c_int
     lib.moe_gather.argtypes = [P, c_int64, c_int64, P, c_int64, P, P, P, P]

@@ -19,6 +19,8 @@
 //           leaves the prefix inside its (s, r) block.
 //   write : one block per tile; the same ballots give each token's position
 //           inside its wave, LDS gives the wave's offset inside the tile.
+#include <mutex>
+
 #include "plan.hpp"
 
 namespace moe {
@@ -479,22 +481,35 @@ extern "C" int moe_dispatch_plan_workspace_size(int64_t T, int G, size_t* ws_byt
 namespace moe {
 namespace {
 
-int plan_entry(const int32_t* topk, const float* gates, const int32_t* perm, int64_t T, int k,
-               int E, const int32_t* expert_rank, int G, int ranks_per_node,
-               const int32_t* src_offsets, int64_t row_capacity, int32_t* send_counts,
-               int32_t* send_offsets, int32_t* row_token, float* row_weight,
-               int32_t* token_rows, int32_t* slot_row, int64_t* counters, int32_t* topk_out,
-               float* gates_out, int32_t* d_err, void* ws, size_t ws_bytes, void* stream) {
+// Host checks of a plan call's sizes and pointers (the workspace aside).
+int plan_check(const int32_t* topk, int64_t T, int k, int E, const int32_t* expert_rank, int G,
+               int ranks_per_node, const int32_t* src_offsets, int64_t row_capacity,
+               const int32_t* send_counts, const int32_t* send_offsets, const int32_t* row_token,
+               const int32_t* token_rows, const int64_t* counters) {
   if (k < 1 || k > MOE_MAX_K || E < 1 || E > MOE_MAX_E || G < 1 || G > MOE_MAX_G || T < 0 ||
       ranks_per_node < 1 || G % ranks_per_node != 0 || row_capacity < 0 ||
       row_capacity > INT32_MAX || T * static_cast<int64_t>(k) >= (int64_t{1} << 31))
     return MOE_ERR_SHAPE;
   if (src_offsets == nullptr && T % G != 0) return MOE_ERR_SHAPE;
   if (expert_rank == nullptr || send_counts == nullptr || send_offsets == nullptr ||
-      counters == nullptr || ws == nullptr)
+      counters == nullptr)
     return MOE_ERR_NULL;
   if (T > 0 && (topk == nullptr || token_rows == nullptr)) return MOE_ERR_NULL;
   if (row_capacity > 0 && row_token == nullptr) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+int plan_entry(const int32_t* topk, const float* gates, const int32_t* perm, int64_t T, int k,
+               int E, const int32_t* expert_rank, int G, int ranks_per_node,
+               const int32_t* src_offsets, int64_t row_capacity, int32_t* send_counts,
+               int32_t* send_offsets, int32_t* row_token, float* row_weight,
+               int32_t* token_rows, int32_t* slot_row, int64_t* counters, int32_t* topk_out,
+               float* gates_out, int32_t* d_err, void* ws, size_t ws_bytes, void* stream) {
+  const int st = plan_check(topk, T, k, E, expert_rank, G, ranks_per_node, src_offsets,
+                            row_capacity, send_counts, send_offsets, row_token, token_rows,
+                            counters);
+  if (st != MOE_OK) return st;
+  if (ws == nullptr) return MOE_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return MOE_ERR_ALIGN;
   if (ws_bytes < plan_workspace_bytes(T, G)) return MOE_ERR_WORKSPACE;
   PlanArgs a{topk,         gates,        static_cast<int>(T), k,         E,
@@ -521,6 +536,65 @@ extern "C" int moe_dispatch_plan(const int32_t* topk, const float* gates, int64_
                          src_offsets, row_capacity, send_counts, send_offsets, row_token,
                          row_weight, token_rows, slot_row, counters, nullptr, nullptr, d_err, ws,
                          ws_bytes, stream);
+}
+
+// ------------------------------------------------- no-allocation variant
+//
+// The plan's per-tile counts live in a device array of fixed size instead of
+// a caller workspace, for callers that cannot allocate.  Every call on one
+// device shares that device's copy of the array; the count kernel writes
+// every entry the scan and write kernels then read, so nothing needs
+// clearing between calls, but calls that overlap on one device race.
+
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace moe {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The address of the current device's copy of `scratch`, looked up once per
+// device.  (The array's name in host code is only a stand-in; kernels must
+// be given this address.)
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_dispatch_plan_noalloc(const int32_t* topk, const float* gates, int64_t T,
+                                         int k, int E, const int32_t* expert_rank, int G,
+                                         int ranks_per_node, const int32_t* src_offsets,
+                                         int64_t row_capacity, int32_t* send_counts,
+                                         int32_t* send_offsets, int32_t* row_token,
+                                         float* row_weight, int32_t* token_rows,
+                                         int32_t* slot_row, int64_t* counters, int32_t* d_err,
+                                         void* stream) {
+  int st = moe::plan_check(topk, T, k, E, expert_rank, G, ranks_per_node, src_offsets,
+                           row_capacity, send_counts, send_offsets, row_token, token_rows,
+                           counters);
+  if (st != MOE_OK) return st;
+  if (moe::plan_workspace_bytes(T, G) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = moe::device_scratch(&ws);
+  if (st != MOE_OK) return st;
+  return moe::plan_entry(topk, gates, nullptr, T, k, E, expert_rank, G, ranks_per_node,
+                         src_offsets, row_capacity, send_counts, send_offsets, row_token,
+                         row_weight, token_rows, slot_row, counters, nullptr, nullptr, d_err, ws,
+                         MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" int moe_dispatch_plan_gathered(

@@ -178,6 +178,44 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
     return Plan(sc, so, rt, rw, tr, sr, cn)
 
 
+def dispatch_plan_noalloc(topk: torch.Tensor, gates: Optional[torch.Tensor],
+                          expert_rank: torch.Tensor, G: int, ranks_per_node: int,
+                          src_offsets: Optional[torch.Tensor] = None, *, out: dict,
+                          d_err: Optional[torch.Tensor] = None) -> Plan:
+    """moe_dispatch_plan_noalloc: moe_dispatch_plan with the library's fixed
+    device scratch instead of a workspace.  The caller passes every output in
+    ``out`` (keys as ``Plan``'s fields; row_weight and slot_row may be
+    None), so this call allocates nothing.  Calls that overlap on one device
+    race on the shared scratch."""
+    _want(topk, "topk", torch.int32)
+    T, k = topk.shape
+    E = expert_rank.numel()
+    _want(expert_rank, "expert_rank", torch.int32, (E,))
+    if gates is not None:
+        _want(gates, "gates", torch.float32, (T, k))
+    if src_offsets is not None:
+        _want(src_offsets, "src_offsets", torch.int32, (G + 1,))
+    sc = _want(out["send_counts"], "send_counts", torch.int32, (G, G))
+    so = _want(out["send_offsets"], "send_offsets", torch.int32, (G * G + 1,))
+    rt = _want(out["row_token"], "row_token", torch.int32)
+    if rt.dim() != 1:
+        raise ValueError("row_token must be one-dimensional")
+    cap = rt.shape[0]
+    rw = out.get("row_weight")
+    if rw is not None:
+        _want(rw, "row_weight", torch.float32, (cap,))
+    tr = _want(out["token_rows"], "token_rows", torch.int32, (T, k))
+    sr = out.get("slot_row")
+    if sr is not None:
+        _want(sr, "slot_row", torch.int32, (T, k))
+    cn = _want(out["counters"], "counters", torch.int64, (8,))
+    st = _lib.lib().moe_dispatch_plan_noalloc(
+        _p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node, _p(src_offsets), cap,
+        _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(d_err), _stream(topk))
+    check("moe_dispatch_plan_noalloc", st)
+    return Plan(sc, so, rt, rw, tr, sr, cn)
+
+
 # ----------------------------------------------------------------- permute
 
 def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,

@@ -32,7 +32,9 @@
  *   - Pointers are DEVICE pointers unless marked (host).  Every buffer is
  *     owned by the caller; the library allocates nothing and keeps no state
  *     between calls, so calls on different streams may run concurrently as
- *     long as their buffers differ.
+ *     long as their buffers differ.  The one exception is
+ *     moe_dispatch_plan_noalloc, whose scratch is a fixed device array
+ *     shared by all its calls on a device (see there).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued on it and the call returns without synchronising.
  *   - The return value is a moe_status.  A negative status other than
@@ -167,6 +169,33 @@ int moe_dispatch_plan(const int32_t* topk, const float* gates, int64_t T, int k,
                       float* row_weight, int32_t* token_rows, int32_t* slot_row,
                       int64_t* counters, int32_t* d_err, void* ws, size_t ws_bytes,
                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_dispatch_plan_noalloc -- moe_dispatch_plan without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, outputs and d_err bits as moe_dispatch_plan minus ws and
+ * ws_bytes; the results are identical.  The per-tile scratch lives in a
+ * device array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends; the call allocates nothing and
+ * calls no allocating routine.  Its address is looked up once per device on
+ * the first call there, so the calling thread's current device must be the
+ * stream's device.  Every call on one device shares that device's array:
+ * calls whose work overlaps on one device (other streams, other threads)
+ * race and give wrong plans.
+ * Returns MOE_ERR_WORKSPACE (nothing enqueued) when
+ * moe_dispatch_plan_workspace_size(T, G) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ * (e.g. T above about 3.9 million tokens at G = 64), and MOE_ERR_HIP when
+ * the device or the array's address cannot be obtained.
+ * ---------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_dispatch_plan_noalloc(const int32_t* topk, const float* gates, int64_t T, int k, int E,
+                              const int32_t* expert_rank, int G, int ranks_per_node,
+                              const int32_t* src_offsets, int64_t row_capacity,
+                              int32_t* send_counts, int32_t* send_offsets, int32_t* row_token,
+                              float* row_weight, int32_t* token_rows, int32_t* slot_row,
+                              int64_t* counters, int32_t* d_err, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_dispatch_plan_gathered -- the plan of a shuffled batch.

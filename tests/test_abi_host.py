@@ -84,6 +84,31 @@ def test_plan_rejects(built_lib):
     assert _plan(L, wsb=16) == -5        # workspace too small
 
 
+def test_noalloc_plan_rejects(built_lib):
+    """The allocation-free plan checks its arguments like the workspace plan
+    and refuses inputs whose per-tile scratch exceeds its fixed array, all
+    before any HIP call."""
+    L = built_lib
+    f = L.moe_dispatch_plan_noalloc
+
+    def call(T=64, k=2, E=8, G=4, Rn=4, er=FAKE, tr=FAKE, cap=128):
+        return f(FAKE, NULL, T, k, E, er, G, Rn, NULL, cap, FAKE, FAKE, FAKE, NULL, tr, NULL, FAKE,
+                 NULL, NULL)
+    assert call(G=65) == -2
+    assert call(Rn=3) == -2
+    assert call(T=63) == -2
+    assert call(er=NULL) == -1
+    assert call(tr=NULL) == -1
+    limit = _lib.NOALLOC_SCRATCH_BYTES
+    n = ctypes.c_size_t()
+    for T, G in ((3_931_136, 64), (4_000_000, 64), (22_367_488, 8), (22_400_000, 8)):
+        assert L.moe_dispatch_plan_workspace_size(T, G, ctypes.byref(n)) == 0
+        if n.value > limit:
+            assert call(T=T, k=1, E=G, G=G, Rn=G, cap=T) == -5   # beyond the scratch array
+        else:
+            assert T in (3_931_136, 22_367_488)                  # the largest that fit
+
+
 def test_gathered_plan_rejects(built_lib):
     L = built_lib
     f = L.moe_dispatch_plan_gathered
