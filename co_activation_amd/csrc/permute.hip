@@ -98,51 +98,6 @@ __global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void permu
   }
 }
 
-// Fan-out permute (more than two destinations per token): the same copy,
-// launched with at most two resident blocks per CU (see kFanoutLds).  The
-// destination list is loaded without per-entry checks, so its loads issue
-// together; a destination past out_rows is reported and skipped in the copy.
-template <typename V, int TPT, int U>
-__global__ __launch_bounds__(TPT) void permute_fanout_kernel(
-    const V* __restrict__ x, int T, int64_t vec_per_row, const int32_t* __restrict__ dest,
-    int width, V* __restrict__ out, int64_t out_rows, const int32_t* __restrict__ n_valid,
-    int32_t* d_err) {
-  const int t = blockIdx.x;
-  if (t >= T || (n_valid != nullptr && t >= *n_valid)) return;
-  const int l = static_cast<int>(threadIdx.x);
-  int drow[MOE_MAX_K];
-#pragma unroll
-  for (int q = 0; q < MOE_MAX_K; ++q)
-    drow[q] = q < width ? __builtin_amdgcn_readfirstlane(dest[static_cast<int64_t>(t) * width + q])
-                        : -1;
-  int errbits = 0;
-  const V* src = x + static_cast<int64_t>(t) * vec_per_row;
-  for (int64_t c0 = l; c0 < vec_per_row; c0 += TPT * U) {
-    V v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + u * TPT;
-      if (c < vec_per_row) v[u] = load_row<false>(src + c);
-    }
-#pragma unroll
-    for (int q = 0; q < MOE_MAX_K; ++q) {
-      if (q >= width) break;
-      if (drow[q] < 0) continue;
-      if (drow[q] >= out_rows) {
-        errbits = MOE_DERR_ROW_RANGE;
-        continue;
-      }
-      V* dst = out + static_cast<int64_t>(drow[q]) * vec_per_row;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + u * TPT;
-        if (c < vec_per_row) __builtin_nontemporal_store(v[u], dst + c);
-      }
-    }
-  }
-  if (l == 0) report(d_err, errbits);
-}
-
 // Rows narrower than one wave's width of vectors: one thread per
 // (token, vector), so every lane moves data.
 template <typename V>
@@ -168,45 +123,90 @@ __global__ __launch_bounds__(kPermThreads) void permute_flat_kernel(
   report(d_err, errbits);
 }
 
-// Wide rows (more than 512 vectors): a row is split into parts of
-// kSplitVec vectors, and one wave (block) moves one part of one token to
-// every destination; block (t, part) covers [part, part + 1) * kSplitVec.
-// Measured on MI355X for 14 KiB rows with 8 destinations: 5% faster than a
-// 256-thread block per token (two-KiB pieces per wave beat one-KiB pieces
-// and four-KiB blocks); for 8 KiB and narrower rows it was slower.
-constexpr int kSplitVec = 128;
+// Wide rows: a row is cut into parts of kPartVec vectors (2 KiB of 16-byte
+// vectors) and one block of kPartVec threads (two waves, one vector per
+// lane) moves one part of one position's row: block b takes position
+// b / parts, part b % parts.  The position is the token itself (permute) or
+// shuffled position p holding token perm[p], whose row also goes to x_out[p]
+// (the shuffle dispatch).  The row piece is loaded once and stored to every
+// destination with nontemporal 16-byte stores.
+//
+// How many such blocks a CU holds at once sets how many write streams are
+// open, and HBM absorbs the scattered writes best with about 96 of them per
+// CU (waves times the places each row goes).  Blocks therefore reserve LDS
+// they do not use so that a CU holds about 48 / writes of them (see
+// parts_lds_bytes).  Measured on MI355X (stage medians of the benchmark
+// step, cold caches): 14 KiB rows to up to 8 ranks 686 -> 646 us against a
+// wave per 2 KiB part with no cap; 8 KiB rows to up to 6 ranks 507 -> 499 us
+// against 256-thread blocks per token capped at two per CU; the fused
+// shuffle dispatch of 8 KiB rows with up to 2 ranks 351 us, as with 512
+// threads per position.  Other part sizes (1-16 KiB) and caps were slower.
+constexpr int kPartWaves = 2;
+constexpr int kPartVec = kPartWaves * kWave;
+constexpr unsigned kLdsPerCu = 160 * 1024;
 
-template <typename V>
-__global__ __launch_bounds__(kWave) void permute_split_kernel(
+// LDS reserved per block so that a CU holds about 48 / writes part blocks;
+// none once that reaches the CU's 16 two-wave blocks.
+inline unsigned parts_lds_bytes(int writes) {
+  const int blocks = 48 / (writes < 1 ? 1 : writes);
+  if (blocks >= 16) return 0;
+  return (kLdsPerCu / static_cast<unsigned>(blocks < 2 ? 2 : blocks)) & ~1023u;
+}
+
+template <typename V, bool SHUFFLE>
+__global__ __launch_bounds__(kPartVec) void permute_parts_kernel(
     const V* __restrict__ x, int T, int64_t vec_per_row, int parts,
-    const int32_t* __restrict__ dest, int width, V* __restrict__ out, int64_t out_rows,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ dest, int width,
+    V* __restrict__ x_out, V* __restrict__ out, int64_t out_rows,
     const int32_t* __restrict__ n_valid, int32_t* d_err) {
-  const int t = static_cast<int>(blockIdx.x / parts);
-  const int part = static_cast<int>(blockIdx.x % parts);
-  if (t >= T || (n_valid != nullptr && t >= *n_valid)) return;
-  const int64_t c_lo = static_cast<int64_t>(part) * kSplitVec;
-  const int64_t c_hi = c_lo + kSplitVec < vec_per_row ? c_lo + kSplitVec : vec_per_row;
+  const int p = static_cast<int>(blockIdx.x / static_cast<unsigned>(parts));
+  const int part = static_cast<int>(blockIdx.x - static_cast<unsigned>(p) * parts);
+  if (p >= T || (n_valid != nullptr && p >= *n_valid)) return;
+  int t = p;
+  if constexpr (SHUFFLE) {
+    t = __builtin_amdgcn_readfirstlane(perm[p]);
+    if (t < 0 || t >= T) {
+      if (threadIdx.x == 0 && part == 0) report(d_err, MOE_DERR_ROW_RANGE);
+      return;
+    }
+  }
   int drow[MOE_MAX_K];
 #pragma unroll
   for (int q = 0; q < MOE_MAX_K; ++q)
-    drow[q] = q < width ? __builtin_amdgcn_readfirstlane(dest[static_cast<int64_t>(t) * width + q])
+    drow[q] = q < width ? __builtin_amdgcn_readfirstlane(dest[static_cast<int64_t>(p) * width + q])
                         : -1;
+  const int64_t c = static_cast<int64_t>(part) * kPartVec + threadIdx.x;
+  if (c >= vec_per_row) return;
+  const V v = load_row<false>(x + static_cast<int64_t>(t) * vec_per_row + c);
+  if constexpr (SHUFFLE)
+    __builtin_nontemporal_store(v, x_out + static_cast<int64_t>(p) * vec_per_row + c);
   int errbits = 0;
-  const V* src = x + static_cast<int64_t>(t) * vec_per_row;
-  for (int64_t c = c_lo + threadIdx.x; c < c_hi; c += kWave) {
-    const V v = load_row<false>(src + c);
 #pragma unroll
-    for (int q = 0; q < MOE_MAX_K; ++q) {
-      if (q >= width) break;
-      if (drow[q] < 0) continue;
-      if (drow[q] >= out_rows) {
-        errbits = MOE_DERR_ROW_RANGE;
-        continue;
-      }
-      __builtin_nontemporal_store(v, out + static_cast<int64_t>(drow[q]) * vec_per_row + c);
+  for (int q = 0; q < MOE_MAX_K; ++q) {
+    if (q >= width) break;
+    if (drow[q] < 0) continue;
+    if (drow[q] >= out_rows) {
+      errbits = MOE_DERR_ROW_RANGE;
+      continue;
     }
+    __builtin_nontemporal_store(v, out + static_cast<int64_t>(drow[q]) * vec_per_row + c);
   }
-  if (threadIdx.x == 0) report(d_err, errbits);
+  if (threadIdx.x == 0 && part == 0) report(d_err, errbits);
+}
+
+template <typename V, bool SHUFFLE>
+int launch_parts(const void* x, int T, int64_t vec_per_row, const int32_t* perm,
+                 const int32_t* dest, int width, void* x_out, void* out, int64_t out_rows,
+                 const int32_t* n_valid, int32_t* d_err, hipStream_t s) {
+  const int64_t parts = (vec_per_row + kPartVec - 1) / kPartVec;
+  if (parts > INT32_MAX || !grid_ok(static_cast<int64_t>(T) * parts, kPartVec)) return MOE_ERR_SHAPE;
+  const unsigned lds = parts_lds_bytes(width + (SHUFFLE ? 1 : 0));
+  permute_parts_kernel<V, SHUFFLE>
+      <<<static_cast<unsigned>(static_cast<int64_t>(T) * parts), kPartVec, lds, s>>>(
+          static_cast<const V*>(x), T, vec_per_row, static_cast<int>(parts), perm, dest, width,
+          static_cast<V*>(x_out), static_cast<V*>(out), out_rows, n_valid, d_err);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
 }
 
 template <typename V, int TPT, int U>
@@ -229,23 +229,14 @@ int launch_rows(const void* x, int T, int64_t vec_per_row, const int32_t* dest, 
   return MOE_OK;
 }
 
-// Blocks of a fan-out launch reserve this much LDS (unused) so that at most
-// two are resident per CU (160 KB of LDS).  With many destinations per token,
-// fewer tokens in flight keep HBM writing efficiently: 5% faster on MI355X
-// for 8 KiB rows with 6 destinations inside the full step.  (Measured slower
-// for 14 KiB rows with 8 destinations, which keep the plain launch.)
-constexpr unsigned kFanoutLds = 64 * 1024;
-
 // Launch shape by row size (vectors per row R) and destinations per token
 // (width), as measured on MI355X:
 //   R < 64                 one thread per (token, vector)
 //   64 <= R < 256          one wave per token, 4 vectors per lane per pass
-//   384 < R <= 512, width > 2
-//                          fan-out kernel, two blocks per CU, 256 threads per
-//                          token with two vectors each
 //   384 < R <= 512 and at most 2 destinations
 //                          512 threads per token, one vector each
-//   R > 512                one wave per 128-vector part of a row
+//   R > 384 otherwise      two-wave blocks per 2 KiB part, residency capped
+//                          by the destinations (permute_parts_kernel)
 //   otherwise              256 threads per token, one vector per pass
 template <typename V>
 int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
@@ -262,21 +253,13 @@ int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* des
     const int rc = launch_rows<V, 64, 4>(x, T, vec_per_row, dest, width, out, out_rows, n_valid,
                                          d_err, s);
     if (rc != MOE_OK) return rc;
-  } else if (vec_per_row > 384 && vec_per_row <= 512 && width > 2) {
-    if (!grid_ok(T, 256)) return MOE_ERR_SHAPE;
-    permute_fanout_kernel<V, 256, 2><<<static_cast<unsigned>(T), 256, kFanoutLds, s>>>(
-        static_cast<const V*>(x), T, vec_per_row, dest, width, static_cast<V*>(out), out_rows,
-        n_valid, d_err);
   } else if (vec_per_row > 384 && vec_per_row <= 512 && width <= 2) {
     const int rc = launch_rows<V, 512, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid,
                                           d_err, s);
     if (rc != MOE_OK) return rc;
-  } else if (vec_per_row > 512) {
-    const int64_t parts = (vec_per_row + kSplitVec - 1) / kSplitVec;
-    if (parts > INT32_MAX || !grid_ok(static_cast<int64_t>(T) * parts, kWave)) return MOE_ERR_SHAPE;
-    permute_split_kernel<V><<<static_cast<unsigned>(static_cast<int64_t>(T) * parts), kWave, 0, s>>>(
-        static_cast<const V*>(x), T, vec_per_row, static_cast<int>(parts), dest, width,
-        static_cast<V*>(out), out_rows, n_valid, d_err);
+  } else if (vec_per_row > 384) {
+    return launch_parts<V, false>(x, T, vec_per_row, nullptr, dest, width, nullptr, out, out_rows,
+                                  n_valid, d_err, s);
   } else {
     const int rc = launch_rows<V, 256, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid,
                                           d_err, s);
@@ -377,7 +360,8 @@ int launch_gather(const void* x, int64_t x_rows, int64_t vec_per_row, const int3
 // ------------------------------------------------- shuffle + dispatch
 
 // The token shuffle's move and the next layer's dispatch in one pass, in
-// the shuffled order: TPT threads own position p, read the row of token
+// the shuffled order, for rows narrower than 256 vectors (wider rows take
+// permute_parts_kernel): TPT threads own position p, read the row of token
 // t = perm[p] once and write it to x_out[p] and to the send rows
 // token_rows[p][*].  Writes stay in few dense streams (x_out in order, the
 // send rows of one source rank's positions in G blocks); the reads gather.
@@ -437,25 +421,21 @@ __global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void shuff
 }
 
 // Launch shape by row size R (vectors): a wave per position below 256 (four
-// vectors per lane per pass), else 512 threads per position.
+// vectors per lane per pass), else two-wave blocks per 2 KiB part of a row
+// (permute_parts_kernel with the shuffle's move).
 template <typename V>
 int launch_shuffle_dispatch(const void* x, int T, int64_t vec_per_row, const int32_t* perm,
                             const int32_t* token_rows, int k, void* x_out, void* send,
                             int64_t send_rows, int32_t* d_err, hipStream_t s) {
-  const V* xv = static_cast<const V*>(x);
-  if (vec_per_row < 256) {
-    constexpr int kTokens = kPermThreads / 64;
-    const int64_t nb = (static_cast<int64_t>(T) + kTokens - 1) / kTokens;
-    if (!grid_ok(nb, kPermThreads)) return MOE_ERR_SHAPE;
-    shuffle_dispatch_kernel<V, 64, 4><<<static_cast<unsigned>(nb), kPermThreads, 0, s>>>(
-        xv, T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
-        static_cast<V*>(send), send_rows, d_err);
-  } else {
-    if (!grid_ok(T, 512)) return MOE_ERR_SHAPE;
-    shuffle_dispatch_kernel<V, 512, 1><<<static_cast<unsigned>(T), 512, 0, s>>>(
-        xv, T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
-        static_cast<V*>(send), send_rows, d_err);
-  }
+  if (vec_per_row >= 256)
+    return launch_parts<V, true>(x, T, vec_per_row, perm, token_rows, k, x_out, send, send_rows,
+                                 nullptr, d_err, s);
+  constexpr int kTokens = kPermThreads / 64;
+  const int64_t nb = (static_cast<int64_t>(T) + kTokens - 1) / kTokens;
+  if (!grid_ok(nb, kPermThreads)) return MOE_ERR_SHAPE;
+  shuffle_dispatch_kernel<V, 64, 4><<<static_cast<unsigned>(nb), kPermThreads, 0, s>>>(
+      static_cast<const V*>(x), T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
+      static_cast<V*>(send), send_rows, d_err);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
