@@ -2,9 +2,9 @@
 """Benchmark of the co-activation-aware MoE dispatch path on one MI355X.
 
 One step = one pass of the whole path over one batch:
-  workload 5 (default; two MoE layers, T=65536, H=4096 bf16, E=64, k=2, G=8):
-    layer-1 co-activation stats (+ transitions) -> shuffle prediction ->
-    layer-2 dedup plan over the shuffled order -> the token rows moved to
+  workload 5 (the headline; two MoE layers, T=65536, H=4096 bf16, E=64, k=2,
+    G=8): layer-1 co-activation stats (+ transitions) -> shuffle prediction
+    -> layer-2 dedup plan over the shuffled order -> the token rows moved to
     their shuffled places and into the layer-2 send rows in one pass ->
     combine
   workloads 1-4: stats -> plan -> permute -> combine of one layer.
@@ -12,12 +12,18 @@ Inputs are seeded synthetic routings already resident in HBM when timing
 starts.  The timed region runs K batches (default 200, so that filling the
 pipeline costs about 1 us per batch) with two in flight: each batch's
 routing-only phase (statistics, prediction, plan) runs on a second stream
-beside the previous batch's combine (workload 5) or its whole move (k >= 6);
-the same K batches run one after another are reported beside it.  Prints ONE
-JSON line.  Its value is dispatched rows per second of the whole step (every
-stage, batches back to back); permute+combine HBM GB/s with its share of peak
-(the metric's second half) and the dominant kernel's roofline fraction ride
-along, with the CPU oracle timed on a bounded sample.
+beside the previous batch's combine (k <= 2) or its whole move (k >= 6);
+the same K batches run one after another are reported beside it.
+
+Prints ONE JSON line.  Its value is workload 5's dispatched rows per second
+of the whole step (every stage, batches back to back); permute+combine HBM
+GB/s with its share of peak (the metric's second half) and the dominant
+kernel's roofline fraction ride along, with the CPU oracle timed on a bounded
+sample.  Unless --workload picks a single workload, the same line carries
+``workloads``: workloads 1-4 measured the same way (each with its second
+placement where it has one), and ``ceilings``: the read, write, copy and
+dense fan-out rates of plain streaming probe kernels on this GPU, against
+which each dominant kernel's read/write mix is also placed.
 """
 
 from __future__ import annotations
@@ -38,11 +44,13 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="run only this workload (as the headline); default: workload 5 as the "
+                         "headline plus workloads 1-4")
     ap.add_argument("--placement", default="main", choices=["main", "alt"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
-    ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the HBM ceiling probes")
     ap.add_argument("--no-expert-side", action="store_true")
     return ap.parse_args()
 
@@ -190,9 +198,10 @@ def shuffle_modes(w, x, z, steps: int) -> dict:
     return out
 
 
-def cpu_baseline(w, sample_tokens: int) -> dict:
+def cpu_baseline(w, sample_tokens: int, x_host=None) -> dict:
     """The CPU oracle on the first `sample_tokens` tokens of the same
-    workload, single-threaded; rows/s of the same step definition."""
+    workload, single-threaded; rows/s of the same step definition.  x_host
+    holds those tokens' rows when the workload's x lives only on the device."""
     import numpy as np
 
     import oracle
@@ -200,6 +209,7 @@ def cpu_baseline(w, sample_tokens: int) -> dict:
 
     Ts = max(w.G, (min(sample_tokens, w.T) // w.G) * w.G)
     sl = slice(0, Ts)
+    x = x_host if x_host is not None else w.x[sl]
     try:  # keep any BLAS call the oracle makes on one thread, as reported
         from threadpoolctl import threadpool_limits
         limit = threadpool_limits(1)
@@ -207,13 +217,13 @@ def cpu_baseline(w, sample_tokens: int) -> dict:
         limit = None
     t0 = time.perf_counter()
     if w.cfg == 5:
-        res = oracle.two_layer_pipeline(w.topk[sl], w.topk2[sl], w.gates2[sl], w.x[sl],
+        res = oracle.two_layer_pipeline(w.topk[sl], w.topk2[sl], w.gates2[sl], x,
                                         w.expert_rank2, w.E, w.E, w.G, w.ranks_per_node)
         plan, gates = res["plan"], res["gates2_shuffled"]
     else:
         oracle.coact_stats(w.topk[sl], w.E)
         plan = oracle.dispatch_plan(w.topk[sl], w.gates[sl], w.expert_rank, w.G, w.ranks_per_node)
-        oracle.permute_rows(w.x[sl], plan["row_token"])
+        oracle.permute_rows(x, plan["row_token"])
         gates = w.gates[sl]
     t_mid = time.perf_counter()
     N = int(plan["N"])
@@ -230,101 +240,140 @@ def cpu_baseline(w, sample_tokens: int) -> dict:
                       f"({os.cpu_count()} host threads visible)"}
 
 
-def main() -> int:
-    args = _args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the engine models "
-                                   "the expert-parallel group inside one GPU and has no "
-                                   "multi-GPU exchange", "n_gpus": args.gpus}))
-        return 2
-
+def shuffle_at_scale(w, steps: int) -> dict:
+    """The free and the capacity-balanced shuffle at a one-layer workload's
+    shape (G ranks, T tokens), the next layer taken to route like this one
+    (its transitions are this layer's pair counts, its placement this
+    placement): per-call time of each, the largest shard and how many
+    tokens each keeps on their source shard's rank."""
     import numpy as np
     import torch
 
-    import co_activation_amd
-    from co_activation_amd.pipeline import (ExpertSideStep, GraphPipeline, GraphStep, LayerStep,
-                                            Pipeline, StageTimers, TwoLayerStep)
+    from co_activation_amd import ops
+    from co_activation_amd.pipeline import StageTimers
+
+    dev = "cuda"
+    tk = torch.from_numpy(np.ascontiguousarray(w.topk, dtype=np.int32)).to(dev)
+    er = torch.from_numpy(np.ascontiguousarray(w.expert_rank, dtype=np.int32)).to(dev)
+    X = ops.coact_stats(tk, w.E, tk, w.E)["transition"]
+    src = np.arange(w.T) // (w.T // w.G)
+    out = {"ranks": w.G, "tokens": w.T}
+    for name, bal in (("free", False), ("balanced", True)):
+        bufs = {"pred_rank": torch.empty(w.T, dtype=torch.int32, device=dev),
+                "dest_pos": torch.empty(w.T, dtype=torch.int32, device=dev),
+                "perm": torch.empty(w.T, dtype=torch.int32, device=dev),
+                "shard_offsets": torch.empty(w.G + 1, dtype=torch.int32, device=dev)}
+        ws = torch.empty(ops.shuffle_workspace_bytes(w.T, w.E, w.G, bal), dtype=torch.uint8,
+                         device=dev)
+        err = ops.new_error_word(dev)
+        ops.shuffle_predict(tk, X, er, w.G, balanced=bal, out=bufs, ws=ws, d_err=err)
+        torch.cuda.synchronize()
+        timers = StageTimers(("shuffle",), steps)
+        for _ in range(steps):
+            pair = timers.begin("shuffle")
+            ops.shuffle_predict(tk, X, er, w.G, balanced=bal, out=bufs, ws=ws, d_err=err)
+            timers.end("shuffle", pair)
+        torch.cuda.synchronize()
+        if int(err.item()) != 0:
+            return {"error": f"device data errors {int(err.item())}"}
+        pred = bufs["pred_rank"].cpu().numpy()
+        off = bufs["shard_offsets"].cpu().numpy()
+        us = 1e3 * timers.median_ms()["shuffle"]
+        out[name] = {"us": us, "largest_shard": int(np.diff(off).max()),
+                     "tokens_kept_on_source_rank": int((pred == src).sum())}
+    out["balanced_over_free"] = out["balanced"]["us"] / out["free"]["us"]
+    return out
+
+
+def _i32(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
+
+
+def setup(cfg: int, placement: str, host_x: bool):
+    """Inputs of one workload in HBM and a constructor of its step.  x comes
+    from the host generator (the parity tests' inputs) when host_x, else from
+    the device's seeded generator (same N(0,1) recipe, no host draw)."""
+    import numpy as np
+    import torch
+
+    from co_activation_amd.pipeline import LayerStep, TwoLayerStep
     from workloads import make
     from workloads.gen import device_normal
 
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no HIP device"}))
-        return 1
-    if not co_activation_amd.is_built():
-        from co_activation_amd.build import build
-        build()
-    co_activation_amd.lib()
-
-    w = make(args.workload)
+    w = make(cfg, with_x=host_x)
     dev = "cuda"
-
-    def i32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
-
-    def xdev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    x = xdev(w.x)
+    if host_x:
+        if w.x.dtype == np.uint16:
+            x = torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            x = torch.from_numpy(w.x).to(dev)
+    else:
+        x = device_normal(w.T, w.H, w.dtype, seed=7)
     cap = w.T * min(w.k, w.G)
     z = device_normal(cap, w.H, w.dtype, seed=1)
-    if w.cfg == 5:
+    if cfg == 5:
         def make_step(x, z):
-            return TwoLayerStep(i32(w.topk), i32(w.topk2), torch.from_numpy(w.gates2).to(dev),
-                                i32(w.expert_rank2), x, z, w.G, w.ranks_per_node, E1=w.E)
-        workload = (f"two MoE layers with token shuffle: T={w.T} H={w.H} bf16 E={w.E} k={w.k} "
-                    f"G={w.G} (1 node of {w.ranks_per_node}); layer-1 stats+transitions, shuffle "
-                    f"predict, layer-2 dedup plan, shuffle move fused with the layer-2 permute, "
-                    f"combine")
+            return TwoLayerStep(_i32(w.topk), _i32(w.topk2), torch.from_numpy(w.gates2).to(dev),
+                                _i32(w.expert_rank2), x, z, w.G, w.ranks_per_node, E1=w.E)
+        desc = (f"two MoE layers with token shuffle: T={w.T} H={w.H} bf16 E={w.E} k={w.k} "
+                f"G={w.G} (1 node of {w.ranks_per_node}); layer-1 stats+transitions, shuffle "
+                f"predict, layer-2 dedup plan, shuffle move fused with the layer-2 permute, "
+                f"combine")
     else:
-        er = w.expert_rank if args.placement == "main" else w.alt_expert_rank
+        er = w.expert_rank if placement == "main" else w.alt_expert_rank
 
         def make_step(x, z):
-            return LayerStep(i32(w.topk), torch.from_numpy(w.gates).to(dev), i32(er), x, z, w.G,
+            return LayerStep(_i32(w.topk), torch.from_numpy(w.gates).to(dev), _i32(er), x, z, w.G,
                              w.ranks_per_node)
-        workload = (f"one MoE layer: T={w.T} H={w.H} {w.dtype} E={w.E} k={w.k} G={w.G} "
-                    f"({w.G // w.ranks_per_node} nodes of {w.ranks_per_node}), {args.placement} "
-                    f"placement; stats, dedup plan, permute, combine")
+        which = "co-locating" if placement == "main" and w.alt_expert_rank is not None else (
+            "contiguous" if placement == "alt" or cfg == 1 else placement)
+        desc = (f"one MoE layer: T={w.T} H={w.H} {w.dtype} E={w.E} k={w.k} G={w.G} "
+                f"({w.G // w.ranks_per_node} nodes of {w.ranks_per_node}), {which} "
+                f"placement; stats, dedup plan, permute, combine")
+    return w, x, z, make_step, desc
 
-    # Attainable copy bandwidth (1 GiB device-to-device), outside the timed region.
-    copy_gbs = None
-    if not args.no_copy_probe:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        times = []
-        for _ in range(5):
-            e0.record()
-            b.copy_(a)
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        copy_gbs = 2 * (1 << 30) / (statistics.median(times) * 1e-3) / 1e9
-        del a, b
 
-    # Two batches in flight: each step object owns its inputs and outputs.
+def _rw_bytes(stage: str, T: int, N: int, k: int, rb: int, rb_out: int):
+    """Algorithmic (read, write) bytes of a row-moving stage."""
+    if stage == "permute":
+        return T * rb + 4 * T * k, N * rb
+    if stage == "combine":
+        return N * rb + 4 * T * k + 4 * N, T * rb_out
+    if stage == "shuffle_dispatch":  # perm and the send rows read, x_out and send rows written
+        return T * rb + 4 * T + 4 * T * k, (T + N) * rb
+    raise KeyError(stage)
+
+
+def measure(w, x, z, make_step, steps: int, warmup: int, ceil, graphs: bool = True):
+    """One workload's step: a stage pass (cold caches, one stream), the timed
+    pipelined region (two batches in flight) with events around the
+    dominant kernel, the same batches one after another, and optionally the
+    step and the pipeline replayed as HIP graphs.  Returns (record, step)."""
+    import numpy as np
+    import torch
+
+    from co_activation_amd.hbm_probe import mix_bound_us
+    from co_activation_amd.pipeline import GraphPipeline, GraphStep, Pipeline, StageTimers
+
     step = make_step(x, z)
     step_b = make_step(x.clone(), z.clone())
     pipe = Pipeline([step, step_b])
-
-    pipe.run(max(args.warmup, 2))
+    pipe.run(max(warmup, 2))
     torch.cuda.synchronize()
     for st in (step, step_b):
         if int(st.d_err.item()) != 0:
-            print(json.dumps({"error": f"device data errors {int(st.d_err.item())}"}))
-            return 1
+            raise RuntimeError(f"device data errors {int(st.d_err.item())}")
 
     # Stage breakdown (events around every stage, all on one stream so that
     # each stage is timed alone), outside the timed region.  Before each step
     # a 512 MiB read evicts the step's data from L2 and the 256 MB Infinity
     # Cache, so every stage starts cold.  (A write would leave dirty lines
     # whose write-back the next stage would pay for.)
-    flush = torch.ones(512 << 18, dtype=torch.int32, device=dev)
-    stages = StageTimers(step.STAGES, args.steps)
-    for _ in range(args.steps):
+    flush = torch.ones(512 << 18, dtype=torch.int32, device="cuda")
+    stages = StageTimers(step.STAGES, steps)
+    for _ in range(steps):
         flush.sum()
         step.run(stages, overlap=False)
     torch.cuda.synchronize()
@@ -335,105 +384,69 @@ def main() -> int:
     moves = ("shuffle_dispatch",) if "shuffle_dispatch" in stage_ms else ("permute",)
     dom = max(moves + ("combine",), key=lambda n: stage_ms[n])
 
-    # Timed region: K batches through the two-step pipeline (each batch's
-    # routing-only phase beside the previous batch's combine); events only
+    # Timed region: K batches through the two-step pipeline; events only
     # around the dominant kernel.
-    timers = StageTimers((dom,), args.steps)
+    timers = StageTimers((dom,), steps)
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e_start.record()
-    pipe.run(args.steps, timers)
+    pipe.run(steps, timers)
     e_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    gpu_ms = e_start.elapsed_time(e_end)
-    ms_per_step = gpu_ms / args.steps
+    ms_per_step = e_start.elapsed_time(e_end) / steps
     dom_all = timers.durations_ms(dom)
     dom_ms = statistics.mean(dom_all)
     for st in (step, step_b):
         if int(st.d_err.item()) != 0:
-            print(json.dumps({"error": f"device data errors {int(st.d_err.item())}"}))
-            return 1
+            raise RuntimeError(f"device data errors {int(st.d_err.item())}")
 
     # The same K batches one after another on one step (no batch overlap).
     s0 = torch.cuda.Event(enable_timing=True)
     s1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step.run()
     s1.record()
     torch.cuda.synchronize()
-    seq_ms = s0.elapsed_time(s1) / args.steps
-
-    # The same step captured once as a HIP graph and replayed (outside the
-    # timed region above): the host enqueues one launch per step.
-    graph = GraphStep(step)
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    g0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1) / args.steps
-    del graph
-
-    # The pipeline captured as a graph of ten batches and replayed: what a
-    # caller whose host paces the eager loop (small layers) would use.
-    gbatches = 10
-    gpipe = GraphPipeline(pipe, gbatches)
-    reps = max(1, args.steps // gbatches)
-    torch.cuda.synchronize()
-    g0.record()
-    for _ in range(reps):
-        gpipe.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    gpipe_ms = g0.elapsed_time(g1) / (reps * gbatches)
-    del gpipe
+    seq_ms = s0.elapsed_time(s1) / steps
 
     counters = step.plan.counters.cpu().numpy()
     N = int(counters[0])
-    T, k = w.T, w.k
-    rb = w.row_bytes
-    bytes_perm = (T + N) * rb + 4 * T * k
-    bytes_comb = N * rb + T * rb + 4 * T * k + 4 * N
-    kernels = {"permute": bytes_perm, "combine": bytes_comb}
-    # the shuffle's move fused with the layer-2 permute: each row read once,
-    # written to its shuffled place and its send rows; dest_pos and token_rows
-    kernels["shuffle_dispatch"] = (2 * T + N) * rb + 4 * T + 4 * T * k
+    T, k, rb = w.T, w.k, w.row_bytes
+    kernels = {n: sum(_rw_bytes(n, T, N, k, rb, rb)) for n in ("permute", "combine",
+                                                               "shuffle_dispatch")}
     mv = moves[0]
-    pc_gbs = (kernels[mv] + bytes_comb) / ((stage_ms[mv] + stage_ms["combine"]) * 1e-3) / 1e9
+    pc_gbs = (kernels[mv] + kernels["combine"]) / ((stage_ms[mv] + stage_ms["combine"]) * 1e-3) / 1e9
     achieved = kernels[dom] / (dom_ms * 1e-3) / 1e9
     achieved_alone = kernels[dom] / (stage_ms[dom] * 1e-3) / 1e9
-
-    line = {
-        "metric": "dispatched rows/s and permute+combine HBM GB/s (% of peak) at 1 MI355X",
-        "value": N / (ms_per_step * 1e-3),
-        "unit": "dispatched rows/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    roof = {"bound": "hbm", "kernel": dom, "kernel_us": 1e3 * dom_ms,
+            "kernel_us_median": 1e3 * statistics.median(dom_all),
+            "algorithmic_bytes": kernels[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": counter_traffic(w.cfg, dom),
+            "kernel_us_alone": 1e3 * stage_ms[dom],
+            "frac_alone": achieved_alone / HBM_PEAK_GBS}
+    if ceil is not None:
+        r, wr = _rw_bytes(dom, T, N, k, rb, rb)
+        bound = mix_bound_us(r, wr, ceil)
+        roof["read_bytes"], roof["write_bytes"] = r, wr
+        roof["mix_bound_us"] = bound
+        roof["frac_of_mix_bound"] = bound / (1e3 * dom_ms)
+    rec = {
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded router logits, N(0,1) rows)",
-        "config": {"workload": workload, "tokens": T, "hidden": w.H, "experts": w.E, "top_k": k,
-                   "logical_ranks": w.G, "dispatched_rows": N},
+        "dispatched_rows_per_s": N / (ms_per_step * 1e-3),
+        "sequential": {"ms_per_step": seq_ms, "dispatched_rows_per_s": N / (seq_ms * 1e-3)},
         "dispatched_rows_per_s_of_move_kernel": N / (stage_ms[mv] * 1e-3),
         "permute_combine_gbps": pc_gbs,
         "permute_combine_pct_of_hbm_peak": 100.0 * pc_gbs / HBM_PEAK_GBS,
         "stage_us_median": {n: 1e3 * v for n, v in stage_ms.items()},
         "stage_us_min": {n: 1e3 * v for n, v in stage_min.items()},
         "stage_us_p90": {n: 1e3 * v for n, v in stage_p90.items()},
-        "stage_gbps": {n: b / (stage_ms[n] * 1e-3) / 1e9
-                       for n, b in ((mv, kernels[mv]), ("combine", bytes_comb))},
+        "stage_gbps": {n: kernels[n] / (stage_ms[n] * 1e-3) / 1e9 for n in (mv, "combine")},
         "schedule": ("two batches in flight: each batch's " +
                      ("statistics and plan" if w.cfg != 5 else
                       "statistics, shuffle prediction and layer-2 plan") +
@@ -442,21 +455,143 @@ def main() -> int:
         "counters": {"rows": N, "assignments": int(counters[1]), "local_rows": int(counters[2]),
                      "local_assign": int(counters[3]), "node_rows": int(counters[4]),
                      "cross_node_V": int(counters[5]), "max_recv_rows": int(counters[6])},
-        "copy_probe_gbps": copy_gbs,
         "wall_s_timed": wall,
-        "sequential": {"ms_per_step": seq_ms, "dispatched_rows_per_s": N / (seq_ms * 1e-3)},
-        "graph_replay": {"ms_per_step": graph_ms,
-                         "dispatched_rows_per_s": int(counters[0]) / (graph_ms * 1e-3)},
-        "graph_pipeline": {"batches_per_graph": gbatches, "ms_per_step": gpipe_ms,
-                           "dispatched_rows_per_s": N / (gpipe_ms * 1e-3)},
-        "roofline": {"bound": "hbm", "kernel": dom, "kernel_us": 1e3 * dom_ms,
-                     "kernel_us_median": 1e3 * statistics.median(dom_all),
-                     "algorithmic_bytes": kernels[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counter_traffic(w.cfg, dom),
-                     "kernel_us_alone": 1e3 * stage_ms[dom],
-                     "frac_alone": achieved_alone / HBM_PEAK_GBS},
+        "roofline": roof,
     }
+    if graphs:
+        # The same step captured once as a HIP graph and replayed: the host
+        # enqueues one launch per step.
+        graph = GraphStep(step)
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record()
+        for _ in range(steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / steps
+        del graph
+        # The pipeline captured as a graph of ten batches and replayed: what a
+        # caller whose host paces the eager loop (small layers) would use.
+        gbatches = 10
+        gpipe = GraphPipeline(pipe, gbatches)
+        reps = max(1, steps // gbatches)
+        torch.cuda.synchronize()
+        g0.record()
+        for _ in range(reps):
+            gpipe.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gpipe_ms = g0.elapsed_time(g1) / (reps * gbatches)
+        del gpipe
+        rec["graph_replay"] = {"ms_per_step": graph_ms,
+                               "dispatched_rows_per_s": N / (graph_ms * 1e-3)}
+        rec["graph_pipeline"] = {"batches_per_graph": gbatches, "ms_per_step": gpipe_ms,
+                                 "dispatched_rows_per_s": N / (gpipe_ms * 1e-3)}
+    del step_b, pipe
+    return rec, step
+
+
+# Tokens of each one-layer workload the CPU oracle runs on in the default
+# run (about one to three seconds of single-threaded numpy each).
+CPU_SAMPLE = {1: 2048, 2: 4096, 3: 4096, 4: 2048}
+
+
+def other_workload(cfg: int, args, ceil) -> dict:
+    """A one-layer workload beside the headline: its step measured like the
+    headline's, its second placement's step, a bounded CPU oracle sample;
+    at workload 4 the destination side, backward and placement planner, and
+    at workloads 3 and 4 the free and balanced shuffles at their shapes."""
+    import numpy as np
+    import torch
+
+    from workloads.gen import device_normal
+
+    w, x, z, make_step, desc = setup(cfg, "main", host_x=False)
+    rec, step = measure(w, x, z, make_step, args.steps, args.warmup, ceil)
+    out = {"workload": desc, "value": rec["dispatched_rows_per_s"], "unit": "dispatched rows/s",
+           "dtype": "bf16" if w.dtype == "bf16" else "f32",
+           "config": {"tokens": w.T, "hidden": w.H, "experts": w.E, "top_k": w.k,
+                      "logical_ranks": w.G, "ranks_per_node": w.ranks_per_node,
+                      "dispatched_rows": rec["counters"]["rows"]}}
+    out.update(rec)
+    if cfg == 4 and not args.no_expert_side:
+        out["expert_side"] = expert_side(step, w, args.steps, device_normal)
+        out["placement"] = placement_planner(w)
+    if cfg in (3, 4) and not args.no_expert_side:
+        out["shuffle_at_scale"] = shuffle_at_scale(w, args.steps)
+    if not args.no_cpu_baseline:
+        Ts = max(w.G, (min(CPU_SAMPLE[cfg], w.T) // w.G) * w.G)
+        xs = x[:Ts].cpu()
+        xs = xs.view(torch.int16).numpy().view(np.uint16) if w.dtype == "bf16" else xs.numpy()
+        out["cpu_baseline"] = cpu_baseline(w, Ts, xs)
+    del step, x, z
+    torch.cuda.empty_cache()
+    if w.alt_expert_rank is not None:
+        w2, x2, z2, make_alt, desc2 = setup(cfg, "alt", host_x=False)
+        alt, st2 = measure(w2, x2, z2, make_alt, args.steps, args.warmup, ceil, graphs=False)
+        out["alt_placement"] = {
+            "workload": desc2, "ms_per_step": alt["ms_per_step"],
+            "sequential_ms_per_step": alt["sequential"]["ms_per_step"],
+            "dispatched_rows_per_s": alt["dispatched_rows_per_s"],
+            "permute_combine_pct_of_hbm_peak": alt["permute_combine_pct_of_hbm_peak"],
+            "counters": alt["counters"], "roofline_frac": alt["roofline"]["frac"]}
+        del st2, x2, z2
+        torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    args = _args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the engine models "
+                                   "the expert-parallel group inside one GPU and has no "
+                                   "multi-GPU exchange", "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import co_activation_amd
+    from workloads.gen import device_normal
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no HIP device"}))
+        return 1
+    if not co_activation_amd.is_built():
+        from co_activation_amd.build import build
+        build()
+    co_activation_amd.lib()
+
+    # Measured HBM ceilings (probe kernels), outside every timed region.
+    ceil = None
+    if not args.no_probes:
+        from co_activation_amd.hbm_probe import ceilings
+        ceil = ceilings()
+
+    cfg = args.workload if args.workload is not None else 5
+    w, x, z, make_step, desc = setup(cfg, args.placement, host_x=True)
+    rec, step = measure(w, x, z, make_step, args.steps, args.warmup, ceil)
+    line = {
+        "metric": "dispatched rows/s and permute+combine HBM GB/s (% of peak) at 1 MI355X",
+        "value": rec["dispatched_rows_per_s"],
+        "unit": "dispatched rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded router logits, N(0,1) rows)",
+        "config": {"workload": desc, "tokens": w.T, "hidden": w.H, "experts": w.E,
+                   "top_k": w.k, "logical_ranks": w.G, "dispatched_rows": rec["counters"]["rows"]},
+    }
+    line.update({k: v for k, v in rec.items() if k not in ("ms_per_step", "dispatched_rows_per_s")})
+    if ceil is not None:
+        line["ceilings"] = ceil
     if not args.no_expert_side:
         line["expert_side"] = expert_side(step, w, args.steps, device_normal)
         line["placement"] = placement_planner(w)
@@ -464,6 +599,10 @@ def main() -> int:
             line["shuffle_modes"] = shuffle_modes(w, x, z, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+    del step, x, z
+    torch.cuda.empty_cache()
+    if args.workload is None:
+        line["workloads"] = {str(c): other_workload(c, args, ceil) for c in (1, 2, 3, 4)}
     print(json.dumps(line), flush=True)
     return 0
 

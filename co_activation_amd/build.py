@@ -2,7 +2,9 @@
 
 Usage: python -m co_activation_amd.build  (or co_activation_amd.build.build())
 Compiles every source under csrc/ with hipcc into _build/ and links the
-shared library next to this file.  Always recompiles.
+shared library next to this file; also builds libmoe_hbm_probe.so, the
+bandwidth probes the benchmark measures its ceilings with, from probe/.
+Always recompiles.
 """
 
 from __future__ import annotations
@@ -18,6 +20,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libmoe_coact.so"
+PROBE_SRC = PKG / "probe" / "hbm_probe.hip"
+PROBE_LIB = PKG / "libmoe_hbm_probe.so"
 ARCH = os.environ.get("MOE_COACT_ARCH", "gfx950")
 
 HIP_FLAGS = [
@@ -62,6 +66,12 @@ def build(verbose: bool = False) -> Path:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB.with_suffix(".so.tmp")
+    cmd = [hipcc, *HIP_FLAGS, *inc, "-shared", str(PROBE_SRC), "-o", str(tmp)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

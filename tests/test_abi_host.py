@@ -218,3 +218,18 @@ def test_binding_rejects_a_stream_of_another_device(monkeypatch):
     assert ops._stream(types.SimpleNamespace(device=torch.device("cuda", 1))) == 0x1234
     with pytest.raises(ValueError, match="current device"):
         ops._stream(types.SimpleNamespace(device=torch.device("cuda", 0)))
+
+
+def test_probe_library_rejects(built_lib):
+    """The bandwidth-probe library (include/moe_hbm_probe.h) loads and checks
+    its arguments on the host before any launch."""
+    from co_activation_amd import hbm_probe
+    f = hbm_probe._load().moe_probe_stream
+    assert f(3, 0, FAKE, FAKE, 1024, FAKE, NULL) == -2       # no such mode
+    assert f(0, 4, FAKE, FAKE, 1024, FAKE, NULL) == -2       # no such shape
+    assert f(2, 0, FAKE, FAKE, 1000, FAKE, NULL) == -2       # not a multiple of 16 bytes
+    assert f(2, 0, FAKE, FAKE, 0, FAKE, NULL) == -2
+    assert f(0, 0, NULL, FAKE, 1024, FAKE, NULL) == -1       # read needs src
+    assert f(0, 0, FAKE, NULL, 1024, NULL, NULL) == -1       # read needs sink
+    assert f(1, 0, NULL, NULL, 1024, NULL, NULL) == -1       # write needs dst
+    assert f(2, 0, FAKE + 8, FAKE, 1024, NULL, NULL) == -4   # alignment
