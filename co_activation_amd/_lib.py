@@ -25,12 +25,13 @@ STATUS = {
 MOE_F32, MOE_BF16 = 0, 1
 DERR_BITS = {
     1: "EXPERT_RANGE", 2: "EXPERT_DUP", 4: "RANK_RANGE", 8: "CAPACITY",
-    16: "SRC_OFFSETS", 32: "ROW_RANGE",
+    16: "SRC_OFFSETS", 32: "ROW_RANGE", 64: "SYNC",
 }
 MAX_K, MAX_E, MAX_G = 8, 256, 64
 
 EXPORTS = (
-    "moe_status_string", "moe_coact_stats", "moe_dispatch_plan_workspace_size",
+    "moe_status_string", "moe_coact_stats", "moe_coact_stats_workspace_size",
+    "moe_dispatch_plan_workspace_size",
     "moe_dispatch_plan", "moe_permute", "moe_combine",
     "moe_shuffle_predict_workspace_size", "moe_shuffle_predict",
     "moe_expert_plan_workspace_size", "moe_expert_plan",
@@ -47,8 +48,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     P = c_void_p
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
-    lib.moe_coact_stats.argtypes = [P, c_int64, c_int, c_int, P, c_int, c_int, P, P, P, P, P, P]
+    lib.moe_coact_stats.argtypes = [P, c_int64, c_int, c_int, P, c_int, c_int, P, P, P, P, P, P,
+                                    c_size_t, P]
     lib.moe_coact_stats.restype = c_int
+    lib.moe_coact_stats_workspace_size.argtypes = [c_int64, c_int, c_int, c_int, POINTER(c_size_t)]
+    lib.moe_coact_stats_workspace_size.restype = c_int
     lib.moe_dispatch_plan_workspace_size.argtypes = [c_int64, c_int, POINTER(c_size_t)]
     lib.moe_dispatch_plan_workspace_size.restype = c_int
     lib.moe_dispatch_plan.argtypes = [P, P, c_int64, c_int, c_int, P, c_int, c_int, P, c_int64,

@@ -194,6 +194,9 @@ extern "C" int moe_permute_scaled(const void* x, int x_dtype, int64_t T, int64_t
   if (T == 0) return MOE_OK;
   if (x == nullptr || dest == nullptr || scale == nullptr || out == nullptr) return MOE_ERR_NULL;
   if (!moe::row_ok(H, x_dtype, x) || !moe::row_ok(H, out_dtype, out)) return MOE_ERR_ALIGN;
+  if (moe::overlap(x, T * H * (x_dtype == MOE_BF16 ? 2 : 4), out,
+                   out_rows * H * (out_dtype == MOE_BF16 ? 2 : 4)))
+    return MOE_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (x_dtype == MOE_BF16 && out_dtype == MOE_BF16)
     return moe::launch_scaled<true, true, 8>(x, T, H, dest, width, scale, out, out_rows, n_valid,
@@ -222,6 +225,9 @@ extern "C" int moe_row_dot(const void* a, int a_dtype, int64_t T, int64_t H, con
   const bool ab = a_dtype == MOE_BF16, bb = b_dtype == MOE_BF16;
   // Groups of 8 elements whenever a bf16 operand is involved (16 bytes of it).
   if ((ab || bb) && H % 8 != 0) return MOE_ERR_ALIGN;
+  if (moe::overlap(out, T * width * 4, a, T * H * (ab ? 2 : 4)) ||
+      moe::overlap(out, T * width * 4, b, b_rows * H * (bb ? 2 : 4)))
+    return MOE_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ab && bb)
     return moe::launch_dot<true, true, 8>(a, b, b_rows, T, H, rows, width, out, n_valid, d_err, s);

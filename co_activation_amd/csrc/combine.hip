@@ -145,6 +145,7 @@ extern "C" int moe_combine(const void* z, int z_dtype, int64_t z_rows, int64_t H
   if ((H * zb) % 16 != 0 || (H * yb) % 16 != 0 || reinterpret_cast<uintptr_t>(z) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(y) % 16 != 0)
     return MOE_ERR_ALIGN;
+  if (moe::overlap(z, z_rows * H * zb, y, T * H * yb)) return MOE_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (z_dtype == MOE_BF16 && y_dtype == MOE_BF16)
     return moe::launch<true, true, 8>(z, z_rows, H, rows, k, row_weight, T, y, n_valid, d_err, s);

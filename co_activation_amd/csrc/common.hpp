@@ -17,6 +17,15 @@ inline bool grid_ok(int64_t blocks, int64_t threads) {
   return blocks >= 0 && blocks <= INT32_MAX && blocks * threads < (int64_t{1} << 32);
 }
 
+// True when the byte ranges [a, a + a_bytes) and [b, b + b_bytes) share a
+// byte (an output that overlaps an input: blocks would read rows that
+// others have already overwritten).
+inline bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  if (a == nullptr || b == nullptr || a_bytes <= 0 || b_bytes <= 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + static_cast<uintptr_t>(b_bytes) && pb < pa + static_cast<uintptr_t>(a_bytes);
+}
+
 // Launch-status check used right after every kernel launch.
 #define MOE_CHECK_LAUNCH()                                  \
   do {                                                      \

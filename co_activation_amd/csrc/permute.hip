@@ -18,7 +18,7 @@
 // Shuffle dispatch (moe_shuffle_dispatch): the token shuffle's move and the
 // next layer's permute in one pass, in the shuffled order, reading each row
 // once ("Expert Coupling in MoE Pretraining ...", abstract: tokens are moved
-// to the rank predicted to hold their next-layer experts, then dispatched).
+// toward the rank forecast for their next-layer experts, then dispatched).
 #include "common.hpp"
 
 namespace moe {
@@ -125,10 +125,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_flat_kernel(
 
 // Wide rows: a row is cut into parts of kPartVec vectors (2 KiB of 16-byte
 // vectors) and one block of kPartVec threads (two waves, one vector per
-// lane) moves one part of one position's row: block b takes position
-// b / parts, part b % parts.  The position is the token itself (permute) or
-// shuffled position p holding token perm[p], whose row also goes to x_out[p]
-// (the shuffle dispatch).  The row piece is loaded once and stored to every
+// lane) moves one part of one token's row: block b takes token b / parts,
+// part b % parts.  The row piece is loaded once and stored to every
 // destination with nontemporal 16-byte stores.
 //
 // How many such blocks a CU holds at once sets how many write streams are
@@ -138,9 +136,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_flat_kernel(
 // parts_lds_bytes).  Measured on MI355X (stage medians of the benchmark
 // step, cold caches): 14 KiB rows to up to 8 ranks 686 -> 646 us against a
 // wave per 2 KiB part with no cap; 8 KiB rows to up to 6 ranks 507 -> 499 us
-// against 256-thread blocks per token capped at two per CU; the fused
-// shuffle dispatch of 8 KiB rows with up to 2 ranks 351 us, as with 512
-// threads per position.  Other part sizes (1-16 KiB) and caps were slower.
+// against 256-thread blocks per token capped at two per CU.  Other part
+// sizes (1-16 KiB) and caps were slower.
 constexpr int kPartWaves = 2;
 constexpr int kPartVec = kPartWaves * kWave;
 constexpr unsigned kLdsPerCu = 160 * 1024;
@@ -153,33 +150,22 @@ inline unsigned parts_lds_bytes(int writes) {
   return (kLdsPerCu / static_cast<unsigned>(blocks < 2 ? 2 : blocks)) & ~1023u;
 }
 
-template <typename V, bool SHUFFLE>
+template <typename V>
 __global__ __launch_bounds__(kPartVec) void permute_parts_kernel(
     const V* __restrict__ x, int T, int64_t vec_per_row, int parts,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ dest, int width,
-    V* __restrict__ x_out, V* __restrict__ out, int64_t out_rows,
+    const int32_t* __restrict__ dest, int width, V* __restrict__ out, int64_t out_rows,
     const int32_t* __restrict__ n_valid, int32_t* d_err) {
-  const int p = static_cast<int>(blockIdx.x / static_cast<unsigned>(parts));
-  const int part = static_cast<int>(blockIdx.x - static_cast<unsigned>(p) * parts);
-  if (p >= T || (n_valid != nullptr && p >= *n_valid)) return;
-  int t = p;
-  if constexpr (SHUFFLE) {
-    t = __builtin_amdgcn_readfirstlane(perm[p]);
-    if (t < 0 || t >= T) {
-      if (threadIdx.x == 0 && part == 0) report(d_err, MOE_DERR_ROW_RANGE);
-      return;
-    }
-  }
+  const int t = static_cast<int>(blockIdx.x / static_cast<unsigned>(parts));
+  const int part = static_cast<int>(blockIdx.x - static_cast<unsigned>(t) * parts);
+  if (t >= T || (n_valid != nullptr && t >= *n_valid)) return;
   int drow[MOE_MAX_K];
 #pragma unroll
   for (int q = 0; q < MOE_MAX_K; ++q)
-    drow[q] = q < width ? __builtin_amdgcn_readfirstlane(dest[static_cast<int64_t>(p) * width + q])
+    drow[q] = q < width ? __builtin_amdgcn_readfirstlane(dest[static_cast<int64_t>(t) * width + q])
                         : -1;
   const int64_t c = static_cast<int64_t>(part) * kPartVec + threadIdx.x;
   if (c >= vec_per_row) return;
   const V v = load_row<false>(x + static_cast<int64_t>(t) * vec_per_row + c);
-  if constexpr (SHUFFLE)
-    __builtin_nontemporal_store(v, x_out + static_cast<int64_t>(p) * vec_per_row + c);
   int errbits = 0;
 #pragma unroll
   for (int q = 0; q < MOE_MAX_K; ++q) {
@@ -194,17 +180,16 @@ __global__ __launch_bounds__(kPartVec) void permute_parts_kernel(
   if (threadIdx.x == 0 && part == 0) report(d_err, errbits);
 }
 
-template <typename V, bool SHUFFLE>
-int launch_parts(const void* x, int T, int64_t vec_per_row, const int32_t* perm,
-                 const int32_t* dest, int width, void* x_out, void* out, int64_t out_rows,
-                 const int32_t* n_valid, int32_t* d_err, hipStream_t s) {
+template <typename V>
+int launch_parts(const void* x, int T, int64_t vec_per_row, const int32_t* dest, int width,
+                 void* out, int64_t out_rows, const int32_t* n_valid, int32_t* d_err,
+                 hipStream_t s) {
   const int64_t parts = (vec_per_row + kPartVec - 1) / kPartVec;
   if (parts > INT32_MAX || !grid_ok(static_cast<int64_t>(T) * parts, kPartVec)) return MOE_ERR_SHAPE;
-  const unsigned lds = parts_lds_bytes(width + (SHUFFLE ? 1 : 0));
-  permute_parts_kernel<V, SHUFFLE>
-      <<<static_cast<unsigned>(static_cast<int64_t>(T) * parts), kPartVec, lds, s>>>(
-          static_cast<const V*>(x), T, vec_per_row, static_cast<int>(parts), perm, dest, width,
-          static_cast<V*>(x_out), static_cast<V*>(out), out_rows, n_valid, d_err);
+  permute_parts_kernel<V>
+      <<<static_cast<unsigned>(static_cast<int64_t>(T) * parts), kPartVec, parts_lds_bytes(width),
+         s>>>(static_cast<const V*>(x), T, vec_per_row, static_cast<int>(parts), dest, width,
+              static_cast<V*>(out), out_rows, n_valid, d_err);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -258,8 +243,7 @@ int launch_permute(const void* x, int T, int64_t vec_per_row, const int32_t* des
                                           d_err, s);
     if (rc != MOE_OK) return rc;
   } else if (vec_per_row > 384) {
-    return launch_parts<V, false>(x, T, vec_per_row, nullptr, dest, width, nullptr, out, out_rows,
-                                  n_valid, d_err, s);
+    return launch_parts<V>(x, T, vec_per_row, dest, width, out, out_rows, n_valid, d_err, s);
   } else {
     const int rc = launch_rows<V, 256, 1>(x, T, vec_per_row, dest, width, out, out_rows, n_valid,
                                           d_err, s);
@@ -360,8 +344,7 @@ int launch_gather(const void* x, int64_t x_rows, int64_t vec_per_row, const int3
 // ------------------------------------------------- shuffle + dispatch
 
 // The token shuffle's move and the next layer's dispatch in one pass, in
-// the shuffled order, for rows narrower than 256 vectors (wider rows take
-// permute_parts_kernel): TPT threads own position p, read the row of token
+// the shuffled order: TPT threads own position p, read the row of token
 // t = perm[p] once and write it to x_out[p] and to the send rows
 // token_rows[p][*].  Writes stay in few dense streams (x_out in order, the
 // send rows of one source rank's positions in G blocks); the reads gather.
@@ -421,21 +404,27 @@ __global__ __launch_bounds__(TPT < kPermThreads ? kPermThreads : TPT) void shuff
 }
 
 // Launch shape by row size R (vectors): a wave per position below 256 (four
-// vectors per lane per pass), else two-wave blocks per 2 KiB part of a row
-// (permute_parts_kernel with the shuffle's move).
+// vectors per lane per pass), else 512 threads per position (measured on
+// MI355X for 8 KiB rows with up to 2 ranks: 351 us, against 355 us for the
+// permute's 2 KiB parts at full residency).
 template <typename V>
 int launch_shuffle_dispatch(const void* x, int T, int64_t vec_per_row, const int32_t* perm,
                             const int32_t* token_rows, int k, void* x_out, void* send,
                             int64_t send_rows, int32_t* d_err, hipStream_t s) {
-  if (vec_per_row >= 256)
-    return launch_parts<V, true>(x, T, vec_per_row, perm, token_rows, k, x_out, send, send_rows,
-                                 nullptr, d_err, s);
-  constexpr int kTokens = kPermThreads / 64;
-  const int64_t nb = (static_cast<int64_t>(T) + kTokens - 1) / kTokens;
-  if (!grid_ok(nb, kPermThreads)) return MOE_ERR_SHAPE;
-  shuffle_dispatch_kernel<V, 64, 4><<<static_cast<unsigned>(nb), kPermThreads, 0, s>>>(
-      static_cast<const V*>(x), T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
-      static_cast<V*>(send), send_rows, d_err);
+  const V* xv = static_cast<const V*>(x);
+  if (vec_per_row < 256) {
+    constexpr int kTokens = kPermThreads / 64;
+    const int64_t nb = (static_cast<int64_t>(T) + kTokens - 1) / kTokens;
+    if (!grid_ok(nb, kPermThreads)) return MOE_ERR_SHAPE;
+    shuffle_dispatch_kernel<V, 64, 4><<<static_cast<unsigned>(nb), kPermThreads, 0, s>>>(
+        xv, T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
+        static_cast<V*>(send), send_rows, d_err);
+  } else {
+    if (!grid_ok(T, 512)) return MOE_ERR_SHAPE;
+    shuffle_dispatch_kernel<V, 512, 1><<<static_cast<unsigned>(T), 512, 0, s>>>(
+        xv, T, vec_per_row, perm, token_rows, k, static_cast<V*>(x_out),
+        static_cast<V*>(send), send_rows, d_err);
+  }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -457,6 +446,10 @@ extern "C" int moe_shuffle_dispatch(const void* x, int64_t T, int64_t row_bytes,
   const auto xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(x_out),
              sa = reinterpret_cast<uintptr_t>(send);
   if (row_bytes % 4 != 0 || xa % 4 != 0 || oa % 4 != 0 || sa % 4 != 0) return MOE_ERR_ALIGN;
+  if (moe::overlap(x, T * row_bytes, x_out, T * row_bytes) ||
+      moe::overlap(x, T * row_bytes, send, send_rows * row_bytes) ||
+      moe::overlap(x_out, T * row_bytes, send, send_rows * row_bytes))
+    return MOE_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Ti = static_cast<int>(T);
   if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0 && sa % 16 == 0)
@@ -476,6 +469,7 @@ extern "C" int moe_gather(const void* x, int64_t x_rows, int64_t row_bytes, cons
   if (src == nullptr || out == nullptr || (x == nullptr && x_rows > 0)) return MOE_ERR_NULL;
   const auto xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(out);
   if (row_bytes % 4 != 0 || xa % 4 != 0 || oa % 4 != 0) return MOE_ERR_ALIGN;
+  if (moe::overlap(x, x_rows * row_bytes, out, n_rows * row_bytes)) return MOE_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n = static_cast<int>(n_rows);
   if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0)
@@ -494,6 +488,7 @@ extern "C" int moe_permute(const void* x, int64_t T, int64_t row_bytes, const in
   if (x == nullptr || dest == nullptr || out == nullptr) return MOE_ERR_NULL;
   const auto xa = reinterpret_cast<uintptr_t>(x), oa = reinterpret_cast<uintptr_t>(out);
   if (row_bytes % 4 != 0 || xa % 4 != 0 || oa % 4 != 0) return MOE_ERR_ALIGN;
+  if (moe::overlap(x, T * row_bytes, out, out_rows * row_bytes)) return MOE_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (row_bytes % 16 == 0 && xa % 16 == 0 && oa % 16 == 0)
     return moe::launch_permute<moe::u32x4>(x, static_cast<int>(T), row_bytes / 16, dest, width,

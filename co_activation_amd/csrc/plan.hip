@@ -1,7 +1,8 @@
 // Deduplicated dispatch plan.
 //
-// "Expert Coupling in MoE Pretraining ..." (abstract): a dispatcher sends
-// each token to each GPU once.  "Cobalt: Leveraging Expert Co-activation ..."
+// "Expert Coupling in MoE Pretraining ..." (abstract): deduplicated dispatch,
+// a token reaches a given GPU at most one time however many of its experts
+// live there.  "Cobalt: Leveraging Expert Co-activation ..."
 // (Problem Formulation): token t with expert set D_t on source rank s_t; with
 // one replica per expert the rank of (t, e) is p(e); cross-node volume
 // V = sum_t |{N(p(e)) : e in D_t} minus {N(s_t)}|.

@@ -1,8 +1,8 @@
 // Token shuffle prediction.
 //
-// "Expert Coupling in MoE Pretraining ..." (abstract): token shuffling moves
-// each token to the GPU predicted to hold its next-layer experts; the experts
-// a token picks at one layer predict those it picks at the next.
+// "Expert Coupling in MoE Pretraining ..." (abstract): tokens are reordered
+// by the rank forecast for their next-layer experts, the forecast resting on
+// how well one layer's expert choices anticipate the next layer's.
 //
 //   M[i][r]     = sum_{j : p'(j) = r} X[i][j]       (64-bit, one block per i)
 //   score_t[r]  = sum_{i in D_t} M[i][r],  pred_t = argmax_r, lowest r on ties
@@ -12,10 +12,15 @@
 // rank) and the identity placement, so it reuses the plan kernels: the plan's
 // row of token t is its new position and row_token is the inverse
 // permutation.
+#include <climits>
+#include <mutex>
+
 #include "plan.hpp"
 
 namespace moe {
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
@@ -28,8 +33,11 @@ struct ShuffleWs {
   int64_t* counters;
   int32_t* perm_scratch;
   void* plan_ws;
+  uint64_t* rec;  // exchange words of the exchange form: [2][kXBlocks][G + 1]
   size_t bytes;
 };
+
+constexpr int kXBlocksMax = 128;  // kXBlocks, needed before the kernels
 
 ShuffleWs shuffle_layout(void* base, int64_t T, int E, int G) {
   ShuffleWs w{};
@@ -48,6 +56,7 @@ ShuffleWs shuffle_layout(void* base, int64_t T, int E, int G) {
   w.counters = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * 8));
   w.perm_scratch = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (T > 0 ? T : 1)));
   w.plan_ws = take(plan_workspace_bytes(T, G));
+  w.rec = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 2 * kXBlocksMax * (G + 1)));
   w.bytes = off;
   return w;
 }
@@ -362,6 +371,411 @@ __global__ __launch_bounds__(kBalTile) void balanced_round_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced shuffle in one launch (after the preference lists), for inputs
+// whose tokens fit in at most kXBlocks blocks of kXThreads threads with up
+// to kXMaxTpt tokens per thread, all resident at once (checked on the host);
+// larger inputs take the round-per-launch kernels above.
+//
+// rank_argmax_kernel (the free shuffle's prediction above 16 ranks) and
+// prefs_sort_kernel (the balanced shuffle's preference lists) read each
+// token's rows of M with a group of lanes per token.
+//
+// shuffle_exchange_kernel: block b owns tokens [b * TB, (b + 1) * TB).  Each
+// round every token takes its first preference r with t <= limit[r],
+// limit[r] being the fill index of r under the previous round's choices; the
+// block counts its tokens per (64-token chunk, rank) with LDS atomics and
+// publishes its counts per rank as 64-bit words tagged with the round,
+// double-buffered by round parity, with a flag saying whether any of its
+// tokens changed its choice.  Every block reads all blocks' flags and the
+// counts of the blocks before it.  That prefix and the block's own chunk
+// counts give the next round's limits: a rank full before the block, open
+// after it, or filled at an exact position inside it.  The rounds stop when
+// no token of any block changed its choice (the fixed point; at most G + 1
+// rounds).  The final counts then give each token its position directly:
+// its rank's shard offset r * cap, plus the rank's tokens in earlier blocks,
+// earlier chunks, and earlier lanes of its chunk -- the stable counting sort,
+// without the plan kernels.
+//
+// The blocks wait on each other, so they must all be resident at once; next
+// to a kernel that keeps the CUs busy (another stream) they wait for it to
+// drain.  Waits poll the tagged words with agent-scope atomic loads; every
+// poll loop gives up after a bound, reporting MOE_DERR_SYNC, so a block
+// that waits for a block that never publishes still exits.
+
+constexpr int kXThreads = 1024;
+constexpr int kXWaves = kXThreads / kWave;
+constexpr int kXBlocks = kXBlocksMax;
+constexpr int kXMaxTpt = 4;
+constexpr int kXChunks = kXMaxTpt * kXWaves;  // 64-token chunks per block
+constexpr unsigned kXSpinLimit = 1u << 22;     // polls (about 1 us each) before giving up
+
+inline int group_width(int G) {
+  int w = 1;
+  while (w < G) w <<= 1;
+  return w;
+}
+
+// Preference rows are padded to 16 bytes so that each starts aligned.
+inline int64_t pref_stride(int G) { return (G + 15) / 16 * 16; }
+
+// The free shuffle's prediction: a group of W lanes (W = G rounded up to a
+// power of two) per token; lane r adds the token's rows of M for rank r
+// (coalesced across the group), and a max-reduction over the keys
+// score * 64 + (63 - r) (ties to the lower rank) gives the first rank.
+// Also clears the exchange words.
+__global__ __launch_bounds__(256) void rank_argmax_kernel(
+    const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
+    int W, int32_t* __restrict__ pred, uint64_t* __restrict__ rec, int64_t rec_words,
+    int32_t* d_err) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < rec_words; i += gridDim.x * 256ll) rec[i] = 0;
+  const int per_block = 256 / W;
+  const int t = blockIdx.x * per_block + static_cast<int>(threadIdx.x) / W;
+  const int r = static_cast<int>(threadIdx.x) % W;
+  long long key = LLONG_MIN;
+  int errbits = 0;
+  if (t < T) {
+    long long score = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+      if (j >= k) break;
+      const int e = topk[static_cast<int64_t>(t) * k + j];
+      if (e < 0 || e >= E) {
+        errbits |= MOE_DERR_EXPERT_RANGE;
+        continue;
+      }
+      if (r < G) score += M[static_cast<int64_t>(e) * G + r];
+    }
+    if (r < G) key = score * 64 + (63 - r);
+  }
+  if (r == 0) report(d_err, errbits);
+  long long best = key;
+  for (int d = 1; d < W; d <<= 1) best = max(best, __shfl_xor(best, d, kWave));
+  if (t < T && r < G && key == best) pred[t] = r;
+}
+
+// The balanced shuffle's preference lists: a group of W lanes per token as
+// in rank_argmax_kernel, then a bitonic sort of the group's keys, descending,
+// across its lanes (W log W compare-exchanges on the lanes' shuffled keys,
+// against W^2 comparisons for ranking by counting) leaves the i-th preferred
+// rank in lane i of the group, which writes byte i of the token's row.
+// Also clears the exchange words.
+__global__ __launch_bounds__(256) void prefs_sort_kernel(
+    const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
+    int W, int64_t Gs, uint8_t* __restrict__ prefs, uint64_t* __restrict__ rec, int64_t rec_words,
+    int32_t* d_err) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < rec_words; i += gridDim.x * 256ll) rec[i] = 0;
+  const int per_block = 256 / W;
+  const int t = blockIdx.x * per_block + static_cast<int>(threadIdx.x) / W;
+  const int r = static_cast<int>(threadIdx.x) % W;
+  long long key = LLONG_MIN;
+  int errbits = 0;
+  if (t < T) {
+    long long score = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+      if (j >= k) break;
+      const int e = topk[static_cast<int64_t>(t) * k + j];
+      if (e < 0 || e >= E) {
+        errbits |= MOE_DERR_EXPERT_RANGE;
+        continue;
+      }
+      if (r < G) score += M[static_cast<int64_t>(e) * G + r];
+    }
+    if (r < G) key = score * 64 + (63 - r);
+  }
+  if (r == 0) report(d_err, errbits);
+  for (int size = 2; size <= W; size <<= 1) {
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      const long long other = __shfl_xor(key, j, kWave);
+      const bool lower = (r & j) == 0;
+      const bool desc = (r & size) == 0;
+      key = (lower == desc) ? max(key, other) : min(key, other);
+    }
+  }
+  if (t < T && r < G) prefs[static_cast<int64_t>(t) * Gs + r] = static_cast<uint8_t>(63 - (key & 63));
+}
+
+// One 64-bit exchange word: the round tag (round + 1) above the value.
+__device__ __forceinline__ uint64_t xword(int round, uint32_t v) {
+  return (static_cast<uint64_t>(round + 1) << 32) | v;
+}
+
+// Polls *w until it carries this round's tag; false after the spin bound.
+__device__ __forceinline__ bool xwait(const uint64_t* w, int round, uint32_t& v) {
+  const uint64_t want = static_cast<uint64_t>(round + 1);
+  for (unsigned spin = 0; spin < kXSpinLimit; ++spin) {
+    const uint64_t x = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((x >> 32) == want) {
+      v = static_cast<uint32_t>(x);
+      return true;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
+// First rank in the token's preference order (16 per word, PW words) that
+// is set in feas; the last preference if none is (cannot happen: some rank
+// always has room for the token).
+template <int PW>
+__device__ __forceinline__ int first_feasible(const u32x4 (&pw)[PW], int G, uint64_t feas) {
+  int last = 0;
+#pragma unroll
+  for (int w = 0; w < PW; ++w) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (w * 16 + i >= G) return last;
+      const int p = static_cast<int>((pw[w][i >> 2] >> (8 * (i & 3))) & 0xFFu);
+      if ((feas >> p) & 1ull) return p;
+      last = p;
+    }
+  }
+  return last;
+}
+
+template <int PW>
+__global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
+    const uint8_t* __restrict__ prefs, int64_t Gs, int T, int G, int cap, int TB, int tpt, int nb,
+    uint64_t* __restrict__ rec, int32_t* __restrict__ pred_rank, int32_t* __restrict__ dest_pos,
+    int32_t* __restrict__ perm, int32_t* __restrict__ shard_offsets, int32_t* d_err) {
+  __shared__ uint8_t s_choice[kXMaxTpt * kXThreads];  // each token's current choice
+  __shared__ int s_cc[kXChunks][MOE_MAX_G];  // tokens per (64-token chunk, rank)
+  __shared__ int s_pre[kXWaves][MOE_MAX_G];  // partial sums over earlier blocks
+  __shared__ int s_cnt[MOE_MAX_G], s_P[MOE_MAX_G];
+  __shared__ int s_xlimit[MOE_MAX_G], s_xrank[MOE_MAX_G];
+  __shared__ uint64_t s_open;
+  __shared__ int s_ncross, s_abort, s_changed;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int b = blockIdx.x;
+  const int t0 = b * TB;
+  const int nchunks = tpt * kXWaves;
+  const int64_t words = static_cast<int64_t>(G) + 1;  // per block and round: G counts, a flag
+
+  if (tid == 0) {
+    s_open = G >= 64 ? ~0ull : ((1ull << G) - 1);
+    s_ncross = 0;
+    s_abort = 0;
+  }
+  for (int u = 0; u < tpt; ++u) s_choice[u * kXThreads + tid] = 255;
+  __syncthreads();
+
+  const int max_rounds = G + 2;
+  for (int round = 0; round < max_rounds; ++round) {
+    uint64_t* xr = rec + static_cast<int64_t>(round & 1) * nb * words;
+    // 1. choices, and the tokens of each (chunk, rank) from wave ballots
+    int changed = round == 0 ? 1 : 0;
+    int wc = 0;
+    for (int u = 0; u < tpt; ++u) {
+      const int t = t0 + u * kXThreads + tid;
+      const int idx = u * kXThreads + tid;
+      int c = s_choice[idx];
+      if (t < T) {
+        u32x4 pw[PW];
+#pragma unroll
+        for (int w = 0; w < PW; ++w)
+          pw[w] = *reinterpret_cast<const u32x4*>(prefs + static_cast<int64_t>(t) * Gs + 16 * w);
+        uint64_t feas = s_open;
+        const int nc = s_ncross;
+        for (int i = 0; i < nc; ++i)
+          if (t <= s_xlimit[i]) feas |= 1ull << s_xrank[i];
+        const int nw = first_feasible<PW>(pw, G, feas);
+        changed |= nw != c;
+        c = nw;
+        s_choice[idx] = static_cast<uint8_t>(c);
+      }
+      // the wave's own row of chunk counts: cleared, then one LDS atomic per
+      // token (a wave's LDS operations complete in order)
+      int* row = s_cc[u * kXWaves + wave];
+      if (lane < G) row[lane] = 0;
+      __builtin_amdgcn_wave_barrier();
+      if (c < G) atomicAdd(&row[c], 1);
+      __builtin_amdgcn_wave_barrier();
+      if (lane < G) wc += row[lane];
+    }
+    if (lane < G) s_pre[wave][lane] = wc;  // this block's counts, per wave for now
+    const int any = __syncthreads_or(changed);
+    // 2. publish this block's counts and whether any of its tokens changed
+    if (wave == 0 && lane < G) {
+      int c = 0;
+      for (int w = 0; w < kXWaves; ++w) c += s_pre[w][lane];
+      s_cnt[lane] = c;
+      __hip_atomic_store(xr + static_cast<int64_t>(b) * words + lane,
+                         xword(round, static_cast<uint32_t>(c)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == kWave)
+      __hip_atomic_store(xr + static_cast<int64_t>(b) * words + G,
+                         xword(round, static_cast<uint32_t>(any)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // s_pre is reused below
+    // 3. every block's flag of this round
+    if (wave == 0) {
+      int ch = 0, ok = 1;
+      for (int j = lane; j < nb; j += kWave) {
+        uint32_t v = 0;
+        if (!xwait(xr + static_cast<int64_t>(j) * words + G, round, v)) ok = 0;
+        ch |= v != 0;
+      }
+      ch = ballot(ch != 0) != 0;
+      ok = ballot(!ok) == 0;
+      if (lane == 0) {
+        s_changed = ch;
+        if (!ok) s_abort = 1;
+      }
+    }
+    // 4. counts of the blocks before this one
+    {
+      const int c = tid / MOE_MAX_G, r = tid % MOE_MAX_G;
+      int pre = 0, ok = 1;
+      if (r < G) {
+        for (int j = c; j < b; j += kXWaves) {
+          uint32_t v = 0;
+          if (!xwait(xr + static_cast<int64_t>(j) * words + r, round, v)) {
+            ok = 0;
+            break;
+          }
+          pre += static_cast<int>(v);
+        }
+      }
+      s_pre[c][r] = pre;
+      if (!ok) s_abort = 1;
+    }
+    __syncthreads();
+    if (s_abort) {
+      if (tid == 0) report(d_err, MOE_DERR_SYNC);
+      return;
+    }
+    const bool last = (round > 0 && !s_changed) || round + 1 == max_rounds;
+    // 5. (wave 0) prefix per rank; unless this is the last round,
+    // the next round's feasibility: ranks open for the whole block, and the
+    // ranks whose cap-th taker lies inside it, with its position
+    if (wave == 0) {
+      const int r = lane;
+      int P = 0;
+      if (r < G) {
+#pragma unroll
+        for (int c = 0; c < kXWaves; ++c) P += s_pre[c][r];
+        s_P[r] = P;
+      }
+      if (!last) {
+        const bool open = r < G && P + s_cnt[r] < cap;
+        const bool cross = r < G && P < cap && P + s_cnt[r] >= cap;
+        const uint64_t om = ballot(open);
+        uint64_t cm = ballot(cross);
+        int i = 0;
+        while (cm != 0) {  // uniform: one crossing rank at a time, the whole wave
+          const int rr = __ffsll(static_cast<long long>(cm)) - 1;
+          cm &= cm - 1;
+          const int need = cap - s_P[rr];
+          const int n = lane < nchunks ? s_cc[lane][rr] : 0;
+          const int incl = wave_incl_scan(n);
+          const uint64_t hit = ballot(lane < nchunks && incl >= need);
+          const int q = __ffsll(static_cast<long long>(hit)) - 1;
+          const int rest = need - (__shfl(incl, q, kWave) - __shfl(n, q, kWave));
+          const int base = (q / kXWaves) * kXThreads + (q % kXWaves) * kWave;
+          uint64_t mm = ballot(s_choice[base + lane] == rr);
+          for (int z = 1; z < rest; ++z) mm &= mm - 1;
+          if (lane == 0) {
+            s_xrank[i] = rr;
+            s_xlimit[i] = t0 + base + (__ffsll(static_cast<long long>(mm)) - 1);
+          }
+          ++i;
+        }
+        if (lane == 0) {
+          s_open = om;
+          s_ncross = i;
+        }
+      }
+    }
+    __syncthreads();
+    if (last) break;
+  }
+
+  // Positions: the rank's shard offset r * cap + its tokens in earlier blocks
+  // + in earlier chunks of this block + those before the token in its chunk.
+  // Each wave turns the chunk counts of a sixteenth of the ranks into first
+  // positions (lane = chunk).
+  for (int r = wave; r < G; r += kXWaves) {
+    const int n = lane < nchunks ? s_cc[lane][r] : 0;
+    const int excl = wave_incl_scan(n) - n;
+    if (lane < nchunks) s_cc[lane][r] = r * cap + s_P[r] + excl;
+  }
+  __syncthreads();
+  if (b == 0 && tid <= G) shard_offsets[tid] = tid * cap;
+  for (int u = 0; u < tpt; ++u) {
+    const int t = t0 + u * kXThreads + tid;
+    const int c = s_choice[u * kXThreads + tid];
+    // lanes before this one with the same rank: one ballot per distinct rank
+    int below = 0;
+    uint64_t rest = ballot(t < T && c < G);
+    while (rest != 0) {
+      const int v = __shfl(c, __ffsll(static_cast<long long>(rest)) - 1, kWave);
+      const uint64_t m = ballot(c == v);
+      if (c == v) below = lanes_below(m);
+      rest &= ~m;
+    }
+    if (t < T) {
+      const int pos = s_cc[u * kXWaves + wave][c] + below;
+      pred_rank[t] = c;
+      dest_pos[t] = pos;
+      if (perm != nullptr) perm[pos] = t;
+    }
+  }
+}
+
+// Launch shape of the exchange form for T tokens, or ok = false when it does
+// not apply (no tokens, more than kXBlocks * kXThreads * kXMaxTpt tokens, or
+// more blocks than the device holds at once, which the blocks' waits on each
+// other need): then the round-per-launch kernels and the plan's sort run.
+struct XShape {
+  bool ok;
+  int tpt, TB, nb;
+};
+
+std::mutex g_xres_mu;
+int g_xres[64] = {};  // blocks of the exchange kernel the device holds at once, per device
+
+int exchange_residency() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(g_xres_mu);
+  if (g_xres[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    // the fewest blocks per CU over the kernel's instances
+    const void* kernels[] = {reinterpret_cast<const void*>(shuffle_exchange_kernel<1>),
+                             reinterpret_cast<const void*>(shuffle_exchange_kernel<2>),
+                             reinterpret_cast<const void*>(shuffle_exchange_kernel<3>),
+                             reinterpret_cast<const void*>(shuffle_exchange_kernel<4>)};
+    per_cu = INT32_MAX;
+    for (const void* kern : kernels) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kXThreads, 0) != hipSuccess)
+        return 0;
+      per_cu = n < per_cu ? n : per_cu;
+    }
+    g_xres[dev] = per_cu * cus;
+  }
+  return g_xres[dev];
+}
+
+XShape exchange_shape(int64_t T) {
+  XShape x{false, 0, 0, 0};
+  if (T <= 0) return x;
+  const int64_t per_pass = static_cast<int64_t>(kXBlocks) * kXThreads;
+  const int64_t tpt = (T + per_pass - 1) / per_pass;
+  if (tpt > kXMaxTpt) return x;
+  x.tpt = static_cast<int>(tpt);
+  x.TB = x.tpt * kXThreads;
+  x.nb = static_cast<int>((T + x.TB - 1) / x.TB);
+  x.ok = x.nb <= exchange_residency();
+  return x;
+}
+
 struct BalancedWs {
   ShuffleWs base;
   int64_t* scores;
@@ -369,6 +783,7 @@ struct BalancedWs {
   int32_t* flag;
   int32_t* tile_cnt;   // [2][NT][G]
   uint64_t* tile_mask; // [2][NT][G][waves per tile]
+  uint8_t* prefs;      // [T][pref_stride(G)]: each token's ranks in preference order
   size_t bytes;
 };
 
@@ -389,6 +804,7 @@ BalancedWs balanced_layout(void* base, int64_t T, int E, int G) {
   w.flag = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
   w.tile_cnt = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 2 * ntc * G));
   w.tile_mask = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 2 * ntc * G * kBalWaves));
+  w.prefs = reinterpret_cast<uint8_t*>(take(static_cast<size_t>(T > 0 ? T : 1) * pref_stride(G)));
   w.bytes = off;
   return w;
 }
@@ -429,6 +845,31 @@ extern "C" int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E
                                                           Ti, w.base.M, w.base.identity,
                                                           w.base.src1, d_err);
   MOE_CHECK_LAUNCH();
+  const moe::XShape xs = moe::exchange_shape(T);
+  if (xs.ok) {
+    const int64_t Gs = moe::pref_stride(G);
+    const int64_t rec_words = 2ll * xs.nb * (G + 1);
+    const int W = moe::group_width(G);
+    moe::prefs_sort_kernel<<<(Ti + 256 / W - 1) / (256 / W), 256, 0, s>>>(
+        topk, Ti, k, E, w.base.M, G, W, Gs, w.prefs, w.base.rec, rec_words, d_err);
+    MOE_CHECK_LAUNCH();
+    const int pwords = static_cast<int>(Gs / 16);
+    auto launch = [&](auto kernel) {
+      kernel<<<xs.nb, moe::kXThreads, 0, s>>>(w.prefs, Gs, Ti, G, Ti / G, xs.TB, xs.tpt, xs.nb,
+                                              w.base.rec, pred_rank, dest_pos, perm,
+                                              shard_offsets, d_err);
+    };
+    if (pwords == 1)
+      launch(moe::shuffle_exchange_kernel<1>);
+    else if (pwords == 2)
+      launch(moe::shuffle_exchange_kernel<2>);
+    else if (pwords == 3)
+      launch(moe::shuffle_exchange_kernel<3>);
+    else
+      launch(moe::shuffle_exchange_kernel<4>);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
   moe::balanced_scores_kernel<<<blocks, moe::kBalTile, 0, s>>>(topk, Ti, k, E, w.base.M, G,
                                                                w.scores, w.flag, d_err);
   MOE_CHECK_LAUNCH();
@@ -481,6 +922,24 @@ extern "C" int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E,
   moe::rank_score_kernel<<<E, moe::kScoreThreads, 0, s>>>(transition, E_next, expert_rank_next, G, Ti,
                                                   w.M, w.identity, w.src1, d_err);
   MOE_CHECK_LAUNCH();
+  // The prediction: for up to 16 ranks, fused with the sort's tile counts
+  // (predict_count_kernel below); above, a group of lanes per token reads the
+  // token's rows of M coalesced (rank_argmax_kernel) and the plan's count
+  // kernel takes the tile counts.  Neither waits on other blocks, so the
+  // prediction can run beside other kernels.
+  if (G > 16 && Ti > 0) {
+    const int W = moe::group_width(G);
+    moe::rank_argmax_kernel<<<(Ti + 256 / W - 1) / (256 / W), 256, 0, s>>>(
+        topk, Ti, k, E, w.M, G, W, pred_rank, w.rec, 0, d_err);
+    MOE_CHECK_LAUNCH();
+    moe::PlanArgs a{pred_rank,      nullptr,        Ti,        1,
+                    G,              w.identity,     G,         G,
+                    w.src1,         T,              w.send_counts, w.send_offsets,
+                    perm ? perm : w.perm_scratch,   nullptr,   dest_pos,
+                    nullptr,        w.counters,     d_err,     w.plan_ws,
+                    shard_offsets};
+    return moe::launch_plan(a, s);
+  }
   // the sort's tiles: one source rank, 256 tokens each, numbered from 0
   const moe::PlanTiles tiles = moe::plan_tiles(w.plan_ws, T, G);
   if (Ti > 0) {

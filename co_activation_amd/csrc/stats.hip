@@ -7,46 +7,69 @@
 // together in a layer, and the experts of one layer predicting those of the
 // next (transition counts).
 //
-// Each block owns a slice of matrix rows as a 64 KB LDS histogram and a
-// chunk of tokens; every token adds its slot pairs with LDS atomics; the
-// non-zero bins are then added to the output with global atomics.  Integer
-// addition is associative, so the counts do not depend on scheduling.  The
-// pair matrix is counted on and above the diagonal only (i <= j, the
-// diagonal being the per-expert count); a final pass mirrors it, copies the
-// diagonal out and evaluates Ochiai in double precision.
+// The token range is cut into splits and the matrix rows into slices of at
+// most kSliceBins bins; block (split, slice) counts its split's tokens into a
+// 16 KB LDS histogram of its slice with LDS atomics and writes the histogram
+// to its own partial row in the workspace (each thread loads the ids of its
+// tokens of a pass before counting any, so their latencies overlap).  A sum
+// kernel adds the splits' partials bin by bin (integer addition, so the
+// counts do not depend on scheduling), and a finish kernel mirrors the pair
+// matrix, copies the diagonal out as the per-expert counts and evaluates
+// Ochiai in double precision.  No global atomics; every output element is written, so nothing
+// needs clearing first.  The pair matrix is counted on and above the
+// diagonal only (i <= j).
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
 constexpr int kStatThreads = 256;
-constexpr int kHistBins = 16384;  // 64 KB of int32 per block
-constexpr int kTokensPerBlock = 1024;
+constexpr int kSliceBins = 4096;         // 16 KB of int32 per block
+constexpr int kTokensPerThread = 4;
+constexpr int kSplitTokens = kStatThreads * kTokensPerThread;  // until kMaxSplits
+constexpr int kMaxSplits = 64;
 
 enum StatMode { kCounts = 0, kPairs = 1, kTransitions = 2 };
 
-// Work of one statistics call, split into histogram slices of matrix rows:
-// slices [0, a_slices) belong to matrix A (per-expert counts, or the pair
-// matrix counted on and above its diagonal), slices [a_slices, a_slices +
-// b_slices) to the transition matrix B.
+// Work of one statistics call.  Matrix A is the per-expert counts (one row
+// of E bins) or the pair matrix (E x E, upper triangle counted); matrix B the
+// transitions (E x E_next).  Slices [0, a_slices) cover A's rows, a_rps rows
+// each; [a_slices, a_slices + b_slices) cover B's.  A split's partial row
+// holds A's bins, then B's.
 struct StatsJob {
   int a_mode;  // kCounts or kPairs
   int a_rows, a_cols, a_rps, a_slices;
-  int32_t* a_out;
   int b_rows, b_cols, b_rps, b_slices;
-  int32_t* b_out;
+  int splits, split_tokens;
+  int64_t a_bins, b_bins;  // bins of each matrix in a partial row
 };
 
-// Zeroes the output arrays the count pass accumulates into.
-__global__ void zero_kernel(int32_t* __restrict__ a, int64_t na, int32_t* __restrict__ b, int64_t nb) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < na + nb;
-       i += stride) {
-    if (i < na)
-      a[i] = 0;
-    else
-      b[i - na] = 0;
+StatsJob stats_job(int64_t T, int E, bool pairs, bool transitions, int E_next) {
+  StatsJob j{};
+  j.a_mode = pairs ? kPairs : kCounts;
+  j.a_rows = pairs ? E : 1;
+  j.a_cols = E;
+  j.a_rps = pairs ? kSliceBins / E : 1;
+  j.a_slices = (j.a_rows + j.a_rps - 1) / j.a_rps;
+  j.a_bins = static_cast<int64_t>(j.a_rows) * j.a_cols;
+  if (transitions) {
+    j.b_rows = E;
+    j.b_cols = E_next;
+    j.b_rps = kSliceBins / E_next;
+    j.b_slices = (E + j.b_rps - 1) / j.b_rps;
+    j.b_bins = static_cast<int64_t>(E) * E_next;
   }
+  int64_t splits = (T + kSplitTokens - 1) / kSplitTokens;
+  if (splits < 1) splits = 1;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  j.splits = static_cast<int>(splits);
+  j.split_tokens = static_cast<int>((T + splits - 1) / splits);
+  return j;
+}
+
+size_t stats_workspace_bytes(const StatsJob& j) {
+  const size_t b = sizeof(int32_t) * static_cast<size_t>(j.splits) * (j.a_bins + j.b_bins);
+  return (b + 255) & ~static_cast<size_t>(255);
 }
 
 // Reads one token's ids into e[]; out-of-range slots become -1.
@@ -72,8 +95,9 @@ __device__ __forceinline__ int load_ids(const int32_t* __restrict__ row, int k, 
 
 __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int32_t* __restrict__ topk2,
-    int k2, int E2, StatsJob job, int tokens_per_block, int32_t* d_err) {
-  __shared__ int hist[kHistBins];
+    int k2, int E2, StatsJob job, int32_t* __restrict__ partial, int32_t* d_err) {
+  __shared__ int hist[kSliceBins];
+  const int split = blockIdx.x;
   const int slice = blockIdx.y;
   const bool in_a = slice < job.a_slices;
   const int mode = in_a ? job.a_mode : kTransitions;
@@ -86,46 +110,88 @@ __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
   for (int i = threadIdx.x; i < slice_bins; i += kStatThreads) hist[i] = 0;
   __syncthreads();
 
-  const int tb0 = blockIdx.x * tokens_per_block;
-  const int tb1 = min(T, tb0 + tokens_per_block);
+  const int tb0 = split * job.split_tokens;
+  const int tb1 = min(T, tb0 + job.split_tokens);
   int errbits = 0;
-  for (int t = tb0 + static_cast<int>(threadIdx.x); t < tb1; t += kStatThreads) {
-    int e[MOE_MAX_K];
-    errbits |= load_ids(topk + static_cast<int64_t>(t) * k, k, E, e);
-    if (mode == kCounts) {
+  // kTokensPerThread tokens per pass, their ids loaded before any is counted
+  for (int base = tb0; base < tb1; base += kStatThreads * kTokensPerThread) {
+    int e[kTokensPerThread][MOE_MAX_K];
+    int f[kTokensPerThread][MOE_MAX_K];
 #pragma unroll
-      for (int a = 0; a < MOE_MAX_K; ++a)
-        if (a < k && e[a] >= 0) atomicAdd(&hist[e[a]], 1);
-    } else if (mode == kPairs) {
+    for (int u = 0; u < kTokensPerThread; ++u) {
+      const int t = base + u * kStatThreads + static_cast<int>(threadIdx.x);
 #pragma unroll
-      for (int a = 0; a < MOE_MAX_K; ++a) {
-        if (a >= k || e[a] < 0) continue;
-#pragma unroll
-        for (int b = a; b < MOE_MAX_K; ++b) {
-          if (b >= k || e[b] < 0) continue;
-          const int i = min(e[a], e[b]), j = max(e[a], e[b]);
-          if (i >= r0 && i < r1) atomicAdd(&hist[(i - r0) * ncols + j], 1);
-        }
+      for (int a = 0; a < MOE_MAX_K; ++a) e[u][a] = f[u][a] = -1;
+      if (t < tb1) {
+        errbits |= load_ids(topk + static_cast<int64_t>(t) * k, k, E, e[u]);
+        if (mode == kTransitions) errbits |= load_ids(topk2 + static_cast<int64_t>(t) * k2, k2, E2, f[u]);
       }
-    } else {
-      int f[MOE_MAX_K];
-      errbits |= load_ids(topk2 + static_cast<int64_t>(t) * k2, k2, E2, f);
+    }
 #pragma unroll
-      for (int a = 0; a < MOE_MAX_K; ++a) {
-        if (a >= k || e[a] < r0 || e[a] >= r1) continue;
+    for (int u = 0; u < kTokensPerThread; ++u) {
+      if (mode == kCounts) {
 #pragma unroll
-        for (int b = 0; b < MOE_MAX_K; ++b)
-          if (b < k2 && f[b] >= 0) atomicAdd(&hist[(e[a] - r0) * ncols + f[b]], 1);
+        for (int a = 0; a < MOE_MAX_K; ++a)
+          if (a < k && e[u][a] >= 0) atomicAdd(&hist[e[u][a]], 1);
+      } else if (mode == kPairs) {
+#pragma unroll
+        for (int a = 0; a < MOE_MAX_K; ++a) {
+          if (a >= k || e[u][a] < 0) continue;
+#pragma unroll
+          for (int b = a; b < MOE_MAX_K; ++b) {
+            if (b >= k || e[u][b] < 0) continue;
+            const int i = min(e[u][a], e[u][b]), j = max(e[u][a], e[u][b]);
+            if (i >= r0 && i < r1) atomicAdd(&hist[(i - r0) * ncols + j], 1);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int a = 0; a < MOE_MAX_K; ++a) {
+          if (a >= k || e[u][a] < r0 || e[u][a] >= r1) continue;
+#pragma unroll
+          for (int b = 0; b < MOE_MAX_K; ++b)
+            if (b < k2 && f[u][b] >= 0) atomicAdd(&hist[(e[u][a] - r0) * ncols + f[u][b]], 1);
+        }
       }
     }
   }
   // One slice of each matrix reports the data errors it saw.
   if (slice == 0 || slice == job.a_slices) report(d_err, errbits);
   __syncthreads();
-  int32_t* dst = (in_a ? job.a_out : job.b_out) + static_cast<int64_t>(r0) * ncols;
-  for (int i = threadIdx.x; i < slice_bins; i += kStatThreads) {
-    const int v = hist[i];
-    if (v != 0) atomicAdd(dst + i, v);
+  int32_t* dst = partial + static_cast<int64_t>(split) * (job.a_bins + job.b_bins) +
+                 (in_a ? 0 : job.a_bins) + static_cast<int64_t>(r0) * ncols;
+  for (int i = threadIdx.x; i < slice_bins; i += kStatThreads) dst[i] = hist[i];
+}
+
+// Sum over the splits of one partial bin (independent loads, unrolled).
+__device__ __forceinline__ int split_sum(const int32_t* __restrict__ p, int64_t row, int splits) {
+  int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += p[static_cast<int64_t>(s + q) * row];
+  }
+  for (; s < splits; ++s) acc[0] += p[static_cast<int64_t>(s) * row];
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+// Adds the splits' partials bin by bin: A's bins into pair_count (on and
+// above the diagonal; the finish kernel fills the rest) or expert_count, B's
+// into transition.
+__global__ void stats_sum_kernel(const int32_t* __restrict__ partial, StatsJob job, int E,
+                                 int32_t* __restrict__ a_out, int32_t* __restrict__ b_out) {
+  const int64_t n = job.a_bins + job.b_bins;
+  for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < n;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    if (idx < job.a_bins && job.a_mode == kPairs) {
+      const int64_t i = idx / E, j = idx - i * E;
+      if (j < i) continue;
+    }
+    const int c = split_sum(partial + idx, n, job.splits);
+    if (idx < job.a_bins)
+      a_out[idx] = c;
+    else
+      b_out[idx - job.a_bins] = c;
   }
 }
 
@@ -153,13 +219,9 @@ unsigned grid_for(int64_t n) {
   return static_cast<unsigned>(b < 1 ? 1 : (b > 1024 ? 1024 : b));
 }
 
-}  // namespace
-}  // namespace moe
-
-extern "C" int moe_coact_stats(const int32_t* topk, int64_t T, int k, int E,
-                               const int32_t* topk_next, int k_next, int E_next,
-                               int32_t* expert_count, int32_t* pair_count, float* ochiai,
-                               int32_t* transition, int32_t* d_err, void* stream) {
+int stats_check(int64_t T, int k, int E, const int32_t* topk, const int32_t* topk_next,
+                int k_next, int E_next, const int32_t* expert_count, const int32_t* pair_count,
+                const float* ochiai, const int32_t* transition) {
   if (T < 0 || k < 1 || k > MOE_MAX_K || E < 1 || E > MOE_MAX_E ||
       T * static_cast<int64_t>(k) >= (int64_t{1} << 31))
     return MOE_ERR_SHAPE;
@@ -171,43 +233,43 @@ extern "C" int moe_coact_stats(const int32_t* topk, int64_t T, int k, int E,
   if (ochiai != nullptr && pair_count == nullptr) return MOE_ERR_NULL;
   if (T > 0 && topk == nullptr) return MOE_ERR_NULL;
   if (transition != nullptr && T > 0 && topk_next == nullptr) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_coact_stats_workspace_size(int64_t T, int E, int pairs, int E_next,
+                                              size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return MOE_ERR_NULL;
+  if (T < 0 || E < 1 || E > MOE_MAX_E || E_next < 0 || E_next > MOE_MAX_E) return MOE_ERR_SHAPE;
+  *ws_bytes = moe::stats_workspace_bytes(moe::stats_job(T, E, pairs != 0, E_next > 0, E_next));
+  return MOE_OK;
+}
+
+extern "C" int moe_coact_stats(const int32_t* topk, int64_t T, int k, int E,
+                               const int32_t* topk_next, int k_next, int E_next,
+                               int32_t* expert_count, int32_t* pair_count, float* ochiai,
+                               int32_t* transition, int32_t* d_err, void* ws, size_t ws_bytes,
+                               void* stream) {
+  const int st = moe::stats_check(T, k, E, topk, topk_next, k_next, E_next, expert_count,
+                                  pair_count, ochiai, transition);
+  if (st != MOE_OK) return st;
+  const moe::StatsJob job =
+      moe::stats_job(T, E, pair_count != nullptr, transition != nullptr, E_next);
+  if (ws == nullptr) return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe::stats_workspace_bytes(job)) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Ti = static_cast<int>(T);
-
-  moe::StatsJob job{};
-  if (pair_count != nullptr) {
-    job.a_mode = moe::kPairs;
-    job.a_rows = E;
-    job.a_cols = E;
-    job.a_rps = moe::kHistBins / E;
-    job.a_out = pair_count;
-  } else {
-    job.a_mode = moe::kCounts;
-    job.a_rows = 1;
-    job.a_cols = E;
-    job.a_rps = 1;
-    job.a_out = expert_count;
-  }
-  job.a_slices = (job.a_rows + job.a_rps - 1) / job.a_rps;
-  const int64_t na = static_cast<int64_t>(job.a_rows) * job.a_cols;
-  int64_t nb = 0;
-  if (transition != nullptr) {
-    job.b_rows = E;
-    job.b_cols = E_next;
-    job.b_rps = moe::kHistBins / E_next;
-    job.b_slices = (E + job.b_rps - 1) / job.b_rps;
-    job.b_out = transition;
-    nb = static_cast<int64_t>(E) * E_next;
-  }
-
-  moe::zero_kernel<<<moe::grid_for(na + nb), 256, 0, s>>>(job.a_out, na, job.b_out, nb);
+  int32_t* partial = static_cast<int32_t*>(ws);
+  // count (every partial bin of every split is written, also for T = 0)
+  moe::stats_count_kernel<<<dim3(job.splits, job.a_slices + job.b_slices), moe::kStatThreads, 0,
+                            s>>>(topk, Ti, k, E, topk_next, k_next, E_next, job, partial, d_err);
   MOE_CHECK_LAUNCH();
-  if (Ti > 0) {
-    const int bx = (Ti + moe::kTokensPerBlock - 1) / moe::kTokensPerBlock;
-    moe::stats_count_kernel<<<dim3(bx, job.a_slices + job.b_slices), moe::kStatThreads, 0, s>>>(
-        topk, Ti, k, E, topk_next, k_next, E_next, job, moe::kTokensPerBlock, d_err);
-    MOE_CHECK_LAUNCH();
-  }
+  moe::stats_sum_kernel<<<moe::grid_for(job.a_bins + job.b_bins), 256, 0, s>>>(
+      partial, job, E, pair_count != nullptr ? pair_count : expert_count, transition);
+  MOE_CHECK_LAUNCH();
   if (pair_count != nullptr) {
     moe::stats_finish_kernel<<<moe::grid_for(static_cast<int64_t>(E) * E), 256, 0, s>>>(
         E, pair_count, expert_count, ochiai);

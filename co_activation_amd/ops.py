@@ -52,6 +52,26 @@ def _want(t: torch.Tensor, name: str, dtype=None, shape=None) -> torch.Tensor:
     return t
 
 
+def _same_device(ref: torch.Tensor, *ts) -> None:
+    """Every given tensor lives on ref's device (the kernels run there and
+    would otherwise be handed another device's pointers)."""
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"all tensors of a call must be on {ref.device}, "
+                             f"got one on {t.device}")
+
+
+def _err_word(d_err: Optional[torch.Tensor], ref: torch.Tensor):
+    """The device error word: None, or one int32 element on ref's device."""
+    if d_err is None:
+        return None
+    _want(d_err, "d_err", torch.int32)
+    if d_err.numel() != 1:
+        raise ValueError("d_err must be a single int32 element")
+    _same_device(ref, d_err)
+    return d_err
+
+
 def _alloc(out: Optional[dict], key: str, shape, dtype, device) -> torch.Tensor:
     if out is not None and out.get(key) is not None:
         return _want(out[key], key, dtype, shape)
@@ -74,11 +94,20 @@ def raise_on_errors(d_err: torch.Tensor) -> None:
 
 # ----------------------------------------------------------------- stats
 
+def stats_workspace_bytes(T: int, E: int, pairs: bool = True, E_next: int = 0) -> int:
+    n = ctypes.c_size_t()
+    check("moe_coact_stats_workspace_size",
+          _lib.lib().moe_coact_stats_workspace_size(T, E, int(pairs), E_next, ctypes.byref(n)))
+    return n.value
+
+
 def coact_stats(topk: torch.Tensor, E: int, topk_next: Optional[torch.Tensor] = None,
                 E_next: Optional[int] = None, *, pairs: bool = True, ochiai: bool = True,
-                out: Optional[dict] = None, d_err: Optional[torch.Tensor] = None) -> dict:
+                out: Optional[dict] = None, ws: Optional[torch.Tensor] = None,
+                d_err: Optional[torch.Tensor] = None) -> dict:
     """moe_coact_stats: expert_count [E], pair_count [E,E], ochiai [E,E],
-    transition [E,E_next] (when topk_next is given)."""
+    transition [E,E_next] (when topk_next is given).  ws: the workspace
+    (uint8, at least stats_workspace_bytes); allocated here when not given."""
     _want(topk, "topk", torch.int32)
     T, k = topk.shape
     dev = topk.device
@@ -94,10 +123,17 @@ def coact_stats(topk: torch.Tensor, E: int, topk_next: Optional[torch.Tensor] = 
             raise ValueError("topk_next must cover the same tokens")
         k2 = topk_next.shape[1]
         res["transition"] = _alloc(out, "transition", (E, E_next), torch.int32, dev)
+    need = stats_workspace_bytes(T, E, pairs, E_next if topk_next is not None else 0)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _want(ws, "ws", torch.uint8)
+    err = _err_word(d_err, topk)
+    _same_device(topk, topk_next, ws, res.get("pair_count"), res.get("ochiai"),
+                 res.get("transition"), res["expert_count"])
     st = _lib.lib().moe_coact_stats(
         _p(topk), T, k, E, _p(topk_next), k2, E_next or 0, _p(res["expert_count"]),
-        _p(res.get("pair_count")), _p(res.get("ochiai")), _p(res.get("transition")), _p(d_err),
-        _stream(topk))
+        _p(res.get("pair_count")), _p(res.get("ochiai")), _p(res.get("transition")), _p(err),
+        _p(ws), ws.numel(), _stream(topk))
     check("moe_coact_stats", st)
     return res
 
@@ -156,10 +192,13 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _want(ws, "ws", torch.uint8)
+    err = _err_word(d_err, topk)
     if perm is None:
+        _same_device(topk, gates, expert_rank, src_offsets, sc, so, rt, rw, tr, sr, cn, ws, perm,
+                     topk_out, gates_out)
         st = _lib.lib().moe_dispatch_plan(
             _p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node, _p(src_offsets),
-            cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(d_err), _p(ws),
+            cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(err), _p(ws),
             ws.numel(), _stream(topk))
         check("moe_dispatch_plan", st)
         return Plan(sc, so, rt, rw, tr, sr, cn)
@@ -170,10 +209,12 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
     _want(topk_out, "topk_out", torch.int32, (T, k))
     if gates is not None:
         _want(gates_out, "gates_out", torch.float32, (T, k))
+    _same_device(topk, gates, expert_rank, src_offsets, sc, so, rt, rw, tr, sr, cn, ws, perm,
+                 topk_out, gates_out)
     st = _lib.lib().moe_dispatch_plan_gathered(
         _p(topk), _p(gates), _p(perm), T, k, E, _p(expert_rank), G, ranks_per_node,
         _p(src_offsets), cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn),
-        _p(topk_out), _p(gates_out), _p(d_err), _p(ws), ws.numel(), _stream(topk))
+        _p(topk_out), _p(gates_out), _p(err), _p(ws), ws.numel(), _stream(topk))
     check("moe_dispatch_plan_gathered", st)
     return Plan(sc, so, rt, rw, tr, sr, cn)
 
@@ -209,9 +250,11 @@ def dispatch_plan_noalloc(topk: torch.Tensor, gates: Optional[torch.Tensor],
     if sr is not None:
         _want(sr, "slot_row", torch.int32, (T, k))
     cn = _want(out["counters"], "counters", torch.int64, (8,))
+    err = _err_word(d_err, topk)
+    _same_device(topk, gates, expert_rank, src_offsets, sc, so, rt, rw, tr, sr, cn)
     st = _lib.lib().moe_dispatch_plan_noalloc(
         _p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node, _p(src_offsets), cap,
-        _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(d_err), _stream(topk))
+        _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(err), _stream(topk))
     check("moe_dispatch_plan_noalloc", st)
     return Plan(sc, so, rt, rw, tr, sr, cn)
 
@@ -239,8 +282,10 @@ def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
         raise ValueError("out rows must match x rows")
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
+    err = _err_word(d_err, x)
+    _same_device(x, dest, out, n_valid)
     st = _lib.lib().moe_permute(_p(x), T, row_bytes, _p(dest), width, _p(out), out_rows,
-                                _p(n_valid), _p(d_err), _stream(x))
+                                _p(n_valid), _p(err), _stream(x))
     check("moe_permute", st)
     return out
 
@@ -269,8 +314,10 @@ def shuffle_dispatch(x: torch.Tensor, perm: torch.Tensor, token_rows: torch.Tens
     _want(send, "send", x.dtype)
     if x_out.shape != x.shape or tuple(send.shape[1:]) != row_shape or send.shape[0] < send_rows:
         raise ValueError("x_out must match x; send needs send_rows rows shaped like x's rows")
+    err = _err_word(d_err, x)
+    _same_device(x, perm, token_rows, x_out, send)
     st = _lib.lib().moe_shuffle_dispatch(_p(x), T, row_bytes, _p(perm), _p(token_rows), k,
-                                         _p(x_out), _p(send), send_rows, _p(d_err), _stream(x))
+                                         _p(x_out), _p(send), send_rows, _p(err), _stream(x))
     check("moe_shuffle_dispatch", st)
     return x_out, send
 
@@ -294,8 +341,10 @@ def gather(x: torch.Tensor, src: torch.Tensor, *, out: Optional[torch.Tensor] = 
         raise ValueError("out must have n rows shaped like x's rows")
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
+    err = _err_word(d_err, x)
+    _same_device(x, src, out, n_valid)
     st = _lib.lib().moe_gather(_p(x), x.shape[0], row_bytes, _p(src), n, _p(out), _p(n_valid),
-                               _p(d_err), _stream(x))
+                               _p(err), _stream(x))
     check("moe_gather", st)
     return out
 
@@ -315,14 +364,19 @@ def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tens
     H = z.shape[1]
     if row_weight is not None:
         _want(row_weight, "row_weight", torch.float32)
+        if row_weight.dim() != 1 or row_weight.numel() < z.shape[0]:
+            raise ValueError("row_weight needs one weight per row of z (the kernel reads "
+                             "row_weight[r] for every row id r < z.shape[0])")
     out_dtype = out_dtype or z.dtype
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=z.device)
     _want(out, "out", out_dtype, (T, H))
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
+    err = _err_word(d_err, z)
+    _same_device(z, rows, row_weight, out, n_valid)
     st = _lib.lib().moe_combine(_p(z), _DT[z.dtype], z.shape[0], H, _p(rows), k, _p(row_weight),
-                                T, _p(out), _DT[out_dtype], _p(n_valid), _p(d_err), _stream(z))
+                                T, _p(out), _DT[out_dtype], _p(n_valid), _p(err), _stream(z))
     check("moe_combine", st)
     return out
 
@@ -359,8 +413,11 @@ def shuffle_predict(topk: torch.Tensor, transition: torch.Tensor, expert_rank_ne
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _want(ws, "ws", torch.uint8)
     fn = _lib.lib().moe_shuffle_balanced if balanced else _lib.lib().moe_shuffle_predict
+    err = _err_word(d_err, topk)
+    _same_device(topk, transition, expert_rank_next, ws, res["pred_rank"], res["dest_pos"],
+                 res["perm"], res["shard_offsets"])
     st = fn(_p(topk), T, k, E, _p(transition), E2, _p(expert_rank_next), G, _p(res["pred_rank"]),
-            _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(d_err), _p(ws),
+            _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(err), _p(ws),
             ws.numel(), _stream(topk))
     check("moe_shuffle_balanced" if balanced else "moe_shuffle_predict", st)
     return res
@@ -404,11 +461,13 @@ def expert_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank: 
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _want(ws, "ws", torch.uint8)
+    err = _err_word(d_err, topk)
+    _same_device(topk, gates, expert_rank, slot_row, ws, *res.values())
     st = _lib.lib().moe_expert_plan(
         _p(topk), _p(gates), T, k, E, _p(expert_rank), G, _p(slot_row), send_rows, _p(res["erow"]),
         _p(res["expert_first"]), _p(res["expert_count"]), _p(res["rank_offsets"]),
         _p(res["erow_weight"]), _p(res["erow_slot"]), _p(res["erow_src"]), _p(res["row_dest"]),
-        _p(d_err), _p(ws), ws.numel(), _stream(topk))
+        _p(err), _p(ws), ws.numel(), _stream(topk))
     check("moe_expert_plan", st)
     return res
 
@@ -435,8 +494,10 @@ def permute_scaled(x: torch.Tensor, dest: torch.Tensor, scale: torch.Tensor, out
         raise ValueError("scale and out need out_rows rows")
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
+    err = _err_word(d_err, x)
+    _same_device(x, dest, scale, out, n_valid)
     st = _lib.lib().moe_permute_scaled(_p(x), _DT[x.dtype], T, H, _p(dest), width, _p(scale),
-                                       _p(out), _DT[out_dtype], out_rows, _p(n_valid), _p(d_err),
+                                       _p(out), _DT[out_dtype], out_rows, _p(n_valid), _p(err),
                                        _stream(x))
     check("moe_permute_scaled", st)
     return out
@@ -460,8 +521,10 @@ def row_dot(a: torch.Tensor, b: torch.Tensor, rows: torch.Tensor, *,
     _want(out, "out", torch.float32)
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
+    err = _err_word(d_err, a)
+    _same_device(a, b, rows, out, n_valid)
     st = _lib.lib().moe_row_dot(_p(a), _DT[a.dtype], T, H, _p(b), _DT[b.dtype], b.shape[0],
-                                _p(rows), width, _p(out), _p(n_valid), _p(d_err), _stream(a))
+                                _p(rows), width, _p(out), _p(n_valid), _p(err), _stream(a))
     check("moe_row_dot", st)
     return out
 

@@ -4,7 +4,7 @@ steps.
 Single layer (workloads 1-4), ``LayerStep``:
     stats(topk) -> plan(topk, gates, placement) -> permute(x) -> combine(z)
 Two layers with token shuffling (workload 5, "Expert Coupling in MoE
-Pretraining ..." abstract: shuffle each token to the rank predicted to hold
+Pretraining ..." abstract: shuffle each token toward the rank forecast for
 its next-layer experts), ``TwoLayerStep``:
     stats(topk1, topk2) -> shuffle_predict(topk1, transition, placement2)
     -> plan(topk2, gates2, placement2, src_offsets = shard_offsets) over the
@@ -248,6 +248,8 @@ class LayerStep:
             "pair_count": torch.empty(E, E, dtype=torch.int32, device=dev),
             "ochiai": torch.empty(E, E, dtype=torch.float32, device=dev),
         }
+        self.stats_ws = torch.empty(ops.stats_workspace_bytes(self.T, E, True), dtype=torch.uint8,
+                                    device=dev)
         self.plan_out = self._plan_buffers(self.T, self.k, G, self.cap, dev)
         self.plan_ws = torch.empty(ops.plan_workspace_bytes(self.T, G), dtype=torch.uint8, device=dev)
         self.send = torch.empty((self.cap,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
@@ -281,7 +283,8 @@ class LayerStep:
 
     def _stats(self, timers):
         with _timed(timers, "stats"):
-            ops.coact_stats(self.topk, self.E, out=self.stats_out, d_err=self.d_err)
+            ops.coact_stats(self.topk, self.E, out=self.stats_out, ws=self.stats_ws,
+                            d_err=self.d_err)
 
     def _plan(self, timers):
         with _timed(timers, "plan"):
@@ -361,6 +364,12 @@ class TwoLayerStep:
         }
         self.shuffle_ws = torch.empty(ops.shuffle_workspace_bytes(T, E1, G, balanced),
                                       dtype=torch.uint8, device=dev)
+        # the statistics with transitions; without them (the pair counts on
+        # the second stream of the separate-pass step) in a workspace of their own
+        self.stats_ws = torch.empty(ops.stats_workspace_bytes(T, E1, True, E2), dtype=torch.uint8,
+                                    device=dev)
+        self.stats_ws2 = torch.empty(ops.stats_workspace_bytes(T, E1, True), dtype=torch.uint8,
+                                     device=dev)
         self.x_s = torch.empty_like(x)
         self.topk2_s = torch.empty_like(topk2)
         self.gates2_s = torch.empty_like(gates2)
@@ -402,10 +411,11 @@ class TwoLayerStep:
                 # and Ochiai are computed on the second stream below.
                 ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, pairs=False,
                                 out={"expert_count": self._counts_tmp,
-                                     "transition": st["transition"]}, d_err=self.d_err)
+                                     "transition": st["transition"]}, ws=self.stats_ws,
+                                d_err=self.d_err)
             else:
                 ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=st,
-                                d_err=self.d_err)
+                                ws=self.stats_ws, d_err=self.d_err)
         with _timed(timers, "shuffle_predict"):
             self.shuffle = ops.shuffle_predict(self.topk1, st["transition"], self.expert_rank2,
                                                self.G, balanced=self.balanced,
@@ -418,7 +428,7 @@ class TwoLayerStep:
             if overlap:
                 ops.coact_stats(self.topk1, self.E1, out={k: st[k] for k in
                                                           ("expert_count", "pair_count", "ochiai")},
-                                d_err=self.d_err)
+                                ws=self.stats_ws2, d_err=self.d_err)
         with _timed(timers, "shuffle_permute"):
             ops.gather(self.x, perm, out=self.x_s, d_err=self.d_err)
         fork.join()
@@ -434,7 +444,7 @@ class TwoLayerStep:
         and the layer-2 plan over the shuffled order."""
         with _timed(timers, "stats"):
             ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
-                            d_err=self.d_err)
+                            ws=self.stats_ws, d_err=self.d_err)
         with _timed(timers, "shuffle_predict"):
             self.shuffle = ops.shuffle_predict(self.topk1, self.stats_out["transition"],
                                                self.expert_rank2, self.G, balanced=self.balanced,

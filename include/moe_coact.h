@@ -49,6 +49,11 @@
  *     outputs are unspecified, except as stated per bit, but no kernel reads
  *     or writes outside the buffers described here.
  *   - Index arrays are int32; T*k must stay below 2^31.
+ *   - The row-moving calls (moe_permute, moe_gather, moe_shuffle_dispatch,
+ *     moe_combine, moe_permute_scaled, moe_row_dot) run many blocks at once,
+ *     so an output that shares bytes with an input would be read after other
+ *     blocks overwrote it: they return MOE_ERR_SHAPE, launching nothing,
+ *     when an output's extent (rows times row bytes) overlaps an input's.
  */
 #ifndef MOE_COACT_H
 #define MOE_COACT_H
@@ -80,6 +85,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
                                     valid; rows >= capacity are not written)             */
 #define MOE_DERR_SRC_OFFSETS 16  /* src_offsets not nondecreasing from 0 to T            */
 #define MOE_DERR_ROW_RANGE 32    /* permute/combine: a row index >= the buffer's rows    */
+#define MOE_DERR_SYNC 64         /* shuffle: blocks waiting on each other gave up after
+                                    their bound (outputs unspecified)                    */
 
 /* Limits checked on the host.  Besides these, the row-moving calls
    (moe_permute, moe_gather, moe_shuffle_dispatch, moe_combine,
@@ -113,19 +120,28 @@ const char* moe_status_string(int status);
  *                         rounded once to float; 0 where n_i * n_j == 0
  *   transition    [E*E_next] int32 out or NULL (needs topk_next):
  *                         X[i*E_next+j] = #{t : i in D_t, j in D'_t}
+ *   ws, ws_bytes  workspace of at least
+ *                 moe_coact_stats_workspace_size(T, E, pair_count != NULL,
+ *                 transition != NULL ? E_next : 0) bytes, 16-byte aligned:
+ *                 per-split partial counts (at most 64 splits of the tokens)
  * Limits: 1 <= k, k_next <= 8; 1 <= E, E_next <= 256; T >= 0.
  * d_err bits: EXPERT_RANGE (slot skipped), EXPERT_DUP.
- * Integer outputs are exact and independent of scheduling.
+ * Integer outputs are exact and independent of scheduling; every output
+ * element is written.
  * ---------------------------------------------------------------------- */
+int moe_coact_stats_workspace_size(int64_t T, int E, int pairs, int E_next,
+                                   size_t* ws_bytes /* host */);
 int moe_coact_stats(const int32_t* topk, int64_t T, int k, int E,
                     const int32_t* topk_next, int k_next, int E_next,
                     int32_t* expert_count, int32_t* pair_count, float* ochiai,
-                    int32_t* transition, int32_t* d_err, void* stream);
+                    int32_t* transition, int32_t* d_err, void* ws, size_t ws_bytes,
+                    void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_dispatch_plan -- deduplicated dispatch plan.
  *
- * [EC] abstract: a dispatcher that sends each token to each GPU once.
+ * [EC] abstract: deduplicated dispatch -- a token reaches a given GPU at
+ * most one time, however many of its experts live there.
  * [CB] Problem Formulation: tokens t with selected experts D_t, source rank
  * s_t, node N(r) of rank r, cross-node volume
  * V = sum_t |{N(r_t^e) : e in D_t} minus {N(s_t)}|; with one replica per
@@ -200,7 +216,7 @@ int moe_dispatch_plan_noalloc(const int32_t* topk, const float* gates, int64_t T
 /* ------------------------------------------------------------------------
  * moe_dispatch_plan_gathered -- the plan of a shuffled batch.
  *
- * [EC] abstract: tokens are shuffled to the rank predicted to hold their
+ * [EC] abstract: tokens are shuffled toward the rank forecast for their
  * next-layer experts, and the next layer's dispatch starts from there.  This
  * is moe_dispatch_plan on the routing in the shuffled order -- position p
  * holds token perm[p], i.e. topk'[p] = topk[perm[p]], gates'[p] =
@@ -313,8 +329,8 @@ int moe_combine(const void* z, int z_dtype, int64_t z_rows, int64_t H, const int
                 const int32_t* n_valid, int32_t* d_err, void* stream);
 
 /* ------------------------------------------------------------------------
- * moe_shuffle_predict -- token shuffling ([EC] abstract: move each token to
- * the GPU predicted to hold its next-layer experts).
+ * moe_shuffle_predict -- token shuffling ([EC] abstract: tokens reordered by
+ * the rank forecast for their next-layer experts).
  *
  * score_t[r] = sum_{i in D_t} sum_{j : expert_rank_next[j] == r} X[i][j]
  * (64-bit integer sums of the transition counts), pred_t = the highest

@@ -10,9 +10,10 @@ narrower type.
 Sources (cited by page title and section):
   [EC]  "Expert Coupling in MoE Pretraining: Reducing All-to-All Overhead with
         Correlated Placement and Token Shuffling" -- abstract: co-selection of
-        experts within a layer, cross-layer predictability, a dispatcher that
-        sends each token to each GPU once, token shuffling toward the GPU
-        predicted to hold the token's next-layer experts.
+        experts within a layer, cross-layer predictability, deduplicated
+        dispatch (a token reaches a given GPU at most one time), token
+        shuffling (tokens reordered by the rank forecast for their
+        next-layer experts).
   [CB]  "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
         Training" -- Key Observation (Ochiai similarity over the token sets of
         two experts; node-level deduplication) and Problem Formulation (the
@@ -163,8 +164,9 @@ def coact_stats(topk: np.ndarray, E: int, topk_next: Optional[np.ndarray] = None
 def dispatch_plan(topk: np.ndarray, gates: Optional[np.ndarray], expert_rank: np.ndarray,
                   G: int, ranks_per_node: int, src_offsets=None) -> dict:
     """Deduplicated dispatch plan: every token goes to every rank that holds
-    at least one of its experts exactly once ([EC] abstract, the dispatcher
-    that sends each token to each GPU once).
+    at least one of its experts exactly once ([EC] abstract: deduplicated
+    dispatch, one visit per GPU however many of the token's experts it
+    holds).
 
     With one replica per expert the rank of task (t, e) is forced,
     r_t^e = p(e) ([CB] Problem Formulation).  R_t = {p(e) : e in D_t} is the
@@ -362,8 +364,8 @@ def combine_unweighted(Z: np.ndarray, z_dtype: str, token_rows: np.ndarray,
 def shuffle_predict(topk: np.ndarray, transition: np.ndarray, expert_rank_next: np.ndarray,
                     G: int) -> dict:
     """Predict the rank holding each token's next-layer experts and order the
-    tokens by it ([EC] abstract: token shuffling moves each token to the GPU
-    predicted to hold its next-layer experts).
+    tokens by it ([EC] abstract: token shuffling, tokens reordered by the rank
+    forecast for their next-layer experts).
 
     Readings: the prediction scores rank r by the transition counts from the
     token's current experts into the next-layer experts placed on r,

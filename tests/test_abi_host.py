@@ -47,14 +47,37 @@ def test_workspace_queries(built_lib):
 
 def test_stats_rejects(built_lib):
     f = built_lib.moe_coact_stats
-    assert f(FAKE, 10, 9, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, NULL) == -2  # k > 8
-    assert f(FAKE, 10, 2, 257, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, NULL) == -2  # E > 256
-    assert f(FAKE, -1, 2, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, NULL) == -2
-    assert f(FAKE, 10, 2, 8, NULL, 0, 0, NULL, NULL, NULL, NULL, NULL, NULL) == -1  # counts
-    assert f(FAKE, 10, 2, 8, NULL, 0, 0, FAKE, NULL, FAKE, NULL, NULL, NULL) == -1  # ochiai w/o pairs
-    assert f(FAKE, 10, 2, 8, NULL, 2, 8, FAKE, NULL, NULL, FAKE, NULL, NULL) == -1  # no topk_next
-    assert f(FAKE, 10, 2, 8, FAKE, 0, 8, FAKE, NULL, NULL, FAKE, NULL, NULL) == -2  # k_next 0
-    assert f(FAKE, 2**30, 2, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, NULL) == -2  # T*k
+    W = (FAKE, 1 << 24, NULL)  # workspace, its bytes, stream
+    assert f(FAKE, 10, 9, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, *W) == -2  # k > 8
+    assert f(FAKE, 10, 2, 257, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, *W) == -2  # E > 256
+    assert f(FAKE, -1, 2, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, *W) == -2
+    assert f(FAKE, 10, 2, 8, NULL, 0, 0, NULL, NULL, NULL, NULL, NULL, *W) == -1  # counts
+    assert f(FAKE, 10, 2, 8, NULL, 0, 0, FAKE, NULL, FAKE, NULL, NULL, *W) == -1  # ochiai w/o pairs
+    assert f(FAKE, 10, 2, 8, NULL, 2, 8, FAKE, NULL, NULL, FAKE, NULL, *W) == -1  # no topk_next
+    assert f(FAKE, 10, 2, 8, FAKE, 0, 8, FAKE, NULL, NULL, FAKE, NULL, *W) == -2  # k_next 0
+    assert f(FAKE, 2**30, 2, 8, NULL, 0, 0, FAKE, NULL, NULL, NULL, NULL, *W) == -2  # T*k
+    assert f(FAKE, 10, 2, 8, NULL, 0, 0, FAKE, FAKE, NULL, NULL, NULL, NULL, 1 << 24, NULL) == -1
+    assert f(FAKE, 10, 2, 8, NULL, 0, 0, FAKE, FAKE, NULL, NULL, NULL, FAKE + 4, 1 << 24,
+             NULL) == -4                                                          # alignment
+    n = ctypes.c_size_t()
+    assert built_lib.moe_coact_stats_workspace_size(10, 8, 1, 0, ctypes.byref(n)) == 0
+    assert f(FAKE, 10, 2, 8, NULL, 0, 0, FAKE, FAKE, NULL, NULL, NULL, FAKE, n.value - 16,
+             NULL) == -5                                                          # too small
+
+
+def test_stats_workspace_sizes(built_lib):
+    """At most 64 splits of the tokens, each a partial of the counted bins."""
+    n = ctypes.c_size_t()
+    q = built_lib.moe_coact_stats_workspace_size
+    assert q(32768, 256, 1, 0, ctypes.byref(n)) == 0
+    assert n.value == 32 * 256 * 256 * 4                      # 32 splits of 1024 tokens
+    assert q(65536, 64, 1, 64, ctypes.byref(n)) == 0
+    assert n.value == 64 * (64 * 64 + 64 * 64) * 4            # pairs and transitions
+    assert q(1 << 24, 8, 0, 0, ctypes.byref(n)) == 0
+    assert n.value == 64 * 8 * 4                              # 64 splits of 8 counts
+    assert q(0, 8, 1, 0, ctypes.byref(n)) == 0 and n.value >= 8 * 8 * 4
+    assert q(10, 257, 1, 0, ctypes.byref(n)) == -2
+    assert q(10, 8, 1, 0, None) == -1
 
 
 def _plan(lib, **kw):
@@ -233,3 +256,28 @@ def test_probe_library_rejects(built_lib):
     assert f(0, 0, FAKE, NULL, 1024, NULL, NULL) == -1       # read needs sink
     assert f(1, 0, NULL, NULL, 1024, NULL, NULL) == -1       # write needs dst
     assert f(2, 0, FAKE + 8, FAKE, 1024, NULL, NULL) == -4   # alignment
+
+
+def test_overlapping_outputs_rejected(built_lib):
+    """An output sharing bytes with an input is refused with MOE_ERR_SHAPE
+    before any launch (blocks would read rows others already overwrote)."""
+    L = built_lib
+    RB = 256  # row bytes
+    # permute: x = 8 rows at FAKE, out = 8 rows starting inside x
+    assert L.moe_permute(FAKE, 8, RB, FAKE + 8192, 1, FAKE + 4 * RB, 8, NULL, NULL, NULL) == -2
+    assert L.moe_permute(FAKE, 8, RB, FAKE + 8192, 1, FAKE, 8, NULL, NULL, NULL) == -2  # in place
+    # gather: out ends inside x
+    assert L.moe_gather(FAKE + 2 * RB, 8, RB, FAKE + 8192, 4, FAKE, NULL, NULL, NULL) == -2
+    # shuffle dispatch: x_out over x, send over x, send over x_out
+    sd = L.moe_shuffle_dispatch
+    big = FAKE + (1 << 20)
+    assert sd(FAKE, 8, RB, big, big + 64, 2, FAKE, big + 4096, 16, NULL, NULL) == -2
+    assert sd(FAKE, 8, RB, big, big + 64, 2, big + 4096, FAKE + RB, 16, NULL, NULL) == -2
+    assert sd(FAKE, 8, RB, big, big + 64, 2, big + 4096, big + 4096 + RB, 16, NULL, NULL) == -2
+    # combine: y over z (bf16, H = 128: 256-byte rows)
+    assert L.moe_combine(FAKE, 1, 8, 128, big, 2, NULL, 4, FAKE + RB, 1, NULL, NULL, NULL) == -2
+    # backward: scaled permute out over x; row dot out over a
+    assert L.moe_permute_scaled(FAKE, 1, 8, 128, big, 1, big + 64, FAKE, 1, 8, NULL, NULL,
+                                NULL) == -2
+    assert L.moe_row_dot(FAKE, 1, 8, 128, big, 1, 8, big + 4096, 1, FAKE + 16, NULL, NULL,
+                         NULL) == -2

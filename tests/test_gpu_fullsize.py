@@ -1,7 +1,8 @@
 """Parity at the full workload sizes, through the same step objects the
-benchmark times.  Statistics, shuffle and plans are compared in full (bit for
-bit); send rows and combined tokens on seeded samples that the oracle computes
-one by one."""
+benchmark times.  Statistics, shuffles, plans, every send row (bit for bit)
+and every combined token (to the combine's bound) are compared in full, the
+rows and tokens in chunks so that host memory stays bounded; the destination
+side and the backward on a seeded sample of tokens."""
 
 import numpy as np
 import pytest
@@ -10,6 +11,7 @@ import torch
 import oracle
 from co_activation_amd.pipeline import (ExpertSideBackward, ExpertSideStep, LayerStep,
                                         TwoLayerStep)
+import gpu_util
 from gpu_util import assert_equal, bf16_ulps, check_combine, dev, host, i32, say, x_tensor
 from workloads import make
 from workloads.gen import device_normal
@@ -37,24 +39,53 @@ def _check_plan_full(plan, ref):
     assert_equal(host(plan.slot_row), ref["slot_row"], "slot_row")
 
 
-def _check_samples(step, ref_plan, x_rows_of_token, gates, zdt, rng):
-    """Sampled send rows and combined tokens."""
+ROW_CHUNK = 16384
+TOKEN_CHUNK = 2048
+
+
+def _check_rows_full(step, ref_plan, source_of_token):
+    """Every send row: send[i] == x[source_of_token(row_token[i])] bit for bit
+    (oracle.permute_rows on chunks of rows)."""
     N = int(ref_plan["N"])
-    rows = np.sort(rng.choice(N, size=min(SAMPLES, N), replace=False))
-    got = host(step.send[torch.from_numpy(rows).to("cuda")])
-    want = x_rows_of_token(ref_plan["row_token"][rows])
-    assert_equal(got, want, "sampled send rows")
+    x = source_of_token(None)
+    for a in range(0, N, ROW_CHUNK):
+        b = min(N, a + ROW_CHUNK)
+        want = oracle.permute_rows(x, source_of_token(ref_plan["row_token"][a:b]))
+        assert_equal(host(step.send[a:b]), want, f"send rows {a}..{b}")
+
+
+def _check_combine_full(step, ref_plan, gates, zdt):
+    """Every combined token against oracle.combine, in chunks of tokens (the
+    chunks' numpy checks on a few threads; the device reads stay on this
+    one); the bf16 elements held to the fp32 bound are counted and
+    bounded."""
+    from concurrent.futures import ThreadPoolExecutor
+
     T = ref_plan["token_rows"].shape[0]
-    toks = np.sort(rng.choice(T, size=min(SAMPLES, T), replace=False))
-    slot = ref_plan["slot_row"][toks]
-    uniq, inv = np.unique(slot, return_inverse=True)
-    Zs = host(step.z[torch.from_numpy(uniq).to("cuda")])
-    y_sample = step.y[torch.from_numpy(toks).to("cuda")]
-    check_combine(y_sample, Zs, zdt, inv.reshape(slot.shape), gates[toks], zdt, "sampled combine")
+    start = len(gpu_util.FALLBACKS)
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        futures = []
+        for a in range(0, T, TOKEN_CHUNK):
+            b = min(T, a + TOKEN_CHUNK)
+            slot = ref_plan["slot_row"][a:b]
+            uniq, inv = np.unique(slot, return_inverse=True)
+            Zs = host(step.z[torch.from_numpy(uniq).to("cuda")])
+            futures.append(pool.submit(gpu_util.check_combine_host, host(step.y[a:b]), Zs, zdt,
+                                       inv.reshape(slot.shape), gates[a:b], zdt,
+                                       f"combine tokens {a}..{b}"))
+            if len(futures) >= 16:  # bound the chunks held at once
+                futures.pop(0).result()
+        for f in futures:
+            f.result()
+    fb = gpu_util.FALLBACKS[start:]
+    n = sum(c for _, c, _ in fb)
+    total = sum(e for _, _, e in fb)
+    say("combine elements held to the fp32 bound (cancellation):", n, "of", total)
+    assert n <= max(16, 1e-5 * total), f"{n} of {total} elements needed the fp32 bound"
 
 
 @pytest.mark.parametrize("cfg,placement", [(1, "main"), (2, "main"), (2, "alt"), (3, "main"),
-                                           (4, "main"), (4, "alt")])
+                                           (3, "alt"), (4, "main"), (4, "alt")])
 def test_layer_fullsize(cfg, placement):
     w = make(cfg)
     er = w.expert_rank if placement == "main" else w.alt_expert_rank
@@ -71,7 +102,8 @@ def test_layer_fullsize(cfg, placement):
     assert_equal(host(step.stats_out["ochiai"]), st["ochiai"], "ochiai")
     ref = oracle.dispatch_plan(w.topk, w.gates, er, w.G, w.ranks_per_node)
     _check_plan_full(step.plan, ref)
-    _check_samples(step, ref, lambda t: w.x[t], w.gates, w.dtype, np.random.default_rng(cfg))
+    _check_rows_full(step, ref, lambda t: w.x if t is None else t)
+    _check_combine_full(step, ref, w.gates, w.dtype)
 
 
 @pytest.mark.parametrize("balanced", [False, True])
@@ -93,20 +125,65 @@ def test_two_layer_fullsize(balanced):
     for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
         assert_equal(host(step.shuffle[key]), sh[key], key)
     perm = sh["perm"]
-    rng = np.random.default_rng(5)
-    q = rng.choice(w.T, size=SAMPLES, replace=False)
-    assert_equal(host(step.x_s[torch.from_numpy(q).to("cuda")]), w.x[perm[q]], "x shuffled")
+    for a in range(0, w.T, ROW_CHUNK):  # every shuffled row
+        b = min(w.T, a + ROW_CHUNK)
+        assert_equal(host(step.x_s[a:b]), oracle.permute_rows(w.x, perm[a:b]), "x shuffled")
     assert_equal(host(step.topk2_s), w.topk2[perm], "topk2 shuffled")
     assert_equal(host(step.gates2_s), w.gates2[perm], "gates2 shuffled")
     ref = oracle.dispatch_plan(w.topk2[perm], w.gates2[perm], w.expert_rank2, w.G,
                                w.ranks_per_node, src_offsets=sh["shard_offsets"])
     _check_plan_full(step.plan, ref)
-    _check_samples(step, ref, lambda t: w.x[perm[t]], w.gates2[perm], w.dtype, rng)
+    _check_rows_full(step, ref, lambda t: w.x if t is None else perm[t])
+    _check_combine_full(step, ref, w.gates2[perm], w.dtype)
     before = oracle.dispatch_plan(w.topk2, None, w.expert_rank2, w.G, w.ranks_per_node)
     share_before = before["counters"][3] / (w.T * w.k)
     share_after = ref["counters"][3] / (w.T * w.k)
     say("local share before/after shuffle", share_before, share_after)
     assert share_after > share_before
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("balanced", [False, True])
+def test_shuffle_at_scale_fullsize(cfg, balanced):
+    """Both shuffles at workload 3's and 4's full shapes (G = 32 and 64 ranks,
+    T = 65 536 and 32 768 tokens), the next layer routing like this one
+    (transitions = this layer's pair counts, computed by the oracle), against
+    the oracle in full."""
+    from co_activation_amd import ops
+    w = make(cfg, with_x=False)
+    say("fullsize shuffle", cfg, w.T, w.G, "balanced" if balanced else "free")
+    st = oracle.coact_stats(w.topk, w.E, w.topk, w.E)
+    err = ops.new_error_word()
+    got = ops.shuffle_predict(i32(w.topk), i32(st["transition"]), i32(w.expert_rank), w.G,
+                              balanced=balanced, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, ops.decode_errors(int(err.item()))
+    ref = (oracle.shuffle_balanced if balanced else oracle.shuffle_predict)(
+        w.topk, st["transition"], w.expert_rank, w.G)
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert_equal(host(got[key]), ref[key], key)
+
+
+@pytest.mark.parametrize("balanced", [False, True])
+def test_shuffle_past_exchange_limit(balanced):
+    """More tokens than the one-launch exchange form takes (over 2^20): the
+    shuffles fall back to one launch per round and the plan's sort; checked
+    in full against the oracle."""
+    from co_activation_amd import ops
+    T, E, k, G = 1_100_000, 16, 2, 8
+    rng = np.random.default_rng(11)
+    topk = np.stack([rng.choice(E, size=k, replace=False) for _ in range(512)])[
+        rng.integers(0, 512, size=T)].astype(np.int32)
+    X = rng.integers(0, 50, size=(E, E)).astype(np.int32)
+    er = (np.arange(E) // (E // G)).astype(np.int32)
+    say("shuffle past the exchange limit", T, G, balanced)
+    err = ops.new_error_word()
+    got = ops.shuffle_predict(i32(topk), i32(X), i32(er), G, balanced=balanced, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, ops.decode_errors(int(err.item()))
+    ref = (oracle.shuffle_balanced if balanced else oracle.shuffle_predict)(topk, X, er, G)
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert_equal(host(got[key]), ref[key], key)
 
 
 def _check_sum(got, ref32, scale, dt, what):
