@@ -7,72 +7,107 @@
 // together in a layer, and the experts of one layer predicting those of the
 // next (transition counts).
 //
-// The token range is cut into splits and the matrix rows into slices of at
-// most kSliceBins bins; block (split, slice) counts its split's tokens into a
-// 16 KB LDS histogram of its slice with LDS atomics and writes the histogram
-// to its own partial row in the workspace (each thread loads the ids of its
-// tokens of a pass before counting any, so their latencies overlap).  A sum
-// kernel adds the splits' partials bin by bin (integer addition, so the
-// counts do not depend on scheduling), and a finish kernel mirrors the pair
-// matrix, copies the diagonal out as the per-expert counts and evaluates
-// Ochiai in double precision.  No global atomics; every output element is written, so nothing
-// needs clearing first.  The pair matrix is counted on and above the
-// diagonal only (i <= j).
+// Three kernels, no global atomics:
+//   count  : the tokens are cut into splits and the counted matrices into
+//            slices of whole rows; block (split, slice) counts its split's
+//            tokens into an LDS histogram of its slice (16-bit counters, two
+//            per word, while a split has fewer than 2^16 tokens) and copies
+//            the histogram to its own region of the workspace.  The pair
+//            matrix is counted on and above the diagonal only, its rows
+//            packed (row i holds columns i..E-1): a token adds one to (i, j)
+//            for each of its experts i inside the slice's rows and each of
+//            its experts j >= i.
+//   sum    : one block per output row; the splits' partials of each bin are
+//            added in a fixed order (integer addition, so the counts do not
+//            depend on scheduling).
+//   finish : mirrors the pair matrix, copies the diagonal out as the
+//            per-expert counts and evaluates Ochiai in double precision.
+// Every output element is written, so nothing needs clearing first.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kStatThreads = 256;
-constexpr int kSliceBins = 4096;         // 16 KB of int32 per block
-constexpr int kTokensPerThread = 4;
-constexpr int kSplitTokens = kStatThreads * kTokensPerThread;  // until kMaxSplits
+constexpr int kStatThreads = 512;   // one token per thread per pass
+constexpr int kSplitTokens = 512;   // tokens per split, until kMaxSplits
 constexpr int kMaxSplits = 64;
+constexpr int kSliceBytes = 32768;  // LDS histogram of one block
+constexpr int kMaxSlices = 16;      // at most 5 + 8 for E = E_next = 256
 
 enum StatMode { kCounts = 0, kPairs = 1, kTransitions = 2 };
 
-// Work of one statistics call.  Matrix A is the per-expert counts (one row
-// of E bins) or the pair matrix (E x E, upper triangle counted); matrix B the
-// transitions (E x E_next).  Slices [0, a_slices) cover A's rows, a_rps rows
-// each; [a_slices, a_slices + b_slices) cover B's.  A split's partial row
-// holds A's bins, then B's.
+// First bin of packed row i of an E x E upper triangle.
+__host__ __device__ __forceinline__ int tri_row(int i, int E) { return i * E - (i * (i - 1)) / 2; }
+
+// Work of one statistics call.  Matrix A is the per-expert counts (E bins,
+// one slice) or the packed pair triangle (E (E + 1) / 2 bins); matrix B the
+// transitions (E x E_next bins).  Slices [0, a_slices) cover rows of A, the
+// rest rows of B: slice q holds rows [r0[q], r1[q]) starting at bin bin0[q]
+// of its matrix and at word w0[q] of a split's partial row (row_words words;
+// a 32-bit word holds two 16-bit bins, or one 32-bit bin when wide).
 struct StatsJob {
   int a_mode;  // kCounts or kPairs
-  int a_rows, a_cols, a_rps, a_slices;
-  int b_rows, b_cols, b_rps, b_slices;
+  int E, E_next;
+  int a_slices, b_slices;
+  int wide;
   int splits, split_tokens;
-  int64_t a_bins, b_bins;  // bins of each matrix in a partial row
+  int64_t row_words;
+  int r0[kMaxSlices], r1[kMaxSlices], bin0[kMaxSlices], w0[kMaxSlices];
 };
 
 StatsJob stats_job(int64_t T, int E, bool pairs, bool transitions, int E_next) {
   StatsJob j{};
   j.a_mode = pairs ? kPairs : kCounts;
-  j.a_rows = pairs ? E : 1;
-  j.a_cols = E;
-  j.a_rps = pairs ? kSliceBins / E : 1;
-  j.a_slices = (j.a_rows + j.a_rps - 1) / j.a_rps;
-  j.a_bins = static_cast<int64_t>(j.a_rows) * j.a_cols;
-  if (transitions) {
-    j.b_rows = E;
-    j.b_cols = E_next;
-    j.b_rps = kSliceBins / E_next;
-    j.b_slices = (E + j.b_rps - 1) / j.b_rps;
-    j.b_bins = static_cast<int64_t>(E) * E_next;
-  }
+  j.E = E;
+  j.E_next = transitions ? E_next : 0;
   int64_t splits = (T + kSplitTokens - 1) / kSplitTokens;
   if (splits < 1) splits = 1;
   if (splits > kMaxSplits) splits = kMaxSplits;
   j.splits = static_cast<int>(splits);
   j.split_tokens = static_cast<int>((T + splits - 1) / splits);
+  j.wide = j.split_tokens > 65535;
+  const int cap = (kSliceBytes / 4) * (j.wide ? 1 : 2);  // bins per slice
+  int n = 0;
+  int64_t w = 0;
+  auto add = [&](int r0, int r1, int b0, int nb) {
+    j.r0[n] = r0;
+    j.r1[n] = r1;
+    j.bin0[n] = b0;
+    j.w0[n] = static_cast<int>(w);
+    w += j.wide ? nb : (nb + 1) / 2;
+    w = (w + 3) & ~int64_t{3};  // 16-byte aligned slice regions
+    ++n;
+  };
+  if (!pairs) {
+    add(0, E, 0, E);
+  } else {
+    for (int r = 0; r < E;) {
+      int r1 = r, nb = 0;
+      while (r1 < E && nb + (E - r1) <= cap) nb += E - r1++;
+      add(r, r1, tri_row(r, E), nb);
+      r = r1;
+    }
+  }
+  j.a_slices = n;
+  if (transitions) {
+    const int per = cap / E_next;
+    for (int r = 0; r < E; r += per) {
+      const int r1 = r + per < E ? r + per : E;
+      add(r, r1, r * E_next, (r1 - r) * E_next);
+    }
+  }
+  j.b_slices = n - j.a_slices;
+  j.row_words = w;
   return j;
 }
 
 size_t stats_workspace_bytes(const StatsJob& j) {
-  const size_t b = sizeof(int32_t) * static_cast<size_t>(j.splits) * (j.a_bins + j.b_bins);
+  const size_t b = sizeof(uint32_t) * static_cast<size_t>(j.splits) * j.row_words;
   return (b + 255) & ~static_cast<size_t>(255);
 }
 
-// Reads one token's ids into e[]; out-of-range slots become -1.
+// Reads one token's ids into e[]; an out-of-range slot, and a slot that
+// repeats an earlier one, become -1 (so a token adds at most one to a bin).
 __device__ __forceinline__ int load_ids(const int32_t* __restrict__ row, int k, int E,
                                         int (&e)[MOE_MAX_K]) {
   int err = 0;
@@ -81,117 +116,132 @@ __device__ __forceinline__ int load_ids(const int32_t* __restrict__ row, int k, 
     e[j] = -1;
     if (j < k) {
       const int v = row[j];
+      bool dup = false;
 #pragma unroll
-      for (int q = 0; q < j; ++q)
-        if (e[q] == v && v >= 0 && v < E) err |= MOE_DERR_EXPERT_DUP;
-      if (v >= 0 && v < E)
-        e[j] = v;
-      else
+      for (int q = 0; q < j; ++q) dup |= e[q] == v;
+      if (v < 0 || v >= E)
         err |= MOE_DERR_EXPERT_RANGE;
+      else if (dup)
+        err |= MOE_DERR_EXPERT_DUP;
+      else
+        e[j] = v;
     }
   }
   return err;
 }
 
+// Adds one to local bin b of the slice.
+template <bool WIDE>
+__device__ __forceinline__ void bump(unsigned* hist, int b) {
+  if constexpr (WIDE)
+    atomicAdd(&hist[b], 1u);
+  else
+    atomicAdd(&hist[b >> 1], 1u << ((b & 1) * 16));
+}
+
+template <bool WIDE>
 __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int32_t* __restrict__ topk2,
-    int k2, int E2, StatsJob job, int32_t* __restrict__ partial, int32_t* d_err) {
-  __shared__ int hist[kSliceBins];
+    int k2, int E2, StatsJob job, uint32_t* __restrict__ partial, int32_t* d_err) {
+  __shared__ __align__(16) unsigned hist[kSliceBytes / 4];
   const int split = blockIdx.x;
-  const int slice = blockIdx.y;
-  const bool in_a = slice < job.a_slices;
+  const int q = blockIdx.y;
+  const bool in_a = q < job.a_slices;
   const int mode = in_a ? job.a_mode : kTransitions;
-  const int rps = in_a ? job.a_rps : job.b_rps;
-  const int nrows = in_a ? job.a_rows : job.b_rows;
-  const int ncols = in_a ? job.a_cols : job.b_cols;
-  const int r0 = (in_a ? slice : slice - job.a_slices) * rps;
-  const int r1 = min(r0 + rps, nrows);
-  const int slice_bins = (r1 - r0) * ncols;
-  for (int i = threadIdx.x; i < slice_bins; i += kStatThreads) hist[i] = 0;
+  const int r0 = job.r0[q], r1 = job.r1[q], bin0 = job.bin0[q];
+  const int nb = mode == kPairs ? tri_row(r1, E) - bin0 : (mode == kCounts ? E : (r1 - r0) * E2);
+  const int vecs = ((WIDE ? nb : (nb + 1) / 2) + 3) / 4;  // 16-byte vectors of the slice
+  uint4* hv = reinterpret_cast<uint4*>(hist);
+  for (int i = threadIdx.x; i < vecs; i += kStatThreads) hv[i] = uint4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   const int tb0 = split * job.split_tokens;
   const int tb1 = min(T, tb0 + job.split_tokens);
   int errbits = 0;
-  // kTokensPerThread tokens per pass, their ids loaded before any is counted
-  for (int base = tb0; base < tb1; base += kStatThreads * kTokensPerThread) {
-    int e[kTokensPerThread][MOE_MAX_K];
-    int f[kTokensPerThread][MOE_MAX_K];
+  for (int t = tb0 + static_cast<int>(threadIdx.x); t < tb1; t += kStatThreads) {
+    int e[MOE_MAX_K];
+    errbits |= load_ids(topk + static_cast<int64_t>(t) * k, k, E, e);
+    if (mode == kCounts) {
 #pragma unroll
-    for (int u = 0; u < kTokensPerThread; ++u) {
-      const int t = base + u * kStatThreads + static_cast<int>(threadIdx.x);
+      for (int a = 0; a < MOE_MAX_K; ++a)
+        if (e[a] >= 0) bump<WIDE>(hist, e[a]);
+    } else if (mode == kPairs) {
 #pragma unroll
-      for (int a = 0; a < MOE_MAX_K; ++a) e[u][a] = f[u][a] = -1;
-      if (t < tb1) {
-        errbits |= load_ids(topk + static_cast<int64_t>(t) * k, k, E, e[u]);
-        if (mode == kTransitions) errbits |= load_ids(topk2 + static_cast<int64_t>(t) * k2, k2, E2, f[u]);
+      for (int a = 0; a < MOE_MAX_K; ++a) {
+        const int i = e[a];
+        if (i < r0 || i >= r1) continue;
+        const int base = tri_row(i, E) - i - bin0;
+#pragma unroll
+        for (int b = 0; b < MOE_MAX_K; ++b)
+          if (e[b] >= i) bump<WIDE>(hist, base + e[b]);
       }
-    }
+    } else {
+      int f[MOE_MAX_K];
+      errbits |= load_ids(topk2 + static_cast<int64_t>(t) * k2, k2, E2, f);
 #pragma unroll
-    for (int u = 0; u < kTokensPerThread; ++u) {
-      if (mode == kCounts) {
+      for (int a = 0; a < MOE_MAX_K; ++a) {
+        const int i = e[a];
+        if (i < r0 || i >= r1) continue;
+        const int base = (i - r0) * E2;
 #pragma unroll
-        for (int a = 0; a < MOE_MAX_K; ++a)
-          if (a < k && e[u][a] >= 0) atomicAdd(&hist[e[u][a]], 1);
-      } else if (mode == kPairs) {
-#pragma unroll
-        for (int a = 0; a < MOE_MAX_K; ++a) {
-          if (a >= k || e[u][a] < 0) continue;
-#pragma unroll
-          for (int b = a; b < MOE_MAX_K; ++b) {
-            if (b >= k || e[u][b] < 0) continue;
-            const int i = min(e[u][a], e[u][b]), j = max(e[u][a], e[u][b]);
-            if (i >= r0 && i < r1) atomicAdd(&hist[(i - r0) * ncols + j], 1);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int a = 0; a < MOE_MAX_K; ++a) {
-          if (a >= k || e[u][a] < r0 || e[u][a] >= r1) continue;
-#pragma unroll
-          for (int b = 0; b < MOE_MAX_K; ++b)
-            if (b < k2 && f[u][b] >= 0) atomicAdd(&hist[(e[u][a] - r0) * ncols + f[u][b]], 1);
-        }
+        for (int b = 0; b < MOE_MAX_K; ++b)
+          if (f[b] >= 0) bump<WIDE>(hist, base + f[b]);
       }
     }
   }
   // One slice of each matrix reports the data errors it saw.
-  if (slice == 0 || slice == job.a_slices) report(d_err, errbits);
+  if (q == 0 || q == job.a_slices) report(d_err, errbits);
   __syncthreads();
-  int32_t* dst = partial + static_cast<int64_t>(split) * (job.a_bins + job.b_bins) +
-                 (in_a ? 0 : job.a_bins) + static_cast<int64_t>(r0) * ncols;
-  for (int i = threadIdx.x; i < slice_bins; i += kStatThreads) dst[i] = hist[i];
+  uint4* dst = reinterpret_cast<uint4*>(partial + static_cast<int64_t>(split) * job.row_words +
+                                        job.w0[q]);
+  for (int i = threadIdx.x; i < vecs; i += kStatThreads) dst[i] = hv[i];
 }
 
-// Sum over the splits of one partial bin (independent loads, unrolled).
-__device__ __forceinline__ int split_sum(const int32_t* __restrict__ p, int64_t row, int splits) {
-  int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  int s = 0;
-  for (; s + 8 <= splits; s += 8) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += p[static_cast<int64_t>(s + q) * row];
-  }
-  for (; s < splits; ++s) acc[0] += p[static_cast<int64_t>(s) * row];
-  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-}
-
-// Adds the splits' partials bin by bin: A's bins into pair_count (on and
-// above the diagonal; the finish kernel fills the rest) or expert_count, B's
-// into transition.
-__global__ void stats_sum_kernel(const int32_t* __restrict__ partial, StatsJob job, int E,
+// One block per output row: the pair matrix's rows (columns j >= i; the
+// finish kernel fills the rest) or the single row of per-expert counts,
+// then the transition rows.  The splits' partials of a bin are added with
+// eight independent loads in flight.
+template <bool WIDE>
+__global__ void stats_sum_kernel(const uint32_t* __restrict__ partial, StatsJob job,
                                  int32_t* __restrict__ a_out, int32_t* __restrict__ b_out) {
-  const int64_t n = job.a_bins + job.b_bins;
-  for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < n;
-       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    if (idx < job.a_bins && job.a_mode == kPairs) {
-      const int64_t i = idx / E, j = idx - i * E;
-      if (j < i) continue;
-    }
-    const int c = split_sum(partial + idx, n, job.splits);
-    if (idx < job.a_bins)
-      a_out[idx] = c;
+  const int E = job.E;
+  const int a_rows = job.a_mode == kPairs ? E : 1;
+  int row = blockIdx.x;
+  const bool in_a = row < a_rows;
+  if (!in_a) row -= a_rows;
+  const int cols = in_a ? E : job.E_next;
+  int q = in_a ? 0 : job.a_slices;
+  const int q_end = in_a ? job.a_slices : job.a_slices + job.b_slices;
+  while (q + 1 < q_end && job.r0[q + 1] <= row) ++q;
+  const uint32_t* p = partial + job.w0[q];
+  for (int j = threadIdx.x; j < cols; j += blockDim.x) {
+    int b;  // bin inside the slice
+    if (!in_a)
+      b = (row - job.r0[q]) * job.E_next + j;
+    else if (job.a_mode == kCounts)
+      b = j;
+    else if (j >= row)
+      b = tri_row(row, E) - job.bin0[q] + (j - row);
     else
-      b_out[idx - job.a_bins] = c;
+      continue;
+    const int64_t word = WIDE ? b : (b >> 1);
+    const int sh = WIDE ? 0 : (b & 1) * 16;
+    const uint32_t mask = WIDE ? 0xFFFFFFFFu : 0xFFFFu;
+    uint32_t acc[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    int sp = 0;
+    for (; sp + 8 <= job.splits; sp += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] += (p[(sp + u) * job.row_words + word] >> sh) & mask;
+    }
+    for (; sp < job.splits; ++sp) acc[0] += (p[sp * job.row_words + word] >> sh) & mask;
+    const int c = static_cast<int>(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
+                                   ((acc[4] + acc[5]) + (acc[6] + acc[7])));
+    if (!in_a)
+      b_out[static_cast<int64_t>(row) * job.E_next + j] = c;
+    else if (job.a_mode == kCounts)
+      a_out[j] = c;
+    else
+      a_out[static_cast<int64_t>(row) * E + j] = c;
   }
 }
 
@@ -262,13 +312,23 @@ extern "C" int moe_coact_stats(const int32_t* topk, int64_t T, int k, int E,
   if (ws_bytes < moe::stats_workspace_bytes(job)) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Ti = static_cast<int>(T);
-  int32_t* partial = static_cast<int32_t*>(ws);
-  // count (every partial bin of every split is written, also for T = 0)
-  moe::stats_count_kernel<<<dim3(job.splits, job.a_slices + job.b_slices), moe::kStatThreads, 0,
-                            s>>>(topk, Ti, k, E, topk_next, k_next, E_next, job, partial, d_err);
+  uint32_t* partial = static_cast<uint32_t*>(ws);
+  // count (every slice region of every split's partial row is written, also
+  // for T = 0)
+  const dim3 grid(job.splits, job.a_slices + job.b_slices);
+  if (job.wide)
+    moe::stats_count_kernel<true><<<grid, moe::kStatThreads, 0, s>>>(
+        topk, Ti, k, E, topk_next, k_next, E_next, job, partial, d_err);
+  else
+    moe::stats_count_kernel<false><<<grid, moe::kStatThreads, 0, s>>>(
+        topk, Ti, k, E, topk_next, k_next, E_next, job, partial, d_err);
   MOE_CHECK_LAUNCH();
-  moe::stats_sum_kernel<<<moe::grid_for(job.a_bins + job.b_bins), 256, 0, s>>>(
-      partial, job, E, pair_count != nullptr ? pair_count : expert_count, transition);
+  const unsigned rows = (pair_count != nullptr ? E : 1) + (transition != nullptr ? E : 0);
+  int32_t* a_out = pair_count != nullptr ? pair_count : expert_count;
+  if (job.wide)
+    moe::stats_sum_kernel<true><<<rows, 256, 0, s>>>(partial, job, a_out, transition);
+  else
+    moe::stats_sum_kernel<false><<<rows, 256, 0, s>>>(partial, job, a_out, transition);
   MOE_CHECK_LAUNCH();
   if (pair_count != nullptr) {
     moe::stats_finish_kernel<<<moe::grid_for(static_cast<int64_t>(E) * E), 256, 0, s>>>(

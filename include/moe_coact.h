@@ -125,7 +125,7 @@ const char* moe_status_string(int status);
  *                 transition != NULL ? E_next : 0) bytes, 16-byte aligned:
  *                 per-split partial counts (at most 64 splits of the tokens)
  * Limits: 1 <= k, k_next <= 8; 1 <= E, E_next <= 256; T >= 0.
- * d_err bits: EXPERT_RANGE (slot skipped), EXPERT_DUP.
+ * d_err bits: EXPERT_RANGE (slot skipped), EXPERT_DUP (the repeat is skipped).
  * Integer outputs are exact and independent of scheduling; every output
  * element is written.
  * ---------------------------------------------------------------------- */

@@ -66,16 +66,26 @@ def test_stats_rejects(built_lib):
 
 
 def test_stats_workspace_sizes(built_lib):
-    """At most 64 splits of the tokens, each a partial of the counted bins."""
+    """Up to 64 splits of at least 512 tokens; each split holds a partial of
+    the counted bins (the pair triangle i <= j, the transitions) as 16-bit
+    counters while a split has fewer than 2^16 tokens, else 32-bit, with each
+    slice of rows padded to 16 bytes."""
     n = ctypes.c_size_t()
     q = built_lib.moe_coact_stats_workspace_size
+
+    def within(splits, bins, bytes_per_bin, slices):
+        lo = splits * bins * bytes_per_bin
+        return lo <= n.value <= lo + splits * slices * 16 + 256
+
     assert q(32768, 256, 1, 0, ctypes.byref(n)) == 0
-    assert n.value == 32 * 256 * 256 * 4                      # 32 splits of 1024 tokens
+    assert within(64, 256 * 257 // 2, 2, 3)                   # 64 splits of 512 tokens
     assert q(65536, 64, 1, 64, ctypes.byref(n)) == 0
-    assert n.value == 64 * (64 * 64 + 64 * 64) * 4            # pairs and transitions
+    assert within(64, 64 * 65 // 2 + 64 * 64, 2, 2)           # pairs and transitions
+    assert q(2048, 8, 0, 0, ctypes.byref(n)) == 0
+    assert within(4, 8, 2, 1)
     assert q(1 << 24, 8, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == 64 * 8 * 4                              # 64 splits of 8 counts
-    assert q(0, 8, 1, 0, ctypes.byref(n)) == 0 and n.value >= 8 * 8 * 4
+    assert n.value == 64 * 8 * 4                              # 2^18 tokens a split: 32-bit
+    assert q(0, 8, 1, 0, ctypes.byref(n)) == 0 and n.value >= 36 * 2
     assert q(10, 257, 1, 0, ctypes.byref(n)) == -2
     assert q(10, 8, 1, 0, None) == -1
 

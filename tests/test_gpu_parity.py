@@ -789,6 +789,30 @@ def test_device_error_bits():
     assert int(err.item()) == 32
 
 
+def test_stats_repeated_ids_count_once():
+    """A token that lists an expert twice is flagged and still counted as the
+    set D_t: counts equal the products of the token-by-expert 0/1 matrices."""
+    rng = np.random.default_rng(17)
+    T, E, k, E2 = 3000, 256, 8, 64
+    topk = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    nxt = np.stack([rng.permutation(E2)[:k] for _ in range(T)]).astype(np.int32)
+    rows = rng.choice(T, 500, replace=False)
+    topk[rows, 3] = topk[rows, 0]
+    topk[rows[:100], 7] = topk[rows[:100], 0]
+    A = np.zeros((T, E), np.int64)
+    np.put_along_axis(A, topk.astype(np.int64), 1, axis=1)
+    B = np.zeros((T, E2), np.int64)
+    np.put_along_axis(B, nxt.astype(np.int64), 1, axis=1)
+    say("stats with repeated ids")
+    err = _err()
+    res = ops.coact_stats(i32(topk), E, i32(nxt), E2, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 2
+    assert_equal(host(res["expert_count"]), A.sum(0), "expert_count")
+    assert_equal(host(res["pair_count"]), A.T @ A, "pair_count")
+    assert_equal(host(res["transition"]), A.T @ B, "transition")
+
+
 @pytest.mark.parametrize("H,width", [(4096, 1), (7168, 1), (4096, 2), (2048, 1)])
 def test_permute_token_moves(H, width):
     """One destination per token (the shuffle's move) and two, on the
