@@ -409,6 +409,7 @@ constexpr int kXBlocks = kXBlocksMax;
 constexpr int kXMaxTpt = 4;
 constexpr int kXChunks = kXMaxTpt * kXWaves;  // 64-token chunks per block
 constexpr unsigned kXSpinLimit = 1u << 22;     // polls (about 1 us each) before giving up
+constexpr int kXGroups = 16;  // thread groups that share out the earlier blocks' counts
 
 inline int group_width(int G) {
   int w = 1;
@@ -418,6 +419,47 @@ inline int group_width(int G) {
 
 // Preference rows are padded to 16 bytes so that each starts aligned.
 inline int64_t pref_stride(int G) { return (G + 15) / 16 * 16; }
+
+// A lane group handles kScoreTokens tokens, t0 + u (u < kScoreTokens), so
+// that the id loads of all of them and then their row loads are in flight
+// together.
+constexpr int kScoreTokens = 4;
+
+// Scores of tokens t0 + u for rank r (lane r of the group): the sums of the
+// tokens' rows of M (0 for tokens at or past T).
+__device__ __forceinline__ void token_scores(const int32_t* __restrict__ topk, int t0, int T,
+                                             int k, int E, const int64_t* __restrict__ M, int G,
+                                             int r, long long (&score)[kScoreTokens],
+                                             int& errbits) {
+  int e[kScoreTokens][MOE_MAX_K];
+#pragma unroll
+  for (int u = 0; u < kScoreTokens; ++u) {
+    const int t = t0 + u;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j)
+      e[u][j] = (j < k && t < T) ? topk[static_cast<int64_t>(t) * k + j] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kScoreTokens; ++u) {
+    long long sc = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) {
+      if (j >= k) break;
+      const int x = e[u][j];
+      if (x < 0 || x >= E) {
+        if (t0 + u < T) errbits |= MOE_DERR_EXPERT_RANGE;
+      } else if (r < G) {
+        sc += M[static_cast<int64_t>(x) * G + r];
+      }
+    }
+    score[u] = sc;
+  }
+}
+
+// Scores below 2^25 (scores are counts, never negative) make keys
+// score * 64 + (63 - r) below 2^31 that order exactly as the 64-bit ones; a
+// wave takes the 32-bit form when all its lanes' scores allow it.
+constexpr long long kKey32Limit = 1ll << 25;
 
 // The free shuffle's prediction: a group of W lanes (W = G rounded up to a
 // power of two) per token; lane r adds the token's rows of M for rank r
@@ -430,28 +472,30 @@ __global__ __launch_bounds__(256) void rank_argmax_kernel(
     int32_t* d_err) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < rec_words; i += gridDim.x * 256ll) rec[i] = 0;
   const int per_block = 256 / W;
-  const int t = blockIdx.x * per_block + static_cast<int>(threadIdx.x) / W;
+  const int tg = (blockIdx.x * per_block + static_cast<int>(threadIdx.x) / W) * kScoreTokens;
   const int r = static_cast<int>(threadIdx.x) % W;
-  long long key = LLONG_MIN;
   int errbits = 0;
-  if (t < T) {
-    long long score = 0;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_K; ++j) {
-      if (j >= k) break;
-      const int e = topk[static_cast<int64_t>(t) * k + j];
-      if (e < 0 || e >= E) {
-        errbits |= MOE_DERR_EXPERT_RANGE;
-        continue;
-      }
-      if (r < G) score += M[static_cast<int64_t>(e) * G + r];
-    }
-    if (r < G) key = score * 64 + (63 - r);
-  }
+  long long score[kScoreTokens];
+  token_scores(topk, tg, T, k, E, M, G, r, score, errbits);
   if (r == 0) report(d_err, errbits);
-  long long best = key;
-  for (int d = 1; d < W; d <<= 1) best = max(best, __shfl_xor(best, d, kWave));
-  if (t < T && r < G && key == best) pred[t] = r;
+#pragma unroll
+  for (int u = 0; u < kScoreTokens; ++u) {
+    const int t = tg + u;
+    const bool live = t < T && r < G;
+    bool top;
+    if (ballot(score[u] >= kKey32Limit) == 0) {
+      const int key = live ? static_cast<int>(score[u]) * 64 + (63 - r) : -1;
+      int best = key;
+      for (int d = 1; d < W; d <<= 1) best = max(best, __shfl_xor(best, d, kWave));
+      top = key == best;
+    } else {
+      const long long key = live ? score[u] * 64 + (63 - r) : LLONG_MIN;
+      long long best = key;
+      for (int d = 1; d < W; d <<= 1) best = max(best, __shfl_xor(best, d, kWave));
+      top = key == best;
+    }
+    if (live && top) pred[t] = r;
+  }
 }
 
 // The balanced shuffle's preference lists: a group of W lanes per token as
@@ -460,40 +504,47 @@ __global__ __launch_bounds__(256) void rank_argmax_kernel(
 // against W^2 comparisons for ranking by counting) leaves the i-th preferred
 // rank in lane i of the group, which writes byte i of the token's row.
 // Also clears the exchange words.
+template <typename K>
+__device__ __forceinline__ K bitonic_desc(K key, int r, int W) {
+  for (int size = 2; size <= W; size <<= 1) {
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      const K other = __shfl_xor(key, j, kWave);
+      const bool lower = (r & j) == 0;
+      const bool desc = (r & size) == 0;
+      key = (lower == desc) ? max(key, other) : min(key, other);
+    }
+  }
+  return key;
+}
+
 __global__ __launch_bounds__(256) void prefs_sort_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
     int W, int64_t Gs, uint8_t* __restrict__ prefs, uint64_t* __restrict__ rec, int64_t rec_words,
     int32_t* d_err) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < rec_words; i += gridDim.x * 256ll) rec[i] = 0;
   const int per_block = 256 / W;
-  const int t = blockIdx.x * per_block + static_cast<int>(threadIdx.x) / W;
+  const int tg = (blockIdx.x * per_block + static_cast<int>(threadIdx.x) / W) * kScoreTokens;
   const int r = static_cast<int>(threadIdx.x) % W;
-  long long key = LLONG_MIN;
   int errbits = 0;
-  if (t < T) {
-    long long score = 0;
-#pragma unroll
-    for (int j = 0; j < MOE_MAX_K; ++j) {
-      if (j >= k) break;
-      const int e = topk[static_cast<int64_t>(t) * k + j];
-      if (e < 0 || e >= E) {
-        errbits |= MOE_DERR_EXPERT_RANGE;
-        continue;
-      }
-      if (r < G) score += M[static_cast<int64_t>(e) * G + r];
-    }
-    if (r < G) key = score * 64 + (63 - r);
-  }
+  long long score[kScoreTokens];
+  token_scores(topk, tg, T, k, E, M, G, r, score, errbits);
   if (r == 0) report(d_err, errbits);
-  for (int size = 2; size <= W; size <<= 1) {
-    for (int j = size >> 1; j > 0; j >>= 1) {
-      const long long other = __shfl_xor(key, j, kWave);
-      const bool lower = (r & j) == 0;
-      const bool desc = (r & size) == 0;
-      key = (lower == desc) ? max(key, other) : min(key, other);
+#pragma unroll
+  for (int u = 0; u < kScoreTokens; ++u) {
+    const int t = tg + u;
+    const bool live = t < T && r < G;
+    int rank;
+    if (ballot(score[u] >= kKey32Limit) == 0) {
+      const int key =
+          bitonic_desc<int>(live ? static_cast<int>(score[u]) * 64 + (63 - r) : -1, r, W);
+      rank = 63 - (key & 63);
+    } else {
+      const long long key =
+          bitonic_desc<long long>(live ? score[u] * 64 + (63 - r) : LLONG_MIN, r, W);
+      rank = 63 - static_cast<int>(key & 63);
     }
+    if (live) prefs[static_cast<int64_t>(t) * Gs + r] = static_cast<uint8_t>(rank);
   }
-  if (t < T && r < G) prefs[static_cast<int64_t>(t) * Gs + r] = static_cast<uint8_t>(63 - (key & 63));
 }
 
 // One 64-bit exchange word: the round tag (round + 1) above the value.
@@ -515,22 +566,84 @@ __device__ __forceinline__ bool xwait(const uint64_t* w, int round, uint32_t& v)
   return false;
 }
 
-// First rank in the token's preference order (16 per word, PW words) that
-// is set in feas; the last preference if none is (cannot happen: some rank
-// always has room for the token).
-template <int PW>
-__device__ __forceinline__ int first_feasible(const u32x4 (&pw)[PW], int G, uint64_t feas) {
-  int last = 0;
+// Sum of the words w[c * stride], w[(c + ng) * stride], ... for indices
+// below n once each carries this round's tag: the loads go out four at a
+// time, all four before the first wait.
+__device__ __forceinline__ bool xsum(const uint64_t* w, int64_t stride, int c, int ng, int n,
+                                     int round, int& sum) {
+  const uint64_t want = static_cast<uint64_t>(round + 1);
+  int acc = 0;
+  for (int j0 = c; j0 < n; j0 += 4 * ng) {
+    uint64_t x[4];
 #pragma unroll
-  for (int w = 0; w < PW; ++w) {
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + q * ng;
+      x[q] = j < n ? __hip_atomic_load(w + j * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : 0;
+    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (w * 16 + i >= G) return last;
-      const int p = static_cast<int>((pw[w][i >> 2] >> (8 * (i & 3))) & 0xFFu);
-      if ((feas >> p) & 1ull) return p;
-      last = p;
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + q * ng;
+      if (j < n) {
+        uint32_t v = static_cast<uint32_t>(x[q]);
+        if ((x[q] >> 32) != want && !xwait(w + j * stride, round, v)) return false;
+        acc += static_cast<int>(v);
+      }
     }
   }
+  sum = acc;
+  return true;
+}
+
+// The ranks in each group of 16 preferences.
+template <int PW>
+__device__ __forceinline__ void group_masks(const u32x4 (&pw)[PW], int G, uint64_t (&gm)[PW]) {
+#pragma unroll
+  for (int w = 0; w < PW; ++w) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t p = (pw[w][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      if (w * 16 + i < G) m |= 1ull << p;
+    }
+    gm[w] = m;
+  }
+}
+
+// The first rank at position >= start of the preference list pw that feas
+// holds, and its position (the last preference, position G - 1, when none
+// does).  gm holds the ranks of each group of 16 preferences, so that groups
+// with no feasible rank are passed over whole.
+template <int PW>
+__device__ __forceinline__ int first_feasible(const u32x4 (&pw)[PW], const uint64_t (&gm)[PW],
+                                              int G, uint64_t feas, int start, int& pos) {
+  const uint32_t lo = static_cast<uint32_t>(feas), hi = static_cast<uint32_t>(feas >> 32);
+#pragma unroll
+  for (int w = 0; w < PW; ++w) {
+    if (w * 16 >= G) break;
+    if (w * 16 + 16 <= start || (gm[w] & feas) == 0) continue;
+    const int n = G - w * 16 < 16 ? G - w * 16 : 16;
+    uint32_t m = 0;  // feasible positions among this group
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t p = (pw[w][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      const uint32_t bit = p < 32 ? (lo >> p) : (hi >> (p - 32));
+      m |= (bit & 1u) << i;
+    }
+    if (n < 16) m &= (1u << n) - 1u;
+    if (start > w * 16) m &= ~((1u << (start - w * 16)) - 1u);
+    if (m != 0) {
+      const int i = __ffs(m) - 1;
+      pos = w * 16 + i;
+      return static_cast<int>((pw[w][i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    }
+  }
+  const int i = (G - 1) & 15, w = (G - 1) >> 4;
+  int last = 0;
+#pragma unroll
+  for (int q = 0; q < PW; ++q)
+    if (q == w) last = static_cast<int>((pw[q][i >> 2] >> (8 * (i & 3))) & 0xFFu);
+  pos = G - 1;
   return last;
 }
 
@@ -540,11 +653,15 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
     uint64_t* __restrict__ rec, int32_t* __restrict__ pred_rank, int32_t* __restrict__ dest_pos,
     int32_t* __restrict__ perm, int32_t* __restrict__ shard_offsets, int32_t* d_err) {
   __shared__ uint8_t s_choice[kXMaxTpt * kXThreads];  // each token's current choice
+  __shared__ uint8_t s_cursor[kXMaxTpt * kXThreads];  // its position in the token's list
+  // Rank r takes tokens t <= s_lim[r] of this block: INT_MAX for a rank
+  // still open after the block, -1 for one full before it, else the position
+  // of its cap-th taker.
+  __shared__ int s_lim[MOE_MAX_G];
   __shared__ int s_cc[kXChunks][MOE_MAX_G];  // tokens per (64-token chunk, rank)
-  __shared__ int s_pre[kXWaves][MOE_MAX_G];  // partial sums over earlier blocks
+  __shared__ int s_pre[kXGroups][MOE_MAX_G];  // partial sums over earlier blocks
   __shared__ int s_cnt[MOE_MAX_G], s_P[MOE_MAX_G];
-  __shared__ int s_xlimit[MOE_MAX_G], s_xrank[MOE_MAX_G];
-  __shared__ uint64_t s_open;
+  __shared__ int s_xrank[MOE_MAX_G];  // ranks whose cap-th taker is in this block
   __shared__ int s_ncross, s_abort, s_changed;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = lane_id();
@@ -553,14 +670,34 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   const int t0 = b * TB;
   const int nchunks = tpt * kXWaves;
   const int64_t words = static_cast<int64_t>(G) + 1;  // per block and round: G counts, a flag
+  constexpr int ng = kXGroups;  // thread (c, r), c < 16, r < G <= 64
 
-  if (tid == 0) {
-    s_open = G >= 64 ? ~0ull : ((1ull << G) - 1);
-    s_ncross = 0;
-    s_abort = 0;
+  if (tid < MOE_MAX_G) s_lim[tid] = INT_MAX;
+  if (tid == 0) s_abort = 0;
+  for (int u = 0; u < tpt; ++u) {
+    s_choice[u * kXThreads + tid] = 255;
+    s_cursor[u * kXThreads + tid] = 0;
   }
-  for (int u = 0; u < tpt; ++u) s_choice[u * kXThreads + tid] = 255;
   __syncthreads();
+
+  // A token's preferences and the ranks of each group of 16 of them; with
+  // one token per thread they stay in registers for all rounds.
+  //
+  // The fill positions only move earlier from round to round (a rank that
+  // closes earlier sends its later takers to their next choices, which fill
+  // those ranks no later), so a rank a token once found full stays full: a
+  // choice stands while it is feasible, and otherwise the search resumes
+  // after it.
+  u32x4 pw1[PW];
+  uint64_t gm1[PW];
+#pragma unroll
+  for (int w = 0; w < PW; ++w) pw1[w] = u32x4{0u, 0u, 0u, 0u};
+  if (tpt == 1 && t0 + tid < T) {
+#pragma unroll
+    for (int w = 0; w < PW; ++w)
+      pw1[w] = *reinterpret_cast<const u32x4*>(prefs + static_cast<int64_t>(t0 + tid) * Gs + 16 * w);
+  }
+  group_masks<PW>(pw1, G, gm1);
 
   const int max_rounds = G + 2;
   for (int round = 0; round < max_rounds; ++round) {
@@ -572,19 +709,36 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
       const int t = t0 + u * kXThreads + tid;
       const int idx = u * kXThreads + tid;
       int c = s_choice[idx];
-      if (t < T) {
-        u32x4 pw[PW];
+      // no choice yet, or its rank is full
+      const bool walk = t < T && (c >= G || t > s_lim[c]);
+      if (ballot(walk) != 0) {
+        // The ranks feasible for the wave's tokens base .. base + 63: those
+        // taking all of them, and those whose cap-th taker is among them
+        // (feasible for the tokens up to it).
+        const int base = t0 + u * kXThreads + wave * kWave;
+        const int lim = lane < G ? s_lim[lane] : -1;
+        uint64_t feas = ballot(lim >= base + kWave - 1);
+        uint64_t part = ballot(lim >= base && lim < base + kWave - 1);
+        while (part != 0) {
+          const int r = __ffsll(static_cast<long long>(part)) - 1;
+          part &= part - 1;
+          if (__builtin_amdgcn_readlane(lim, r) >= t) feas |= 1ull << r;
+        }
+        if (walk) {
+          if (tpt != 1) {  // several tokens per thread: this one's preferences
 #pragma unroll
-        for (int w = 0; w < PW; ++w)
-          pw[w] = *reinterpret_cast<const u32x4*>(prefs + static_cast<int64_t>(t) * Gs + 16 * w);
-        uint64_t feas = s_open;
-        const int nc = s_ncross;
-        for (int i = 0; i < nc; ++i)
-          if (t <= s_xlimit[i]) feas |= 1ull << s_xrank[i];
-        const int nw = first_feasible<PW>(pw, G, feas);
-        changed |= nw != c;
-        c = nw;
-        s_choice[idx] = static_cast<uint8_t>(c);
+            for (int w = 0; w < PW; ++w)
+              pw1[w] = *reinterpret_cast<const u32x4*>(prefs + static_cast<int64_t>(t) * Gs + 16 * w);
+            group_masks<PW>(pw1, G, gm1);
+          }
+          const int start = c >= G ? 0 : s_cursor[idx] + 1;
+          int pos = 0;
+          const int nw = first_feasible<PW>(pw1, gm1, G, feas, start, pos);
+          s_cursor[idx] = static_cast<uint8_t>(pos);
+          changed |= nw != c;
+          c = nw;
+          s_choice[idx] = static_cast<uint8_t>(c);
+        }
       }
       // the wave's own row of chunk counts: cleared, then one LDS atomic per
       // token (a wave's LDS operations complete in order)
@@ -611,14 +765,11 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
                          xword(round, static_cast<uint32_t>(any)), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();  // s_pre is reused below
-    // 3. every block's flag of this round
+    // 3. every block's flag of this round (the flags are 0 or 1: their sum
+    // is nonzero when any is set)
     if (wave == 0) {
-      int ch = 0, ok = 1;
-      for (int j = lane; j < nb; j += kWave) {
-        uint32_t v = 0;
-        if (!xwait(xr + static_cast<int64_t>(j) * words + G, round, v)) ok = 0;
-        ch |= v != 0;
-      }
+      int ch = 0;
+      int ok = xsum(xr + G, words, lane, kWave, nb, round, ch) ? 1 : 0;
       ch = ballot(ch != 0) != 0;
       ok = ballot(!ok) == 0;
       if (lane == 0) {
@@ -626,22 +777,13 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
         if (!ok) s_abort = 1;
       }
     }
-    // 4. counts of the blocks before this one
+    // 4. counts of the blocks before this one: thread (c, r) adds rank r's
+    // counts of blocks c, c + ng, ... below b
     {
       const int c = tid / MOE_MAX_G, r = tid % MOE_MAX_G;
-      int pre = 0, ok = 1;
-      if (r < G) {
-        for (int j = c; j < b; j += kXWaves) {
-          uint32_t v = 0;
-          if (!xwait(xr + static_cast<int64_t>(j) * words + r, round, v)) {
-            ok = 0;
-            break;
-          }
-          pre += static_cast<int>(v);
-        }
-      }
+      int pre = 0;
+      if (r < G && !xsum(xr + r, words, c, ng, b, round, pre)) s_abort = 1;
       s_pre[c][r] = pre;
-      if (!ok) s_abort = 1;
     }
     __syncthreads();
     if (s_abort) {
@@ -649,49 +791,47 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
       return;
     }
     const bool last = (round > 0 && !s_changed) || round + 1 == max_rounds;
-    // 5. (wave 0) prefix per rank; unless this is the last round,
-    // the next round's feasibility: ranks open for the whole block, and the
-    // ranks whose cap-th taker lies inside it, with its position
+    // 5. (wave 0) prefix per rank; unless this is the last round, the ranks
+    // open for the whole block and those whose cap-th taker lies inside it
     if (wave == 0) {
       const int r = lane;
       int P = 0;
       if (r < G) {
 #pragma unroll
-        for (int c = 0; c < kXWaves; ++c) P += s_pre[c][r];
+        for (int c = 0; c < kXGroups; ++c) P += s_pre[c][r];
         s_P[r] = P;
       }
       if (!last) {
         const bool open = r < G && P + s_cnt[r] < cap;
         const bool cross = r < G && P < cap && P + s_cnt[r] >= cap;
-        const uint64_t om = ballot(open);
-        uint64_t cm = ballot(cross);
-        int i = 0;
-        while (cm != 0) {  // uniform: one crossing rank at a time, the whole wave
-          const int rr = __ffsll(static_cast<long long>(cm)) - 1;
-          cm &= cm - 1;
-          const int need = cap - s_P[rr];
-          const int n = lane < nchunks ? s_cc[lane][rr] : 0;
-          const int incl = wave_incl_scan(n);
-          const uint64_t hit = ballot(lane < nchunks && incl >= need);
-          const int q = __ffsll(static_cast<long long>(hit)) - 1;
-          const int rest = need - (__shfl(incl, q, kWave) - __shfl(n, q, kWave));
-          const int base = (q / kXWaves) * kXThreads + (q % kXWaves) * kWave;
-          uint64_t mm = ballot(s_choice[base + lane] == rr);
-          for (int z = 1; z < rest; ++z) mm &= mm - 1;
-          if (lane == 0) {
-            s_xrank[i] = rr;
-            s_xlimit[i] = t0 + base + (__ffsll(static_cast<long long>(mm)) - 1);
-          }
-          ++i;
-        }
-        if (lane == 0) {
-          s_open = om;
-          s_ncross = i;
-        }
+        const uint64_t cm = ballot(cross);
+        if (cross) s_xrank[lanes_below(cm)] = r;
+        if (r < G) s_lim[r] = open ? INT_MAX : -1;  // crossing ranks: below
+        if (lane == 0) s_ncross = __popcll(cm);
       }
     }
     __syncthreads();
     if (last) break;
+    // 6. each wave places some crossing ranks' cap-th takers: the chunk from
+    // a scan of the chunk counts (lane = chunk), the lane from the chunk's
+    // ballot of that rank
+    const int nc = s_ncross;
+    if (nc == 0) continue;  // uniform: no rank fills inside this block
+    for (int i = wave; i < nc; i += kXWaves) {
+      const int rr = s_xrank[i];
+      const int need = cap - s_P[rr];
+      const int n = lane < nchunks ? s_cc[lane][rr] : 0;
+      const int incl = wave_incl_scan(n);
+      const uint64_t hit = ballot(lane < nchunks && incl >= need);
+      const int q = __ffsll(static_cast<long long>(hit)) - 1;
+      const int rest = need - (__shfl(incl, q, kWave) - __shfl(n, q, kWave));
+      const int base = (q / kXWaves) * kXThreads + (q % kXWaves) * kWave;
+      const uint64_t mm = ballot(s_choice[base + lane] == rr);
+      const bool at = ((mm >> lane) & 1ull) && lanes_below(mm) == rest - 1;
+      const uint64_t am = ballot(at);
+      if (lane == 0) s_lim[rr] = t0 + base + (__ffsll(static_cast<long long>(am)) - 1);
+    }
+    __syncthreads();
   }
 
   // Positions: the rank's shard offset r * cap + its tokens in earlier blocks
@@ -850,7 +990,8 @@ extern "C" int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E
     const int64_t Gs = moe::pref_stride(G);
     const int64_t rec_words = 2ll * xs.nb * (G + 1);
     const int W = moe::group_width(G);
-    moe::prefs_sort_kernel<<<(Ti + 256 / W - 1) / (256 / W), 256, 0, s>>>(
+    const int per_block = 256 / W * moe::kScoreTokens;
+    moe::prefs_sort_kernel<<<(Ti + per_block - 1) / per_block, 256, 0, s>>>(
         topk, Ti, k, E, w.base.M, G, W, Gs, w.prefs, w.base.rec, rec_words, d_err);
     MOE_CHECK_LAUNCH();
     const int pwords = static_cast<int>(Gs / 16);
@@ -929,7 +1070,8 @@ extern "C" int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E,
   // prediction can run beside other kernels.
   if (G > 16 && Ti > 0) {
     const int W = moe::group_width(G);
-    moe::rank_argmax_kernel<<<(Ti + 256 / W - 1) / (256 / W), 256, 0, s>>>(
+    const int per_block = 256 / W * moe::kScoreTokens;
+    moe::rank_argmax_kernel<<<(Ti + per_block - 1) / per_block, 256, 0, s>>>(
         topk, Ti, k, E, w.M, G, W, pred_rank, w.rec, 0, d_err);
     MOE_CHECK_LAUNCH();
     moe::PlanArgs a{pred_rank,      nullptr,        Ti,        1,
