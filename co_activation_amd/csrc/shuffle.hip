@@ -420,10 +420,10 @@ inline int group_width(int G) {
 // Preference rows are padded to 16 bytes so that each starts aligned.
 inline int64_t pref_stride(int G) { return (G + 15) / 16 * 16; }
 
-// A lane group handles kScoreTokens tokens, t0 + u (u < kScoreTokens), so
-// that the id loads of all of them and then their row loads are in flight
-// together.
-constexpr int kScoreTokens = 4;
+// Tokens per lane group (t0 + u, u < kScoreTokens): their id loads and then
+// their row loads go out together.  One measured fastest (rows of M are read
+// from L2, which more tokens in flight per wave do not speed up).
+constexpr int kScoreTokens = 1;
 
 // Scores of tokens t0 + u for rank r (lane r of the group): the sums of the
 // tokens' rows of M (0 for tokens at or past T).
