@@ -612,30 +612,40 @@ __device__ __forceinline__ void group_masks(const u32x4 (&pw)[PW], int G, uint64
 
 // The first rank at position >= start of the preference list pw that feas
 // holds, and its position (the last preference, position G - 1, when none
-// does).  gm holds the ranks of each group of 16 preferences, so that groups
-// with no feasible rank are passed over whole.
+// does).  gm holds the ranks of each group of 16 preferences: the group of
+// the answer is the first one at or after start's whose ranks meet feas
+// (ranks listed before start are infeasible), so that only that group's 16
+// positions are tested one by one.
 template <int PW>
 __device__ __forceinline__ int first_feasible(const u32x4 (&pw)[PW], const uint64_t (&gm)[PW],
                                               int G, uint64_t feas, int start, int& pos) {
-  const uint32_t lo = static_cast<uint32_t>(feas), hi = static_cast<uint32_t>(feas >> 32);
+  int gsel = -1;
 #pragma unroll
-  for (int w = 0; w < PW; ++w) {
-    if (w * 16 >= G) break;
-    if (w * 16 + 16 <= start || (gm[w] & feas) == 0) continue;
-    const int n = G - w * 16 < 16 ? G - w * 16 : 16;
-    uint32_t m = 0;  // feasible positions among this group
+  for (int w = PW - 1; w >= 0; --w)
+    if (w * 16 < G && w * 16 + 16 > start && (gm[w] & feas) != 0) gsel = w;
+  if (gsel >= 0) {
+    uint32_t g[4] = {pw[0][0], pw[0][1], pw[0][2], pw[0][3]};
+#pragma unroll
+    for (int w = 1; w < PW; ++w) {
+      const bool sel = w == gsel;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g[j] = sel ? pw[w][j] : g[j];
+    }
+    const uint32_t lo = static_cast<uint32_t>(feas), hi = static_cast<uint32_t>(feas >> 32);
+    uint32_t m = 0;  // feasible positions among the group
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t p = (pw[w][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      const uint32_t p = (g[i >> 2] >> (8 * (i & 3))) & 0xFFu;
       const uint32_t bit = p < 32 ? (lo >> p) : (hi >> (p - 32));
       m |= (bit & 1u) << i;
     }
+    const int n = G - gsel * 16;
     if (n < 16) m &= (1u << n) - 1u;
-    if (start > w * 16) m &= ~((1u << (start - w * 16)) - 1u);
+    if (start > gsel * 16) m &= ~((1u << (start - gsel * 16)) - 1u);
     if (m != 0) {
       const int i = __ffs(m) - 1;
-      pos = w * 16 + i;
-      return static_cast<int>((pw[w][i >> 2] >> (8 * (i & 3))) & 0xFFu);
+      pos = gsel * 16 + i;
+      return static_cast<int>((g[i >> 2] >> (8 * (i & 3))) & 0xFFu);
     }
   }
   const int i = (G - 1) & 15, w = (G - 1) >> 4;
@@ -659,10 +669,10 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   // of its cap-th taker.
   __shared__ int s_lim[MOE_MAX_G];
   __shared__ int s_cc[kXChunks][MOE_MAX_G];  // tokens per (64-token chunk, rank)
+  __shared__ int s_wc[kXWaves][MOE_MAX_G];    // this block's counts per wave
   __shared__ int s_pre[kXGroups][MOE_MAX_G];  // partial sums over earlier blocks
-  __shared__ int s_cnt[MOE_MAX_G], s_P[MOE_MAX_G];
-  __shared__ int s_xrank[MOE_MAX_G];  // ranks whose cap-th taker is in this block
-  __shared__ int s_ncross, s_abort, s_changed;
+  __shared__ int s_cnt[MOE_MAX_G];
+  __shared__ int s_abort, s_changed;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = lane_id();
   const int wave = wave_id();
@@ -700,6 +710,7 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   group_masks<PW>(pw1, G, gm1);
 
   const int max_rounds = G + 2;
+  int P = 0;  // lane r: tokens rank r took in earlier blocks (this round)
   for (int round = 0; round < max_rounds; ++round) {
     uint64_t* xr = rec + static_cast<int64_t>(round & 1) * nb * words;
     // 1. choices, and the tokens of each (chunk, rank) from wave ballots
@@ -709,6 +720,7 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
       const int t = t0 + u * kXThreads + tid;
       const int idx = u * kXThreads + tid;
       int c = s_choice[idx];
+      const int c0 = c;
       // no choice yet, or its rank is full
       const bool walk = t < T && (c >= G || t > s_lim[c]);
       if (ballot(walk) != 0) {
@@ -740,34 +752,36 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
           s_choice[idx] = static_cast<uint8_t>(c);
         }
       }
-      // the wave's own row of chunk counts: cleared, then one LDS atomic per
-      // token (a wave's LDS operations complete in order)
+      // the wave's own row of chunk counts, recounted when one of its
+      // tokens changed (cleared, then one LDS atomic per token; a wave's LDS
+      // operations complete in order), else as the last round left it
       int* row = s_cc[u * kXWaves + wave];
-      if (lane < G) row[lane] = 0;
-      __builtin_amdgcn_wave_barrier();
-      if (c < G) atomicAdd(&row[c], 1);
-      __builtin_amdgcn_wave_barrier();
+      if (round == 0 || ballot(c != c0) != 0) {
+        if (lane < G) row[lane] = 0;
+        __builtin_amdgcn_wave_barrier();
+        if (c < G) atomicAdd(&row[c], 1);
+        __builtin_amdgcn_wave_barrier();
+      }
       if (lane < G) wc += row[lane];
     }
-    if (lane < G) s_pre[wave][lane] = wc;  // this block's counts, per wave for now
+    if (lane < G) s_wc[wave][lane] = wc;
     const int any = __syncthreads_or(changed);
-    // 2. publish this block's counts and whether any of its tokens changed
-    if (wave == 0 && lane < G) {
-      int c = 0;
-      for (int w = 0; w < kXWaves; ++w) c += s_pre[w][lane];
-      s_cnt[lane] = c;
-      __hip_atomic_store(xr + static_cast<int64_t>(b) * words + lane,
-                         xword(round, static_cast<uint32_t>(c)), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (tid == kWave)
-      __hip_atomic_store(xr + static_cast<int64_t>(b) * words + G,
-                         xword(round, static_cast<uint32_t>(any)), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();  // s_pre is reused below
-    // 3. every block's flag of this round (the flags are 0 or 1: their sum
-    // is nonzero when any is set)
+    // 2. (wave 0) publish this block's counts and whether any of its tokens
+    // changed; 3. then every block's flag of this round (the flags are 0 or
+    // 1: their sum is nonzero when any is set)
     if (wave == 0) {
+      if (lane < G) {
+        int c = 0;
+        for (int w = 0; w < kXWaves; ++w) c += s_wc[w][lane];
+        s_cnt[lane] = c;
+        __hip_atomic_store(xr + static_cast<int64_t>(b) * words + lane,
+                           xword(round, static_cast<uint32_t>(c)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0)
+        __hip_atomic_store(xr + static_cast<int64_t>(b) * words + G,
+                           xword(round, static_cast<uint32_t>(any)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       int ch = 0;
       int ok = xsum(xr + G, words, lane, kWave, nb, round, ch) ? 1 : 0;
       ch = ballot(ch != 0) != 0;
@@ -791,45 +805,38 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
       return;
     }
     const bool last = (round > 0 && !s_changed) || round + 1 == max_rounds;
-    // 5. (wave 0) prefix per rank; unless this is the last round, the ranks
-    // open for the whole block and those whose cap-th taker lies inside it
-    if (wave == 0) {
-      const int r = lane;
-      int P = 0;
-      if (r < G) {
+    // 5. (every wave) the tokens each rank took in earlier blocks (lane = rank)
+    P = 0;
+    if (lane < G) {
 #pragma unroll
-        for (int c = 0; c < kXGroups; ++c) P += s_pre[c][r];
-        s_P[r] = P;
-      }
-      if (!last) {
-        const bool open = r < G && P + s_cnt[r] < cap;
-        const bool cross = r < G && P < cap && P + s_cnt[r] >= cap;
-        const uint64_t cm = ballot(cross);
-        if (cross) s_xrank[lanes_below(cm)] = r;
-        if (r < G) s_lim[r] = open ? INT_MAX : -1;  // crossing ranks: below
-        if (lane == 0) s_ncross = __popcll(cm);
-      }
+      for (int c = 0; c < kXGroups; ++c) P += s_pre[c][lane];
     }
-    __syncthreads();
     if (last) break;
-    // 6. each wave places some crossing ranks' cap-th takers: the chunk from
-    // a scan of the chunk counts (lane = chunk), the lane from the chunk's
+    // 6. the ranks open for the whole block, and those whose cap-th taker
+    // lies inside it; each wave places some of the latter: the chunk from a
+    // scan of the chunk counts (lane = chunk), the lane from the chunk's
     // ballot of that rank
-    const int nc = s_ncross;
-    if (nc == 0) continue;  // uniform: no rank fills inside this block
-    for (int i = wave; i < nc; i += kXWaves) {
-      const int rr = s_xrank[i];
-      const int need = cap - s_P[rr];
-      const int n = lane < nchunks ? s_cc[lane][rr] : 0;
-      const int incl = wave_incl_scan(n);
-      const uint64_t hit = ballot(lane < nchunks && incl >= need);
-      const int q = __ffsll(static_cast<long long>(hit)) - 1;
-      const int rest = need - (__shfl(incl, q, kWave) - __shfl(n, q, kWave));
-      const int base = (q / kXWaves) * kXThreads + (q % kXWaves) * kWave;
-      const uint64_t mm = ballot(s_choice[base + lane] == rr);
-      const bool at = ((mm >> lane) & 1ull) && lanes_below(mm) == rest - 1;
-      const uint64_t am = ballot(at);
-      if (lane == 0) s_lim[rr] = t0 + base + (__ffsll(static_cast<long long>(am)) - 1);
+    {
+      const int cnt = lane < G ? s_cnt[lane] : 0;
+      const bool open = lane < G && P + cnt < cap;
+      const bool cross = lane < G && P < cap && P + cnt >= cap;
+      if (wave == 0 && lane < G && !cross) s_lim[lane] = open ? INT_MAX : -1;
+      uint64_t cm = ballot(cross);
+      for (int i = 0; cm != 0; ++i, cm &= cm - 1) {
+        if (i % kXWaves != wave) continue;
+        const int rr = __ffsll(static_cast<long long>(cm)) - 1;
+        const int need = cap - __builtin_amdgcn_readlane(P, rr);
+        const int n = lane < nchunks ? s_cc[lane][rr] : 0;
+        const int incl = wave_incl_scan(n);
+        const uint64_t hit = ballot(lane < nchunks && incl >= need);
+        const int q = __ffsll(static_cast<long long>(hit)) - 1;
+        const int rest = need - (__shfl(incl, q, kWave) - __shfl(n, q, kWave));
+        const int base = (q / kXWaves) * kXThreads + (q % kXWaves) * kWave;
+        const uint64_t mm = ballot(s_choice[base + lane] == rr);
+        const bool at = ((mm >> lane) & 1ull) && lanes_below(mm) == rest - 1;
+        const uint64_t am = ballot(at);
+        if (lane == 0) s_lim[rr] = t0 + base + (__ffsll(static_cast<long long>(am)) - 1);
+      }
     }
     __syncthreads();
   }
@@ -841,7 +848,7 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   for (int r = wave; r < G; r += kXWaves) {
     const int n = lane < nchunks ? s_cc[lane][r] : 0;
     const int excl = wave_incl_scan(n) - n;
-    if (lane < nchunks) s_cc[lane][r] = r * cap + s_P[r] + excl;
+    if (lane < nchunks) s_cc[lane][r] = r * cap + __builtin_amdgcn_readlane(P, r) + excl;
   }
   __syncthreads();
   if (b == 0 && tid <= G) shard_offsets[tid] = tid * cap;
