@@ -186,6 +186,28 @@ def test_shuffle_past_exchange_limit(balanced):
         assert_equal(host(got[key]), ref[key], key)
 
 
+@pytest.mark.parametrize("T,G,E,k", [(200_000, 8, 16, 2), (300_000, 32, 64, 2),
+                                     (409_600, 64, 256, 4)])
+def test_balanced_exchange_several_tokens_per_thread(T, G, E, k):
+    """The one-launch balanced shuffle with two to four tokens per thread
+    (more than 2^17 tokens, up to its limit of 2^19): checked in full
+    against the oracle."""
+    from co_activation_amd import ops
+    rng = np.random.default_rng(T + G)
+    topk = np.stack([rng.choice(E, size=k, replace=False) for _ in range(1024)])[
+        rng.integers(0, 1024, size=T)].astype(np.int32)
+    X = rng.integers(0, 50, size=(E, E)).astype(np.int32)
+    er = rng.permutation(np.arange(E) // (E // G)).astype(np.int32)
+    say("balanced exchange, several tokens per thread", T, G)
+    err = ops.new_error_word()
+    got = ops.shuffle_predict(i32(topk), i32(X), i32(er), G, balanced=True, d_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, ops.decode_errors(int(err.item()))
+    ref = oracle.shuffle_balanced(topk, X, er, G)
+    for key in ("pred_rank", "dest_pos", "perm", "shard_offsets"):
+        assert_equal(host(got[key]), ref[key], key)
+
+
 def _check_sum(got, ref32, scale, dt, what):
     """A sum of several terms: fp32 within 1e-5 of the terms' magnitude; bf16
     within 1 ulp of the oracle's fp32 value rounded once, or within the fp32
