@@ -34,8 +34,11 @@ namespace {
 // faster alone (workload 5: 15.9 against 18.9 us) but wait for whole CUs to
 // drain, which made the two-batch pipelined step 0.612 -> 0.671 ms.
 constexpr int kStatThreads = 256;
-constexpr int kSplitTokens = 512;   // tokens per split (two per thread), until kMaxSplits
-constexpr int kMaxSplits = 64;
+// Tokens per split, one per thread, until kMaxSplits: more, smaller splits
+// keep every CU counting (512-token splits took 11.4 us to count at T = 32768,
+// E = 256, k = 8, these 8.2) at the price of twice the partials to sum.
+constexpr int kSplitTokens = 256;
+constexpr int kMaxSplits = 128;
 constexpr int kSliceBytes = 32768;  // LDS histogram of one block
 constexpr int kMaxSlices = 16;      // at most 5 + 8 for E = E_next = 256
 
@@ -102,6 +105,11 @@ StatsJob stats_job(int64_t T, int E, bool pairs, bool transitions, int E_next) {
     }
   }
   j.b_slices = n - j.a_slices;
+  // Split stride: an odd number of 256-byte units, so that the copies of a
+  // bin in the splits' rows do not all fall on the same memory channels
+  // (a stride near a multiple of 64 KB made the sum several times slower).
+  w = (w + 63) & ~int64_t{63};
+  if (((w / 64) & 1) == 0) w += 64;
   j.row_words = w;
   return j;
 }
@@ -205,7 +213,8 @@ __global__ __launch_bounds__(kStatThreads) void stats_count_kernel(
 // One block per output row: the pair matrix's rows (columns j >= i; the
 // finish kernel fills the rest) or the single row of per-expert counts,
 // then the transition rows.  The splits' partials of a bin are added with
-// eight independent loads in flight.
+// sixteen independent loads in flight (eight left the latency exposed,
+// thirty-two slowed the memory side).
 template <bool WIDE>
 __global__ void stats_sum_kernel(const uint32_t* __restrict__ partial, StatsJob job,
                                  int32_t* __restrict__ a_out, int32_t* __restrict__ b_out) {
@@ -232,15 +241,20 @@ __global__ void stats_sum_kernel(const uint32_t* __restrict__ partial, StatsJob 
     const int64_t word = WIDE ? b : (b >> 1);
     const int sh = WIDE ? 0 : (b & 1) * 16;
     const uint32_t mask = WIDE ? 0xFFFFFFFFu : 0xFFFFu;
-    uint32_t acc[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    int sp = 0;
-    for (; sp + 8 <= job.splits; sp += 8) {
+    constexpr int kLoads = 16;
+    uint32_t acc[kLoads];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] += (p[(sp + u) * job.row_words + word] >> sh) & mask;
+    for (int u = 0; u < kLoads; ++u) acc[u] = 0u;
+    int sp = 0;
+    for (; sp + kLoads <= job.splits; sp += kLoads) {
+#pragma unroll
+      for (int u = 0; u < kLoads; ++u) acc[u] += (p[(sp + u) * job.row_words + word] >> sh) & mask;
     }
     for (; sp < job.splits; ++sp) acc[0] += (p[sp * job.row_words + word] >> sh) & mask;
-    const int c = static_cast<int>(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
-                                   ((acc[4] + acc[5]) + (acc[6] + acc[7])));
+    uint32_t total = 0u;
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) total += acc[u];
+    const int c = static_cast<int>(total);
     if (!in_a)
       b_out[static_cast<int64_t>(row) * job.E_next + j] = c;
     else if (job.a_mode == kCounts)

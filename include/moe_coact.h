@@ -123,7 +123,7 @@ const char* moe_status_string(int status);
  *   ws, ws_bytes  workspace of at least
  *                 moe_coact_stats_workspace_size(T, E, pair_count != NULL,
  *                 transition != NULL ? E_next : 0) bytes, 16-byte aligned:
- *                 per-split partial counts (at most 64 splits of the tokens)
+ *                 per-split partial counts (at most 128 splits of the tokens)
  * Limits: 1 <= k, k_next <= 8; 1 <= E, E_next <= 256; T >= 0.
  * d_err bits: EXPERT_RANGE (slot skipped), EXPERT_DUP (the repeat is skipped).
  * Integer outputs are exact and independent of scheduling; every output

@@ -66,26 +66,27 @@ def test_stats_rejects(built_lib):
 
 
 def test_stats_workspace_sizes(built_lib):
-    """Up to 64 splits of at least 512 tokens; each split holds a partial of
+    """Up to 128 splits of at least 256 tokens; each split holds a partial of
     the counted bins (the pair triangle i <= j, the transitions) as 16-bit
-    counters while a split has fewer than 2^16 tokens, else 32-bit, with each
-    slice of rows padded to 16 bytes."""
+    counters while a split has fewer than 2^16 tokens, else 32-bit, each
+    slice of rows padded to 16 bytes and each split's row to an odd number of
+    256-byte units."""
     n = ctypes.c_size_t()
     q = built_lib.moe_coact_stats_workspace_size
 
     def within(splits, bins, bytes_per_bin, slices):
         lo = splits * bins * bytes_per_bin
-        return lo <= n.value <= lo + splits * slices * 16 + 256
+        return lo <= n.value <= lo + splits * (slices * 16 + 512) + 256
 
     assert q(32768, 256, 1, 0, ctypes.byref(n)) == 0
-    assert within(64, 256 * 257 // 2, 2, 3)                   # 64 splits of 512 tokens
+    assert within(128, 256 * 257 // 2, 2, 3)                  # 128 splits of 256 tokens
     assert q(65536, 64, 1, 64, ctypes.byref(n)) == 0
-    assert within(64, 64 * 65 // 2 + 64 * 64, 2, 2)           # pairs and transitions
+    assert within(128, 64 * 65 // 2 + 64 * 64, 2, 2)          # pairs and transitions
     assert q(2048, 8, 0, 0, ctypes.byref(n)) == 0
-    assert within(4, 8, 2, 1)
+    assert within(8, 8, 2, 1)
     assert q(1 << 24, 8, 0, 0, ctypes.byref(n)) == 0
-    assert n.value == 64 * 8 * 4                              # 2^18 tokens a split: 32-bit
-    assert q(0, 8, 1, 0, ctypes.byref(n)) == 0 and n.value >= 36 * 2
+    assert n.value == 128 * 256                               # 2^17 tokens a split: 32-bit,
+    assert q(0, 8, 1, 0, ctypes.byref(n)) == 0 and n.value >= 36 * 2  # one 256-byte row
     assert q(10, 257, 1, 0, ctypes.byref(n)) == -2
     assert q(10, 8, 1, 0, None) == -1
 
