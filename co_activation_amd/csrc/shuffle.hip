@@ -383,7 +383,9 @@ __global__ __launch_bounds__(kBalTile) void balanced_round_kernel(
 //
 // shuffle_exchange_kernel: block b owns tokens [b * TB, (b + 1) * TB).  Each
 // round every token takes its first preference r with t <= limit[r],
-// limit[r] being the fill index of r under the previous round's choices; the
+// limit[r] being the fill index of r under the previous round's choices (a
+// choice stands while its rank still takes the token: the limits only move
+// earlier from round to round); the
 // block counts its tokens per (64-token chunk, rank) with LDS atomics and
 // publishes its counts per rank as 64-bit words tagged with the round,
 // double-buffered by round parity, with a flag saying whether any of its
