@@ -130,29 +130,22 @@ __global__ __launch_bounds__(kPermThreads) void permute_flat_kernel(
 // destination with nontemporal 16-byte stores.
 //
 // How many such blocks a CU holds at once sets how many write streams are
-// open, and HBM absorbs the scattered writes best with about a hundred of
-// them per CU (waves times the places each row goes).  Blocks therefore
-// reserve LDS they do not use so that a CU holds about 56 / writes of them
-// (see parts_lds_bytes).  The reserve also counts against the LDS of the
-// plan-phase kernels that a pipelined step runs beside the move (the
-// statistics' 32 KB histograms), so the cap is set for that case: measured
-// on MI355X inside the pipelined step, 14 KiB rows to up to 8 ranks run in
-// 642 us (56 / writes) against 649 us (48 / writes) and the step takes 1.284
-// against 1.290 ms; 8 KiB rows to up to 6 ranks 492 against 497 us, steps
-// 0.989 against 1.002 ms.  Alone, with cold caches, the tighter 48 / writes
-// cap is the faster one (663 against 683 us and 499 against 560 us).
-// Against other shapes (stage medians, cold caches): 14 KiB rows 686 ->
-// 646 us against a wave per 2 KiB part with no cap; 8 KiB rows 507 -> 499
-// us against 256-thread blocks per token capped at two per CU.  Other part
-// sizes (1-16 KiB) were slower.
+// open, and HBM absorbs the scattered writes best with about 96 of them per
+// CU (waves times the places each row goes).  Blocks therefore reserve LDS
+// they do not use so that a CU holds about 48 / writes of them (see
+// parts_lds_bytes).  Measured on MI355X (stage medians of the benchmark
+// step, cold caches): 14 KiB rows to up to 8 ranks 686 -> 646 us against a
+// wave per 2 KiB part with no cap; 8 KiB rows to up to 6 ranks 507 -> 499 us
+// against 256-thread blocks per token capped at two per CU.  Other part
+// sizes (1-16 KiB) and caps were slower.
 constexpr int kPartWaves = 2;
 constexpr int kPartVec = kPartWaves * kWave;
 constexpr unsigned kLdsPerCu = 160 * 1024;
 
-// LDS reserved per block so that a CU holds about 56 / writes part blocks;
+// LDS reserved per block so that a CU holds about 48 / writes part blocks;
 // none once that reaches the CU's 16 two-wave blocks.
 inline unsigned parts_lds_bytes(int writes) {
-  const int blocks = 56 / (writes < 1 ? 1 : writes);
+  const int blocks = 48 / (writes < 1 ? 1 : writes);
   if (blocks >= 16) return 0;
   return (kLdsPerCu / static_cast<unsigned>(blocks < 2 ? 2 : blocks)) & ~1023u;
 }
