@@ -118,12 +118,17 @@ __global__ __launch_bounds__(kPlanTile) void plan_count_kernel(
   }
   if (t < t1 && src >= 0) {
     const int32_t* row = topk + static_cast<int64_t>(src) * k;
-    int ex[MOE_MAX_K];
+    // every id load, then every rank lookup, goes out before any is used
+    int ex[MOE_MAX_K], rk[MOE_MAX_K];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) ex[j] = j < k ? row[j] : -1;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j)
+      rk[j] = (j < k && ex[j] >= 0 && ex[j] < E) ? expert_rank[ex[j]] : -1;
 #pragma unroll
     for (int j = 0; j < MOE_MAX_K; ++j) {
       if (j >= k) break;
-      const int e = row[j];
-      ex[j] = e;
+      const int e = ex[j];
 #pragma unroll
       for (int q = 0; q < j; ++q)
         if (ex[q] == e) errbits |= MOE_DERR_EXPERT_DUP;
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(kPlanTile) void plan_count_kernel(
         errbits |= MOE_DERR_EXPERT_RANGE;
         continue;
       }
-      const int r = expert_rank[e];
+      const int r = rk[j];
       if (r < 0 || r >= G) {
         errbits |= MOE_DERR_RANK_RANGE;
         continue;
@@ -363,24 +368,24 @@ __global__ __launch_bounds__(kPlanTile) void plan_write_kernel(
 
   const int t = t0 + static_cast<int>(threadIdx.x);
   const bool valid = t < t1;
-  int rk[MOE_MAX_K];
+  // every id and gate load, then every rank lookup, goes out before any is
+  // used
+  int ex[MOE_MAX_K], rk[MOE_MAX_K];
   float w[MOE_MAX_K];
   uint64_t mask = 0;
 #pragma unroll
   for (int j = 0; j < MOE_MAX_K; ++j) {
-    rk[j] = -1;
-    w[j] = 0.f;
-    if (valid && j < k) {
-      const int e = topk[static_cast<int64_t>(t) * k + j];
-      if (gates != nullptr) w[j] = gates[static_cast<int64_t>(t) * k + j];
-      if (e >= 0 && e < E) {
-        const int r = expert_rank[e];
-        if (r >= 0 && r < G) {
-          rk[j] = r;
-          mask |= 1ull << r;
-        }
-      }
-    }
+    const bool in = valid && j < k;
+    ex[j] = in ? topk[static_cast<int64_t>(t) * k + j] : -1;
+    w[j] = (in && gates != nullptr) ? gates[static_cast<int64_t>(t) * k + j] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_K; ++j)
+    rk[j] = (ex[j] >= 0 && ex[j] < E) ? expert_rank[ex[j]] : -1;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_K; ++j) {
+    if (rk[j] < 0 || rk[j] >= G) rk[j] = -1;
+    if (rk[j] >= 0) mask |= 1ull << rk[j];
   }
 
   int mine = 0;

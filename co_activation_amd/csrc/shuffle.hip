@@ -33,11 +33,12 @@ struct ShuffleWs {
   int64_t* counters;
   int32_t* perm_scratch;
   void* plan_ws;
-  uint64_t* rec;  // exchange words of the exchange form: [2][kXBlocks][G + 1]
+  uint64_t* rec;  // exchange words of the exchange form: [kXSlots][kXBlocks][G + 1]
   size_t bytes;
 };
 
 constexpr int kXBlocksMax = 128;  // kXBlocks, needed before the kernels
+constexpr int kXSlots = 4;        // rounds whose exchange words are kept at once
 
 ShuffleWs shuffle_layout(void* base, int64_t T, int E, int G) {
   ShuffleWs w{};
@@ -56,7 +57,7 @@ ShuffleWs shuffle_layout(void* base, int64_t T, int E, int G) {
   w.counters = reinterpret_cast<int64_t*>(take(sizeof(int64_t) * 8));
   w.perm_scratch = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (T > 0 ? T : 1)));
   w.plan_ws = take(plan_workspace_bytes(T, G));
-  w.rec = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 2 * kXBlocksMax * (G + 1)));
+  w.rec = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * kXSlots * kXBlocksMax * (G + 1)));
   w.bytes = off;
   return w;
 }
@@ -387,14 +388,19 @@ __global__ __launch_bounds__(kBalTile) void balanced_round_kernel(
 // choice stands while its rank still takes the token: the limits only move
 // earlier from round to round); the
 // block counts its tokens per (64-token chunk, rank) with LDS atomics and
-// publishes its counts per rank as 64-bit words tagged with the round,
-// double-buffered by round parity, with a flag saying whether any of its
-// tokens changed its choice.  Every block reads all blocks' flags and the
-// counts of the blocks before it.  That prefix and the block's own chunk
-// counts give the next round's limits: a rank full before the block, open
-// after it, or filled at an exact position inside it.  The rounds stop when
-// no token of any block changed its choice (the fixed point; at most G + 1
-// rounds).  The final counts then give each token its position directly:
+// publishes its counts per rank as 64-bit words tagged with the round, in a
+// ring of kXSlots rounds, with a flag saying whether any of its tokens
+// changed its choice.  Every block reads the counts of the blocks before it
+// for this round, and all blocks' flags of the previous round (not of this
+// one, so that no block waits for a later, slower block's current round).
+// That prefix and the block's own chunk counts give the next round's limits:
+// a rank full before the block, open after it, or filled at an exact
+// position inside it.  The rounds stop one round after the first in which no
+// token of any block changed its choice (the fixed point, reached within
+// G + 1 rounds; the extra round repeats it).  Every block has published the
+// previous round before a block moves on, so a block writing round n + 1
+// knows that all blocks have read round n - 3: four slots suffice.  The
+// final counts then give each token its position directly:
 // its rank's shard offset r * cap, plus the rank's tokens in earlier blocks,
 // earlier chunks, and earlier lanes of its chunk -- the stable counting sort,
 // without the plan kernels.
@@ -711,10 +717,10 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   }
   group_masks<PW>(pw1, G, gm1);
 
-  const int max_rounds = G + 2;
+  const int max_rounds = G + 3;
   int P = 0;  // lane r: tokens rank r took in earlier blocks (this round)
   for (int round = 0; round < max_rounds; ++round) {
-    uint64_t* xr = rec + static_cast<int64_t>(round & 1) * nb * words;
+    uint64_t* xr = rec + static_cast<int64_t>(round % kXSlots) * nb * words;
     // 1. choices, and the tokens of each (chunk, rank) from wave ballots
     int changed = round == 0 ? 1 : 0;
     int wc = 0;
@@ -769,8 +775,8 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
     if (lane < G) s_wc[wave][lane] = wc;
     const int any = __syncthreads_or(changed);
     // 2. (wave 0) publish this block's counts and whether any of its tokens
-    // changed; 3. then every block's flag of this round (the flags are 0 or
-    // 1: their sum is nonzero when any is set)
+    // changed; 3. then every block's flag of the previous round (the flags
+    // are 0 or 1: their sum is nonzero when any is set)
     if (wave == 0) {
       if (lane < G) {
         int c = 0;
@@ -784,8 +790,11 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
         __hip_atomic_store(xr + static_cast<int64_t>(b) * words + G,
                            xword(round, static_cast<uint32_t>(any)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-      int ch = 0;
-      int ok = xsum(xr + G, words, lane, kWave, nb, round, ch) ? 1 : 0;
+      int ch = 1, ok = 1;
+      if (round > 0) {
+        const uint64_t* xp = rec + static_cast<int64_t>((round - 1) % kXSlots) * nb * words;
+        ok = xsum(xp + G, words, lane, kWave, nb, round - 1, ch) ? 1 : 0;
+      }
       ch = ballot(ch != 0) != 0;
       ok = ballot(!ok) == 0;
       if (lane == 0) {
@@ -806,7 +815,9 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
       if (tid == 0) report(d_err, MOE_DERR_SYNC);
       return;
     }
-    const bool last = (round > 0 && !s_changed) || round + 1 == max_rounds;
+    // No token of any block changed in the previous round: this round's
+    // choices and counts repeat it, so they are the fixed point.
+    const bool last = !s_changed || round + 1 == max_rounds;
     // 5. (every wave) the tokens each rank took in earlier blocks (lane = rank)
     P = 0;
     if (lane < G) {
@@ -997,7 +1008,7 @@ extern "C" int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E
   const moe::XShape xs = moe::exchange_shape(T);
   if (xs.ok) {
     const int64_t Gs = moe::pref_stride(G);
-    const int64_t rec_words = 2ll * xs.nb * (G + 1);
+    const int64_t rec_words = static_cast<int64_t>(moe::kXSlots) * xs.nb * (G + 1);
     const int W = moe::group_width(G);
     const int per_block = 256 / W * moe::kScoreTokens;
     moe::prefs_sort_kernel<<<(Ti + per_block - 1) / per_block, 256, 0, s>>>(
