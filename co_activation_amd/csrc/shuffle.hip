@@ -510,8 +510,17 @@ __global__ __launch_bounds__(256) void rank_argmax_kernel(
 // in rank_argmax_kernel, then a bitonic sort of the group's keys, descending,
 // across its lanes (W log W compare-exchanges on the lanes' shuffled keys,
 // against W^2 comparisons for ranking by counting) leaves the i-th preferred
-// rank in lane i of the group, which writes byte i of the token's row.
-// Also clears the exchange words.
+// rank in lane i of the group, which writes it at byte pref_byte(i) of the
+// token's row.  Also clears the exchange words.
+//
+// A row holds groups of 16 positions, each group transposed: its 32-bit
+// word d holds positions d, d + 4, d + 8, d + 12 (byte j: position 4j + d),
+// so that a test of all 16 positions a word at a time (first_feasible)
+// yields its result bits in position order.
+__host__ __device__ inline int pref_byte(int i) {
+  return (i & ~15) | ((i & 3) << 2) | ((i >> 2) & 3);
+}
+
 template <typename K>
 __device__ __forceinline__ K bitonic_desc(K key, int r, int W) {
   for (int size = 2; size <= W; size <<= 1) {
@@ -551,7 +560,7 @@ __global__ __launch_bounds__(256) void prefs_sort_kernel(
           bitonic_desc<long long>(live ? score[u] * 64 + (63 - r) : LLONG_MIN, r, W);
       rank = 63 - static_cast<int>(key & 63);
     }
-    if (live) prefs[static_cast<int64_t>(t) * Gs + r] = static_cast<uint8_t>(rank);
+    if (live) prefs[static_cast<int64_t>(t) * Gs + pref_byte(r)] = static_cast<uint8_t>(rank);
   }
 }
 
@@ -610,8 +619,8 @@ __device__ __forceinline__ void group_masks(const u32x4 (&pw)[PW], int G, uint64
   for (int w = 0; w < PW; ++w) {
     uint64_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t p = (pw[w][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    for (int i = 0; i < 16; ++i) {  // position w * 16 + i: word i & 3, byte i >> 2
+      const uint32_t p = (pw[w][i & 3] >> (8 * (i >> 2))) & 0xFFu;
       if (w * 16 + i < G) m |= 1ull << p;
     }
     gm[w] = m;
@@ -623,7 +632,10 @@ __device__ __forceinline__ void group_masks(const u32x4 (&pw)[PW], int G, uint64
 // does).  gm holds the ranks of each group of 16 preferences: the group of
 // the answer is the first one at or after start's whose ranks meet feas
 // (ranks listed before start are infeasible), so that only that group's 16
-// positions are tested one by one.
+// positions are tested, four at a time: the bit of feas for rank p is bit
+// p & 7 of byte p >> 3, so one byte permute of feas fetches each position's
+// byte, a second turns p & 7 into a one-hot byte, and a byte that keeps a
+// bit after the AND sets its bit 7 in x + 0x7f (no carry leaves a byte).
 template <int PW>
 __device__ __forceinline__ int first_feasible(const u32x4 (&pw)[PW], const uint64_t (&gm)[PW],
                                               int G, uint64_t feas, int start, int& pos) {
@@ -640,27 +652,32 @@ __device__ __forceinline__ int first_feasible(const u32x4 (&pw)[PW], const uint6
       for (int j = 0; j < 4; ++j) g[j] = sel ? pw[w][j] : g[j];
     }
     const uint32_t lo = static_cast<uint32_t>(feas), hi = static_cast<uint32_t>(feas >> 32);
-    uint32_t m = 0;  // feasible positions among the group
+    // bit 8j + d of m: position 4j + d of the group is feasible (bit order
+    // is position order)
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t p = (g[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-      const uint32_t bit = p < 32 ? (lo >> p) : (hi >> (p - 32));
-      m |= (bit & 1u) << i;
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t fb = __builtin_amdgcn_perm(hi, lo, (g[d] >> 3) & 0x07070707u);
+      const uint32_t oh = __builtin_amdgcn_perm(0x80402010u, 0x08040201u, g[d] & 0x07070707u);
+      m |= (((fb & oh) + 0x7F7F7F7Fu) & 0x80808080u) >> (7 - d);
     }
-    const int n = G - gsel * 16;
-    if (n < 16) m &= (1u << n) - 1u;
-    if (start > gsel * 16) m &= ~((1u << (start - gsel * 16)) - 1u);
+    const int n = G - gsel * 16;  // positions the group holds
+    if (n < 16) m &= (1u << ((n >> 2) * 8 + (n & 3))) - 1u;
+    const int s0 = start - gsel * 16;
+    if (s0 > 0) m &= ~((1u << ((s0 >> 2) * 8 + (s0 & 3))) - 1u);
     if (m != 0) {
-      const int i = __ffs(m) - 1;
-      pos = gsel * 16 + i;
-      return static_cast<int>((g[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+      const int b = __ffs(m) - 1;
+      const int j = b >> 3, d = b & 7;
+      pos = gsel * 16 + 4 * j + d;
+      const uint32_t gd = d == 0 ? g[0] : d == 1 ? g[1] : d == 2 ? g[2] : g[3];
+      return static_cast<int>((gd >> (8 * j)) & 0xFFu);
     }
   }
   const int i = (G - 1) & 15, w = (G - 1) >> 4;
   int last = 0;
 #pragma unroll
   for (int q = 0; q < PW; ++q)
-    if (q == w) last = static_cast<int>((pw[q][i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    if (q == w) last = static_cast<int>((pw[q][i & 3] >> (8 * (i >> 2))) & 0xFFu);
   pos = G - 1;
   return last;
 }
