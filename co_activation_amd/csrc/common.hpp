@@ -65,25 +65,49 @@ __device__ __forceinline__ int wave_max(int v) {
   return v;
 }
 
-// Inclusive prefix sum across the 64 lanes.
+// Lane `src`'s value of v, for a src that is the same in every lane.
+__device__ __forceinline__ int lane_value(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
+}
+
+// Inclusive prefix sum across the 64 lanes, with DPP lane moves instead of
+// LDS permutes: shifts by 1, 2, 4 and 8 lanes inside each row of 16, then
+// lane 15 of a row broadcast into the next row (row_bcast:15, added in rows
+// 1 and 3) and lane 31 into the upper half (row_bcast:31).
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int u = __shfl_up(v, d, kWave);
-    if (lane >= d) v += u;
-  }
+  const int rl = lane & 15;
+  int t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  if (rl >= 1) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  if (rl >= 2) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  if (rl >= 4) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  if (rl >= 8) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x142, 0xF, 0xF, false);  // row_bcast:15
+  if ((lane & 31) >= 16) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x143, 0xF, 0xF, false);  // row_bcast:31
+  if (lane >= 32) v += t;
   return v;
 }
 
-// Inclusive prefix max across the 64 lanes.
+// Inclusive prefix max across the 64 lanes (the same lane moves).
 __device__ __forceinline__ int wave_incl_max(int v) {
   const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int u = __shfl_up(v, d, kWave);
-    if (lane >= d) v = max(v, u);
-  }
+  const int rl = lane & 15;
+  int t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  if (rl >= 1) v = max(v, t);
+  t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  if (rl >= 2) v = max(v, t);
+  t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  if (rl >= 4) v = max(v, t);
+  t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  if (rl >= 8) v = max(v, t);
+  t = __builtin_amdgcn_update_dpp(0, v, 0x142, 0xF, 0xF, false);
+  if ((lane & 31) >= 16) v = max(v, t);
+  t = __builtin_amdgcn_update_dpp(0, v, 0x143, 0xF, 0xF, false);
+  if (lane >= 32) v = max(v, t);
   return v;
 }
 

@@ -125,14 +125,14 @@ __global__ __launch_bounds__(kExScanThreads) void expert_scan_kernel(
       const int j = c * kWave + lane;
       const int incl = wave_incl_scan(pre[c]) + carry;
       if (j < NT) tile_cnt[static_cast<int64_t>(e) * NT + j] = incl - pre[c];
-      carry = __shfl(incl, kWave - 1, kWave);
+      carry = lane_value(incl, kWave - 1);
     }
     for (int base = kPre * kWave; base < NT; base += kWave) {
       const int j = base + lane;
       const int v = j < NT ? tile_cnt[static_cast<int64_t>(e) * NT + j] : 0;
       const int incl = wave_incl_scan(v) + carry;
       if (j < NT) tile_cnt[static_cast<int64_t>(e) * NT + j] = incl - v;
-      carry = __shfl(incl, kWave - 1, kWave);
+      carry = lane_value(incl, kWave - 1);
     }
     if (lane == 0) s_count[e] = carry;
   }
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kExScanThreads) void expert_scan_kernel(
     const int v = lane < G ? s_rtot[lane] : 0;
     const int incl = wave_incl_scan(v);
     if (lane < G) s_roff[lane] = incl - v;
-    if (lane == 0) s_roff[G] = __shfl(incl, kWave - 1, kWave);
+    if (lane == 0) s_roff[G] = lane_value(incl, kWave - 1);
   }
   __syncthreads();
   int tpe = kExScanThreads / E;

@@ -58,7 +58,7 @@ __device__ __forceinline__ int load_shards(const int32_t* off, int T, int G, int
   const int nt = lane < G ? (hi - lo + kPlanTile - 1) / kPlanTile : 0;
   incl = wave_incl_scan(nt);
   first = incl - nt;
-  total = __shfl(incl, kWave - 1, kWave);
+  total = lane_value(incl, kWave - 1);
   return ballot(bad) ? MOE_DERR_SRC_OFFSETS : 0;
 }
 
@@ -71,9 +71,9 @@ __device__ __forceinline__ bool block_tile(const int32_t* off, int T, int G, int
   const int j = blockIdx.x;
   if (j >= total) return false;
   s = __popcll(ballot(lane_id() < G && incl <= j));
-  const int s_lo = __shfl(lo, s, kWave);
-  const int s_hi = __shfl(hi, s, kWave);
-  const int s_first = __shfl(first, s, kWave);
+  const int s_lo = lane_value(lo, s);
+  const int s_hi = lane_value(hi, s);
+  const int s_first = lane_value(first, s);
   t0 = s_lo + (j - s_first) * kPlanTile;
   t1 = min(t0 + kPlanTile, s_hi);
   return true;
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
         if (!flag) val += carry[g];
         if (in) tile_cnt[static_cast<int64_t>(r) * stride + j] = val - v;
         if (last) s_S[s * G + r] = val;
-        carry[g] = __shfl(val, kWave - 1, kWave);
+        carry[g] = lane_value(val, kWave - 1);
       }
     }
   }
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kPlanTile) void plan_write_kernel(
   for (int r = 0; r < G; ++r) {
     const uint64_t b = ballot((mask >> r) & 1ull);
     if (b == 0) continue;
-    const int rbase = __shfl(mybase, r, kWave);
+    const int rbase = lane_value(mybase, r);
     if ((mask >> r) & 1ull) {
       const int row = rbase + lanes_below(b);
       trow[q++] = row;

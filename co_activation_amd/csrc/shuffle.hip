@@ -255,9 +255,9 @@ __device__ void balanced_fill(const int32_t* __restrict__ tile_cnt,
         if (b) {
           const int first = __ffsll(static_cast<long long>(b)) - 1;
           hit = base + first;
-          need = cap - (__shfl(incl, first, kWave) - __shfl(v, first, kWave));
+          need = cap - (lane_value(incl, first) - lane_value(v, first));
         }
-        carry = __shfl(incl, kWave - 1, kWave);
+        carry = lane_value(incl, kWave - 1);
       }
       int nf = INT32_MAX;
       if (hit >= 0) {
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
         const int incl = wave_incl_scan(n);
         const uint64_t hit = ballot(lane < nchunks && incl >= need);
         const int q = __ffsll(static_cast<long long>(hit)) - 1;
-        const int rest = need - (__shfl(incl, q, kWave) - __shfl(n, q, kWave));
+        const int rest = need - (lane_value(incl, q) - lane_value(n, q));
         const int base = (q / kXWaves) * kXThreads + (q % kXWaves) * kWave;
         const uint64_t mm = ballot(s_choice[base + lane] == rr);
         const bool at = ((mm >> lane) & 1ull) && lanes_below(mm) == rest - 1;
@@ -889,7 +889,7 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
     int below = 0;
     uint64_t rest = ballot(t < T && c < G);
     while (rest != 0) {
-      const int v = __shfl(c, __ffsll(static_cast<long long>(rest)) - 1, kWave);
+      const int v = lane_value(c, __ffsll(static_cast<long long>(rest)) - 1);
       const uint64_t m = ballot(c == v);
       if (c == v) below = lanes_below(m);
       rest &= ~m;
