@@ -447,21 +447,48 @@ __device__ __forceinline__ void token_scores(const int32_t* __restrict__ topk, i
     for (int j = 0; j < MOE_MAX_K; ++j)
       e[u][j] = (j < k && t < T) ? topk[static_cast<int64_t>(t) * k + j] : -1;
   }
+  // every row load goes out before the first add
 #pragma unroll
   for (int u = 0; u < kScoreTokens; ++u) {
-    long long sc = 0;
+    long long m[MOE_MAX_K];
 #pragma unroll
     for (int j = 0; j < MOE_MAX_K; ++j) {
-      if (j >= k) break;
       const int x = e[u][j];
-      if (x < 0 || x >= E) {
-        if (t0 + u < T) errbits |= MOE_DERR_EXPERT_RANGE;
-      } else if (r < G) {
-        sc += M[static_cast<int64_t>(x) * G + r];
-      }
+      const bool ok = j < k && x >= 0 && x < E && r < G;
+      m[j] = ok ? M[static_cast<int64_t>(x) * G + r] : 0;
+      if (j < k && (x < 0 || x >= E) && t0 + u < T) errbits |= MOE_DERR_EXPERT_RANGE;
     }
+    long long sc = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K; ++j) sc += m[j];
     score[u] = sc;
   }
+}
+
+// The value of lane (lane ^ j), j a power of two below 64 that is a
+// constant once the caller's loop is unrolled: DPP lane moves for j = 1, 2
+// (quad permutes), 4 (row shifts) and 8 (row rotate), a swizzle inside 32
+// lanes for j = 16, an LDS permute only for j = 32.
+__device__ __forceinline__ int xor_lane(int v, int j) {
+  switch (j) {
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    case 4: {
+      const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);  // row_shl:4
+      const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+      return (lane_id() & 4) ? dn : up;
+    }
+    case 8: return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    case 16: return __builtin_amdgcn_ds_swizzle(v, 0x401F);  // and 0x1f, xor 0x10
+    default: return __shfl_xor(v, j, kWave);
+  }
+}
+
+__device__ __forceinline__ long long xor_lane(long long v, int j) {
+  const int lo = xor_lane(static_cast<int>(static_cast<unsigned long long>(v)), j);
+  const int hi = xor_lane(static_cast<int>(static_cast<unsigned long long>(v) >> 32), j);
+  return static_cast<long long>((static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) |
+                                static_cast<uint32_t>(lo));
 }
 
 // Scores below 2^25 (scores are counts, never negative) make keys
@@ -474,10 +501,10 @@ constexpr long long kKey32Limit = 1ll << 25;
 // (coalesced across the group), and a max-reduction over the keys
 // score * 64 + (63 - r) (ties to the lower rank) gives the first rank.
 // Also clears the exchange words.
+template <int W>
 __global__ __launch_bounds__(256) void rank_argmax_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
-    int W, int32_t* __restrict__ pred, uint64_t* __restrict__ rec, int64_t rec_words,
-    int32_t* d_err) {
+    int32_t* __restrict__ pred, uint64_t* __restrict__ rec, int64_t rec_words, int32_t* d_err) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < rec_words; i += gridDim.x * 256ll) rec[i] = 0;
   const int per_block = 256 / W;
   const int tg = (blockIdx.x * per_block + static_cast<int>(threadIdx.x) / W) * kScoreTokens;
@@ -494,12 +521,14 @@ __global__ __launch_bounds__(256) void rank_argmax_kernel(
     if (ballot(score[u] >= kKey32Limit) == 0) {
       const int key = live ? static_cast<int>(score[u]) * 64 + (63 - r) : -1;
       int best = key;
-      for (int d = 1; d < W; d <<= 1) best = max(best, __shfl_xor(best, d, kWave));
+#pragma unroll
+      for (int d = 1; d < W; d <<= 1) best = max(best, xor_lane(best, d));
       top = key == best;
     } else {
       const long long key = live ? score[u] * 64 + (63 - r) : LLONG_MIN;
       long long best = key;
-      for (int d = 1; d < W; d <<= 1) best = max(best, __shfl_xor(best, d, kWave));
+#pragma unroll
+      for (int d = 1; d < W; d <<= 1) best = max(best, xor_lane(best, d));
       top = key == best;
     }
     if (live && top) pred[t] = r;
@@ -521,11 +550,13 @@ __host__ __device__ inline int pref_byte(int i) {
   return (i & ~15) | ((i & 3) << 2) | ((i >> 2) & 3);
 }
 
-template <typename K>
-__device__ __forceinline__ K bitonic_desc(K key, int r, int W) {
+template <int W, typename K>
+__device__ __forceinline__ K bitonic_desc(K key, int r) {
+#pragma unroll
   for (int size = 2; size <= W; size <<= 1) {
+#pragma unroll
     for (int j = size >> 1; j > 0; j >>= 1) {
-      const K other = __shfl_xor(key, j, kWave);
+      const K other = xor_lane(key, j);
       const bool lower = (r & j) == 0;
       const bool desc = (r & size) == 0;
       key = (lower == desc) ? max(key, other) : min(key, other);
@@ -534,9 +565,10 @@ __device__ __forceinline__ K bitonic_desc(K key, int r, int W) {
   return key;
 }
 
+template <int W>
 __global__ __launch_bounds__(256) void prefs_sort_kernel(
     const int32_t* __restrict__ topk, int T, int k, int E, const int64_t* __restrict__ M, int G,
-    int W, int64_t Gs, uint8_t* __restrict__ prefs, uint64_t* __restrict__ rec, int64_t rec_words,
+    int64_t Gs, uint8_t* __restrict__ prefs, uint64_t* __restrict__ rec, int64_t rec_words,
     int32_t* d_err) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < rec_words; i += gridDim.x * 256ll) rec[i] = 0;
   const int per_block = 256 / W;
@@ -553,11 +585,11 @@ __global__ __launch_bounds__(256) void prefs_sort_kernel(
     int rank;
     if (ballot(score[u] >= kKey32Limit) == 0) {
       const int key =
-          bitonic_desc<int>(live ? static_cast<int>(score[u]) * 64 + (63 - r) : -1, r, W);
+          bitonic_desc<W, int>(live ? static_cast<int>(score[u]) * 64 + (63 - r) : -1, r);
       rank = 63 - (key & 63);
     } else {
       const long long key =
-          bitonic_desc<long long>(live ? score[u] * 64 + (63 - r) : LLONG_MIN, r, W);
+          bitonic_desc<W, long long>(live ? score[u] * 64 + (63 - r) : LLONG_MIN, r);
       rank = 63 - static_cast<int>(key & 63);
     }
     if (live) prefs[static_cast<int64_t>(t) * Gs + pref_byte(r)] = static_cast<uint8_t>(rank);
@@ -1028,8 +1060,19 @@ extern "C" int moe_shuffle_balanced(const int32_t* topk, int64_t T, int k, int E
     const int64_t rec_words = static_cast<int64_t>(moe::kXSlots) * xs.nb * (G + 1);
     const int W = moe::group_width(G);
     const int per_block = 256 / W * moe::kScoreTokens;
-    moe::prefs_sort_kernel<<<(Ti + per_block - 1) / per_block, 256, 0, s>>>(
-        topk, Ti, k, E, w.base.M, G, W, Gs, w.prefs, w.base.rec, rec_words, d_err);
+    auto sort = [&](auto kernel) {
+      kernel<<<(Ti + per_block - 1) / per_block, 256, 0, s>>>(topk, Ti, k, E, w.base.M, G, Gs,
+                                                            w.prefs, w.base.rec, rec_words, d_err);
+    };
+    switch (W) {
+      case 1: sort(moe::prefs_sort_kernel<1>); break;
+      case 2: sort(moe::prefs_sort_kernel<2>); break;
+      case 4: sort(moe::prefs_sort_kernel<4>); break;
+      case 8: sort(moe::prefs_sort_kernel<8>); break;
+      case 16: sort(moe::prefs_sort_kernel<16>); break;
+      case 32: sort(moe::prefs_sort_kernel<32>); break;
+      default: sort(moe::prefs_sort_kernel<64>); break;
+    }
     MOE_CHECK_LAUNCH();
     const int pwords = static_cast<int>(Gs / 16);
     auto launch = [&](auto kernel) {
@@ -1108,8 +1151,12 @@ extern "C" int moe_shuffle_predict(const int32_t* topk, int64_t T, int k, int E,
   if (G > 16 && Ti > 0) {
     const int W = moe::group_width(G);
     const int per_block = 256 / W * moe::kScoreTokens;
-    moe::rank_argmax_kernel<<<(Ti + per_block - 1) / per_block, 256, 0, s>>>(
-        topk, Ti, k, E, w.M, G, W, pred_rank, w.rec, 0, d_err);
+    if (W == 32)
+      moe::rank_argmax_kernel<32><<<(Ti + per_block - 1) / per_block, 256, 0, s>>>(
+          topk, Ti, k, E, w.M, G, pred_rank, w.rec, 0, d_err);
+    else
+      moe::rank_argmax_kernel<64><<<(Ti + per_block - 1) / per_block, 256, 0, s>>>(
+          topk, Ti, k, E, w.M, G, pred_rank, w.rec, 0, d_err);
     MOE_CHECK_LAUNCH();
     moe::PlanArgs a{pred_rank,      nullptr,        Ti,        1,
                     G,              w.identity,     G,         G,
