@@ -726,9 +726,11 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   // of its cap-th taker.
   __shared__ int s_lim[MOE_MAX_G];
   __shared__ int s_cc[kXChunks][MOE_MAX_G];  // tokens per (64-token chunk, rank)
-  __shared__ int s_wc[kXWaves][MOE_MAX_G];    // this block's counts per wave
-  __shared__ int s_pre[kXGroups][MOE_MAX_G];  // partial sums over earlier blocks
-  __shared__ int s_cnt[MOE_MAX_G];
+  // This block's tokens per rank, and the earlier blocks' (the prefix), each
+  // summed by LDS atomics into the half of the round's parity; the other
+  // half, last read in the previous round, is cleared for the next one.
+  __shared__ int s_cnt[2][MOE_MAX_G];
+  __shared__ int s_pre[2][MOE_MAX_G];
   __shared__ int s_abort, s_changed;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = lane_id();
@@ -739,7 +741,11 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   const int64_t words = static_cast<int64_t>(G) + 1;  // per block and round: G counts, a flag
   constexpr int ng = kXGroups;  // thread (c, r), c < 16, r < G <= 64
 
-  if (tid < MOE_MAX_G) s_lim[tid] = INT_MAX;
+  if (tid < MOE_MAX_G) {
+    s_lim[tid] = INT_MAX;
+    s_cnt[0][tid] = 0;
+    s_pre[0][tid] = 0;
+  }
   if (tid == 0) s_abort = 0;
   for (int u = 0; u < tpt; ++u) {
     s_choice[u * kXThreads + tid] = 255;
@@ -768,15 +774,21 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
 
   const int max_rounds = G + 3;
   int P = 0;  // lane r: tokens rank r took in earlier blocks (this round)
+  int c1 = 255, cur1 = 0;  // with one token per thread: its choice and cursor
   for (int round = 0; round < max_rounds; ++round) {
     uint64_t* xr = rec + static_cast<int64_t>(round % kXSlots) * nb * words;
+    const int par = round & 1;
+    if (tid < MOE_MAX_G) {
+      s_cnt[par ^ 1][tid] = 0;
+      s_pre[par ^ 1][tid] = 0;
+    }
     // 1. choices, and the tokens of each (chunk, rank) from wave ballots
     int changed = round == 0 ? 1 : 0;
     int wc = 0;
     for (int u = 0; u < tpt; ++u) {
       const int t = t0 + u * kXThreads + tid;
       const int idx = u * kXThreads + tid;
-      int c = s_choice[idx];
+      int c = tpt == 1 ? c1 : s_choice[idx];
       const int c0 = c;
       // no choice yet, or its rank is full
       const bool walk = t < T && (c >= G || t > s_lim[c]);
@@ -800,12 +812,14 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
               pw1[w] = *reinterpret_cast<const u32x4*>(prefs + static_cast<int64_t>(t) * Gs + 16 * w);
             group_masks<PW>(pw1, G, gm1);
           }
-          const int start = c >= G ? 0 : s_cursor[idx] + 1;
+          const int start = c >= G ? 0 : (tpt == 1 ? cur1 : s_cursor[idx]) + 1;
           int pos = 0;
           const int nw = first_feasible<PW>(pw1, gm1, G, feas, start, pos);
           s_cursor[idx] = static_cast<uint8_t>(pos);
+          cur1 = pos;
           changed |= nw != c;
           c = nw;
+          c1 = c;
           s_choice[idx] = static_cast<uint8_t>(c);
         }
       }
@@ -821,16 +835,14 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
       }
       if (lane < G) wc += row[lane];
     }
-    if (lane < G) s_wc[wave][lane] = wc;
+    if (lane < G && wc != 0) atomicAdd(&s_cnt[par][lane], wc);
     const int any = __syncthreads_or(changed);
     // 2. (wave 0) publish this block's counts and whether any of its tokens
     // changed; 3. then every block's flag of the previous round (the flags
     // are 0 or 1: their sum is nonzero when any is set)
     if (wave == 0) {
       if (lane < G) {
-        int c = 0;
-        for (int w = 0; w < kXWaves; ++w) c += s_wc[w][lane];
-        s_cnt[lane] = c;
+        const int c = s_cnt[par][lane];
         __hip_atomic_store(xr + static_cast<int64_t>(b) * words + lane,
                            xword(round, static_cast<uint32_t>(c)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -856,8 +868,12 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
     {
       const int c = tid / MOE_MAX_G, r = tid % MOE_MAX_G;
       int pre = 0;
-      if (r < G && !xsum(xr + r, words, c, ng, b, round, pre)) s_abort = 1;
-      s_pre[c][r] = pre;
+      if (r < G) {
+        if (!xsum(xr + r, words, c, ng, b, round, pre))
+          s_abort = 1;
+        else if (pre != 0)
+          atomicAdd(&s_pre[par][r], pre);
+      }
     }
     __syncthreads();
     if (s_abort) {
@@ -868,18 +884,14 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
     // choices and counts repeat it, so they are the fixed point.
     const bool last = !s_changed || round + 1 == max_rounds;
     // 5. (every wave) the tokens each rank took in earlier blocks (lane = rank)
-    P = 0;
-    if (lane < G) {
-#pragma unroll
-      for (int c = 0; c < kXGroups; ++c) P += s_pre[c][lane];
-    }
+    P = lane < G ? s_pre[par][lane] : 0;
     if (last) break;
     // 6. the ranks open for the whole block, and those whose cap-th taker
     // lies inside it; each wave places some of the latter: the chunk from a
     // scan of the chunk counts (lane = chunk), the lane from the chunk's
     // ballot of that rank
     {
-      const int cnt = lane < G ? s_cnt[lane] : 0;
+      const int cnt = lane < G ? s_cnt[par][lane] : 0;
       const bool open = lane < G && P + cnt < cap;
       const bool cross = lane < G && P < cap && P + cnt >= cap;
       if (wave == 0 && lane < G && !cross) s_lim[lane] = open ? INT_MAX : -1;
