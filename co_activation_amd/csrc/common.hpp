@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "moe_coact.h"
@@ -47,23 +48,38 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
 
+// Sum over the 64 lanes, every lane receiving it: the DPP inclusive scan of
+// wave_incl_scan on 64-bit values (each half moved separately), then lane
+// 63's total.
 __device__ __forceinline__ long long wave_sum64(long long v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  const int lane = lane_id();
+  const int rl = lane & 15;
+  auto mv = [](long long x, auto ctrl) {
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<unsigned long long>(x)),
+                                               decltype(ctrl)::value, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<unsigned long long>(x) >> 32),
+                                               decltype(ctrl)::value, 0xF, 0xF, false);
+    return static_cast<long long>((static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) |
+                                  static_cast<uint32_t>(lo));
+  };
+  long long t = mv(v, std::integral_constant<int, 0x111>{});  // row_shr:1
+  if (rl >= 1) v += t;
+  t = mv(v, std::integral_constant<int, 0x112>{});  // row_shr:2
+  if (rl >= 2) v += t;
+  t = mv(v, std::integral_constant<int, 0x114>{});  // row_shr:4
+  if (rl >= 4) v += t;
+  t = mv(v, std::integral_constant<int, 0x118>{});  // row_shr:8
+  if (rl >= 8) v += t;
+  t = mv(v, std::integral_constant<int, 0x142>{});  // row_bcast:15
+  if ((lane & 31) >= 16) v += t;
+  t = mv(v, std::integral_constant<int, 0x143>{});  // row_bcast:31
+  if (lane >= 32) v += t;
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<unsigned long long>(v)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<unsigned long long>(v) >> 32), 63);
+  return static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo);
 }
 
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d, kWave));
-  return v;
-}
 
 // Lane `src`'s value of v, for a src that is the same in every lane.
 __device__ __forceinline__ int lane_value(int v, int src) {
@@ -109,6 +125,43 @@ __device__ __forceinline__ int wave_incl_max(int v) {
   t = __builtin_amdgcn_update_dpp(0, v, 0x143, 0xF, 0xF, false);
   if (lane >= 32) v = max(v, t);
   return v;
+}
+
+// Sum and maximum over the 64 lanes, every lane receiving them: lane 63 of
+// the inclusive scan.
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_max(v), 63);
+}
+
+// Segmented inclusive prefix sum across the 64 lanes: a lane whose flag is
+// set starts a new segment.  The combine of (value, flag) pairs -- a later
+// pair that starts a segment keeps its value, otherwise it adds the earlier
+// one; flags or together -- is associative, so the DPP steps of
+// wave_incl_scan apply.  On return flag says whether a segment starts at or
+// before the lane.
+__device__ __forceinline__ void wave_seg_scan(int& val, int& flag) {
+  const int lane = lane_id();
+  const int rl = lane & 15;
+#define MOE_SEG_STEP(CTRL, COND)                                             \
+  {                                                                          \
+    const int uv = __builtin_amdgcn_update_dpp(0, val, CTRL, 0xF, 0xF, false); \
+    const int uf = __builtin_amdgcn_update_dpp(0, flag, CTRL, 0xF, 0xF, false); \
+    if (COND) {                                                              \
+      if (!flag) val += uv;                                                  \
+      flag |= uf;                                                            \
+    }                                                                        \
+  }
+  MOE_SEG_STEP(0x111, rl >= 1)             // row_shr:1
+  MOE_SEG_STEP(0x112, rl >= 2)             // row_shr:2
+  MOE_SEG_STEP(0x114, rl >= 4)             // row_shr:4
+  MOE_SEG_STEP(0x118, rl >= 8)             // row_shr:8
+  MOE_SEG_STEP(0x142, (lane & 31) >= 16)   // row_bcast:15
+  MOE_SEG_STEP(0x143, lane >= 32)          // row_bcast:31
+#undef MOE_SEG_STEP
 }
 
 __device__ __forceinline__ void report(int32_t* d_err, int bits) {

@@ -265,15 +265,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(
         }
         int val = v;
         int flag = head ? 1 : 0;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-          const int uv = __shfl_up(val, d, kWave);
-          const int uf = __shfl_up(flag, d, kWave);
-          if (lane >= d) {
-            if (!flag) val += uv;
-            flag |= uf;
-          }
-        }
+        wave_seg_scan(val, flag);
         if (!flag) val += carry[g];
         if (in) tile_cnt[static_cast<int64_t>(r) * stride + j] = val - v;
         if (last) s_S[s * G + r] = val;
