@@ -726,10 +726,11 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   // of its cap-th taker.
   __shared__ int s_lim[MOE_MAX_G];
   __shared__ int s_cc[kXChunks][MOE_MAX_G];  // tokens per (64-token chunk, rank)
-  // This block's tokens per rank, and the earlier blocks' (the prefix), each
-  // summed by LDS atomics into the half of the round's parity; the other
-  // half, last read in the previous round, is cleared for the next one.
-  __shared__ int s_cnt[2][MOE_MAX_G];
+  // This block's tokens per rank, kept by LDS atomics as tokens change
+  // their choices; the earlier blocks' (the prefix), summed by LDS atomics
+  // into the half of the round's parity, the other half, last read in the
+  // previous round, cleared for the next one.
+  __shared__ int s_cnt[MOE_MAX_G];
   __shared__ int s_pre[2][MOE_MAX_G];
   __shared__ int s_abort, s_changed;
   const int tid = static_cast<int>(threadIdx.x);
@@ -743,7 +744,7 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
 
   if (tid < MOE_MAX_G) {
     s_lim[tid] = INT_MAX;
-    s_cnt[0][tid] = 0;
+    s_cnt[tid] = 0;
     s_pre[0][tid] = 0;
   }
   if (tid == 0) s_abort = 0;
@@ -778,13 +779,9 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
   for (int round = 0; round < max_rounds; ++round) {
     uint64_t* xr = rec + static_cast<int64_t>(round % kXSlots) * nb * words;
     const int par = round & 1;
-    if (tid < MOE_MAX_G) {
-      s_cnt[par ^ 1][tid] = 0;
-      s_pre[par ^ 1][tid] = 0;
-    }
+    if (tid < MOE_MAX_G) s_pre[par ^ 1][tid] = 0;
     // 1. choices, and the tokens of each (chunk, rank) from wave ballots
     int changed = round == 0 ? 1 : 0;
-    int wc = 0;
     for (int u = 0; u < tpt; ++u) {
       const int t = t0 + u * kXThreads + tid;
       const int idx = u * kXThreads + tid;
@@ -823,26 +820,32 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
           s_choice[idx] = static_cast<uint8_t>(c);
         }
       }
-      // the wave's own row of chunk counts, recounted when one of its
-      // tokens changed (cleared, then one LDS atomic per token; a wave's LDS
-      // operations complete in order), else as the last round left it
+      // the wave's own row of chunk counts and the block's counts: a token
+      // that changed its choice moves one count (round 0: every row cleared
+      // first; a wave's LDS operations complete in order)
       int* row = s_cc[u * kXWaves + wave];
-      if (round == 0 || ballot(c != c0) != 0) {
+      if (round == 0) {
         if (lane < G) row[lane] = 0;
         __builtin_amdgcn_wave_barrier();
-        if (c < G) atomicAdd(&row[c], 1);
-        __builtin_amdgcn_wave_barrier();
       }
-      if (lane < G) wc += row[lane];
+      if (c != c0) {
+        if (c0 < G) {
+          atomicSub(&row[c0], 1);
+          atomicSub(&s_cnt[c0], 1);
+        }
+        if (c < G) {
+          atomicAdd(&row[c], 1);
+          atomicAdd(&s_cnt[c], 1);
+        }
+      }
     }
-    if (lane < G && wc != 0) atomicAdd(&s_cnt[par][lane], wc);
     const int any = __syncthreads_or(changed);
     // 2. (wave 0) publish this block's counts and whether any of its tokens
     // changed; 3. then every block's flag of the previous round (the flags
     // are 0 or 1: their sum is nonzero when any is set)
     if (wave == 0) {
       if (lane < G) {
-        const int c = s_cnt[par][lane];
+        const int c = s_cnt[lane];
         __hip_atomic_store(xr + static_cast<int64_t>(b) * words + lane,
                            xword(round, static_cast<uint32_t>(c)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -891,7 +894,7 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
     // scan of the chunk counts (lane = chunk), the lane from the chunk's
     // ballot of that rank
     {
-      const int cnt = lane < G ? s_cnt[par][lane] : 0;
+      const int cnt = lane < G ? s_cnt[lane] : 0;
       const bool open = lane < G && P + cnt < cap;
       const bool cross = lane < G && P < cap && P + cnt >= cap;
       if (wave == 0 && lane < G && !cross) s_lim[lane] = open ? INT_MAX : -1;
