@@ -780,7 +780,8 @@ __global__ __launch_bounds__(kXThreads) void shuffle_exchange_kernel(
     uint64_t* xr = rec + static_cast<int64_t>(round % kXSlots) * nb * words;
     const int par = round & 1;
     if (tid < MOE_MAX_G) s_pre[par ^ 1][tid] = 0;
-    // 1. choices, and the tokens of each (chunk, rank) from wave ballots
+    // 1. choices; a token that changes moves its counts (per chunk and rank,
+    // per rank)
     int changed = round == 0 ? 1 : 0;
     for (int u = 0; u < tpt; ++u) {
       const int t = t0 + u * kXThreads + tid;
