@@ -18,15 +18,12 @@ namespace moe {
 namespace {
 
 constexpr int kCombThreads = 256;
-constexpr int kCombUnroll = 2;
 
-// One wave per (token, chunk of kChunkGroups element groups): a row is split
-// into chunks of 2 groups per lane, and each chunk of each token is an
+// One wave per (token, chunk of kWave * U element groups): a row is split
+// into chunks of U groups per lane, and each chunk of each token is an
 // independent work item (four per 256-thread block).  The token's row list
 // and weights are read per wave into scalar registers.
-constexpr int kChunkGroups = kWave * kCombUnroll;
-
-template <bool ZBF16, bool YBF16, int EPL>
+template <bool ZBF16, bool YBF16, int EPL, int U>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     const u32x4* __restrict__ z, int64_t z_rows, int64_t groups, int chunks,
     const int32_t* __restrict__ rows, int k, const float* __restrict__ weight, int T,
@@ -71,10 +68,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   if (chunk == 0 && lane == 0) report(d_err, errbits);
 
   u32x4* yrow = y + static_cast<int64_t>(t) * yvec;
-  const int64_t g0 = static_cast<int64_t>(chunk) * kChunkGroups + lane;
-  float acc[kCombUnroll][EPL];
+  const int64_t g0 = static_cast<int64_t>(chunk) * (kWave * U) + lane;
+  float acc[U][EPL];
 #pragma unroll
-  for (int u = 0; u < kCombUnroll; ++u)
+  for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int i = 0; i < EPL; ++i) acc[u][i] = 0.f;
 #pragma unroll
@@ -82,19 +79,19 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     if (q >= k) break;
     if (rid[q] < 0) continue;
     const u32x4* zrow = z + static_cast<int64_t>(rid[q]) * zvec;
-    float f[kCombUnroll][EPL];
+    float f[U][EPL];
 #pragma unroll
-    for (int u = 0; u < kCombUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t g = g0 + u * kWave;
       if (g < groups) load_group<ZBF16, EPL>(zrow, g, f[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kCombUnroll; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < EPL; ++i) acc[u][i] = __builtin_fmaf(a[q], f[u][i], acc[u][i]);
   }
 #pragma unroll
-  for (int u = 0; u < kCombUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int64_t g = g0 + u * kWave;
     if (g < groups) store_group<YBF16, EPL>(yrow, g, acc[u]);
   }
@@ -102,29 +99,48 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 
 // Tokens with many rows (k >= 6 slots and at least 6 rows of z per output
 // row, so that most slots are in use -- not so for the expert side's reply
-// rows, whose k slots hold one or two rows): blocks reserve this much LDS
-// (unused) so that at most six are resident per CU (160 KB of LDS), which
-// keeps fewer rows streaming at once.  Measured on MI355X inside the
-// one-layer step: 8 KiB rows with k = 6 combine in 481 instead of 505 us,
-// 14 KiB rows with k = 8 in 623 instead of 667 us; with one or two rows per
-// output row the cap costs 8-14%.
-constexpr unsigned kCombLdsManyRows = 24 * 1024;
+// rows, whose k slots hold one or two rows): blocks reserve LDS they do not
+// use, to cap how many are resident per CU (160 KB of LDS).  Measured on
+// MI355X:
+//  - rows of at most 8 KiB: one group per lane (1 KiB of each row per wave)
+//    and at most eight blocks per CU; k = 6 with 8 KiB rows combines in 460
+//    us inside the one-layer step against 480 with two groups per lane and
+//    six blocks (466 against 507 alone);
+//  - wider rows: two groups per lane and at most six blocks per CU; k = 8
+//    with 14 KiB rows in 635 us inside the step against 651 with one group
+//    and eight blocks, and against 667 with no cap;
+//  - one or two rows per output row: two groups per lane and no cap (k = 2:
+//    240 us against 272 with one group; the cap costs 8-14% there).
+constexpr unsigned kCombLdsNarrow = 20 * 1024;  // eight blocks per CU
+constexpr unsigned kCombLdsWide = 24 * 1024;    // six blocks per CU
 
-template <bool ZBF16, bool YBF16, int EPL>
-int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k, const float* w,
-           int64_t T, void* y, const int32_t* n_valid, int32_t* d_err, hipStream_t s) {
+template <bool ZBF16, bool YBF16, int EPL, int U>
+int launch_u(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k, const float* w,
+             int64_t T, void* y, const int32_t* n_valid, int32_t* d_err, unsigned lds,
+             hipStream_t s) {
   const int64_t groups = H / EPL;
-  const int chunks = static_cast<int>((groups + kChunkGroups - 1) / kChunkGroups);
+  const int chunks = static_cast<int>((groups + kWave * U - 1) / (kWave * U));
   const int64_t items = T * chunks;
   constexpr int kItemsPerBlock = kCombThreads / kWave;
   const int64_t blocks = (items + kItemsPerBlock - 1) / kItemsPerBlock;
   if (!grid_ok(blocks, kCombThreads)) return MOE_ERR_SHAPE;
-  const unsigned lds = (k >= 6 && z_rows >= 6 * T) ? kCombLdsManyRows : 0;
-  combine_kernel<ZBF16, YBF16, EPL><<<static_cast<unsigned>(blocks), kCombThreads, lds, s>>>(
+  combine_kernel<ZBF16, YBF16, EPL, U><<<static_cast<unsigned>(blocks), kCombThreads, lds, s>>>(
       static_cast<const u32x4*>(z), z_rows, groups, chunks, rows, k, w, static_cast<int>(T),
       static_cast<u32x4*>(y), n_valid, d_err);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+
+template <bool ZBF16, bool YBF16, int EPL>
+int launch(const void* z, int64_t z_rows, int64_t H, const int32_t* rows, int k, const float* w,
+           int64_t T, void* y, const int32_t* n_valid, int32_t* d_err, hipStream_t s) {
+  const bool many = k >= 6 && z_rows >= 6 * T;
+  const int64_t z_row_bytes = H * (ZBF16 ? 2 : 4);
+  if (many && z_row_bytes <= 8192)
+    return launch_u<ZBF16, YBF16, EPL, 1>(z, z_rows, H, rows, k, w, T, y, n_valid, d_err,
+                                          kCombLdsNarrow, s);
+  return launch_u<ZBF16, YBF16, EPL, 2>(z, z_rows, H, rows, k, w, T, y, n_valid, d_err,
+                                        many ? kCombLdsWide : 0u, s);
 }
 
 }  // namespace
