@@ -21,9 +21,9 @@ GB/s with its share of peak (the metric's second half) and the dominant
 kernel's roofline fraction ride along, with the CPU oracle timed on a bounded
 sample.  Unless --workload picks a single workload, the same line carries
 ``workloads``: workloads 1-4 measured the same way (each with its second
-placement where it has one), and ``ceilings``: the read, write, copy and
-dense fan-out rates of plain streaming probe kernels on this GPU, against
-which each dominant kernel's read/write mix is also placed.
+placement where it has one), and ``ceilings``: the read, write, copy, dense
+fan-out and dense fan-in rates of plain streaming probe kernels on this GPU,
+against which each row-moving stage's read/write mix is also placed.
 """
 
 from __future__ import annotations
@@ -354,7 +354,7 @@ def measure(w, x, z, make_step, steps: int, warmup: int, ceil, graphs: bool = Tr
     import numpy as np
     import torch
 
-    from co_activation_amd.hbm_probe import mix_bound_us
+    from co_activation_amd.hbm_probe import mix_bound_us, same_mix_bound_us
     from co_activation_amd.pipeline import GraphPipeline, GraphStep, Pipeline, StageTimers
 
     step = make_step(x, z)
@@ -436,6 +436,10 @@ def measure(w, x, z, make_step, steps: int, warmup: int, ceil, graphs: bool = Tr
         roof["read_bytes"], roof["write_bytes"] = r, wr
         roof["mix_bound_us"] = bound
         roof["frac_of_mix_bound"] = bound / (1e3 * dom_ms)
+        sb = same_mix_bound_us(r, wr, ceil)
+        if sb is not None:
+            roof["same_mix_bound_us"] = sb
+            roof["frac_of_same_mix_bound"] = sb / (1e3 * dom_ms)
     rec = {
         "ms_per_step": ms_per_step,
         "dispatched_rows_per_s": N / (ms_per_step * 1e-3),
@@ -447,6 +451,10 @@ def measure(w, x, z, make_step, steps: int, warmup: int, ceil, graphs: bool = Tr
         "stage_us_min": {n: 1e3 * v for n, v in stage_min.items()},
         "stage_us_p90": {n: 1e3 * v for n, v in stage_p90.items()},
         "stage_gbps": {n: kernels[n] / (stage_ms[n] * 1e-3) / 1e9 for n in (mv, "combine")},
+        "stage_frac_of_same_mix_bound": (
+            None if ceil is None else
+            {n: (lambda b: None if b is None else b / (1e3 * stage_ms[n]))(
+                same_mix_bound_us(*_rw_bytes(n, T, N, k, rb, rb), ceil)) for n in (mv, "combine")}),
         "schedule": ("two batches in flight: each batch's " +
                      ("statistics and plan" if w.cfg != 5 else
                       "statistics, shuffle prediction and layer-2 plan") +

@@ -21,6 +21,28 @@
  *           device word (mode 0).
  * Returns 0, -1 (null pointer), -2 (bad mode, shape or size), -4
  * (alignment) or -6 (launch failed).  Enqueued on `stream` (a hipStream_t).
+ *
+ * moe_probe_fanout(shape, src, dst, bytes, region_stride, fan, cap, stream):
+ *   the dense ideal of a permute with `fan` destinations per row: every
+ *   16-byte vector i of src[0, bytes) is loaded once (nontemporal) and stored
+ *   (nontemporal) to vector i of each of `fan` regions of dst, region f being
+ *   dst[f*region_stride, f*region_stride + bytes).  region_stride >= bytes, a
+ *   multiple of 16 (a stride that is not a power of two keeps the regions'
+ *   same offsets off the same HBM channels, as the permute's irregular
+ *   segment offsets do); dst must hold (fan-1)*region_stride + bytes bytes
+ *   and must not overlap src.  shape as above; 1 <= fan <= 64.  cap = 0
+ *   leaves residency to the hardware; 2 <= cap <= 32 makes each block reserve
+ *   160 KiB / cap of LDS it does not use, so that a CU holds at most cap
+ *   blocks (how many write streams are open per CU is what sets the rate of
+ *   fan-out writes).  Same return codes; enqueued on `stream`.
+ *
+ * moe_probe_fanin(shape, src, region_stride, dst, bytes, fan, cap, stream):
+ *   the dense ideal of a combine over `fan` rows per output row: vector i of
+ *   dst[0, bytes) is stored (nontemporal) as the XOR of vector i of each of
+ *   `fan` regions of src, region f being src[f*region_stride,
+ *   f*region_stride + bytes), each loaded once (nontemporal).  src must hold
+ *   (fan-1)*region_stride + bytes bytes and must not overlap dst; the other
+ *   arguments and the return codes as for moe_probe_fanout.
  */
 #ifndef MOE_HBM_PROBE_H
 #define MOE_HBM_PROBE_H
@@ -33,6 +55,10 @@ extern "C" {
 
 int moe_probe_stream(int mode, int shape, const void* src, void* dst, int64_t bytes,
                      uint32_t* sink, void* stream);
+int moe_probe_fanout(int shape, const void* src, void* dst, int64_t bytes,
+                     int64_t region_stride, int fan, int cap, void* stream);
+int moe_probe_fanin(int shape, const void* src, int64_t region_stride, void* dst, int64_t bytes,
+                    int fan, int cap, void* stream);
 
 #ifdef __cplusplus
 }

@@ -267,6 +267,48 @@ def test_probe_library_rejects(built_lib):
     assert f(0, 0, FAKE, NULL, 1024, NULL, NULL) == -1       # read needs sink
     assert f(1, 0, NULL, NULL, 1024, NULL, NULL) == -1       # write needs dst
     assert f(2, 0, FAKE + 8, FAKE, 1024, NULL, NULL) == -4   # alignment
+    g = hbm_probe._load().moe_probe_fanout
+    D = FAKE + 4096
+    assert g(4, FAKE, D, 1024, 1024, 2, 0, NULL) == -2   # no such shape
+    assert g(0, FAKE, D, 1024, 1024, 0, 0, NULL) == -2   # fan-out below 1
+    assert g(0, FAKE, D, 1024, 1024, 65, 0, NULL) == -2  # fan-out above 64
+    assert g(0, FAKE, D, 1024, 1024, 2, 1, NULL) == -2   # cap of one block
+    assert g(0, FAKE, D, 1024, 1024, 2, 33, NULL) == -2  # cap above 32
+    assert g(0, FAKE, D, 1000, 1008, 2, 0, NULL) == -2   # not a multiple of 16 bytes
+    assert g(0, FAKE, D, 1024, 1008, 2, 0, NULL) == -2   # regions would overlap
+    assert g(0, FAKE, D, 1024, 1032, 2, 0, NULL) == -2   # stride not a multiple of 16
+    assert g(0, NULL, FAKE, 1024, 1024, 2, 0, NULL) == -1
+    assert g(0, FAKE, NULL, 1024, 1024, 2, 0, NULL) == -1
+    assert g(0, FAKE, FAKE + 4100, 1024, 1024, 2, 0, NULL) == -4   # alignment
+    h = hbm_probe._load().moe_probe_fanin  # (shape, src, stride, dst, bytes, fan, cap, stream)
+    assert h(4, D, 1024, FAKE, 1024, 2, 0, NULL) == -2   # no such shape
+    assert h(0, D, 1024, FAKE, 1024, 0, 0, NULL) == -2   # fan-in below 1
+    assert h(0, D, 1008, FAKE, 1024, 2, 0, NULL) == -2   # regions would overlap
+    assert h(0, D, 1024, FAKE, 1024, 2, 1, NULL) == -2   # cap of one block
+    assert h(0, NULL, 1024, FAKE, 1024, 2, 0, NULL) == -1
+    assert h(0, D, 1024, NULL, 1024, 2, 0, NULL) == -1
+    assert h(0, D + 4, 1024, FAKE, 1024, 2, 0, NULL) == -4  # alignment
+
+
+def test_fanout_bound_arithmetic():
+    """fanout_bound_us: at a whole fan-out it is the probe's own time for the
+    same bytes, between two it is linear in the time per byte read; the
+    fan-in bound mirrors it, and the same-mix bound picks by direction."""
+    from co_activation_amd.hbm_probe import fanin_bound_us, fanout_bound_us, same_mix_bound_us
+    g = {f"fanout{f}": 6000.0 - 100 * f for f in range(1, 9)}
+    g.update({f"fanin{f}": 7000.0 - 50 * f for f in range(1, 9)})
+    ceil = {"gbps": g}
+    W = 2e8
+    assert fanin_bound_us(5 * W, W, ceil) == pytest.approx(6 * W / (g["fanin5"] * 1e9) * 1e6)
+    assert same_mix_bound_us(5 * W, W, ceil) == fanin_bound_us(5 * W, W, ceil)
+    assert same_mix_bound_us(W, 5 * W, ceil) == fanout_bound_us(W, 5 * W, ceil)
+    R = 1e9
+    assert fanout_bound_us(R, 3 * R, ceil) == pytest.approx(4 * R / (g["fanout3"] * 1e9) * 1e6)
+    assert fanout_bound_us(R, 8 * R, ceil) == pytest.approx(9 * R / (g["fanout8"] * 1e9) * 1e6)
+    lo = fanout_bound_us(R, 3 * R, ceil)
+    hi = fanout_bound_us(R, 4 * R, ceil)
+    assert fanout_bound_us(R, 3.25 * R, ceil) == pytest.approx(lo + 0.25 * (hi - lo))
+    assert fanout_bound_us(R, 0.5 * R, ceil) is None and fanout_bound_us(R, 9 * R, ceil) is None
 
 
 def test_overlapping_outputs_rejected(built_lib):

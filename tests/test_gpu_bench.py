@@ -50,6 +50,13 @@ def test_bench_line_contract(built_lib):
         (rf["read_bytes"] / (g["read"] * 1e9) + rf["write_bytes"] / (g["write"] * 1e9)) * 1e6)
     assert rf["read_bytes"] + rf["write_bytes"] == rf["algorithmic_bytes"]
     assert 0.3 < rf["frac_of_mix_bound"] < 1.05
+    for f in range(1, 9):
+        assert 1000 < g[f"fanout{f}"] < 8000, (f, g[f"fanout{f}"])
+        assert 1000 < g[f"fanin{f}"] < 8000, (f, g[f"fanin{f}"])
+    # the fused dispatch writes about 2.8x what it reads: inside the fan-out probe's range
+    assert rf["same_mix_bound_us"] > 0 and 0.3 < rf["frac_of_same_mix_bound"] < 1.1
+    fr = d["stage_frac_of_same_mix_bound"]
+    assert set(fr) == {"shuffle_dispatch", "combine"} and all(0.3 < v < 1.1 for v in fr.values())
     # workloads 1-4 beside the headline, each measured the same way
     ws = d["workloads"]
     assert sorted(ws) == ["1", "2", "3", "4"]
