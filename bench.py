@@ -51,6 +51,9 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--no-probes", action="store_true", help="skip the HBM ceiling probes")
+    ap.add_argument("--copy-probe-only", action="store_true",
+                    help="of the ceiling probes run only read, write and copy (the copy calibrates "
+                         "the HBM byte counters; the mix probes add many launches under a profiler)")
     ap.add_argument("--no-expert-side", action="store_true")
     return ap.parse_args()
 
@@ -576,7 +579,7 @@ def main() -> int:
     ceil = None
     if not args.no_probes:
         from co_activation_amd.hbm_probe import ceilings
-        ceil = ceilings()
+        ceil = ceilings(mixes=not args.copy_probe_only)
 
     cfg = args.workload if args.workload is not None else 5
     w, x, z, make_step, desc = setup(cfg, args.placement, host_x=True)

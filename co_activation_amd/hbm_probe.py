@@ -74,8 +74,9 @@ def fanin_cap(shape: int, fan: int) -> int:
     return 0 if blocks >= 16 else max(2, blocks)
 
 
-def ceilings(bytes_=1 << 30, reps=5, device="cuda") -> dict:
-    """GB/s (decimal) per probe: the best shape's median over ``reps``.  The
+def ceilings(bytes_=1 << 30, reps=5, device="cuda", mixes: bool = True) -> dict:
+    """GB/s (decimal) per probe: the best shape's median over ``reps``
+    (read, write and copy; with ``mixes`` also fan-out and fan-in).  The
     fan-out probe's rate counts the bytes read and written (1 + F per byte of
     its 1 GiB source); it runs each shape uncapped and with the residency cap
     of ``fanout_cap``, with its regions exactly 1 GiB apart and ``STAGGER``
@@ -83,7 +84,8 @@ def ceilings(bytes_=1 << 30, reps=5, device="cuda") -> dict:
     probe the same way (F source regions of 1 GiB, caps of ``fanin_cap``)."""
     lib = _load()
     src = torch.ones(bytes_, dtype=torch.uint8, device=device)
-    dst = torch.empty(max(FANOUTS) * (bytes_ + STAGGER), dtype=torch.uint8, device=device)
+    dst = torch.empty(max(FANOUTS) * (bytes_ + STAGGER) if mixes else bytes_, dtype=torch.uint8,
+                      device=device)
     sink = torch.zeros(1, dtype=torch.int32, device=device)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -123,8 +125,9 @@ def ceilings(bytes_=1 << 30, reps=5, device="cuda") -> dict:
     best = {}
     probes = [("read", 0, bytes_, bytes_), ("write", 1, bytes_, bytes_),
               ("copy", 2, bytes_, 2 * bytes_)]
-    probes += [(f"fanout{f}", 100 + f, bytes_, (1 + f) * bytes_) for f in FANOUTS]
-    probes += [(f"fanin{f}", 1100 + f, bytes_, (1 + f) * bytes_) for f in FANOUTS]
+    if mixes:
+        probes += [(f"fanout{f}", 100 + f, bytes_, (1 + f) * bytes_) for f in FANOUTS]
+        probes += [(f"fanin{f}", 1100 + f, bytes_, (1 + f) * bytes_) for f in FANOUTS]
     for name, mode, nbytes, moved in probes:
         rates = {SHAPES[sh]: timed(mode, sh, nbytes, moved) for sh in SHAPES}
         if mode >= 100:
