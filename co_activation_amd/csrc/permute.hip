@@ -158,20 +158,14 @@ __global__ __launch_bounds__(kPartVec) void permute_parts_kernel(
   const int t = static_cast<int>(blockIdx.x / static_cast<unsigned>(parts));
   const int part = static_cast<int>(blockIdx.x - static_cast<unsigned>(t) * parts);
   if (t >= T || (n_valid != nullptr && t >= *n_valid)) return;
-  const int64_t c = static_cast<int64_t>(part) * kPartVec + threadIdx.x;
-  if (c >= vec_per_row) return;
-  // The row's load goes out before the destination loads, which it does not
-  // depend on, so the two latencies overlap and a block frees its slot
-  // sooner (measured on MI355X inside the benchmark step: 14 KiB rows to up
-  // to 8 ranks 646 -> 640 us, 8 KiB rows to up to 6 ranks 508 -> 501 us).
-  // The combine and the fused shuffle dispatch measured slower with their
-  // index and data loads overlapped the same way, so they keep their order.
-  const V v = load_row<false>(x + static_cast<int64_t>(t) * vec_per_row + c);
   int drow[MOE_MAX_K];
 #pragma unroll
   for (int q = 0; q < MOE_MAX_K; ++q)
     drow[q] = q < width ? __builtin_amdgcn_readfirstlane(dest[static_cast<int64_t>(t) * width + q])
                         : -1;
+  const int64_t c = static_cast<int64_t>(part) * kPartVec + threadIdx.x;
+  if (c >= vec_per_row) return;
+  const V v = load_row<false>(x + static_cast<int64_t>(t) * vec_per_row + c);
   int errbits = 0;
 #pragma unroll
   for (int q = 0; q < MOE_MAX_K; ++q) {
