@@ -490,7 +490,8 @@ def permute_scaled(x: torch.Tensor, dest: torch.Tensor, scale: torch.Tensor, out
     if out is None:
         out = torch.empty((out_rows, H), dtype=out_dtype, device=x.device)
     _want(out, "out", out_dtype)
-    if scale.numel() < out_rows or out.shape[0] < out_rows or out.shape[1] != H:
+    if (scale.dim() != 1 or scale.numel() < out_rows or out.dim() != 2 or out.shape[0] < out_rows
+            or out.shape[1] != H):
         raise ValueError("scale and out need out_rows rows")
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
@@ -519,6 +520,8 @@ def row_dot(a: torch.Tensor, b: torch.Tensor, rows: torch.Tensor, *,
     if out is None:
         out = torch.empty((T, width), dtype=torch.float32, device=a.device)
     _want(out, "out", torch.float32)
+    if out.numel() != T * width:
+        raise ValueError(f"out must hold T x width = {T} x {width} values")
     if n_valid is not None:
         _want(n_valid, "n_valid", torch.int32)
     err = _err_word(d_err, a)

@@ -1,7 +1,7 @@
 """The torch binding's argument checks (raised before anything is
 enqueued): tensors of one call on one device, the error word a single int32
 element on that device, the combine's row weights covering every row id the
-kernel may read."""
+kernel may read, outputs as large as the kernels write."""
 
 import pytest
 import torch
@@ -44,3 +44,26 @@ def test_tensors_on_another_device_rejected():
     rows = torch.zeros(4, 2, dtype=torch.int32, device="cuda:1")
     with pytest.raises(ValueError, match="must be on"):
         ops.combine(z, rows)
+
+
+def test_row_dot_out_must_match_rows():
+    a = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(8, 128, dtype=torch.bfloat16, device="cuda")
+    rows = torch.zeros(4, 2, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="out"):
+        ops.row_dot(a, b, rows, out=torch.zeros(4, 1, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match="out"):
+        ops.row_dot(a, b, rows, out=torch.zeros(6, dtype=torch.float32, device="cuda"))
+    ops.row_dot(a, b, rows, out=torch.zeros(4, 2, dtype=torch.float32, device="cuda"))
+    ops.row_dot(a, b, rows, out=torch.zeros(8, dtype=torch.float32, device="cuda"))  # same memory
+
+
+def test_permute_scaled_out_and_scale_shapes():
+    x = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")
+    dest = torch.zeros(4, 2, dtype=torch.int32, device="cuda")
+    scale = torch.ones(8, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="out_rows"):
+        ops.permute_scaled(x, dest, scale, 8,
+                           out=torch.zeros(8 * 128, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="out_rows"):
+        ops.permute_scaled(x, dest, torch.ones(2, 4, dtype=torch.float32, device="cuda"), 8)
