@@ -6,6 +6,12 @@ be on the tensors' device) to the library, and returns the output tensors.
 All compute happens in the HIP kernels; outputs may be preallocated through
 ``out=`` to keep allocations out of a timed loop.  Device-side data errors are OR-ed into ``d_err`` (an int32
 tensor of one element); ``raise_on_errors`` reads it back.
+
+``coact_stats``, ``dispatch_plan``, ``permute`` and ``combine`` also take
+``bind=True``: they check their arguments as usual but, instead of calling
+the library, return ``(result, Bound)``, the call with its arguments already
+converted, which a loop that the host paces replays on a stream with no
+further checks (the buffers are read and written in place at each replay).
 """
 
 from __future__ import annotations
@@ -36,6 +42,45 @@ def _stream(ref: torch.Tensor) -> int:
 
 def _p(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
+
+
+try:  # the raw hipStream_t of a device's current stream, without a Stream object
+    _raw_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:  # pragma: no cover
+    def _raw_stream(idx):
+        return torch.cuda.current_stream(idx).cuda_stream
+
+
+class Bound:
+    """One library call whose arguments an ops function has checked, with
+    the arguments converted once.  ``bound(stream)`` enqueues it on
+    ``stream`` (a hipStream_t as an int); ``bound()`` on the current stream
+    of the device it was bound on.  The buffers are the ones given at bind
+    time: keep them alive and do not replace them."""
+
+    __slots__ = ("name", "fn", "args", "device")
+
+    def __init__(self, name: str, args: tuple, device: torch.device):
+        self.name = name
+        self.fn = getattr(_lib.lib(), name)
+        self.args = tuple(t(a) for t, a in zip(self.fn.argtypes, args))
+        self.device = device.index
+
+    def __call__(self, stream: Optional[int] = None) -> None:
+        if stream is None:
+            stream = _raw_stream(self.device)
+        st = self.fn(*self.args, stream)
+        if st != 0:
+            check(self.name, st)
+
+
+def _run(name: str, args: tuple, ref: torch.Tensor, bind: bool):
+    """Calls entry point ``name`` with ``args`` and the current stream of
+    ``ref``'s device, or with ``bind`` returns the call as a ``Bound``."""
+    if bind:
+        return Bound(name, args, ref.device)
+    check(name, getattr(_lib.lib(), name)(*args, _stream(ref)))
+    return None
 
 
 def _want(t: torch.Tensor, name: str, dtype=None, shape=None) -> torch.Tensor:
@@ -104,7 +149,7 @@ def stats_workspace_bytes(T: int, E: int, pairs: bool = True, E_next: int = 0) -
 def coact_stats(topk: torch.Tensor, E: int, topk_next: Optional[torch.Tensor] = None,
                 E_next: Optional[int] = None, *, pairs: bool = True, ochiai: bool = True,
                 out: Optional[dict] = None, ws: Optional[torch.Tensor] = None,
-                d_err: Optional[torch.Tensor] = None) -> dict:
+                d_err: Optional[torch.Tensor] = None, bind: bool = False):
     """moe_coact_stats: expert_count [E], pair_count [E,E], ochiai [E,E],
     transition [E,E_next] (when topk_next is given).  ws: the workspace
     (uint8, at least stats_workspace_bytes); allocated here when not given."""
@@ -130,12 +175,11 @@ def coact_stats(topk: torch.Tensor, E: int, topk_next: Optional[torch.Tensor] = 
     err = _err_word(d_err, topk)
     _same_device(topk, topk_next, ws, res.get("pair_count"), res.get("ochiai"),
                  res.get("transition"), res["expert_count"])
-    st = _lib.lib().moe_coact_stats(
-        _p(topk), T, k, E, _p(topk_next), k2, E_next or 0, _p(res["expert_count"]),
-        _p(res.get("pair_count")), _p(res.get("ochiai")), _p(res.get("transition")), _p(err),
-        _p(ws), ws.numel(), _stream(topk))
-    check("moe_coact_stats", st)
-    return res
+    b = _run("moe_coact_stats",
+             (_p(topk), T, k, E, _p(topk_next), k2, E_next or 0, _p(res["expert_count"]),
+              _p(res.get("pair_count")), _p(res.get("ochiai")), _p(res.get("transition")),
+              _p(err), _p(ws), ws.numel()), topk, bind)
+    return (res, b) if bind else res
 
 
 # ----------------------------------------------------------------- plan
@@ -164,7 +208,7 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
                   ws: Optional[torch.Tensor] = None,
                   d_err: Optional[torch.Tensor] = None, perm: Optional[torch.Tensor] = None,
                   topk_out: Optional[torch.Tensor] = None,
-                  gates_out: Optional[torch.Tensor] = None) -> Plan:
+                  gates_out: Optional[torch.Tensor] = None, bind: bool = False):
     """moe_dispatch_plan.  row_capacity defaults to T * min(k, G).
 
     With ``perm`` (moe_dispatch_plan_gathered): the plan of the batch in the
@@ -196,12 +240,12 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
     if perm is None:
         _same_device(topk, gates, expert_rank, src_offsets, sc, so, rt, rw, tr, sr, cn, ws, perm,
                      topk_out, gates_out)
-        st = _lib.lib().moe_dispatch_plan(
-            _p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node, _p(src_offsets),
-            cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn), _p(err), _p(ws),
-            ws.numel(), _stream(topk))
-        check("moe_dispatch_plan", st)
-        return Plan(sc, so, rt, rw, tr, sr, cn)
+        b = _run("moe_dispatch_plan",
+                 (_p(topk), _p(gates), T, k, E, _p(expert_rank), G, ranks_per_node,
+                  _p(src_offsets), cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn),
+                  _p(err), _p(ws), ws.numel()), topk, bind)
+        plan = Plan(sc, so, rt, rw, tr, sr, cn)
+        return (plan, b) if bind else plan
     _want(perm, "perm", torch.int32, (T,))
     if topk_out is None or (gates is not None and gates_out is None):
         raise ValueError("a gathered plan writes the routing in the new order: give topk_out "
@@ -211,12 +255,12 @@ def dispatch_plan(topk: torch.Tensor, gates: Optional[torch.Tensor], expert_rank
         _want(gates_out, "gates_out", torch.float32, (T, k))
     _same_device(topk, gates, expert_rank, src_offsets, sc, so, rt, rw, tr, sr, cn, ws, perm,
                  topk_out, gates_out)
-    st = _lib.lib().moe_dispatch_plan_gathered(
-        _p(topk), _p(gates), _p(perm), T, k, E, _p(expert_rank), G, ranks_per_node,
-        _p(src_offsets), cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn),
-        _p(topk_out), _p(gates_out), _p(err), _p(ws), ws.numel(), _stream(topk))
-    check("moe_dispatch_plan_gathered", st)
-    return Plan(sc, so, rt, rw, tr, sr, cn)
+    b = _run("moe_dispatch_plan_gathered",
+             (_p(topk), _p(gates), _p(perm), T, k, E, _p(expert_rank), G, ranks_per_node,
+              _p(src_offsets), cap, _p(sc), _p(so), _p(rt), _p(rw), _p(tr), _p(sr), _p(cn),
+              _p(topk_out), _p(gates_out), _p(err), _p(ws), ws.numel()), topk, bind)
+    plan = Plan(sc, so, rt, rw, tr, sr, cn)
+    return (plan, b) if bind else plan
 
 
 def dispatch_plan_noalloc(topk: torch.Tensor, gates: Optional[torch.Tensor],
@@ -263,7 +307,7 @@ def dispatch_plan_noalloc(topk: torch.Tensor, gates: Optional[torch.Tensor],
 
 def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
             out: Optional[torch.Tensor] = None, n_valid: Optional[torch.Tensor] = None,
-            d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+            d_err: Optional[torch.Tensor] = None, bind: bool = False):
     """moe_permute: out[dest[t, q]] = x[t] (bit copy).  dest is [T, width] or
     [T] int32; out has out_rows rows shaped like x's rows; n_valid (an int32
     device element, e.g. a plan's row count) limits the tokens moved."""
@@ -284,10 +328,9 @@ def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
         _want(n_valid, "n_valid", torch.int32)
     err = _err_word(d_err, x)
     _same_device(x, dest, out, n_valid)
-    st = _lib.lib().moe_permute(_p(x), T, row_bytes, _p(dest), width, _p(out), out_rows,
-                                _p(n_valid), _p(err), _stream(x))
-    check("moe_permute", st)
-    return out
+    b = _run("moe_permute", (_p(x), T, row_bytes, _p(dest), width, _p(out), out_rows, _p(n_valid),
+                             _p(err)), x, bind)
+    return (out, b) if bind else out
 
 
 def shuffle_dispatch(x: torch.Tensor, perm: torch.Tensor, token_rows: torch.Tensor,
@@ -354,7 +397,7 @@ def gather(x: torch.Tensor, src: torch.Tensor, *, out: Optional[torch.Tensor] = 
 def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tensor] = None, *,
             out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
             n_valid: Optional[torch.Tensor] = None,
-            d_err: Optional[torch.Tensor] = None) -> torch.Tensor:
+            d_err: Optional[torch.Tensor] = None, bind: bool = False):
     """moe_combine: y[t] = sum_q a(rows[t,q]) z[rows[t,q]], a = row_weight or 1."""
     _want(z, "z")
     if z.dtype not in _DT:
@@ -375,10 +418,9 @@ def combine(z: torch.Tensor, rows: torch.Tensor, row_weight: Optional[torch.Tens
         _want(n_valid, "n_valid", torch.int32)
     err = _err_word(d_err, z)
     _same_device(z, rows, row_weight, out, n_valid)
-    st = _lib.lib().moe_combine(_p(z), _DT[z.dtype], z.shape[0], H, _p(rows), k, _p(row_weight),
-                                T, _p(out), _DT[out_dtype], _p(n_valid), _p(err), _stream(z))
-    check("moe_combine", st)
-    return out
+    b = _run("moe_combine", (_p(z), _DT[z.dtype], z.shape[0], H, _p(rows), k, _p(row_weight), T,
+                             _p(out), _DT[out_dtype], _p(n_valid), _p(err)), z, bind)
+    return (out, b) if bind else out
 
 
 # ----------------------------------------------------------------- shuffle

@@ -254,8 +254,20 @@ class LayerStep:
         self.plan_ws = torch.empty(ops.plan_workspace_bytes(self.T, G), dtype=torch.uint8, device=dev)
         self.send = torch.empty((self.cap,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
         self.y = torch.empty((self.T, x.shape[1]), dtype=self.out_dtype, device=dev)
-        self.plan = None
         self._fork = _Fork(dev)
+        # The step's four calls, checked once here and bound to its buffers:
+        # each stage then replays its call with no per-call checks, which is
+        # what paces small layers, whose kernels take a few microseconds.
+        _, self._stats_call = ops.coact_stats(self.topk, E, out=self.stats_out, ws=self.stats_ws,
+                                              d_err=self.d_err, bind=True)
+        self.plan, self._plan_call = ops.dispatch_plan(
+            self.topk, self.gates, self.expert_rank, G, self.Rn, self.src_offsets,
+            out=self.plan_out, ws=self.plan_ws, d_err=self.d_err, bind=True)
+        _, self._permute_call = ops.permute(self.x, self.plan.token_rows, self.cap, out=self.send,
+                                            d_err=self.d_err, bind=True)
+        _, self._combine_call = ops.combine(self.z, self.plan.token_rows, self.plan.row_weight,
+                                            out_dtype=self.out_dtype, out=self.y,
+                                            d_err=self.d_err, bind=True)
 
     @staticmethod
     def _plan_buffers(T, k, G, cap, dev):
@@ -283,14 +295,11 @@ class LayerStep:
 
     def _stats(self, timers):
         with _timed(timers, "stats"):
-            ops.coact_stats(self.topk, self.E, out=self.stats_out, ws=self.stats_ws,
-                            d_err=self.d_err)
+            self._stats_call()
 
     def _plan(self, timers):
         with _timed(timers, "plan"):
-            self.plan = ops.dispatch_plan(self.topk, self.gates, self.expert_rank, self.G, self.Rn,
-                                          self.src_offsets, out=self.plan_out, ws=self.plan_ws,
-                                          d_err=self.d_err)
+            self._plan_call()
 
     def plan_phase(self, timers: Optional[StageTimers] = None):
         """Everything that reads only the routing: statistics and plan."""
@@ -301,14 +310,13 @@ class LayerStep:
     def dispatch_phase(self, timers: Optional[StageTimers] = None):
         """The send rows, which need the plan: the permute."""
         with _timed(timers, "permute"):
-            ops.permute(self.x, self.plan.token_rows, self.cap, out=self.send, d_err=self.d_err)
+            self._permute_call()
         return self
 
     def combine_phase(self, timers: Optional[StageTimers] = None):
         """The returned rows back in token order: the combine."""
         with _timed(timers, "combine"):
-            ops.combine(self.z, self.plan.token_rows, self.plan.row_weight,
-                        out_dtype=self.out_dtype, out=self.y, d_err=self.d_err)
+            self._combine_call()
         return self
 
     def move_phase(self, timers: Optional[StageTimers] = None):

@@ -334,3 +334,20 @@ def test_overlapping_outputs_rejected(built_lib):
                                 NULL) == -2
     assert L.moe_row_dot(FAKE, 1, 8, 128, big, 1, 8, big + 4096, 1, FAKE + 16, NULL, NULL,
                          NULL) == -2
+
+
+def test_bound_call_converts_once_and_checks_status(built_lib):
+    """ops.Bound: the arguments are converted to the entry point's ctypes
+    once; a replay that the library refuses on the host raises MoeError (here
+    width 0, refused before anything is enqueued)."""
+    import ctypes
+
+    import torch
+
+    from co_activation_amd import _lib, ops
+    args = (FAKE, 8, 256, FAKE + 8192, 0, FAKE + 16384, 8, NULL, NULL)
+    b = ops.Bound("moe_permute", args, torch.device("cuda", 0))
+    assert len(b.args) == len(args) and isinstance(b.args[0], ctypes.c_void_p)
+    assert isinstance(b.args[1], ctypes.c_int64) and b.args[4].value == 0
+    with pytest.raises(_lib.MoeError, match="MOE_ERR_SHAPE"):
+        b(0)
