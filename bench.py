@@ -90,7 +90,7 @@ def counter_traffic(workload: int, stage: str):
     return None if k is None else k["read_bytes"] + k["write_bytes"]
 
 
-def expert_side(step, w, steps: int, device_normal) -> dict:
+def expert_side(step, w, steps: int, device_normal, ceil=None) -> dict:
     """Destination side after the step's dispatch (outside the timed step):
     expert layout, expansion of the received rows into expert rows, reply
     rows from stand-in expert outputs, the reply combine, and the backward
@@ -123,18 +123,28 @@ def expert_side(step, w, steps: int, device_normal) -> dict:
     N = int(step.plan.counters[0].item())
     k = side.k
     TK, rb, T = side.T * k, w.row_bytes, side.T
-    # each received row read once, each expert row written once, one index per expert row
-    bytes_ = {"expand": N * rb + TK * rb + 4 * TK,
-              "partial_combine": TK * rb + 4 * TK + N * rb + 4 * N * k,
-              "reply_combine": N * rb + T * rb + 4 * T * k,
-              "grad_replies": T * rb + N * rb + 4 * T * k,
-              "grad_expert_out": N * rb + TK * rb + 4 * N * k + 4 * TK,
-              "grad_gates": T * rb + TK * rb + 8 * TK,
-              "grad_send": TK * rb + N * rb + 4 * N * k,
-              "grad_tokens": N * rb + T * rb + 4 * T * k}
+    # (read, written) bytes: each received row read once, each expert row
+    # written once, one index per expert row
+    rw = {"expand": (N * rb + 4 * TK, TK * rb),
+          "partial_combine": (TK * rb + 4 * TK + 4 * N * k, N * rb),
+          "reply_combine": (N * rb + 4 * T * k, T * rb),
+          "grad_replies": (T * rb + 4 * T * k, N * rb),
+          "grad_expert_out": (N * rb + 4 * N * k + 4 * TK, TK * rb),
+          "grad_gates": (T * rb + TK * rb + 4 * TK, 4 * TK),
+          "grad_send": (TK * rb + 4 * N * k, N * rb),
+          "grad_tokens": (N * rb + 4 * T * k, T * rb)}
+    bytes_ = {n: r + w_ for n, (r, w_) in rw.items()}
     out = {"rows_expert": TK, "stage_us": {n: round(1e3 * v, 2) for n, v in ms.items()},
            "gbps": {n: round(b / (ms[n] * 1e-3) / 1e9, 1) for n, b in bytes_.items()},
            "algorithmic_bytes": bytes_}
+    if ceil is not None:
+        from co_activation_amd.hbm_probe import same_mix_bound_us
+
+        # share of the fan-out / fan-in probe at each stage's own mix (None
+        # where the mix is outside F = 1..8: the gate gradients only read)
+        out["frac_of_same_mix_bound"] = {
+            n: (lambda b: None if b is None else round(b / (1e3 * ms[n]), 4))(
+                same_mix_bound_us(r, w_, ceil)) for n, (r, w_) in rw.items()}
     return out
 
 
@@ -532,7 +542,7 @@ def other_workload(cfg: int, args, ceil) -> dict:
                       "dispatched_rows": rec["counters"]["rows"]}}
     out.update(rec)
     if cfg == 4 and not args.no_expert_side:
-        out["expert_side"] = expert_side(step, w, args.steps, device_normal)
+        out["expert_side"] = expert_side(step, w, args.steps, device_normal, ceil)
         out["placement"] = placement_planner(w)
     if cfg in (3, 4) and not args.no_expert_side:
         out["shuffle_at_scale"] = shuffle_at_scale(w, args.steps)
@@ -608,7 +618,7 @@ def main() -> int:
     if ceil is not None:
         line["ceilings"] = ceil
     if not args.no_expert_side:
-        line["expert_side"] = expert_side(step, w, args.steps, device_normal)
+        line["expert_side"] = expert_side(step, w, args.steps, device_normal, ceil)
         line["placement"] = placement_planner(w)
         if w.cfg == 5:
             line["shuffle_modes"] = shuffle_modes(w, x, z, args.steps)
