@@ -7,8 +7,8 @@ All compute happens in the HIP kernels; outputs may be preallocated through
 ``out=`` to keep allocations out of a timed loop.  Device-side data errors are OR-ed into ``d_err`` (an int32
 tensor of one element); ``raise_on_errors`` reads it back.
 
-``coact_stats``, ``dispatch_plan``, ``permute`` and ``combine`` also take
-``bind=True``: they check their arguments as usual but, instead of calling
+``coact_stats``, ``dispatch_plan``, ``permute``, ``combine``,
+``shuffle_predict`` and ``shuffle_dispatch`` also take ``bind=True``: they check their arguments as usual but, instead of calling
 the library, return ``(result, Bound)``, the call with its arguments already
 converted, which a loop that the host paces replays on a stream with no
 further checks (the buffers are read and written in place at each replay).
@@ -336,7 +336,7 @@ def permute(x: torch.Tensor, dest: torch.Tensor, out_rows: int, *,
 def shuffle_dispatch(x: torch.Tensor, perm: torch.Tensor, token_rows: torch.Tensor,
                      send_rows: int, *, x_out: Optional[torch.Tensor] = None,
                      send: Optional[torch.Tensor] = None,
-                     d_err: Optional[torch.Tensor] = None) -> tuple:
+                     d_err: Optional[torch.Tensor] = None, bind: bool = False) -> tuple:
     """moe_shuffle_dispatch: x_out[p] = x[perm[p]] and
     send[token_rows[p, q]] = x[perm[p]] (bit copies); token_rows [T, k] is
     indexed by shuffled position.  Returns (x_out, send)."""
@@ -359,10 +359,9 @@ def shuffle_dispatch(x: torch.Tensor, perm: torch.Tensor, token_rows: torch.Tens
         raise ValueError("x_out must match x; send needs send_rows rows shaped like x's rows")
     err = _err_word(d_err, x)
     _same_device(x, perm, token_rows, x_out, send)
-    st = _lib.lib().moe_shuffle_dispatch(_p(x), T, row_bytes, _p(perm), _p(token_rows), k,
-                                         _p(x_out), _p(send), send_rows, _p(err), _stream(x))
-    check("moe_shuffle_dispatch", st)
-    return x_out, send
+    b = _run("moe_shuffle_dispatch", (_p(x), T, row_bytes, _p(perm), _p(token_rows), k, _p(x_out),
+                                      _p(send), send_rows, _p(err)), x, bind)
+    return ((x_out, send), b) if bind else (x_out, send)
 
 
 def gather(x: torch.Tensor, src: torch.Tensor, *, out: Optional[torch.Tensor] = None,
@@ -435,7 +434,7 @@ def shuffle_workspace_bytes(T: int, E: int, G: int, balanced: bool = False) -> i
 def shuffle_predict(topk: torch.Tensor, transition: torch.Tensor, expert_rank_next: torch.Tensor,
                     G: int, *, balanced: bool = False, with_perm: bool = True,
                     out: Optional[dict] = None, ws: Optional[torch.Tensor] = None,
-                    d_err: Optional[torch.Tensor] = None) -> dict:
+                    d_err: Optional[torch.Tensor] = None, bind: bool = False):
     """moe_shuffle_predict (or moe_shuffle_balanced with balanced=True):
     pred_rank [T], dest_pos [T], perm [T], shard_offsets [G+1]."""
     _want(topk, "topk", torch.int32)
@@ -454,15 +453,14 @@ def shuffle_predict(topk: torch.Tensor, transition: torch.Tensor, expert_rank_ne
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _want(ws, "ws", torch.uint8)
-    fn = _lib.lib().moe_shuffle_balanced if balanced else _lib.lib().moe_shuffle_predict
     err = _err_word(d_err, topk)
     _same_device(topk, transition, expert_rank_next, ws, res["pred_rank"], res["dest_pos"],
                  res["perm"], res["shard_offsets"])
-    st = fn(_p(topk), T, k, E, _p(transition), E2, _p(expert_rank_next), G, _p(res["pred_rank"]),
-            _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(err), _p(ws),
-            ws.numel(), _stream(topk))
-    check("moe_shuffle_balanced" if balanced else "moe_shuffle_predict", st)
-    return res
+    b = _run("moe_shuffle_balanced" if balanced else "moe_shuffle_predict",
+             (_p(topk), T, k, E, _p(transition), E2, _p(expert_rank_next), G, _p(res["pred_rank"]),
+              _p(res["dest_pos"]), _p(res["perm"]), _p(res["shard_offsets"]), _p(err), _p(ws),
+              ws.numel()), topk, bind)
+    return (res, b) if bind else res
 
 
 # ----------------------------------------------------------------- expert side

@@ -386,10 +386,25 @@ class TwoLayerStep:
         self.plan_ws = torch.empty(ops.plan_workspace_bytes(T, G), dtype=torch.uint8, device=dev)
         self.send = torch.empty((self.cap,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
         self.y = torch.empty((T, x.shape[1]), dtype=x.dtype, device=dev)
-        self.plan = None
-        self.shuffle = None
         self._fork = _Fork(dev)
         self._counts_tmp = torch.empty(E1, dtype=torch.int32, device=dev)
+        # The calls of the statistics, the prediction, the plan, the fused
+        # dispatch and the combine, checked once and bound (see LayerStep).
+        _, self._stats_call = ops.coact_stats(self.topk1, E1, self.topk2, E2, out=self.stats_out,
+                                              ws=self.stats_ws, d_err=self.d_err, bind=True)
+        self.shuffle, self._shuffle_call = ops.shuffle_predict(
+            self.topk1, self.stats_out["transition"], self.expert_rank2, G, balanced=balanced,
+            out=self.shuffle_out, ws=self.shuffle_ws, d_err=self.d_err, bind=True)
+        perm = self.shuffle["perm"]
+        self.plan, self._plan_call = ops.dispatch_plan(
+            self.topk2, self.gates2, self.expert_rank2, G, self.Rn, self.shuffle["shard_offsets"],
+            out=self.plan_out, ws=self.plan_ws, d_err=self.d_err, perm=perm,
+            topk_out=self.topk2_s, gates_out=self.gates2_s, bind=True)
+        _, self._dispatch_call = ops.shuffle_dispatch(
+            self.x, perm, self.plan.token_rows, self.cap, x_out=self.x_s, send=self.send,
+            d_err=self.d_err, bind=True)
+        _, self._combine_call = ops.combine(self.z, self.plan.token_rows, self.plan.row_weight,
+                                            out=self.y, d_err=self.d_err, bind=True)
 
     STAGES_FUSED = ("stats", "shuffle_predict", "plan", "shuffle_dispatch", "combine")
     STAGES_SPLIT = ("stats", "shuffle_predict", "shuffle_permute", "plan", "permute", "combine")
@@ -422,17 +437,13 @@ class TwoLayerStep:
                                      "transition": st["transition"]}, ws=self.stats_ws,
                                 d_err=self.d_err)
             else:
-                ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=st,
-                                ws=self.stats_ws, d_err=self.d_err)
+                self._stats_call()
         with _timed(timers, "shuffle_predict"):
-            self.shuffle = ops.shuffle_predict(self.topk1, st["transition"], self.expert_rank2,
-                                               self.G, balanced=self.balanced,
-                                               out=self.shuffle_out, ws=self.shuffle_ws,
-                                               d_err=self.d_err)
+            self._shuffle_call()
         perm = self.shuffle["perm"]
         with fork.fork():
             with _timed(timers, "plan"):
-                self._plan(perm)
+                self._plan_call()
             if overlap:
                 ops.coact_stats(self.topk1, self.E1, out={k: st[k] for k in
                                                           ("expert_count", "pair_count", "ochiai")},
@@ -443,32 +454,21 @@ class TwoLayerStep:
         with _timed(timers, "permute"):
             ops.permute(self.x_s, self.plan.token_rows, self.cap, out=self.send, d_err=self.d_err)
         with _timed(timers, "combine"):
-            ops.combine(self.z, self.plan.token_rows, self.plan.row_weight, out=self.y,
-                        d_err=self.d_err)
+            self._combine_call()
         return self
 
     def plan_phase(self, timers: Optional[StageTimers] = None):
         """Everything that reads only the routing: statistics, prediction,
-        and the layer-2 plan over the shuffled order."""
+        and the layer-2 plan over the shuffled order (reading the routing
+        through the shuffle's permutation and leaving it in that order in
+        topk2_s / gates2_s)."""
         with _timed(timers, "stats"):
-            ops.coact_stats(self.topk1, self.E1, self.topk2, self.E2, out=self.stats_out,
-                            ws=self.stats_ws, d_err=self.d_err)
+            self._stats_call()
         with _timed(timers, "shuffle_predict"):
-            self.shuffle = ops.shuffle_predict(self.topk1, self.stats_out["transition"],
-                                               self.expert_rank2, self.G, balanced=self.balanced,
-                                               out=self.shuffle_out, ws=self.shuffle_ws,
-                                               d_err=self.d_err)
+            self._shuffle_call()
         with _timed(timers, "plan"):
-            self._plan(self.shuffle["perm"])
+            self._plan_call()
         return self
-
-    def _plan(self, perm):
-        """The layer-2 plan over the shuffled order, reading the routing
-        through perm and leaving it in that order in topk2_s / gates2_s."""
-        self.plan = ops.dispatch_plan(self.topk2, self.gates2, self.expert_rank2, self.G, self.Rn,
-                                      self.shuffle["shard_offsets"], out=self.plan_out,
-                                      ws=self.plan_ws, d_err=self.d_err, perm=perm,
-                                      topk_out=self.topk2_s, gates_out=self.gates2_s)
 
     def dispatch_phase(self, timers: Optional[StageTimers] = None):
         """The token rows moved to their shuffled places and dispatched into
@@ -477,8 +477,7 @@ class TwoLayerStep:
         perm = self.shuffle["perm"]
         if self.fused:
             with _timed(timers, "shuffle_dispatch"):
-                ops.shuffle_dispatch(self.x, perm, self.plan.token_rows, self.cap,
-                                     x_out=self.x_s, send=self.send, d_err=self.d_err)
+                self._dispatch_call()
         else:
             with _timed(timers, "shuffle_permute"):
                 ops.gather(self.x, perm, out=self.x_s, d_err=self.d_err)
@@ -490,8 +489,7 @@ class TwoLayerStep:
     def combine_phase(self, timers: Optional[StageTimers] = None):
         """The returned rows back in (shuffled) token order: the combine."""
         with _timed(timers, "combine"):
-            ops.combine(self.z, self.plan.token_rows, self.plan.row_weight, out=self.y,
-                        d_err=self.d_err)
+            self._combine_call()
         return self
 
     def move_phase(self, timers: Optional[StageTimers] = None):
