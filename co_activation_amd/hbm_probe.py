@@ -2,8 +2,9 @@
 (include/moe_hbm_probe.h) timed with HIP events.
 
 ``ceilings()`` returns the best sustained rate of each probe over its block
-shapes -- read only, write only, copy, and the fan-out probe (each vector read
-once and written to F dense regions) for F = 1..8 -- and ``mix_bound_us``
+shapes -- read only, write only, copy, and for F = 1..8 the fan-out probe
+(each vector read once and written to F dense regions) and the fan-in probe
+(F regions read and folded into one) -- and ``mix_bound_us``
 turns the read-only and write-only rates into the shortest time HBM allows a
 kernel that reads R and writes W bytes, R / read + W / write (reads and
 writes share the HBM interface, so they do not overlap to a shorter time).
