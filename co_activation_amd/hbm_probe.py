@@ -18,7 +18,6 @@ into one written region) for a combine that reads R / W rows per output row.
 from __future__ import annotations
 
 import ctypes
-import statistics
 from pathlib import Path
 
 import torch
@@ -76,8 +75,9 @@ def fanin_cap(shape: int, fan: int) -> int:
 
 
 def ceilings(bytes_=1 << 30, reps=5, device="cuda", mixes: bool = True) -> dict:
-    """GB/s (decimal) per probe: the best shape's median over ``reps``
-    (read, write and copy; with ``mixes`` also fan-out and fan-in).  The
+    """GB/s (decimal) per probe: the best shape's mean over ``reps`` launches
+    back to back (read, write and copy; with ``mixes`` also fan-out and
+    fan-in).  The
     fan-out probe's rate counts the bytes read and written (1 + F per byte of
     its 1 GiB source); it runs each shape uncapped and with the residency cap
     of ``fanout_cap``, with its regions exactly 1 GiB apart and ``STAGGER``
@@ -112,15 +112,17 @@ def ceilings(bytes_=1 << 30, reps=5, device="cuda", mixes: bool = True) -> dict:
             raise RuntimeError(f"HBM probe ({mode}, {shape}) returned {rc}")
 
     def timed(mode, shape, nbytes, moved):
+        # one untimed launch, then ``reps`` launches back to back between one
+        # event pair: an event pair around each launch alone would add the
+        # launch latency to every sample (3-13% of these kernels' durations)
         run(mode, shape, nbytes)
-        ts = []
+        torch.cuda.synchronize()
+        e0.record()
         for _ in range(reps):
-            e0.record()
             run(mode, shape, nbytes)
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return moved / (statistics.median(ts) * 1e-3) / 1e9
+        e1.record()
+        torch.cuda.synchronize()
+        return moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
     by_shape = {}
     best = {}
@@ -195,3 +197,10 @@ def same_mix_bound_us(read_bytes: float, write_bytes: float, ceil: dict) -> floa
     if write_bytes >= read_bytes:
         return fanout_bound_us(read_bytes, write_bytes, ceil)
     return fanin_bound_us(read_bytes, write_bytes, ceil)
+
+
+if __name__ == "__main__":
+    # python -m co_activation_amd.hbm_probe: this GPU's ceilings as one JSON line
+    import json
+
+    print(json.dumps(ceilings()))
