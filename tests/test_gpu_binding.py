@@ -67,3 +67,46 @@ def test_permute_scaled_out_and_scale_shapes():
                            out=torch.zeros(8 * 128, dtype=torch.bfloat16, device="cuda"))
     with pytest.raises(ValueError, match="out_rows"):
         ops.permute_scaled(x, dest, torch.ones(2, 4, dtype=torch.float32, device="cuda"), 8)
+
+
+def test_bound_calls_replay_on_the_buffers_given():
+    """A bound call replays the checked call on the same buffers: after the
+    input is overwritten in place, a replay gives what an unbound call on the
+    new input gives, bit for bit, on the current stream or a given one."""
+    g = torch.Generator().manual_seed(5)
+    T, H, G, k = 300, 256, 8, 2
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16).cuda()
+    dest = torch.stack([torch.arange(T), torch.arange(T) + T], 1).to(torch.int32).cuda()
+    send = torch.empty(2 * T, H, dtype=torch.bfloat16, device="cuda")
+    out, call = ops.permute(x, dest, 2 * T, out=send, bind=True)
+    assert out is send and isinstance(call, ops.Bound)
+    call()
+    assert torch.equal(send, ops.permute(x, dest, 2 * T))
+    x.copy_(torch.randn(T, H, generator=g).to(torch.bfloat16))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())  # the copy above runs on the current stream
+    call(s.cuda_stream)
+    s.synchronize()
+    assert torch.equal(send, ops.permute(x, dest, 2 * T))
+    rows = dest
+    w = torch.rand(2 * T, generator=g).cuda()
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    _, comb = ops.combine(send, rows, w, out=y, bind=True)
+    comb()
+    assert torch.equal(y, ops.combine(send, rows, w))
+
+
+def test_bound_call_reports_data_errors():
+    """A replay with a row id past the buffer sets the error word it was
+    bound with, as the unbound call does."""
+    x = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")
+    dest = torch.tensor([[0], [1], [2], [3]], dtype=torch.int32, device="cuda")
+    err = ops.new_error_word()
+    _, call = ops.permute(x, dest, 4, d_err=err, bind=True)
+    call()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    dest[2, 0] = 9  # past the 4 output rows
+    call()
+    torch.cuda.synchronize()
+    assert "ROW_RANGE" in ops.decode_errors(int(err.item()))
